@@ -1,0 +1,172 @@
+/*
+ * kda_ref.c - fp64 CPU oracle for Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE ONLY (see kda_ref.h).  A plain, slow, obviously correct
+ * token-by-token recurrence; no chunking, blocking or reordering.
+ *
+ * Source of each step (page "[Paper Review] Kimi K3: Open Frontier
+ * Intelligence", section "Method / Architecture" -> "Kimi Delta Attention
+ * (KDA)"):
+ *   - the per-head recurrence: Diag(alpha_t) decays the prior state per key
+ *     channel, (I - beta_t k_t k_t^T) erases the key direction, then k_t v_t^T
+ *     is written with strength beta_t (the update paragraph; its displayed
+ *     equation was lost in extraction, so the form used is the pinned one:
+ *     S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T, o_t = S_t^T q_t);
+ *   - q and k are L2-normalised (the projections paragraph);
+ *   - the log-decay is a scaled sigmoid bounded below by g_min = -5 (the
+ *     "Lower-bounded decay" paragraph), read as g = -5 * sigmoid(a) with the
+ *     per-head log-scale A_h at its initial value 0;
+ *   - the output passes a full-rank sigmoid gate (the "Full-rank gate"
+ *     paragraph), channel-wise over dv.
+ */
+#include "kda_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Logistic function; sigmoid(-inf) = 0 and sigmoid(+inf) = 1 exactly. */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+typedef struct {
+  int32_t num_seqs, H, dk, dv;
+  const int64_t* cu;
+  const double *q, *k, *v, *a, *b, *gate, *s0;
+  double *o, *s_final;
+  atomic_long next;
+} fwd_job;
+
+/* One token of the recurrence for one head.  S is dk x dv (row = key channel),
+ * updated in place; y receives the gated output row.  Work buffers:
+ * qh, kh, alpha (dk), u (dv). */
+static void kda_ref_token(int32_t dk, int32_t dv, double* S, const double* q, const double* k,
+                          const double* v, const double* a, double b, const double* gate,
+                          double* y, double* qh, double* kh, double* alpha, double* u) {
+  /* L2 normalisation of q and k over the key channels. */
+  double sq = 0.0, sk = 0.0;
+  for (int32_t c = 0; c < dk; ++c) {
+    sq += q[c] * q[c];
+    sk += k[c] * k[c];
+  }
+  double rq = 1.0 / sqrt(sq + KDA_REF_EPS), rk = 1.0 / sqrt(sk + KDA_REF_EPS);
+  for (int32_t c = 0; c < dk; ++c) {
+    qh[c] = q[c] * rq;
+    kh[c] = k[c] * rk;
+  }
+  /* Retention per key channel and write strength per token. */
+  for (int32_t c = 0; c < dk; ++c) alpha[c] = exp(KDA_REF_GMIN * sigmoid(a[c]));
+  double beta = sigmoid(b);
+
+  /* S' = Diag(alpha) S. */
+  for (int32_t c = 0; c < dk; ++c)
+    for (int32_t j = 0; j < dv; ++j) S[(size_t)c * dv + j] *= alpha[c];
+  /* u = beta (v - S'^T kh): the delta-rule correction. */
+  for (int32_t j = 0; j < dv; ++j) {
+    double w = 0.0;
+    for (int32_t c = 0; c < dk; ++c) w += kh[c] * S[(size_t)c * dv + j];
+    u[j] = beta * (v[j] - w);
+  }
+  /* S = S' + kh u^T  (== (I - beta kh kh^T) S' + beta kh v^T). */
+  for (int32_t c = 0; c < dk; ++c)
+    for (int32_t j = 0; j < dv; ++j) S[(size_t)c * dv + j] += kh[c] * u[j];
+  /* o = S^T qh, then the output gate. */
+  for (int32_t j = 0; j < dv; ++j) {
+    double acc = 0.0;
+    for (int32_t c = 0; c < dk; ++c) acc += qh[c] * S[(size_t)c * dv + j];
+    y[j] = gate ? sigmoid(gate[j]) * acc : acc;
+  }
+}
+
+static void* fwd_worker(void* p) {
+  fwd_job* J = (fwd_job*)p;
+  const int32_t H = J->H, dk = J->dk, dv = J->dv;
+  double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+  double* wk = (double*)malloc(sizeof(double) * (size_t)(3 * dk + dv));
+  if (!S || !wk) abort();
+  double *qh = wk, *kh = wk + dk, *alpha = wk + 2 * dk, *u = wk + 3 * dk;
+  const long total = (long)J->num_seqs * H;
+  for (;;) {
+    long item = atomic_fetch_add(&J->next, 1);
+    if (item >= total) break;
+    int32_t n = (int32_t)(item / H), h = (int32_t)(item % H);
+    size_t soff = ((size_t)n * H + h) * (size_t)dk * dv;
+    if (J->s0)
+      memcpy(S, J->s0 + soff, sizeof(double) * (size_t)dk * dv);
+    else
+      memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    for (int64_t t = J->cu[n]; t < J->cu[n + 1]; ++t) {
+      size_t th = (size_t)t * H + h;
+      kda_ref_token(dk, dv, S, J->q + th * dk, J->k + th * dk, J->v + th * dv, J->a + th * dk,
+                    J->b[th], J->gate ? J->gate + th * dv : NULL, J->o + th * dv, qh, kh, alpha,
+                    u);
+    }
+    if (J->s_final) memcpy(J->s_final + soff, S, sizeof(double) * (size_t)dk * dv);
+  }
+  free(S);
+  free(wk);
+  return NULL;
+}
+
+static int run_threads(void* (*fn)(void*), void* job, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 512) nthreads = 512;
+  pthread_t th[512];
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, fn, job) != 0) break;
+    ++started;
+  }
+  fn(job);
+  for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+  return 0;
+}
+
+int kda_ref_fwd(int32_t num_seqs, const int64_t* cu_seqlens, int32_t H, int32_t dk, int32_t dv,
+                const double* q, const double* k, const double* v, const double* a,
+                const double* b, const double* gate, const double* s0, double* o,
+                double* s_final, int nthreads) {
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return -1;
+  if (cu_seqlens[0] != 0) return -1;
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !a || !b || !o)) return -1;
+  fwd_job J = {num_seqs, H, dk, dv, cu_seqlens, q, k, v, a, b, gate, s0, o, s_final, 0};
+  return run_threads(fwd_worker, &J, nthreads);
+}
+
+typedef struct {
+  int32_t num_seqs, H, dk, dv;
+  const double *q, *k, *v, *a, *b, *gate;
+  double *state, *o;
+  atomic_long next;
+} dec_job;
+
+static void* dec_worker(void* p) {
+  dec_job* J = (dec_job*)p;
+  const int32_t H = J->H, dk = J->dk, dv = J->dv;
+  double* wk = (double*)malloc(sizeof(double) * (size_t)(3 * dk + dv));
+  if (!wk) abort();
+  double *qh = wk, *kh = wk + dk, *alpha = wk + 2 * dk, *u = wk + 3 * dk;
+  const long total = (long)J->num_seqs * H;
+  for (;;) {
+    long item = atomic_fetch_add(&J->next, 1);
+    if (item >= total) break;
+    size_t th = (size_t)item;
+    kda_ref_token(dk, dv, J->state + th * (size_t)dk * dv, J->q + th * dk, J->k + th * dk,
+                  J->v + th * dv, J->a + th * dk, J->b[th], J->gate ? J->gate + th * dv : NULL,
+                  J->o + th * dv, qh, kh, alpha, u);
+  }
+  free(wk);
+  return NULL;
+}
+
+int kda_ref_decode_step(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, const double* q,
+                        const double* k, const double* v, const double* a, const double* b,
+                        const double* gate, double* state, double* o, int nthreads) {
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (num_seqs > 0 && (!q || !k || !v || !a || !b || !state || !o)) return -1;
+  dec_job J = {num_seqs, H, dk, dv, q, k, v, a, b, gate, state, o, 0};
+  return run_threads(dec_worker, &J, nthreads);
+}

@@ -1,0 +1,330 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form the recurrence reduces to, brute-force dense matrix products, an
+independent chunked (UT/WY) formulation, linearity/contraction properties, or
+the constants the pages print.  A plausible slip in the oracle (a dropped
+term, a wrong sign, decay applied after instead of before the erase, a
+transposed state, the output read before the update, a wrong g_min) fails at
+least one of them; ``test_planted_mistakes_are_caught`` demonstrates that on
+mutated copies of the recurrence.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import chunk_model
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sig(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def l2n(x):
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + oracle.EPS)
+
+
+def rand_inputs(T, H, dk, dv, seed=0, a_std=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    a = rng.standard_normal((T, H, dk)) * a_std
+    b = rng.standard_normal((T, H))
+    gate = rng.standard_normal((T, H, dv))
+    return q, k, v, a, b, gate
+
+
+# --- P1: zero values and zero state give zero --------------------------------
+def test_zero_v_zero_state():
+    q, k, v, a, b, gate = rand_inputs(40, 2, 8, 6, seed=1)
+    o, s = oracle.fwd(q, k, np.zeros_like(v), a, b, gate, [0, 17, 40])
+    assert np.all(o == 0.0) and np.all(s == 0.0)
+
+
+# --- P2: beta = 0 leaves only the decayed initial state -----------------------
+def test_beta_zero_is_decayed_readout():
+    T, H, dk, dv = 24, 2, 8, 5
+    q, k, v, a, _, gate = rand_inputs(T, H, dk, dv, seed=2)
+    b = np.full((T, H), -np.inf)                       # sigmoid(-inf) = 0
+    s0 = np.random.default_rng(3).standard_normal((1, H, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, None, [0, T], s0)
+    g = -5.0 * sig(a)
+    Gam = np.exp(np.cumsum(g, axis=0))                 # [T, H, dk]
+    qh = l2n(q)
+    for h in range(H):
+        exp_o = np.einsum("tc,cj->tj", Gam[:, h] * qh[:, h], s0[0, h])
+        np.testing.assert_allclose(o[:, h], exp_o, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(s[0, h], Gam[-1, h][:, None] * s0[0, h], rtol=1e-12)
+
+
+# --- P3: beta = 0 and g = 0 keep the state fixed ------------------------------
+def test_beta_zero_g_zero_is_static_readout():
+    T, H, dk, dv = 12, 1, 6, 4
+    q, k, v, _, _, gate = rand_inputs(T, H, dk, dv, seed=4)
+    a = np.full((T, H, dk), -np.inf)                   # g = -5 sigmoid(-inf) = 0
+    b = np.full((T, H), -np.inf)
+    s0 = np.random.default_rng(5).standard_normal((1, H, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, T], s0)
+    exp_o = sig(gate[:, 0]) * (l2n(q)[:, 0] @ s0[0, 0])
+    np.testing.assert_allclose(o[:, 0], exp_o, rtol=1e-13)
+    np.testing.assert_array_equal(s, s0)
+
+
+# --- g_min: a = +inf gives exactly alpha = e^-5 --------------------------------
+def test_decay_floor_is_e_minus_5():
+    T, dk, dv = 7, 4, 3
+    q, k, v, _, _, _ = rand_inputs(T, 1, dk, dv, seed=6)
+    a = np.full((T, 1, dk), np.inf)                    # sigmoid(+inf) = 1 -> g = g_min
+    b = np.full((T, 1), -np.inf)
+    s0 = np.random.default_rng(7).standard_normal((1, 1, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, None, [0, T], s0)
+    for t in range(T):
+        np.testing.assert_allclose(o[t, 0], np.exp(-5.0 * (t + 1)) * (l2n(q)[t, 0] @ s0[0, 0]),
+                                   rtol=1e-13)
+    np.testing.assert_allclose(s[0, 0], np.exp(-5.0 * T) * s0[0, 0], rtol=1e-13)
+
+
+# --- P4: distinct one-hot keys give the gated-linear-attention closed form -----
+def test_one_hot_keys_closed_form():
+    T, dk, dv = 10, 12, 5
+    rng = np.random.default_rng(8)
+    chans = rng.permutation(dk)[:T]
+    q, _, v, a, b, gate = rand_inputs(T, 1, dk, dv, seed=9)
+    k = np.zeros((T, 1, dk))
+    k[np.arange(T), 0, chans] = 3.7                    # any positive scale; normalised away
+    o, s = oracle.fwd(q, k, v, a, b, None, [0, T])
+    kn = 3.7 / np.sqrt(3.7 ** 2 + oracle.EPS)          # |k_hat| carries 1/sqrt(1+eps/|k|^2)
+    g = -5.0 * sig(a[:, 0])
+    bc = np.cumsum(g, axis=0)
+    beta = sig(b[:, 0])
+    qh = l2n(q)[:, 0]
+    for t in range(T):
+        ref = np.zeros(dv)
+        for s_ in range(t + 1):
+            c = chans[s_]
+            ref += beta[s_] * kn * qh[t, c] * np.exp(bc[t, c] - bc[s_, c]) * v[s_, 0]
+        np.testing.assert_allclose(o[t, 0], ref, rtol=1e-12, atol=1e-15)
+
+
+# --- P5: orthonormal keys, beta = 1, g = 0 give causal linear attention --------
+def test_orthonormal_keys_causal_linear_attention():
+    T, dk, dv = 9, 16, 6
+    rng = np.random.default_rng(10)
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T][:, None, :]                             # orthonormal rows
+    q, _, v, _, _, gate = rand_inputs(T, 1, dk, dv, seed=11)
+    a = np.full((T, 1, dk), -np.inf)
+    b = np.full((T, 1), np.inf)                        # beta = 1
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, T])
+    kh = l2n(k)[:, 0]
+    qh = l2n(q)[:, 0]
+    ref = np.tril(qh @ kh.T) @ v[:, 0]
+    np.testing.assert_allclose(o[:, 0], sig(gate[:, 0]) * ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s[0, 0], kh.T @ v[:, 0], rtol=1e-12, atol=1e-14)
+
+
+# --- P6: tiny cases against explicit dense transition products ----------------
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_dense_product_form(T):
+    dk, dv = 5, 3
+    q, k, v, a, b, gate = rand_inputs(T, 1, dk, dv, seed=20 + T)
+    s0 = np.random.default_rng(30 + T).standard_normal((1, 1, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, T], s0)
+    kh, qh = l2n(k)[:, 0], l2n(q)[:, 0]
+    alpha = np.exp(-5.0 * sig(a[:, 0]))
+    beta = sig(b[:, 0])
+    M = [(np.eye(dk) - beta[t] * np.outer(kh[t], kh[t])) @ np.diag(alpha[t]) for t in range(T)]
+
+    def prod(lo, hi):                                  # M_hi ... M_lo (inclusive), identity if empty
+        P = np.eye(dk)
+        for t in range(lo, hi + 1):
+            P = M[t] @ P
+        return P
+
+    for t in range(T):
+        St = prod(0, t) @ s0[0, 0]
+        for s_ in range(t + 1):
+            St = St + prod(s_ + 1, t) @ (beta[s_] * np.outer(kh[s_], v[s_, 0]))
+        np.testing.assert_allclose(o[t, 0], sig(gate[t, 0]) * (St.T @ qh[t]), rtol=1e-11,
+                                   atol=1e-14)
+        if t == T - 1:
+            np.testing.assert_allclose(s[0, 0], St, rtol=1e-11, atol=1e-14)
+
+
+# --- P11: independent chunked UT/WY formulation (with ragged chunks) ----------
+@pytest.mark.parametrize("lens,chunk", [([70], 64), ([16, 1, 33, 0, 100], 64), ([48], 16)])
+def test_chunked_model_matches(lens, chunk):
+    H, dk, dv = 2, 16, 8
+    T = sum(lens)
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=40, a_std=np.sqrt(3.0))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    s0 = 0.02 * np.random.default_rng(41).standard_normal((len(lens), H, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, gate, cu, s0)
+    oc, sc = chunk_model.chunk_fwd(q, k, v, a, b, gate, cu, s0, chunk=chunk)
+    np.testing.assert_allclose(o, oc, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(s, sc, rtol=1e-9, atol=1e-12)
+
+
+def test_chunked_model_saturated_decay():
+    """a = +inf everywhere: every channel at g_min, tile sums at -80 exactly;
+    the tiled factors stay finite and the chunk form still matches."""
+    T, H, dk, dv = 64, 1, 8, 4
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=42)
+    a[:] = np.inf
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, T])
+    oc, sc = chunk_model.chunk_fwd(q, k, v, a, b, gate, [0, T])
+    np.testing.assert_allclose(o, oc, rtol=1e-9, atol=1e-30)
+    np.testing.assert_allclose(s, sc, rtol=1e-9, atol=1e-30)
+
+
+# --- P7: splitting a sequence and carrying the state changes nothing ---------
+@pytest.mark.parametrize("tau", [1, 37, 64, 100])
+def test_split_invariance(tau):
+    T, H, dk, dv = 128, 2, 8, 4
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=50)
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, T])
+    o1, s1 = oracle.fwd(q[:tau], k[:tau], v[:tau], a[:tau], b[:tau], gate[:tau], [0, tau])
+    o2, s2 = oracle.fwd(q[tau:], k[tau:], v[tau:], a[tau:], b[tau:], gate[tau:], [0, T - tau], s1)
+    np.testing.assert_array_equal(np.concatenate([o1, o2]), o)
+    np.testing.assert_array_equal(s2, s)
+
+
+# --- P8: (o, S_T) is jointly linear in (v, S0) --------------------------------
+def test_linearity_in_v_and_state():
+    T, H, dk, dv = 30, 1, 6, 4
+    q, k, v1, a, b, gate = rand_inputs(T, H, dk, dv, seed=60)
+    v2 = np.random.default_rng(61).standard_normal(v1.shape)
+    s1 = np.random.default_rng(62).standard_normal((1, H, dk, dv))
+    s2 = np.random.default_rng(63).standard_normal((1, H, dk, dv))
+    oa, sa = oracle.fwd(q, k, v1, a, b, gate, [0, T], s1)
+    ob, sb = oracle.fwd(q, k, v2, a, b, gate, [0, T], s2)
+    oc, sc = oracle.fwd(q, k, 2.0 * v1 - 3.0 * v2, a, b, gate, [0, T], 2.0 * s1 - 3.0 * s2)
+    np.testing.assert_allclose(oc, 2.0 * oa - 3.0 * ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sc, 2.0 * sa - 3.0 * sb, rtol=1e-11, atol=1e-12)
+
+
+# --- P9: contraction: |S_t|_F <= |S_{t-1}|_F + beta_t |v_t| --------------------
+def test_contraction_bound():
+    T, H, dk, dv = 50, 1, 8, 8
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=70)
+    s_prev = np.random.default_rng(71).standard_normal((1, H, dk, dv))
+    for t in range(T):
+        _, s_next = oracle.fwd(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], None,
+                               [0, 1], s_prev)
+        bound = np.linalg.norm(s_prev) + sig(b[t, 0]) * np.linalg.norm(v[t, 0])
+        assert np.linalg.norm(s_next) <= bound * (1 + 1e-12)
+        s_prev = s_next
+
+
+# --- decode: fwd(T) then one decode step equals fwd(T+1) ----------------------
+def test_decode_step_continues_prefill():
+    T, H, dk, dv = 20, 3, 8, 5
+    q, k, v, a, b, gate = rand_inputs(T + 1, H, dk, dv, seed=80)
+    o_full, s_full = oracle.fwd(q, k, v, a, b, gate, [0, T + 1])
+    _, s_T = oracle.fwd(q[:T], k[:T], v[:T], a[:T], b[:T], gate[:T], [0, T])
+    state = s_T.copy()
+    o_dec = oracle.decode_step(q[T:], k[T:], v[T:], a[T:], b[T:], gate[T:], state)
+    np.testing.assert_array_equal(o_dec, o_full[T:])
+    np.testing.assert_array_equal(state, s_full)
+
+
+def test_empty_sequences_copy_state():
+    H, dk, dv = 2, 4, 3
+    q, k, v, a, b, gate = rand_inputs(5, H, dk, dv, seed=90)
+    s0 = np.random.default_rng(91).standard_normal((3, H, dk, dv))
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, 0, 5, 5], s0)
+    np.testing.assert_array_equal(s[0], s0[0])
+    np.testing.assert_array_equal(s[2], s0[2])
+
+
+# --- the pages' printed constants ---------------------------------------------
+def test_page_constants():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        pc = json.load(f)
+    assert oracle.G_MIN == pc["g_min"]["value"]
+    # alpha >= e^{g_min}, printed as 6.7e-3 to two significant digits
+    amin = np.exp(pc["g_min"]["value"])
+    assert float(f"{amin:.{pc['alpha_min_printed']['printed_digits']}g}") == \
+        pc["alpha_min_printed"]["value"]
+    # tile of 16 tokens at the floor: cumulative log-decay just above -80
+    lo, hi = pc["tile_logdecay_open_interval"]["value"]
+    assert pc["tile_tokens"]["value"] * pc["g_min"]["value"] == lo
+    # e^80 and e^-80 are finite, normal bf16 numbers (max ~3.39e38, min normal 2^-126)
+    bf16_max = (2 - 2 ** -7) * 2.0 ** 127
+    assert np.exp(pc["reciprocal_bound_log"]["value"]) < bf16_max
+    assert np.exp(-pc["reciprocal_bound_log"]["value"]) > 2.0 ** -126
+    # the same factor would overflow fp16 (max 65504): the range needs bf16
+    assert np.exp(pc["reciprocal_bound_log"]["value"]) > 65504.0
+    # with A_h = 0 the log-decay of one channel is g_min * sigmoid(a): a -> +inf reaches g_min
+    assert pc["A_h_init"]["value"] == 0.0
+
+
+def test_tile_bounds_on_generated_decay_logits():
+    """With the workload's decay logits (a ~ N(0, 3)), every 16-token tile sum
+    of g = -5 sigmoid(a) lies in (-80, 0) and every alpha >= e^-5."""
+    w = synth.WORKLOADS[1]
+    a = synth.to_f64(synth.host_normal(synth.key(0, "a"), 4096, 128, std=w.a_std))
+    g = -5.0 * sig(a)
+    assert np.all(np.exp(g) >= np.exp(-5.0))
+    tiles = g.reshape(-1, 16, 128).sum(axis=1)
+    assert np.all(tiles > -80.0) and np.all(tiles < 0.0)
+
+
+def test_sigmoid_limits_are_exact():
+    q, k, v, a, b, gate = rand_inputs(4, 1, 4, 4, seed=95)
+    b[:] = np.inf
+    a[:] = -np.inf
+    gate[:] = -np.inf
+    o, s = oracle.fwd(q, k, v, a, b, gate, [0, 4])
+    assert np.all(o == 0.0) and np.all(np.isfinite(s))
+
+
+# --- planted mistakes: mutated recurrences must fail the pins above ----------
+def _mutant_fwd(q, k, v, a, b, gate, cu, s0=None, *, mutation):
+    """Python copy of the recurrence with one deliberate mistake."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv))
+    sf = np.zeros((len(cu) - 1, H, dk, dv))
+    for n in range(len(cu) - 1):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if s0 is None else s0[n, h].copy()
+            for t in range(cu[n], cu[n + 1]):
+                qh, kh = l2n(q[t, h]), l2n(k[t, h])
+                gmin = -4.0 if mutation == "gmin" else -5.0
+                al = np.exp(gmin * sig(a[t, h]))
+                be = sig(b[t, h])
+                if mutation == "decay_after_erase":
+                    u = be * (v[t, h] - S.T @ kh)
+                    S = al[:, None] * (S + np.outer(kh, u))
+                else:
+                    Sp = al[:, None] * S
+                    u = be * (v[t, h] - Sp.T @ kh)
+                    if mutation == "no_erase":
+                        u = be * v[t, h]
+                    S = Sp + np.outer(kh, u)
+                y = (S.T @ qh) if mutation != "read_before" else (Sp.T @ qh)
+                o[t, h] = sig(gate[t, h]) * y if gate is not None else y
+            sf[n, h] = S
+    return o, sf
+
+
+@pytest.mark.parametrize("mutation", ["gmin", "decay_after_erase", "no_erase", "read_before"])
+def test_planted_mistakes_are_caught(mutation):
+    T, H, dk, dv = 8, 1, 5, 3
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=99)
+    s0 = np.random.default_rng(98).standard_normal((1, H, dk, dv))
+    om, sm = _mutant_fwd(q, k, v, a, b, gate, [0, T], s0, mutation=mutation)
+    oc, sc = chunk_model.chunk_fwd(q, k, v, a, b, gate, [0, T], s0, chunk=64)
+    assert not np.allclose(om, oc, rtol=1e-6, atol=1e-9)
+    # and the correct copy of the same code agrees with the chunk model
+    o0, s0_ = _mutant_fwd(q, k, v, a, b, gate, [0, T], s0, mutation="none")
+    np.testing.assert_allclose(o0, oc, rtol=1e-9, atol=1e-12)
