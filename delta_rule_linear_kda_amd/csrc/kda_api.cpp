@@ -1,0 +1,177 @@
+// kda_api.cpp - the libkda C ABI (include/libkda.h): argument validation and
+// dispatch.  Every host-checkable problem is rejected here before any HIP
+// call, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libkda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool valid_dim(int32_t d) { return d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// b is read one element at a time: natural alignment of its dtype suffices.
+bool aligned_elem(const void* p, kda_dtype dt) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) & (dt == KDA_BF16 ? 1u : 3u)) == 0;
+}
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  Span() = default;
+  Span(const void* p, uint64_t bytes)
+      : lo(reinterpret_cast<uintptr_t>(p)), hi(reinterpret_cast<uintptr_t>(p) + bytes) {
+    if (!p || bytes == 0) lo = hi = 0;
+  }
+  bool empty() const { return lo == hi; }
+};
+
+bool overlap(const Span& x, const Span& y) {
+  return !x.empty() && !y.empty() && x.lo < y.hi && y.lo < x.hi;
+}
+
+// Element counts must stay far from overflow of byte offsets.
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+
+kda_status check_shape(const kda_shape* s) {
+  if (!s) return KDA_ERR_NULL_POINTER;
+  if (s->in_dtype != KDA_F32 && s->in_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (s->out_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+  if (s->num_seqs < 0 || s->total_tokens < 0 || s->num_heads < 1) return KDA_ERR_BAD_SHAPE;
+  if (!valid_dim(s->dk) || !valid_dim(s->dv)) return KDA_ERR_BAD_SHAPE;
+  if (s->total_tokens > kMaxElems / (int64_t(s->num_heads) * 128)) return KDA_ERR_BAD_SHAPE;
+  if (int64_t(s->num_seqs) * s->num_heads > (int64_t(1) << 31) / 4) return KDA_ERR_BAD_SHAPE;
+  return KDA_OK;
+}
+
+struct Sizes {
+  uint64_t qk, v, b, o, st;
+};
+
+Sizes byte_sizes(const kda_shape* s, int64_t tokens) {
+  const uint64_t es = s->in_dtype == KDA_BF16 ? 2 : 4;
+  const uint64_t th = uint64_t(tokens) * uint64_t(s->num_heads);
+  Sizes z;
+  z.qk = th * uint64_t(s->dk) * es;
+  z.v = th * uint64_t(s->dv) * es;
+  z.b = th * es;
+  z.o = th * uint64_t(s->dv) * 4;
+  z.st = uint64_t(s->num_seqs) * uint64_t(s->num_heads) * uint64_t(s->dk) * uint64_t(s->dv) * 4;
+  return z;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(kda_status st) {
+  switch (st) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER: a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: sizes out of range or inconsistent";
+    case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: unsupported dtype";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a tensor pointer is not aligned as required";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown kda_status";
+}
+
+kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_POINTER;
+  const kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  *bytes = 0;
+  return KDA_OK;
+}
+
+kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate,
+                           const int32_t* cu_seqlens, const float* initial_state, void* o,
+                           float* final_state, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  size_t need = 0;
+  kda_fwd_workspace_bytes(shape, &need);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+  if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
+  if (s.total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return KDA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+  for (const void* p : {q, k, v, a, gate, (const void*)initial_state, (const void*)o,
+                        (const void*)final_state})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  if (!aligned_elem(b, s.in_dtype)) return KDA_ERR_MISALIGNED;
+
+  const Sizes z = byte_sizes(shape, s.total_tokens);
+  const Span in[] = {Span(q, z.qk), Span(k, z.qk), Span(v, z.v), Span(a, z.qk), Span(b, z.b),
+                     Span(gate, z.v), Span(cu_seqlens, uint64_t(s.num_seqs + 1) * 4),
+                     Span(initial_state, z.st)};
+  const Span so(o, z.o), sf(final_state, z.st);
+  for (const Span& x : in)
+    if (overlap(so, x)) return KDA_ERR_ALIAS;
+  if (overlap(so, sf)) return KDA_ERR_ALIAS;
+  for (int i = 0; i < 7; ++i)
+    if (overlap(sf, in[i])) return KDA_ERR_ALIAS;
+  // final_state may be exactly initial_state (in place), never a partial overlap.
+  if (overlap(sf, in[7]) && (const void*)final_state != (const void*)initial_state)
+    return KDA_ERR_ALIAS;
+
+  kda::FwdArgs p;
+  p.num_seqs = s.num_seqs;
+  p.num_heads = s.num_heads;
+  p.dk = s.dk;
+  p.dv = s.dv;
+  p.total_tokens = s.total_tokens;
+  p.in_bf16 = s.in_dtype == KDA_BF16;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.gate = gate;
+  p.cu_seqlens = cu_seqlens;
+  p.initial_state = initial_state;
+  p.o = o;
+  p.final_state = final_state;
+  if (kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate, float* state,
+                           void* o, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  if (s.total_tokens != s.num_seqs) return KDA_ERR_BAD_SHAPE;
+  if (s.num_seqs == 0) return KDA_OK;
+  if (!q || !k || !v || !a || !b || !state || !o) return KDA_ERR_NULL_POINTER;
+  for (const void* p : {q, k, v, a, gate, (const void*)state, (const void*)o})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  if (!aligned_elem(b, s.in_dtype)) return KDA_ERR_MISALIGNED;
+  const Sizes z = byte_sizes(shape, s.num_seqs);
+  const Span in[] = {Span(q, z.qk), Span(k, z.qk), Span(v, z.v), Span(a, z.qk), Span(b, z.b),
+                     Span(gate, z.v)};
+  const Span so(o, z.o), ss(state, z.st);
+  for (const Span& x : in)
+    if (overlap(so, x) || overlap(ss, x)) return KDA_ERR_ALIAS;
+  if (overlap(so, ss)) return KDA_ERR_ALIAS;
+
+  kda::DecodeArgs p;
+  p.num_seqs = s.num_seqs;
+  p.num_heads = s.num_heads;
+  p.dk = s.dk;
+  p.dv = s.dv;
+  p.in_bf16 = s.in_dtype == KDA_BF16;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.gate = gate;
+  p.state = state;
+  p.o = o;
+  if (kda::launch_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

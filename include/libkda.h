@@ -1,0 +1,148 @@
+/*
+ * libkda.h - C ABI of libkda, a gfx950 (MI355X) implementation of Kimi Delta
+ * Attention (KDA), the per-head delta-rule linear-attention token mixer with a
+ * channel-wise forget gate described on the page "[Paper Review] Kimi K3: Open
+ * Frontier Intelligence", section "Method / Architecture" -> "Kimi Delta
+ * Attention (KDA)", and on the page "atlas.lewiswon.me/arch/moonshot-kimi-k3"
+ * (overview paragraph).
+ *
+ * The operation, per sequence n and head h, with state S (dk x dv, row = key
+ * channel) carried token by token:
+ *     qh = q_t / sqrt(|q_t|^2 + 1e-6),  kh = k_t / sqrt(|k_t|^2 + 1e-6)
+ *     g  = -5 * sigmoid(a_t)     per key channel (the lower-bounded
+ *                                scaled-sigmoid log-decay, g_min = -5,
+ *                                per-head log-scale A_h at its initial 0;
+ *                                a caller with a trained A_h folds it into a)
+ *     alpha = exp(g),  beta = sigmoid(b_t)
+ *     S  = (I - beta kh kh^T) Diag(alpha) S + beta kh v_t^T
+ *     o_t = sigmoid(gate_t) * (S^T qh)        (full-rank output gate)
+ * The pages' displayed equations were lost in extraction; this is the form
+ * their prose describes (retention Diag(alpha) decays the prior state, the
+ * delta rule erases the key direction, then k v^T is written with strength
+ * beta; the output is read from the updated state).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, owned by the
+ *     caller, 16-byte aligned -- except b, which needs only the alignment of
+ *     its element type, and cu_seqlens (4 bytes).  The library never allocates, frees, retains a
+ *     pointer past the call, or synchronises; work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and ordered by it.
+ *   - Host-checkable problems are reported by the return code BEFORE anything
+ *     is enqueued.  Preconditions that live in device memory (cu_seqlens
+ *     starting at 0, nondecreasing, ending at total_tokens) are the caller's
+ *     responsibility; violating them is undefined behaviour.
+ *   - A launch failure is reported as KDA_ERR_HIP.  No C++ exception crosses
+ *     the ABI.  Functions are stateless and may be called from any thread.
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bitwise-identical outputs (no atomics in any reduction).
+ */
+#ifndef LIBKDA_H
+#define LIBKDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1u
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+typedef enum kda_dtype {
+  KDA_F32 = 0,  /* IEEE binary32 */
+  KDA_BF16 = 1  /* bfloat16 */
+} kda_dtype;
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL_POINTER = 1, /* a required pointer (or the shape) is NULL      */
+  KDA_ERR_BAD_SHAPE = 2,    /* sizes out of range or inconsistent            */
+  KDA_ERR_BAD_DTYPE = 3,    /* unsupported in_dtype / out_dtype              */
+  KDA_ERR_MISALIGNED = 4,   /* a tensor pointer is not aligned as required   */
+  KDA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required    */
+  KDA_ERR_ALIAS = 6,        /* an output overlaps an input it must not       */
+  KDA_ERR_HIP = 7           /* the HIP runtime rejected a launch             */
+} kda_status;
+
+/* Problem description shared by both operations. */
+typedef struct kda_shape {
+  int32_t num_seqs;     /* N >= 0 sequences                                     */
+  int64_t total_tokens; /* fwd: packed token count T = cu_seqlens[N];           */
+                        /* decode: must equal num_seqs (one token each)         */
+  int32_t num_heads;    /* H >= 1                                               */
+  int32_t dk;           /* key/query head dim: 64 or 128                        */
+  int32_t dv;           /* value head dim: 64 or 128                            */
+  kda_dtype in_dtype;   /* dtype of q, k, v, a, b, gate: KDA_F32 or KDA_BF16    */
+  kda_dtype out_dtype;  /* dtype of o: KDA_F32 (fp32 output only)               */
+} kda_shape;
+
+/* Bytes of device workspace kda_fwd_chunked needs for `shape` (currently 0:
+ * the chunked kernel keeps everything in registers and LDS).
+ * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_DTYPE. */
+KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes);
+
+/* Chunked forward over packed variable-length sequences.
+ *
+ * Computes the recurrence above for every (sequence, head) with the
+ * chunkwise-parallel form the pages name (page "[Paper Review] Kimi K3...",
+ * section "Kimi Delta Attention (KDA)": recurrent but parallelisable per
+ * chunk; 64-token chunks split into 16-token tiles whose pairwise decay
+ * factors stay inside the bf16 range because g >= -5, "Lower-bounded decay"
+ * paragraph).  The state is carried across chunks in fp32.
+ *
+ *   q, k, a      [T, H, dk]   in_dtype
+ *   v, gate      [T, H, dv]   in_dtype; gate may be NULL (no output gate)
+ *   b            [T, H]       in_dtype (write-strength logit)
+ *   cu_seqlens   [N + 1]      int32, device; cu[0] = 0, nondecreasing,
+ *                             cu[N] = T; sequence n is tokens [cu[n], cu[n+1])
+ *   initial_state [N, H, dk, dv] fp32, or NULL (= zero state)
+ *   o            [T, H, dv]   out_dtype (fp32)
+ *   final_state  [N, H, dk, dv] fp32, or NULL (= not written); it may be the
+ *                same pointer as initial_state (in-place update), but may not
+ *                overlap it partially.
+ *   workspace    workspace_bytes bytes (may be NULL when 0 are required)
+ * A zero-length sequence produces no rows and final_state = initial_state
+ * (or zeros).  o must not overlap any input.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, WORKSPACE, ALIAS, HIP. */
+KDA_API kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate,
+                           const int32_t* cu_seqlens, const float* initial_state, void* o,
+                           float* final_state, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One decode step: one new token for each of N independent sequences, the
+ * recurrent update the pages' serving section runs with dedicated decode
+ * kernels on the fixed-size d_k x d_v per-head state (page "[Paper Review]
+ * Kimi K3...", section "Infrastructure", "Inference serving"; page
+ * "atlas.lewiswon.me/...", hybrid-cache paragraph).
+ *
+ *   q, k, a  [N, H, dk]  in_dtype     v, gate [N, H, dv] in_dtype (gate may be NULL)
+ *   b        [N, H]      in_dtype
+ *   state    [N, H, dk, dv] fp32, read and updated IN PLACE
+ *   o        [N, H, dv]  out_dtype (fp32)
+ * shape->total_tokens must equal shape->num_seqs.  o must not overlap state
+ * or any input.  The same state layout is read and written by
+ * kda_fwd_chunked, so fwd over T tokens followed by one decode step equals fwd
+ * over T + 1 tokens (up to rounding).
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, HIP. */
+KDA_API kda_status kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate, float* state,
+                           void* o, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+KDA_API const char* kda_status_str(kda_status status);
+
+/* KDA_ABI_VERSION of the built library. */
+KDA_API uint32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_H */

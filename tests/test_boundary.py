@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects every host-checkable invalid call with its status code
+before touching the GPU.  No call here launches anything: every call is
+constructed to fail validation (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_linear_kda_amd as kda
+from delta_rule_linear_kda_amd import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULLP, SHAPE, DTYPE, MISAL, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+def header_symbols():
+    syms = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            syms |= set(re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", text))
+    return syms
+
+
+def test_exports_every_declared_symbol():
+    syms = header_symbols()
+    assert syms == set(kda.EXPORTS)
+    L = kda.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_version_and_status_strings():
+    assert kda.abi_version() == 1
+    for code in range(8):
+        assert kda.status_str(code).startswith(kda.STATUS[code])
+    assert kda.status_str(99) == "unknown kda_status"
+
+
+def test_workspace_query():
+    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == 0
+    L = kda.lib()
+    out = ctypes.c_size_t(0)
+    assert L.kda_fwd_workspace_bytes(None, ctypes.byref(out)) == NULLP
+    s = Shape(1, 10, 2, 96, 128, 1, 0)
+    assert L.kda_fwd_workspace_bytes(ctypes.byref(s), ctypes.byref(out)) == SHAPE
+    s = Shape(1, 10, 2, 128, 128, 1, 0)
+    assert L.kda_fwd_workspace_bytes(ctypes.byref(s), None) == NULLP
+
+
+# Fake, distinct, 16-byte aligned addresses, far apart (never dereferenced).
+BASE = 1 << 40
+P = {name: BASE + i * (1 << 36) for i, name in enumerate(
+    ["q", "k", "v", "a", "b", "gate", "cu", "s0", "o", "sf"])}
+
+
+def fwd(shape, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_fwd_chunked(
+        ctypes.byref(shape) if shape is not None else None, args["q"], args["k"], args["v"],
+        args["a"], args["b"], args["gate"], args["cu"], args["s0"], args["o"], args["sf"],
+        args.get("ws"), args.get("ws_bytes", 0), None)
+
+
+def dec(shape, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_decode_step(
+        ctypes.byref(shape) if shape is not None else None, args["q"], args["k"], args["v"],
+        args["a"], args["b"], args["gate"], args["s0"], args["o"], None)
+
+
+def good_shape(**kw):
+    d = dict(num_seqs=2, total_tokens=300, num_heads=4, dk=128, dv=128, in_dtype=1, out_dtype=0)
+    d.update(kw)
+    return Shape(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), SHAPE), (dict(dv=32), SHAPE), (dict(num_heads=0), SHAPE),
+    (dict(num_seqs=-1), SHAPE), (dict(total_tokens=-5), SHAPE),
+    (dict(in_dtype=7), DTYPE), (dict(out_dtype=1), DTYPE),
+    (dict(total_tokens=1 << 60), SHAPE),
+    (dict(num_seqs=0, total_tokens=10), SHAPE),
+])
+def test_fwd_rejects_bad_shape(kw, code):
+    assert fwd(good_shape(**kw)) == code
+
+
+def test_fwd_rejects_null_and_misaligned():
+    assert fwd(None) == NULLP
+    for name in ["q", "k", "v", "a", "b", "o", "cu"]:
+        assert fwd(good_shape(), **{name: None}) == NULLP, name
+    for name in ["q", "k", "v", "a", "gate", "s0", "o", "sf"]:
+        assert fwd(good_shape(), **{name: P[name] + 8}) == MISAL, name
+    assert fwd(good_shape(), cu=P["cu"] + 2) == MISAL
+    assert fwd(good_shape(), b=P["b"] + 1) == MISAL                # bf16 b: 2-byte alignment
+    assert fwd(good_shape(in_dtype=0), b=P["b"] + 2) == MISAL      # fp32 b: 4-byte alignment
+
+
+def test_fwd_rejects_aliasing():
+    assert fwd(good_shape(), o=P["q"]) == ALIAS
+    assert fwd(good_shape(), o=P["k"] + 64) == ALIAS
+    assert fwd(good_shape(), sf=P["v"]) == ALIAS
+    assert fwd(good_shape(), o=P["sf"]) == ALIAS
+    assert fwd(good_shape(), sf=P["s0"] + 16) == ALIAS          # partial overlap with the state
+    assert fwd(good_shape(), o=P["cu"] - 16) == ALIAS            # o runs into cu_seqlens
+
+
+def test_fwd_rejects_small_workspace_never():
+    # zero workspace is required; a NULL workspace is accepted by the check,
+    # so only verify the query path (a passing call would launch).
+    assert kda.fwd_workspace_bytes(2, 300, 4, 128, 128) == 0
+
+
+def test_decode_rejects():
+    s = good_shape(num_seqs=8, total_tokens=8)
+    assert dec(None) == NULLP
+    assert dec(good_shape(num_seqs=8, total_tokens=9)) == SHAPE
+    assert dec(good_shape(num_seqs=8, total_tokens=8, dk=100)) == SHAPE
+    assert dec(good_shape(num_seqs=8, total_tokens=8, in_dtype=5)) == DTYPE
+    for name in ["q", "k", "v", "a", "b", "s0", "o"]:
+        assert dec(s, **{name: None}) == NULLP, name
+    for name in ["q", "gate", "s0", "o"]:
+        assert dec(s, **{name: P[name] + 4}) == MISAL, name
+    assert dec(s, o=P["s0"]) == ALIAS
+    assert dec(s, s0=P["q"]) == ALIAS
+    assert dec(s, o=P["v"] + 32) == ALIAS
+
+
+def test_zero_sequences_is_a_no_op():
+    # N = 0, T = 0: nothing to do, nothing launched.
+    assert fwd(good_shape(num_seqs=0, total_tokens=0)) == OK
+    assert dec(good_shape(num_seqs=0, total_tokens=0)) == OK

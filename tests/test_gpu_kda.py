@@ -1,0 +1,275 @@
+"""GPU parity of libkda against the fp64 oracle, through the C ABI.
+
+Tolerances (max |gpu - ref| / RMS(ref) over the whole compared tensor):
+1e-4 for fp32 inputs, 2e-2 for bf16 inputs, for o and for the final state.
+Inputs are seeded synthetic tensors (synth/); the oracle receives host-
+generated copies of exactly the bits the GPU consumed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import kda_cases as kc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import delta_rule_linear_kda_amd as kda  # noqa: E402
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def tol(w):
+    return kc.TOL_F32 if w.dtype == synth.F32 else kc.TOL_BF16
+
+
+def run_case(w, lens, with_s0=True, gate=True, check=True, label=""):
+    """Host-generated inputs for the packed sequences `lens`; GPU vs oracle."""
+    _require_gpu()
+    print(f"[case] {label} {w.name} lens={lens[:8]}{'...' if len(lens) > 8 else ''} "
+          f"H={w.heads} dk={w.dk} dv={w.dv}", flush=True)
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    s0 = kc.host_state(w, len(lens)) if with_s0 else None
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0_d = torch.from_numpy(s0).cuda() if s0 is not None else None
+    o, sf = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"],
+                            dev["gate"] if gate else None, cu_d, s0_d)
+    torch.cuda.synchronize()
+    o, sf = o.cpu().numpy(), sf.cpu().numpy()
+    xr = {n: kc.f64(x[n]) for n in x}
+    o_ref, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"],
+                               xr["gate"] if gate else None, cu, s0)
+    eo, es = kc.rel_err(o, o_ref), kc.rel_err(sf, sf_ref)
+    print(f"    err o={eo:.3e} state={es:.3e} (tol {tol(w):.0e})", flush=True)
+    if check:
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(sf))
+        assert eo <= tol(w), eo
+        assert es <= tol(w), es
+    return o, sf, o_ref, sf_ref
+
+
+W0, W1, W2, W3, W4 = (synth.WORKLOADS[i] for i in range(5))
+
+
+# --- configuration 0: fp32 everywhere, T=256, H=2, d=64 -------------------
+def test_fwd_config0_fp32():
+    run_case(W0, [256], with_s0=False, label="cfg0")
+
+
+@pytest.mark.parametrize("lens", [[100, 1, 0, 77, 64], [200]])
+def test_fwd_fp32_d128_ragged(lens):
+    w = kc.custom_workload(W0, dk=128, dv=128, heads=3, s0_std=0.5)
+    run_case(w, lens, label="fp32 d128")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128), (128, 128)])
+def test_fwd_bf16_head_dims(dk, dv):
+    w = kc.custom_workload(W1, dk=dk, dv=dv, heads=3, s0_std=0.02)
+    run_case(w, [300, 17, 0, 129], label=f"bf16 {dk}x{dv}")
+
+
+def test_fwd_bf16_no_gate():
+    w = kc.custom_workload(W1, heads=2, s0_std=0.02)
+    run_case(w, [190, 64], gate=False, label="no gate")
+
+
+# --- configuration 1: 4 x 4096, H=32, d=128, bf16, full comparison ----------
+def test_fwd_config1_full():
+    run_case(W1, W1.seq_lens(), with_s0=False, label="cfg1")
+
+
+# --- configuration 2: 16 varlen sequences, H=96, at full size ---------------
+def test_fwd_config2_full_sampled():
+    """Device-generated full-size inputs; the oracle runs sampled (sequence,
+    head) pairs from host-generated copies, checked bitwise first."""
+    _require_gpu()
+    w = W2
+    lens = w.seq_lens()
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    print(f"[case] cfg2 full T={T} lens={lens}", flush=True)
+    dev = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    s0_d = kc.device_state(w, len(lens))
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    o, sf = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                            cu_d, s0_d)
+    torch.cuda.synchronize()
+    longest = int(np.argmax(lens))
+    pairs = [(longest, 0), (longest, 95), (int(np.argmin(lens)), 7), (3, 50), (9, 33), (15, 64)]
+    for n, h in pairs:
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        x = {nm: kc.host_head_slice(w, nm, t0, t1, h) for nm in synth.TOKEN_TENSORS}
+        for nm in synth.TOKEN_TENSORS:  # the device generator produced the same bits
+            d = dev[nm][t0:t1, h]
+            d = d.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if d.dtype == torch.bfloat16 \
+                else d.cpu().numpy()
+            np.testing.assert_array_equal(d.reshape(x[nm].shape), x[nm])
+        s0 = kc.host_state_item(w, n, h)
+        np.testing.assert_array_equal(s0_d[n, h].cpu().numpy(), s0)
+        xr = {nm: kc.f64(x[nm])[:, None] for nm in x}
+        xr["b"] = kc.f64(x["b"])[:, None]
+        o_ref, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], xr["gate"],
+                                   [0, t1 - t0], s0[None, None].astype(np.float64))
+        eo = kc.rel_err(o[t0:t1, h].cpu().numpy(), o_ref[:, 0])
+        es = kc.rel_err(sf[n, h].cpu().numpy(), sf_ref[0, 0])
+        print(f"    seq {n} (len {t1 - t0}) head {h}: err o={eo:.3e} state={es:.3e}", flush=True)
+        assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
+
+
+# --- decode: configuration 4 (256 x 96 heads, 64 steps) ---------------------
+def test_decode_config4_full_sampled():
+    _require_gpu()
+    w = W4
+    N, H, steps = w.num_seqs, w.heads, w.decode_steps
+    print(f"[case] cfg4 decode N={N} H={H} steps={steps}", flush=True)
+    state = kc.device_state(w, N)
+    sub = 8  # sequences re-run by the oracle (all heads)
+    s_ref = kc.host_state(w, N)[:sub].astype(np.float64).copy()
+    np.testing.assert_array_equal(state[:sub].cpu().numpy(), s_ref.astype(np.float32))
+    worst_o = 0.0
+    for s in range(steps):
+        x = {n: kc.host_tokens(w, n, N, step=s) for n in synth.TOKEN_TENSORS}
+        dev = {n: kc.to_torch(x[n]) for n in x}
+        o = kda.decode_step(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"], state)
+        o_ref = oracle.decode_step(*(kc.f64(x[n][:sub]) for n in synth.TOKEN_TENSORS), s_ref)
+        worst_o = max(worst_o, kc.rel_err(o[:sub].cpu().numpy(), o_ref))
+    es = kc.rel_err(state[:sub].cpu().numpy(), s_ref)
+    print(f"    err o(max over steps)={worst_o:.3e} state={es:.3e}", flush=True)
+    assert worst_o <= kc.TOL_BF16 and es <= kc.TOL_BF16
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(synth.F32, 128, 128), (synth.F32, 64, 64),
+                                         (synth.BF16, 64, 128), (synth.BF16, 128, 64)])
+def test_decode_small(dtype, dk, dv):
+    _require_gpu()
+    w = kc.custom_workload(W4, num_seqs=5, heads=3, dk=dk, dv=dv, dtype=dtype)
+    state = torch.from_numpy(kc.host_state(w, 5)).cuda()
+    s_ref = kc.host_state(w, 5).astype(np.float64)
+    for s in range(4):
+        x = {n: kc.host_tokens(w, n, 5, step=s) for n in synth.TOKEN_TENSORS}
+        dev = {n: kc.to_torch(x[n]) for n in x}
+        o = kda.decode_step(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"], state)
+        o_ref = oracle.decode_step(*(kc.f64(x[n]) for n in synth.TOKEN_TENSORS), s_ref)
+        assert kc.rel_err(o.cpu().numpy(), o_ref) <= tol(w)
+    assert kc.rel_err(state.cpu().numpy(), s_ref) <= tol(w)
+
+
+# --- invariants on the GPU --------------------------------------------------
+def _fwd_dev(dev, cu, s0=None, gate=True):
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    return kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"],
+                           dev["gate"] if gate else None, cu_d, s0)
+
+
+@pytest.mark.parametrize("tau", [64, 100, 512])
+def test_split_invariance_gpu(tau):
+    """Running [0, T) whole equals [0, tau) then [tau, T) from the carried state."""
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=2, s0_std=0.02)
+    T = 700
+    x = kc.host_inputs(w, T)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    s0 = torch.from_numpy(kc.host_state(w, 1)).cuda()
+    o, sf = _fwd_dev(dev, [0, T], s0)
+    o1, s1 = _fwd_dev({n: dev[n][:tau].contiguous() for n in dev}, [0, tau], s0)
+    o2, s2 = _fwd_dev({n: dev[n][tau:].contiguous() for n in dev}, [0, T - tau], s1)
+    ref = o.cpu().numpy()
+    assert kc.rel_err(torch.cat([o1, o2]).cpu().numpy(), ref) <= 5e-3
+    assert kc.rel_err(s2.cpu().numpy(), sf.cpu().numpy()) <= 5e-3
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=3, s0_std=0.02)
+    T = 130
+    x = kc.host_inputs(w, T + 1)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    o_full, s_full = _fwd_dev(dev, [0, T + 1])
+    _, s_T = _fwd_dev({n: dev[n][:T].contiguous() for n in dev}, [0, T])
+    # the last token as a view into the same buffers (b is only 2-byte aligned there)
+    o_dec = kda.decode_step(*(dev[n][T:] for n in synth.TOKEN_TENSORS), s_T)
+    assert kc.rel_err(o_dec.cpu().numpy(), o_full[T:].cpu().numpy()) <= 5e-3
+    assert kc.rel_err(s_T.cpu().numpy(), s_full.cpu().numpy()) <= 5e-3
+
+
+def test_in_place_state_and_empty_sequences():
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=2, s0_std=0.02)
+    lens = [0, 65, 0]
+    x = kc.host_inputs(w, 65)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    s0 = torch.from_numpy(kc.host_state(w, 3)).cuda()
+    o_ref, sf_ref = _fwd_dev(dev, [0, 0, 65, 65], s0.clone())
+    st = s0.clone()
+    cu_d = torch.tensor([0, 0, 65, 65], dtype=torch.int32, device="cuda")
+    o, sf = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"], cu_d,
+                            st, final_state=st)
+    assert sf.data_ptr() == st.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(st, sf_ref)
+    assert torch.equal(st[0], s0[0]) and torch.equal(st[2], s0[2])
+
+
+def test_closed_forms_via_infinite_logits():
+    """b = -inf (beta = 0): o_t = S0^T (Gamma_t * qh_t); additionally a = -inf
+    (g = 0): o_t = S0^T qh_t, state unchanged.  The decay logits are shifted
+    by -4 so that Gamma_T stays far above fp32's underflow over 150 tokens."""
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=2, s0_std=0.02)
+    T = 150
+    x = kc.host_inputs(w, T)
+    af = synth.bf16_bits_to_f32(x["a"]) - 4.0
+    x["a"] = (af.view(np.uint32) >> 16).astype(np.uint16)   # truncated to bf16; both sides read these bits
+    ninf = np.uint16(0xFF80)  # bf16 -inf
+    x["b"][:] = ninf
+    s0 = kc.host_state(w, 1)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    o, sf = _fwd_dev(dev, [0, T], torch.from_numpy(s0).cuda())
+    o_ref, sf_ref = oracle.fwd(*(kc.f64(x[n]) for n in synth.TOKEN_TENSORS), [0, T],
+                               s0.astype(np.float64))
+    assert kc.rel_err(o.cpu().numpy(), o_ref) <= kc.TOL_BF16
+    assert kc.rel_err(sf.cpu().numpy(), sf_ref) <= kc.TOL_BF16
+    x["a"][:] = ninf
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    o, sf = _fwd_dev(dev, [0, T], torch.from_numpy(s0).cuda())
+    assert torch.equal(sf.cpu(), torch.from_numpy(s0))
+    o_ref, _ = oracle.fwd(*(kc.f64(x[n]) for n in synth.TOKEN_TENSORS), [0, T],
+                          s0.astype(np.float64))
+    assert kc.rel_err(o.cpu().numpy(), o_ref) <= kc.TOL_BF16
+
+
+def test_zero_values_zero_state_give_zero():
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=2)
+    x = kc.host_inputs(w, 200)
+    x["v"][:] = 0
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    o, sf = _fwd_dev(dev, [0, 120, 200])
+    assert torch.count_nonzero(o) == 0 and torch.count_nonzero(sf) == 0
+
+
+def test_bitwise_repeatable():
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=4, s0_std=0.02)
+    x = kc.host_inputs(w, 333)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    s0 = torch.from_numpy(kc.host_state(w, 2)).cuda()
+    o1, s1 = _fwd_dev(dev, [0, 200, 333], s0)
+    o2, s2 = _fwd_dev(dev, [0, 200, 333], s0)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_device_generator_matches_host():
+    _require_gpu()
+    w = W1
+    for name in ("q", "a", "b"):
+        d = kc.device_tokens(w, name, 64)
+        h = kc.host_tokens(w, name, 64)
+        dn = d.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(dn.reshape(h.shape), h)
