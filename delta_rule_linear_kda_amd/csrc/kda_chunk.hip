@@ -1,5 +1,6 @@
 // kda_chunk.hip - chunked KDA forward over packed variable-length sequences,
-// gfx950 (MI355X).
+// gfx950 (MI355X): the fp32-input kernel (fp32 matrix-core products, for the
+// 1e-4 accuracy of fp32 inputs).  bf16 inputs use kda_chunk_bf16.hip.
 //
 // Method: the KDA recurrence (page "[Paper Review] Kimi K3...", section "Kimi
 // Delta Attention (KDA)") evaluated in its chunkwise-parallel form (same
@@ -59,32 +60,6 @@ struct PolicyF32 {
                                              const float (&b)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
-  }
-};
-
-// bf16 inputs: each fp32 operand is split into hi = bf16(x) and
-// lo = bf16(x - hi) and the product is hi*hi + hi*lo + lo*hi with
-// v_mfma_f32_16x16x32_bf16 (three-term bf16 splitting, Henry, Tang &
-// Heinecke, "Leveraging the bfloat16 artificial intelligence datatype for
-// higher-precision computations", ARITH 2019).  bf16 keeps fp32's exponent
-// range, which the e^80 column factors need.
-struct PolicyBf16x3 {
-  static __device__ __forceinline__ void split(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 h = (__bf16)x[j];
-      hi[j] = h;
-      lo[j] = (__bf16)(x[j] - (float)h);
-    }
-  }
-  static __device__ __forceinline__ void mma(f32x4_t& acc, const float (&a)[8],
-                                             const float (&b)[8]) {
-    bf16x8_t ah, al, bh, bl;
-    split(a, ah, al);
-    split(b, bh, bl);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
   }
 };
 
@@ -233,7 +208,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int j = 0; j < 8; ++j) sV[row * LDV + seg * 8 + j] = vx[j];
     }
     if (t < kC) sBeta[t] = t < nrows ? sigmoidf(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 2: chunk-local inclusive cumsum of g per key channel --------
     {
@@ -244,7 +219,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll 8
       for (int r = part * RPT; r < (part + 1) * RPT; ++r) tot += sG[r * LDK + c];
       sE[part * DK + c] = tot;  // scratch, overwritten in stage 3
-      __syncthreads();
+      lds_barrier();
       float run = 0.f;
       for (int p = 0; p < part; ++p) run += sE[p * DK + c];
 #pragma unroll 8
@@ -253,7 +228,7 @@ __global__ void __launch_bounds__(kThreads)
         sG[r * LDK + c] = run;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 3: per-tile reference factors and scaled operands ----------
     if (t < DK) {
@@ -287,7 +262,7 @@ __global__ void __launch_bounds__(kThreads)
         sKh[row * LDK + c] = kh[it][j] * fast_exp(-x);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 4: A, P tiles (matrix cores) and O = Qbar S ---------------
     for (int idx = t; idx < 6 * 256; idx += kThreads) {  // zero the upper tiles of P
@@ -337,7 +312,7 @@ __global__ void __launch_bounds__(kThreads)
         Pol::mma(O[tt], av, bv);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 5: X = (I + A)^-1, unit lower triangular, into sX ----------
     // Diagonal 16x16 blocks: lane (block l/16, column l%16) runs the 16-step
@@ -360,7 +335,7 @@ __global__ void __launch_bounds__(kThreads)
         sX[(16 * kUpperPairs[pr][0] + e / 16) * L64 + 16 * kUpperPairs[pr][1] + e % 16] = 0.f;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // Off-diagonal blocks: X_st = -X_ss sum_{t<=u<s} A_su X_ut, by levels s - t = 1, 2, 3.
     // Scratch for the inner sums: the (dead) diagonal blocks of A.
 #pragma unroll 1
@@ -379,7 +354,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) tmp[(4 * g + jj) * L64 + li] = acc[jj];
       }
-      __syncthreads();
+      lds_barrier();
       if (wave < nb) {
         const int tb = wave, sb = wave + lev;
         blk_mm(y, sX + (16 * sb) * L64 + 16 * sb, L64, sA + (16 * wave) * L64 + 16 * wave, L64, g,
@@ -387,7 +362,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) sX[(16 * sb + 4 * g + jj) * L64 + 16 * tb + li] = -y[jj];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- stage 6: W = X diag(beta) Kbar (all dk columns), U0 = X diag(beta) V
@@ -423,7 +398,7 @@ __global__ void __launch_bounds__(kThreads)
         Pol::mma(U[tt], av, bv);
       }
     }
-    __syncthreads();  // every wave is done reading Kt
+    lds_barrier();  // every wave is done reading Kt
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -431,7 +406,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           sW[(16 * tt + 4 * g + jj) * LDK + 16 * (wave + 4 * cw) + li] = -Wt[tt][cw][jj];
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 7: the state chain (per wave, registers only) -------------
     // U = U0 - W S
@@ -497,7 +472,7 @@ __global__ void __launch_bounds__(kThreads)
         }
       }
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    lds_barrier();  // LDS is rewritten by the next chunk
   }
 
   if (s_final) {
@@ -532,9 +507,7 @@ hipError_t launch_t(const FwdArgs& p, hipStream_t stream) {
 
 hipError_t launch_fwd_chunked(const FwdArgs& p, hipStream_t stream) {
   if ((int64_t)p.num_seqs * p.num_heads == 0) return hipSuccess;
-  if (p.in_bf16)
-    return p.dk == 128 ? launch_t<uint16_t, 128, PolicyBf16x3>(p, stream)
-                       : launch_t<uint16_t, 64, PolicyBf16x3>(p, stream);
+  if (p.in_bf16) return launch_fwd_chunked_bf16(p, stream);
   return p.dk == 128 ? launch_t<float, 128, PolicyF32>(p, stream)
                      : launch_t<float, 64, PolicyF32>(p, stream);
 }

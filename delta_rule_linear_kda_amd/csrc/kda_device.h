@@ -78,6 +78,18 @@ __device__ __forceinline__ float sigmoidf(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then synchronises the workgroup.  Unlike __syncthreads() it does
+// not wait for outstanding global loads/stores, so register prefetches and
+// output stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Same ordering within one wavefront (LDS written by other lanes of this wave).
+__device__ __forceinline__ void lds_wave_fence() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Sum over the 64 lanes of a wavefront (every lane gets the total).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -28,5 +28,7 @@ struct FwdArgs {
 
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
 hipError_t launch_fwd_chunked(const FwdArgs& p, hipStream_t stream);
+// bf16-input kernel (kda_chunk_bf16.hip); launch_fwd_chunked dispatches to it.
+hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream);
 
 }  // namespace kda

@@ -180,9 +180,11 @@ def test_split_invariance_gpu(tau):
     o, sf = _fwd_dev(dev, [0, T], s0)
     o1, s1 = _fwd_dev({n: dev[n][:tau].contiguous() for n in dev}, [0, tau], s0)
     o2, s2 = _fwd_dev({n: dev[n][tau:].contiguous() for n in dev}, [0, T - tau], s1)
+    # both runs carry their own rounding (<= the bf16 bound each); a state-carry
+    # mistake shows up as an O(0.1-1) difference
     ref = o.cpu().numpy()
-    assert kc.rel_err(torch.cat([o1, o2]).cpu().numpy(), ref) <= 5e-3
-    assert kc.rel_err(s2.cpu().numpy(), sf.cpu().numpy()) <= 5e-3
+    assert kc.rel_err(torch.cat([o1, o2]).cpu().numpy(), ref) <= kc.TOL_BF16
+    assert kc.rel_err(s2.cpu().numpy(), sf.cpu().numpy()) <= kc.TOL_BF16
 
 
 def test_prefill_then_decode_equals_longer_prefill():
@@ -195,8 +197,8 @@ def test_prefill_then_decode_equals_longer_prefill():
     _, s_T = _fwd_dev({n: dev[n][:T].contiguous() for n in dev}, [0, T])
     # the last token as a view into the same buffers (b is only 2-byte aligned there)
     o_dec = kda.decode_step(*(dev[n][T:] for n in synth.TOKEN_TENSORS), s_T)
-    assert kc.rel_err(o_dec.cpu().numpy(), o_full[T:].cpu().numpy()) <= 5e-3
-    assert kc.rel_err(s_T.cpu().numpy(), s_full.cpu().numpy()) <= 5e-3
+    assert kc.rel_err(o_dec.cpu().numpy(), o_full[T:].cpu().numpy()) <= kc.TOL_BF16
+    assert kc.rel_err(s_T.cpu().numpy(), s_full.cpu().numpy()) <= kc.TOL_BF16
 
 
 def test_in_place_state_and_empty_sequences():
