@@ -14,6 +14,14 @@ events recorded on the stream the kernels are launched on.
 
 Prints ONE JSON line.  ``value`` is the forward throughput (tokens/s, a token
 being one position across all 96 heads).
+
+Profiling helpers (not part of a timed run):
+  --copy-probe          after the timed steps, run a plain 2 GiB device copy so
+                        that a hardware-counter run of this same command can
+                        scale FETCH_SIZE / WRITE_SIZE against known bytes;
+  --pmc-summary F W     turn two rocprofv3 --pmc CSV files (FETCH_SIZE run,
+                        WRITE_SIZE run) into the traffic summary text that the
+                        forward line's roofline.traffic is read from.
 """
 from __future__ import annotations
 
@@ -28,11 +36,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
-CHUNK = 64
+CHUNK = 32                   # chunk length of the bf16 forward kernel
+FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 8>"
+FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_chunk_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_T1048576_H96_d128.traffic.txt")
+COPY_PROBE_BYTES = 2 << 30
 
 
 def falg_per_token_head(dk: int, dv: int, C: int = CHUNK) -> float:
-    """Algorithmic flops per token-head of the chunked form (64-token chunks):
+    """Algorithmic flops per token-head of the chunked form with C-token chunks:
     6 dk dv (W S, Qbar S, Kend^T U) + (3C - 1) dk (A, P, W) + 2C dv (U0, P U)
     + C^2 / 3 (the triangular inverse)."""
     return 6 * dk * dv + (3 * C - 1) * dk + 2 * C * dv + C * C / 3.0
@@ -50,26 +62,117 @@ def decode_bytes_per_step(N: int, H: int, dk: int, dv: int, in_bytes: int = 2) -
     return N * H * (2 * 4 * dk * dv + in_bytes * (3 * dk + 2 * dv + 1) + 4 * dv)
 
 
-def cpu_baseline(seconds_hint: float = 20.0) -> dict:
+def cpu_baseline(T: int = 65536, slice_tokens: int = 8192) -> dict:
     """The fp64 oracle timed on this host's cores over a bounded sample of the
-    forward workload (its first 16384 tokens, all 96 heads)."""
+    forward workload: its first T tokens, all 96 heads, fed in slices of
+    ``slice_tokens`` with the state carried from slice to slice (the same
+    recurrence; bounded host memory).  Input generation is outside the timed
+    region."""
     import numpy as np
 
     import oracle
     import synth
-    from tests import kda_cases as kc
 
     w = synth.WORKLOADS[3]
-    T = 16384
-    x = {n: kc.f64(kc.host_tokens(w, n, T)) for n in synth.TOKEN_TENSORS}
+    H = w.heads
     threads = oracle.threads()
-    t0 = time.perf_counter()
-    oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"], np.array([0, T]),
-               nthreads=threads)
-    dt = time.perf_counter() - t0
+    state = None
+    dt = 0.0
+    for t0 in range(0, T, slice_tokens):
+        n = min(slice_tokens, T - t0)
+        x = {}
+        for name in synth.TOKEN_TENSORS:
+            L = synth.token_row_len(w, name)
+            arr = synth.host_normal(synth.key(w.seed, name), n * H, L, dtype=w.dtype,
+                                    std=w.std_of(name), base=t0 * H * L)
+            x[name] = synth.to_f64(arr).reshape((n, H) if name == "b" else (n, H, L))
+        t_start = time.perf_counter()
+        _, state = oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"],
+                              np.array([0, n]), state, nthreads=threads)
+        dt += time.perf_counter() - t_start
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 token recurrence over tokens [0, {T}) of the 1x1048576-token "
-                      f"workload, all 96 heads (d=128), {dt:.1f} s wall"}
+                      f"workload, all 96 heads (d=128), in {slice_tokens}-token slices with "
+                      f"the state carried, {threads} threads, {dt:.1f} s of oracle time"}
+
+
+def _sha256(path: str) -> str:
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic() -> dict | None:
+    """HBM bytes per forward launch from the committed counter summary, or
+    None when it is absent or was taken on a different kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != _sha256(FWD_SOURCE):
+            return None
+        return {"fetch": float(kv["fetch_bytes_per_launch"]),
+                "write": float(kv["write_bytes_per_launch"])}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str) -> str:
+    """Summarise a FETCH_SIZE run and a WRITE_SIZE run of
+    ``bench.py --copy-probe`` (rocprofv3 --pmc, csv output).  Each counter is
+    calibrated on the plain copy of COPY_PROBE_BYTES (it reads and writes
+    exactly that many bytes), then applied to the forward kernel's dispatches."""
+    import csv
+
+    def per_dispatch(path: str, counter: str) -> dict:
+        acc: dict = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                d = acc.setdefault(r["Kernel_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return {k: list(v.values()) for k, v in acc.items()}
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(d: dict, word: str) -> tuple:
+        hits = [(k, v) for k, v in d.items() if word in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {word!r}, got {[h[0] for h in hits]}")
+        return hits[0]
+
+    # The probe's device-to-device copy is the runtime's copy kernel; its
+    # largest dispatch is the probe (others are small staging copies).
+    _, cfl = pick(fetch, "copyBuffer")
+    _, cwl = pick(write, "copyBuffer")
+    cf, cw = max(cfl), max(cwl)
+    kname, kfl = pick(fetch, FWD_KERNEL)
+    _, kwl = pick(write, FWD_KERNEL)
+    kf, kw = sum(kfl) / len(kfl), sum(kwl) / len(kwl)
+    f_scale = COPY_PROBE_BYTES / (cf * 1024.0)
+    w_scale = COPY_PROBE_BYTES / (cw * 1024.0)
+    fb, wb = kf * 1024.0 * f_scale, kw * 1024.0 * w_scale
+    lines = [
+        f"# HBM traffic of {kname}",
+        "# workload: 1 x 1048576 tokens, H=96, dk=dv=128, bf16 inputs, fp32 o, final state",
+        f"copy_probe_bytes: {COPY_PROBE_BYTES}",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"kernel_fetch_kib: {kf:.1f}",
+        f"kernel_write_kib: {kw:.1f}",
+        f"fetch_bytes_per_launch: {fb:.0f}",
+        f"write_bytes_per_launch: {wb:.0f}",
+        f"kernel_source_sha256: {_sha256(FWD_SOURCE)}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def main() -> int:
@@ -80,7 +183,13 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=1 << 20, help="forward sequence length")
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(*args.pmc_summary))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the KDA hot path shards over heads and "
@@ -141,6 +250,13 @@ def main() -> int:
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    if args.copy_probe:
+        n = COPY_PROBE_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
@@ -148,8 +264,9 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
 
     th = T * H
-    flops = falg_per_token_head(dk, dv) * th
-    fbytes = fwd_bytes_per_token_head(dk, dv) * th + 2 * 4 * H * dk * dv * 0  # S0 = 0: no state read
+    falg = falg_per_token_head(dk, dv)
+    flops = falg * th
+    fbytes = fwd_bytes_per_token_head(dk, dv) * th + 4 * H * dk * dv  # + final state (S0 = 0: none read)
     fwd_tps = T / (fwd_avg * 1e-3)
     fwd_gbs = fbytes / (fwd_avg * 1e-3) / 1e9
     dbytes = decode_bytes_per_step(N, wd.heads, wd.dk, wd.dv)
@@ -175,14 +292,19 @@ def main() -> int:
         "fwd": {"ms": fwd_avg, "tokens_per_s": fwd_tps, "GB_per_s": fwd_gbs,
                 "frac_hbm": fwd_gbs / HBM_PEAK_GBS,
                 "TFLOP_per_s_alg": flops / (fwd_avg * 1e-3) / 1e12,
-                "frac_bf16_mfma_alg": flops / (fwd_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                "frac_bf16_mfma_alg": flops / (fwd_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                "falg_per_token_head": falg, "bytes_per_token_head": fwd_bytes_per_token_head(dk, dv)},
         "decode": {"ms_per_step": dec_step_ms, "GB_per_s": dec_gbs,
                    "frac_hbm": dec_gbs / HBM_PEAK_GBS,
                    "tokens_per_s": N / (dec_step_ms * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": fwd_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_kernel<bf16, dk=128>"},
+                     "frac": fwd_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": FWD_KERNEL},
     }
+    tr = read_traffic() if T == 1 << 20 else None
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
+        out["roofline"]["traffic_fetch"] = tr["fetch"]
+        out["roofline"]["traffic_write"] = tr["write"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

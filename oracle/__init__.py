@@ -76,7 +76,13 @@ def _p(x: Optional[np.ndarray]):
 
 
 def threads() -> int:
-    return max(1, os.cpu_count() or 1)
+    """Worker threads for the oracle: the cores this process may run on,
+    capped at 16 (the host share that goes with one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def fwd(q, k, v, a, b, gate, cu_seqlens, s0=None, *, nthreads: Optional[int] = None):
