@@ -84,13 +84,26 @@ __device__ __forceinline__ float dpp0(float x) {  // lanes whose source is outsi
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
-// Inclusive prefix sum over the 16 lanes of each row.
-__device__ __forceinline__ float row_scan16(float x) {
-  x += dpp0<0x111>(x);  // row_shr:1
-  x += dpp0<0x112>(x);  // row_shr:2
-  x += dpp0<0x114>(x);  // row_shr:4
-  x += dpp0<0x118>(x);  // row_shr:8
-  return x;
+template <int CTRL>
+__device__ __forceinline__ void scan_step_x8(float (&x)[2][4]) {
+  float y[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[t][j] = dpp0<CTRL>(x[t][j]);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[t][j] += y[t][j];
+}
+// Inclusive prefix sums over the 16 lanes of each row, for eight independent
+// values, step by step (row_shr 1, 2, 4, 8; lanes whose source is outside the
+// row add 0).
+__device__ __forceinline__ void scan16_x8(float (&x)[2][4]) {
+  scan_step_x8<0x111>(x);
+  scan_step_x8<0x112>(x);
+  scan_step_x8<0x114>(x);
+  scan_step_x8<0x118>(x);
 }
 // Sum over the 16 lanes of each row, in every lane of the row.
 __device__ __forceinline__ float row_sum16(float x) {
@@ -99,6 +112,17 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp0<0x122>(x);  // row_ror:2
   x += dpp0<0x121>(x);  // row_ror:1
   return x;
+}
+// Value held by lane S of each quad of lanes, in all four lanes of the quad.
+template <int S>
+__device__ __forceinline__ float quad_bcast_t(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            S | (S << 2) | (S << 4) | (S << 6), 0xf,
+                                                            0xf, false));
+}
+__device__ __forceinline__ float quad_bcast(float x, int s) {  // s: compile-time after unrolling
+  return s == 0 ? quad_bcast_t<0>(x) : s == 1 ? quad_bcast_t<1>(x) : s == 2 ? quad_bcast_t<2>(x)
+                                                                            : quad_bcast_t<3>(x);
 }
 // Value of lane 15 of each row of 16 lanes, in every lane of the row.
 __device__ __forceinline__ float row_last16(float x) {
@@ -217,7 +241,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
                           const uint16_t* __restrict__ v, const uint16_t* __restrict__ a,
                           const uint16_t* __restrict__ bl, const uint16_t* __restrict__ gate,
                           const int32_t* __restrict__ cu_seqlens, const float* __restrict__ s_init,
-                          float* __restrict__ o, float* __restrict__ s_final, int H) {
+                          float* __restrict__ o, float* __restrict__ s_final, int H,
+                          int num_items, int dvt, int nsl) {
   using L = Cfg<DK, DV>;
   constexpr int NP = L::NP, CPL = L::CPL, RPW = L::RPW;
   constexpr int LB = L::LB, LT = L::LT, LX = L::LX, LA = L::LA;
@@ -247,7 +272,13 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
   auto bW = [&](int p) { return reinterpret_cast<uint16_t*>(buf(p, L::dW)); };
   auto bKE = [&](int p) { return reinterpret_cast<uint16_t*>(buf(p, L::dKE)); };
 
-  const int item = blockIdx.x;  // sequence * H + head
+  // Block -> (item = sequence * H + head, d_v slice): the nsl slices of an item
+  // sit 8 blocks apart, on the same XCD (blocks go round-robin over the 8
+  // XCDs), so the second slice's q, k, a reads hit that XCD's L2.
+  const int blk = blockIdx.x;
+  const int item = (blk / (8 * nsl)) * 8 + blk % 8;
+  const int col0 = ((blk / 8) % nsl) * DV;  // first state / v column of this slice
+  if (item >= num_items) return;            // whole workgroup; before any barrier
   const int n = item / H, h = item % H;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
   const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
@@ -325,23 +356,22 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             beta[tau] = valid ? beta[tau] : 0.f;
           }
         }
-        // decay accumulated within each tile (inclusive), and the tile totals
+        // decay accumulated within each tile (inclusive; the eight scans are
+        // interleaved step by step), and the tile totals
+        scan16_x8(cum);
         float tot[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            cum[tau][j] = row_scan16(cum[tau][j]);
-            tot[tau][j] = row_last16(cum[tau][j]);
-          }
+          for (int j = 0; j < 4; ++j) tot[tau][j] = row_last16(cum[tau][j]);
         if (it + 1 < nch) load(c0 + kC, li, g);  // next chunk, consumed in its E stage
         const int cb = 16 * wave + 4 * g;
         float e0[4], fend[2][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          e0[j] = exp2f_fast(tot[0][j]);                   // exp(p_1): decay over tile 0
-          fend[0][j] = exp2f_fast(tot[0][j] + tot[1][j]);  // exp(b_end - p_0) = Gamma_end
-          fend[1][j] = exp2f_fast(tot[1][j]);              // exp(b_end - p_1)
+          e0[j] = exp2f_fast(tot[0][j]);    // exp(p_1): decay over tile 0
+          fend[1][j] = exp2f_fast(tot[1][j]);  // exp(b_end - p_1)
+          fend[0][j] = e0[j] * fend[1][j];     // exp(b_end - p_0) = Gamma_end
         }
         if (li == 0)
           *reinterpret_cast<float4*>(bGE(p) + cb) =
@@ -351,11 +381,12 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           bBeta(p)[16 + li] = beta[1];
         }
         uint16_t* qbp = bQB(p);
-        uint16_t* kep = bKE(p);
+        uint16_t* kbt = sKBT + cb * LT + li;  // [channel cb + j][token 16 tau + li]
+        uint16_t* ket = bKE(p) + cb * LT + li;
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
           const int r = 16 * tau + li;
-          bf16x4_t ktb, qhb, qlb, khh, khl;
+          bf16x4_t ktb, qhb, qlb, khh, khl, k1h, k1l;
           f16x4_t qbf;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -371,13 +402,12 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             khh[j] = (__bf16)kh;
             khl[j] = (__bf16)(kh - (float)khh[j]);
             qbf[j] = (_Float16)qbar;
-            sKBT[(cb + j) * LT + r] = f16_bits(kbar);
-            kep[(cb + j) * LT + r] = f16_bits(kend);
+            kbt[j * LT + 16 * tau] = f16_bits(kbar);
+            ket[j * LT + 16 * tau] = f16_bits(kend);
             if (tau == 0) {  // column operand of the off-diagonal tile: Kh exp(p_1) <= 1
               const float y = kh * e0[j];
-              const __bf16 yh = (__bf16)y;
-              sK1H[li * LB + cb + j] = __builtin_bit_cast(uint16_t, yh);
-              sK1L[li * LB + cb + j] = bf16_bits(y - (float)yh);
+              k1h[j] = (__bf16)y;
+              k1l[j] = (__bf16)(y - (float)k1h[j]);
             }
           }
           *reinterpret_cast<bf16x4_t*>(sKT + r * LB + cb) = ktb;
@@ -386,6 +416,10 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           *reinterpret_cast<bf16x4_t*>(sKHH + r * LB + cb) = khh;
           *reinterpret_cast<bf16x4_t*>(sKHL + r * LB + cb) = khl;
           *reinterpret_cast<f16x4_t*>(qbp + r * LB + cb) = qbf;
+          if (tau == 0) {
+            *reinterpret_cast<bf16x4_t*>(sK1H + li * LB + cb) = k1h;
+            *reinterpret_cast<bf16x4_t*>(sK1L + li * LB + cb) = k1l;
+          }
         }
       }
       lds_barrier();  // B1: operands, beta (prep) and norms (state) in LDS
@@ -395,83 +429,23 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         const float* nk = bNK(p);
         const float* nq = bNQ(p);
         const float* be = bBeta(p);
-        if (wave == 0) {
-          // A tiles (0,0), (1,0), (1,1); scaled and masked in registers.
-          f32x4_t acc[3];
+        // Row scale beta_r nk_r and column scale nk_i of the A tiles.
+        auto a_tile = [&](int tr, int ti, const uint16_t* col) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int job = 0; job < 3; ++job) {
-            const int tr = job == 0 ? 0 : 1, ti = job == 2 ? 1 : 0;
-            const uint16_t* col = job == 1 ? sK1H + li * LB : sKHH + (16 * ti + li) * LB;
-            acc[job] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-              const int c = 32 * kb + 8 * g;
-              acc[job] = mma_bf16(lds8<bf16x8_t>(sKT + (16 * tr + li) * LB + c),
-                                  lds8<bf16x8_t>(col + c), acc[job]);
-            }
+          for (int kb = 0; kb < NKB; ++kb) {
+            const int c = 32 * kb + 8 * g;
+            acc = mma_bf16(lds8<bf16x8_t>(sKT + (16 * tr + li) * LB + c), lds8<bf16x8_t>(col + c),
+                           acc);
           }
-          const float nkc0 = nk[li], nkc1 = nk[16 + li];
-          const float4 nk0 = *reinterpret_cast<const float4*>(nk + 4 * g);
-          const float4 nk1 = *reinterpret_cast<const float4*>(nk + 16 + 4 * g);
-          const float4 be0 = *reinterpret_cast<const float4*>(be + 4 * g);
-          const float4 be1 = *reinterpret_cast<const float4*>(be + 16 + 4 * g);
-          const float rs0[4] = {be0.x * nk0.x, be0.y * nk0.y, be0.z * nk0.z, be0.w * nk0.w};
-          const float rs1[4] = {be1.x * nk1.x, be1.y * nk1.y, be1.z * nk1.z, be1.w * nk1.w};
-          float a00[4], a11[4], a10[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r = 4 * g + jj;  // row within its tile
-            a00[jj] = li < r ? acc[0][jj] * rs0[jj] * nkc0 : 0.f;
-            a11[jj] = li < r ? acc[2][jj] * rs1[jj] * nkc1 : 0.f;
-            a10[jj] = acc[1][jj] * rs1[jj] * nkc0;
-          }
-          // diagonal blocks transposed (row m of sAT = column m of the block)
-          *reinterpret_cast<float4*>(sAT + li * LA + 4 * g) = make_float4(a00[0], a00[1], a00[2], a00[3]);
-          *reinterpret_cast<float4*>(sAT + (16 + li) * LA + 4 * g) =
-              make_float4(a11[0], a11[1], a11[2], a11[3]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) sA10[(4 * g + jj) * LA + li] = a10[jj];
-          lds_wave_fence();
-          float* xb = bX(p);
-          // Diagonal blocks by forward substitution: lane group g < 2 solves
-          // block g, lane li holding column li of its inverse.
-          if (g < 2) {
-            const float* at = sAT + 16 * g * LA;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = i == li ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < 15; ++m) {
-              float col[16];
-#pragma unroll
-              for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
-                const float4 cv = *reinterpret_cast<const float4*>(at + m * LA + 4 * q4);
-                col[4 * q4] = cv.x; col[4 * q4 + 1] = cv.y; col[4 * q4 + 2] = cv.z; col[4 * q4 + 3] = cv.w;
-              }
-#pragma unroll
-              for (int i = m + 1; i < 16; ++i) x[i] -= col[i] * x[m];
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xb[(16 * g + i) * LX + 16 * g + li] = x[i];
-          }
-          lds_wave_fence();
-          // X10 = -X11 (A10 X00) on the fp32 matrix cores; Y chained from the
-          // accumulator into the B operand with k = 4g + s in step s.
-          f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            y = mma_f32(sA10[li * LA + 4 * s + g], xb[(4 * s + g) * LX + li], y);
-          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) z = mma_f32(xb[(16 + li) * LX + 16 + 4 * g + s], y[s], z);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            xb[(16 + 4 * g + jj) * LX + li] = -z[jj];
-            xb[(4 * g + jj) * LX + 16 + li] = 0.f;
-          }
-        } else if (wave <= 3) {
-          // P tile job: 0 = (0,0), 1 = (1,0), 2 = (1,1)
-          const int job = wave - 1;
+          const float nkc = nk[16 * ti + li];
+          const float4 nkr = *reinterpret_cast<const float4*>(nk + 16 * tr + 4 * g);
+          const float4 ber = *reinterpret_cast<const float4*>(be + 16 * tr + 4 * g);
+          acc[0] *= ber.x * nkr.x * nkc; acc[1] *= ber.y * nkr.y * nkc;
+          acc[2] *= ber.z * nkr.z * nkc; acc[3] *= ber.w * nkr.w * nkc;
+          return acc;
+        };
+        auto p_job = [&](int job) {  // 0 = (0,0), 1 = (1,0), 2 = (1,1)
           const int tr = job == 0 ? 0 : 1, ti = job == 2 ? 1 : 0;
           const uint16_t* colh = job == 1 ? sK1H + li * LB : sKHH + (16 * ti + li) * LB;
           const uint16_t* coll = job == 1 ? sK1L + li * LB : sKHL + (16 * ti + li) * LB;
@@ -503,33 +477,106 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
               pl[(4 * g + jj) * LT + 16 + li] = 0;
             }
           }
+        };
+        if (wave < 2) {
+          // Diagonal block tau = wave: A_tt, then X_tt = (I + A_tt)^-1.
+          const int tau = wave;
+          const f32x4_t acc = a_tile(tau, tau, sKHH + (16 * tau + li) * LB);
+          float4 at;
+          at.x = li < 4 * g + 0 ? acc[0] : 0.f;  // strictly lower: A[4g + jj][li], li < 4g + jj
+          at.y = li < 4 * g + 1 ? acc[1] : 0.f;
+          at.z = li < 4 * g + 2 ? acc[2] : 0.f;
+          at.w = li < 4 * g + 3 ? acc[3] : 0.f;
+          float* atb = sAT + 16 * tau * LA;
+          *reinterpret_cast<float4*>(atb + li * LA + 4 * g) = at;  // row m of sAT = column m of A
+          lds_wave_fence();
+          // Forward substitution, four lanes per column: lane (j = lane/4,
+          // qd = lane%4) holds rows 4qd..4qd+3 of column j; the pivot x[m] is
+          // broadcast within each quad of lanes.  A[r][m] = 0 for r <= m, so
+          // no row needs masking.
+          const int jc = lane >> 2, qd = lane & 3;
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = 4 * qd + i == jc ? 1.f : 0.f;
+#pragma unroll
+          for (int m = 0; m < 15; ++m) {
+            const float4 am = *reinterpret_cast<const float4*>(atb + m * LA + 4 * qd);
+            const float xm = quad_bcast(x[m & 3], m >> 2);
+            x[0] -= am.x * xm;
+            x[1] -= am.y * xm;
+            x[2] -= am.z * xm;
+            x[3] -= am.w * xm;
+          }
+          float* xb = bX(p);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xb[(16 * tau + 4 * qd + i) * LX + 16 * tau + jc] = x[i];
+        } else {
+          if (wave == 2) {  // A10, kept row-major for the W stage
+            const f32x4_t acc = a_tile(1, 0, sK1H + li * LB);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sA10[(4 * g + jj) * LA + li] = acc[jj];
+          }
+          if constexpr (NP >= 6) {
+            if (wave >= 3 && wave < 6) p_job(wave - 3);
+          } else {
+            if (wave == 2) {
+              p_job(0);
+            } else {
+              p_job(1);
+              p_job(2);
+            }
+          }
         }
       }
       lds_barrier();  // B2: X and P in LDS
 
-      // ---- W: W^T = Kbar^T diag(beta nk) X^T (fp16); store -W ----------------
+      // ---- W: X10 = -X11 A10 X00; W^T = Kbar^T diag(beta nk) X^T; store -W ----
       if (act) {
-        const float* xb = bX(p);
+        float* xb = bX(p);
         const float* be = bBeta(p);
         const float* nk = bNK(p);
+        // X10^T = -X00^T (A10^T X11^T) on the fp32 matrix cores (every prep
+        // wave forms it for its own W tiles); lane (li, g) ends with
+        // X10[li][4g + jj] in x10[jj].
+        f32x4_t p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          p1 = mma_f32(sA10[(4 * s + g) * LA + li], xb[(16 + li) * LX + 16 + 4 * s + g], p1);
+        f32x4_t x10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x10 = mma_f32(xb[(4 * g + s) * LX + li], p1[s], x10);
+        x10 = -x10;
+        if (wave == 0) {  // complete X for the state waves: X10, and X01 = 0
+          *reinterpret_cast<float4*>(xb + (16 + li) * LX + 4 * g) =
+              make_float4(x10[0], x10[1], x10[2], x10[3]);
+          *reinterpret_cast<float4*>(xb + li * LX + 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        // beta nk at the tokens of slots j (k order 4g..4g+3, 16+4g..16+4g+3)
         float bs[8];
         {
-          const float4 b0 = *reinterpret_cast<const float4*>(be + 8 * g);
-          const float4 b1 = *reinterpret_cast<const float4*>(be + 8 * g + 4);
-          const float4 n0 = *reinterpret_cast<const float4*>(nk + 8 * g);
-          const float4 n1 = *reinterpret_cast<const float4*>(nk + 8 * g + 4);
+          const float4 b0 = *reinterpret_cast<const float4*>(be + 4 * g);
+          const float4 b1 = *reinterpret_cast<const float4*>(be + 16 + 4 * g);
+          const float4 n0 = *reinterpret_cast<const float4*>(nk + 4 * g);
+          const float4 n1 = *reinterpret_cast<const float4*>(nk + 16 + 4 * g);
           bs[0] = b0.x * n0.x; bs[1] = b0.y * n0.y; bs[2] = b0.z * n0.z; bs[3] = b0.w * n0.w;
           bs[4] = b1.x * n1.x; bs[5] = b1.y * n1.y; bs[6] = b1.z * n1.z; bs[7] = b1.w * n1.w;
         }
-        const f16x8_t kbt = lds8<f16x8_t>(sKBT + (16 * wave + li) * LT + 8 * g);
+        const f16x8_t kbt = lds4x2<f16x8_t>(sKBT + (16 * wave + li) * LT + 4 * g);
         uint16_t* wp = bW(p);
+        float xx[2][8];
+        {
+          const float4 x00 = *reinterpret_cast<const float4*>(xb + li * LX + 4 * g);
+          const float4 x11 = *reinterpret_cast<const float4*>(xb + (16 + li) * LX + 16 + 4 * g);
+          xx[0][0] = x00.x; xx[0][1] = x00.y; xx[0][2] = x00.z; xx[0][3] = x00.w;
+          xx[0][4] = xx[0][5] = xx[0][6] = xx[0][7] = 0.f;
+          xx[1][0] = x10[0]; xx[1][1] = x10[1]; xx[1][2] = x10[2]; xx[1][3] = x10[3];
+          xx[1][4] = x11.x; xx[1][5] = x11.y; xx[1][6] = x11.z; xx[1][7] = x11.w;
+        }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          float xx[8];
-          lds_f32x8(xb + (16 * rt + li) * LX + 8 * g, xx);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xx[j] *= bs[j];
-          const f32x4_t acc = mma_f16(kbt, pack_f16x8(xx), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          for (int j = 0; j < 8; ++j) xx[rt][j] *= bs[j];
+          const f32x4_t acc = mma_f16(kbt, pack_f16x8(xx[rt]), f32x4_t{0.f, 0.f, 0.f, 0.f});
           // acc[jj] = W[16 rt + li][16 wave + 4 g + jj]
           const f16x4_t wv = {(_Float16)(-acc[0]), (_Float16)(-acc[1]), (_Float16)(-acc[2]),
                               (_Float16)(-acc[3])};
@@ -541,17 +588,17 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
   } else {
     // ======================= state waves ======================================
     const int sw = wave - NP;  // owns state columns [16 sw, 16 sw + 16)
-    const int64_t st_off = (int64_t)item * DK * DV;
+    const int64_t st_off = (int64_t)item * DK * dvt + col0;
     f32x4_t S[NCT];
     {
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-      const uint32_t st_lane = 4 * g * DV + 16 * sw + li;  // state element (row 4g, column)
+      const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;  // state element (row 4g, column)
       if (s_init) {
         const auto sp = sbase(s_init + st_off);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * DV];
+          for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * dvt];
       } else {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -560,7 +607,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     typedef __attribute__((ext_vector_type(CPL / 2))) uint32_t uvec_t;
     constexpr int NPASS = RPW / 4;
     uvec_t nq_[NPASS], nk_[NPASS];  // q, k rows for the norms of the next chunk
-    uint32_t rv[8], rg[8];          // v, gate of the chunk the state chain works on
+    uint32_t rv[8], rg[8];          // v, gate (bits, then sigmoid) of the chunk the chain works on
+    f32x4_t O[2], U[2];
     auto load_qk = [&](int64_t c0, int g, int li) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
       const int64_t tb = c0 * H + h;
@@ -575,29 +623,49 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         nk_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(kb_ + off);
       }
     };
-    auto load_vg = [&](int64_t c0, int g, int jcol) {
+    auto load_v = [&](int64_t c0, int g, int jcol) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-      const int64_t tb = c0 * H + h;
-      const auto vb_ = sbase(v + tb * DV);
-      const auto gb_ = sbase(gate ? gate + tb * DV : v + tb * DV);
+      const auto vb_ = sbase(v + (c0 * H + h) * dvt + col0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 16 * (i / 4) + 4 * g + (i % 4);
         const int rr = r < nr ? r : nr - 1;
-        const uint32_t off = (uint32_t)(rr * H * DV) + jcol;
-        rv[i] = vb_[off];
-        rg[i] = gb_[off];
+        rv[i] = vb_[(uint32_t)(rr * H * dvt) + jcol];
+      }
+    };
+    auto load_g = [&](int64_t c0, int g, int jcol) {
+      const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+      const auto gb_ = sbase(gate + (c0 * H + h) * dvt + col0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 16 * (i / 4) + 4 * g + (i % 4);
+        const int rr = r < nr ? r : nr - 1;
+        rg[i] = gb_[(uint32_t)(rr * H * dvt) + jcol];
+      }
+    };
+    // Gated output of chunk c (its O accumulators), stored fp32.
+    auto epilogue = [&](int64_t c0, int g, int jcol) {
+      const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+      const auto ob_ = sbase(o + (c0 * H + h) * dvt + col0);
+      const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 16 * (j >> 2) + 4 * g + (j & 3);
+        if (r < nrows) {
+          float y = O[j >> 2][j & 3];
+          if (gate) y *= __uint_as_float(rg[j]);  // sigmoid(gate), formed in E
+          ob_[vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)] = y;
+        }
       }
     };
     if (nch > 0) {
       const int lane = threadIdx.x % 64;
       load_qk(tok_beg, lane / 16, lane % 16);
     }
-    f32x4_t O[2], U[2];
 
+    // Iteration it: the chain works on chunk c = it - 1.
     for (int it = 0; it <= nch; ++it) {
-      const bool act = it >= 1;  // the state chain works on chunk c = it - 1
-      const int64_t c0 = tok_beg + (int64_t)kC * (it - 1);
+      const bool act = it >= 1;
       const int p = (it - 1) & 1;
       int t_ = threadIdx.x;
       __asm__ volatile("" : "+v"(t_));
@@ -611,7 +679,12 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         return r;
       };
 
-      // ---- E: norms of chunk it; U0, U = U0 - W S, O = diag(nq) Qbar S ---------
+      // ---- E: sigmoid(gate) of c; norms of chunk it; U0, U = U0 - W S, O = Qbar S
+      if (act && gate) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          rg[j] = __float_as_uint(rcpf_fast(1.f + exp2f_fast(-kLog2e * bf16lo(rg[j]))));
+      }
       if (it < nch) {
         float* nqo = bNQ(it & 1);
         float* nko = bNK(it & 1);
@@ -711,55 +784,72 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       lds_barrier();  // B2
 
       // ---- W: gated output of chunk c; requests for the next chunks -----------
-      if (act) {
-        const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-        const auto ob_ = sbase(o + (c0 * H + h) * DV);
-        const uint32_t vo_lane = (4 * g) * H * DV + jcol;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 16 * (j >> 2) + 4 * g + (j & 3);
-          if (r < nrows) {
-            float y = O[j >> 2][j & 3];
-            if (gate) y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * bf16lo(rg[j])));
-            ob_[vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * DV)] = y;
-          }
-        }
+      // (stores first: the loads behind them are not waited for until the next
+      // iteration's E stage)
+      if (act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
+      if (it < nch) {
+        load_v(tok_beg + (int64_t)kC * it, g, jcol);  // chain input at it+1
+        if (gate) load_g(tok_beg + (int64_t)kC * it, g, jcol);
       }
-      if (it < nch) load_vg(tok_beg + (int64_t)kC * it, g, jcol);         // chain input at it+1
       if (it + 1 < nch) load_qk(tok_beg + (int64_t)kC * (it + 1), g, li);  // norms at it+1
       lds_barrier();  // B3
     }
 
     if (s_final) {
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-      const uint32_t st_lane = 4 * g * DV + 16 * sw + li;
+      const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
       const auto sp = sbase(s_final + st_off);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * DV] = S[ct][jj];
+        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj];
     }
   }
 }
 
 template <int DK, int DV>
-hipError_t launch_cfg(const FwdArgs& p, hipStream_t stream) {
+hipError_t launch_cfg(const FwdArgs& p, int nsl, hipStream_t stream) {
   auto kern = chunk_fwd_bf16_kernel<DK, DV>;  // LDS is static (Cfg<DK, DV>::bytes)
-  const int64_t grid = (int64_t)p.num_seqs * p.num_heads;
+  const int64_t items = (int64_t)p.num_seqs * p.num_heads;
+  const int64_t grid = (items + 7) / 8 * 8 * nsl;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg<DK, DV>::NT), 0, stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
                      (const uint16_t*)p.a, (const uint16_t*)p.b, (const uint16_t*)p.gate,
-                     p.cu_seqlens, p.initial_state, (float*)p.o, p.final_state, p.num_heads);
+                     p.cu_seqlens, p.initial_state, (float*)p.o, p.final_state, p.num_heads,
+                     (int)items, p.dv, nsl);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
 }
 
 }  // namespace
 
+// One workgroup per (sequence, head) when that fills the GPU; with fewer
+// items than half the compute units, d_v = 128 is split into two 64-column
+// slices per item (the key-side work is repeated, the state work halves).
 hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream) {
-  if ((int64_t)p.num_seqs * p.num_heads == 0) return hipSuccess;
-  if (p.dk == 128)
-    return p.dv == 128 ? launch_cfg<128, 128>(p, stream) : launch_cfg<128, 64>(p, stream);
-  return p.dv == 128 ? launch_cfg<64, 128>(p, stream) : launch_cfg<64, 64>(p, stream);
+  const int64_t items = (int64_t)p.num_seqs * p.num_heads;
+  if (items == 0) return hipSuccess;
+  const bool split = p.dv == 128 && 2 * items <= device_cus();
+  if (p.dk == 128) {
+    if (p.dv == 128 && !split) return launch_cfg<128, 128>(p, 1, stream);
+    return launch_cfg<128, 64>(p, p.dv / 64, stream);
+  }
+  if (p.dv == 128 && !split) return launch_cfg<64, 128>(p, 1, stream);
+  return launch_cfg<64, 64>(p, p.dv / 64, stream);
 }
 
 }  // namespace kda

@@ -75,6 +75,15 @@ def test_fwd_bf16_head_dims(dk, dv):
     run_case(w, [300, 17, 0, 129], label=f"bf16 {dk}x{dv}")
 
 
+@pytest.mark.parametrize("heads", [3, 136])
+def test_fwd_bf16_dv_slicing(heads):
+    """Few (sequence, head) items split d_v = 128 into two 64-column slices per
+    workgroup pair; many items (2 x 136 x 2 slices > 256 compute units) use one
+    workgroup per item.  Both launch shapes against the oracle."""
+    w = kc.custom_workload(W1, heads=heads, s0_std=0.02)
+    run_case(w, [70, 33], label=f"bf16 H={heads}")
+
+
 def test_fwd_bf16_no_gate():
     w = kc.custom_workload(W1, heads=2, s0_std=0.02)
     run_case(w, [190, 64], gate=False, label="no gate")
