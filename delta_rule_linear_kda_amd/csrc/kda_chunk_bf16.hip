@@ -51,6 +51,8 @@ namespace kda {
 namespace {
 
 constexpr int kC = 32;          // chunk length (tokens)
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx950.
+constexpr int kBufferRsrcFlags = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -290,7 +292,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     // 16 * wave + 4g .. +3.  The tokens of a tile run along the 16 lanes of a
     // DPP row.
     u32x2_t rq[2], rk[2], ra[2];
-    uint32_t rb[2];
+    uint16_t rb[2];
     auto load = [&](int64_t c0, int li, int g) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
       const int64_t tb = c0 * H + h;
@@ -317,7 +319,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       load(tok_beg, lane % 16, lane / 16);
     }
 
-    for (int it = 0; it <= nch; ++it) {
+    // Both wave groups skip the loop together when the sequence is empty.
+    for (int it = 0; nch > 0 && it <= nch; ++it) {
       const int64_t c0 = tok_beg + (int64_t)kC * it;
       const bool act = it < nch;
       const int p = it & 1;
@@ -346,7 +349,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         float beta[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
-          beta[tau] = rcpf_fast(1.f + exp2f_fast(-kLog2e * bf16lo(rb[tau])));
+          beta[tau] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((uint32_t)rb[tau] << 16)));
         if (nrows < kC) {  // padding rows: g = 0, beta = 0
 #pragma unroll
           for (int tau = 0; tau < 2; ++tau) {
@@ -364,7 +367,6 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
           for (int j = 0; j < 4; ++j) tot[tau][j] = row_last16(cum[tau][j]);
-        if (it + 1 < nch) load(c0 + kC, li, g);  // next chunk, consumed in its E stage
         const int cb = 16 * wave + 4 * g;
         float e0[4], fend[2][4];
 #pragma unroll
@@ -421,6 +423,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             *reinterpret_cast<bf16x4_t*>(sK1L + li * LB + cb) = k1l;
           }
         }
+        // Next chunk's inputs, consumed in its E stage.  Requested last, when
+        // this chunk's raw registers are dead, and unconditionally (the last
+        // chunk re-reads itself), so the loads land directly in the registers
+        // carried to the next iteration and nothing here waits for them.
+        load(it + 1 < nch ? c0 + kC : c0, li, g);
       }
       lds_barrier();  // B1: operands, beta (prep) and norms (state) in LDS
 
@@ -603,11 +610,17 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+      // Let the initial state arrive now: otherwise every use of S inside the
+      // loop carries a wait on the memory counter that also covers the
+      // loop's own stores.
+      __builtin_amdgcn_s_waitcnt(0);
     }
     typedef __attribute__((ext_vector_type(CPL / 2))) uint32_t uvec_t;
     constexpr int NPASS = RPW / 4;
     uvec_t nq_[NPASS], nk_[NPASS];  // q, k rows for the norms of the next chunk
-    uint32_t rv[8], rg[8];          // v, gate (bits, then sigmoid) of the chunk the chain works on
+    uint32_t rv[8];                 // v of the chunk the chain works on (word with the bf16)
+    uint32_t rgr[8];                // gate of that chunk (word with the bf16)
+    float rg[8];                    // sigmoid(gate) of that chunk, for its output
     f32x4_t O[2], U[2];
     auto load_qk = [&](int64_t c0, int g, int li) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
@@ -623,54 +636,65 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         nk_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(kb_ + off);
       }
     };
+    // v and gate arrive as the aligned 32-bit word holding the lane's bf16
+    // element (the lane pair (jcol & ~1, jcol | 1) shares it); the half is
+    // picked at use.  Whole-register loads keep the loop-carried registers
+    // free of zero-extension masks, which would have to wait for the loads.
     auto load_v = [&](int64_t c0, int g, int jcol) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-      const auto vb_ = sbase(v + (c0 * H + h) * dvt + col0);
+      const auto vb_ = sbase(reinterpret_cast<const uint32_t*>(v + (c0 * H + h) * dvt + col0));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 16 * (i / 4) + 4 * g + (i % 4);
         const int rr = r < nr ? r : nr - 1;
-        rv[i] = vb_[(uint32_t)(rr * H * dvt) + jcol];
+        rv[i] = vb_[(uint32_t)(rr * H * dvt + (jcol & ~1)) / 2];
       }
     };
     auto load_g = [&](int64_t c0, int g, int jcol) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-      const auto gb_ = sbase(gate + (c0 * H + h) * dvt + col0);
+      // Without a gate the same rows of v are read (and ignored), so the
+      // number of requests in flight never depends on the gate.
+      const auto gb_ = sbase(
+          reinterpret_cast<const uint32_t*>((gate ? gate : v) + (c0 * H + h) * dvt + col0));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 16 * (i / 4) + 4 * g + (i % 4);
         const int rr = r < nr ? r : nr - 1;
-        rg[i] = gb_[(uint32_t)(rr * H * dvt) + jcol];
+        rgr[i] = gb_[(uint32_t)(rr * H * dvt + (jcol & ~1)) / 2];
       }
     };
-    // Gated output of chunk c (its O accumulators), stored fp32.
+    // Gated output of chunk c (its O accumulators), stored fp32 through a
+    // buffer resource whose range ends after the chunk's last valid row: all
+    // eight stores always issue (so the in-order count of outstanding memory
+    // operations is exact for the waits that follow), and the hardware drops
+    // the padding rows of a partial chunk.
     auto epilogue = [&](int64_t c0, int g, int jcol) {
       const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-      const auto ob_ = sbase(o + (c0 * H + h) * dvt + col0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          o + (c0 * H + h) * dvt + col0, 0, nrows * H * dvt * 4, kBufferRsrcFlags);
       const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 16 * (j >> 2) + 4 * g + (j & 3);
-        if (r < nrows) {
-          float y = O[j >> 2][j & 3];
-          if (gate) y *= __uint_as_float(rg[j]);  // sigmoid(gate), formed in E
-          ob_[vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)] = y;
-        }
+        float y = O[j >> 2][j & 3];
+        if (gate) y *= rg[j];  // sigmoid(gate), formed in E
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(y), rs, 4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)),
+            0, 0);
       }
     };
-    if (nch > 0) {
+    if (nch > 0) {  // q, k rows of chunk 0 for its norms
       const int lane = threadIdx.x % 64;
       load_qk(tok_beg, lane / 16, lane % 16);
     }
-
     // Iteration it: the chain works on chunk c = it - 1.
-    for (int it = 0; it <= nch; ++it) {
+    for (int it = 0; nch > 0 && it <= nch; ++it) {
       const bool act = it >= 1;
       const int p = (it - 1) & 1;
       int t_ = threadIdx.x;
       __asm__ volatile("" : "+v"(t_));
       const int lane = t_ % 64, g = lane / 16, li = lane % 16;
       const int jcol = 16 * sw + li;
+      const uint32_t hsh = 16u * (li & 1);  // which half of a loaded word is this lane's
 
       auto s_f16 = [&](int kb) {
         f16x8_t r;
@@ -683,7 +707,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       if (act && gate) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          rg[j] = __float_as_uint(rcpf_fast(1.f + exp2f_fast(-kLog2e * bf16lo(rg[j]))));
+          rg[j] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
       }
       if (it < nch) {
         float* nqo = bNQ(it & 1);
@@ -713,7 +737,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         {
           float rr[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) rr[j] = be[16 * (j >> 2) + 4 * g + (j & 3)] * bf16lo(rv[j]);
+          for (int j = 0; j < 8; ++j)
+            rr[j] = be[16 * (j >> 2) + 4 * g + (j & 3)] * __uint_as_float((rv[j] >> hsh) << 16);
           bf16x8_t rh, rl;
           split_bf16x8(rr, rh, rl);
 #pragma unroll
@@ -783,15 +808,19 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       }
       lds_barrier();  // B2
 
-      // ---- W: gated output of chunk c; requests for the next chunks -----------
-      // (stores first: the loads behind them are not waited for until the next
-      // iteration's E stage)
-      if (act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
-      if (it < nch) {
-        load_v(tok_beg + (int64_t)kC * it, g, jcol);  // chain input at it+1
-        if (gate) load_g(tok_beg + (int64_t)kC * it, g, jcol);
+      // ---- W: requests for the next iteration, then chunk c's gated output ----
+      // The requests are unconditional (chunk index clamped to the last
+      // chunk), so they land directly in the carried registers, and they are
+      // issued before the stores, so the next stage's waits for them never
+      // cover the stores.
+      {
+        const int64_t c_this = tok_beg + (int64_t)kC * (it < nch ? it : nch - 1);
+        const int64_t c_next = tok_beg + (int64_t)kC * (it + 1 < nch ? it + 1 : nch - 1);
+        load_g(c_this, g, jcol);  // chunk it's gate and v, for the chain at it+1
+        load_v(c_this, g, jcol);
+        load_qk(c_next, g, li);   // norms at it+1
       }
-      if (it + 1 < nch) load_qk(tok_beg + (int64_t)kC * (it + 1), g, li);  // norms at it+1
+      if (act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
       lds_barrier();  // B3
     }
 
