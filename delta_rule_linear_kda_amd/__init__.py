@@ -8,7 +8,8 @@ import of any entry point raises -- there is no fallback path.
 Entry points (same names as the C ABI):
   * ``fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, ...)``
   * ``decode_step(q, k, v, a, b, gate, state, ...)``
-  * ``fwd_workspace_bytes(...)``, ``status_str(code)``, ``abi_version()``
+  * ``fwd_workspace_bytes(...)``, ``ckpt_count(...)``, ``status_str(code)``,
+    ``abi_version()``
 """
 from __future__ import annotations
 
@@ -24,8 +25,8 @@ STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
     4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP",
 }
-EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_decode_step", "kda_status_str",
-           "kda_abi_version")
+EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
+           "kda_fwd_ckpt_count", "kda_decode_step", "kda_status_str", "kda_abi_version")
 
 
 class KdaError(RuntimeError):
@@ -56,6 +57,13 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked.restype = ctypes.c_int
         L.kda_fwd_chunked.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+        L.kda_fwd_chunked_ckpt.restype = ctypes.c_int
+        L.kda_fwd_chunked_ckpt.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_int32, vp, ctypes.c_int64, vp,
+                                           ctypes.c_size_t, vp]
+        L.kda_fwd_ckpt_count.restype = ctypes.c_int
+        L.kda_fwd_ckpt_count.argtypes = [ctypes.c_int32, vp, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int64)]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_status_str.restype = ctypes.c_char_p
@@ -110,16 +118,33 @@ def fwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int, dk: in
     return int(out.value)
 
 
+def ckpt_count(cu_seqlens_host, interval: int) -> int:
+    """Recorded-state slots kda_fwd_chunked_ckpt fills (C ABI
+    ``kda_fwd_ckpt_count``) for host offsets ``cu_seqlens_host`` (int32 [N+1])."""
+    import numpy as np
+
+    cu = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    out = ctypes.c_int64(0)
+    rc = lib().kda_fwd_ckpt_count(int(cu.size) - 1, cu.ctypes.data, int(interval), ctypes.byref(out))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_ckpt_count")
+    return int(out.value)
+
+
 def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
                 output_final_state: bool = True, out=None, final_state=None,
-                stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
-    """Chunked KDA forward over packed sequences (C ABI ``kda_fwd_chunked``).
+                checkpoint_interval: Optional[int] = None, checkpoints=None,
+                stream=None):
+    """Chunked KDA forward over packed sequences (C ABI ``kda_fwd_chunked``, or
+    ``kda_fwd_chunked_ckpt`` when ``checkpoint_interval`` is given).
 
     q, k, a: [T, H, dk]; v, gate: [T, H, dv] (gate may be None); b: [T, H]
     (all float32 or all bfloat16); cu_seqlens: int32 [N+1] on the device;
     initial_state: fp32 [N, H, dk, dv] or None.  Returns (o fp32 [T, H, dv],
-    final_state fp32 [N, H, dk, dv] or None).  ``final_state`` may be passed as
-    the same tensor as ``initial_state`` for an in-place update."""
+    final_state fp32 [N, H, dk, dv] or None), plus the recorded states fp32
+    [n_ckpt, H, dk, dv] as a third element when ``checkpoint_interval`` is
+    given (slot layout: see ``kda_fwd_chunked_ckpt``).  ``final_state`` may be
+    passed as the same tensor as ``initial_state`` for an in-place update."""
     import torch
 
     T, H, dk = q.shape
@@ -135,12 +160,25 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     ws_bytes = fwd_workspace_bytes(N, T, H, dk, dv, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
-    rc = lib().kda_fwd_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
-                               _ptr(gate), _ptr(cu_seqlens), _ptr(initial_state), _ptr(out),
-                               _ptr(final_state), _ptr(ws), ws_bytes, _stream(q.device, stream))
+    if checkpoint_interval is None:
+        rc = lib().kda_fwd_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                   _ptr(b), _ptr(gate), _ptr(cu_seqlens), _ptr(initial_state),
+                                   _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
+                                   _stream(q.device, stream))
+        if rc != 0:
+            raise KdaError(rc, "kda_fwd_chunked")
+        return out, final_state
+    if checkpoints is None:
+        n_ckpt = ckpt_count(cu_seqlens.cpu().numpy(), checkpoint_interval)
+        checkpoints = torch.empty((n_ckpt, H, dk, dv), dtype=torch.float32, device=q.device)
+    rc = lib().kda_fwd_chunked_ckpt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                    _ptr(b), _ptr(gate), _ptr(cu_seqlens), _ptr(initial_state),
+                                    _ptr(out), _ptr(final_state), int(checkpoint_interval),
+                                    _ptr(checkpoints), int(checkpoints.shape[0]), _ptr(ws),
+                                    ws_bytes, _stream(q.device, stream))
     if rc != 0:
-        raise KdaError(rc, "kda_fwd_chunked")
-    return out, final_state
+        raise KdaError(rc, "kda_fwd_chunked_ckpt")
+    return out, final_state, checkpoints
 
 
 def decode_step(q, k, v, a, b, gate, state, *, out=None, stream=None):

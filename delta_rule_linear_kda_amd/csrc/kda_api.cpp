@@ -90,11 +90,17 @@ kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes) {
   return KDA_OK;
 }
 
-kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k, const void* v,
-                           const void* a, const void* b, const void* gate,
-                           const int32_t* cu_seqlens, const float* initial_state, void* o,
-                           float* final_state, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool valid_interval(int32_t iv) { return iv > 0 && iv % 64 == 0; }
+
+kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const void* v,
+                    const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
+                    const float* initial_state, void* o, float* final_state,
+                    int32_t ckpt_interval, float* ckpt, int64_t ckpt_capacity, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   kda_status st = check_shape(shape);
   if (st != KDA_OK) return st;
   const kda_shape& s = *shape;
@@ -123,6 +129,14 @@ kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k,
   // final_state may be exactly initial_state (in place), never a partial overlap.
   if (overlap(sf, in[7]) && (const void*)final_state != (const void*)initial_state)
     return KDA_ERR_ALIAS;
+  if (ckpt_interval != 0) {  // recorded states: disjoint from everything else
+    const uint64_t slot = uint64_t(s.num_heads) * uint64_t(s.dk) * uint64_t(s.dv) * 4;
+    if (uint64_t(ckpt_capacity) > uint64_t(kMaxElems) / slot) return KDA_ERR_BAD_SHAPE;
+    const Span sc(ckpt, uint64_t(ckpt_capacity) * slot);
+    for (const Span& x : in)
+      if (overlap(sc, x)) return KDA_ERR_ALIAS;
+    if (overlap(sc, so) || overlap(sc, sf)) return KDA_ERR_ALIAS;
+  }
 
   kda::FwdArgs p;
   p.num_seqs = s.num_seqs;
@@ -136,8 +150,54 @@ kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k,
   p.initial_state = initial_state;
   p.o = o;
   p.final_state = final_state;
+  p.ckpt_interval = ckpt_capacity > 0 ? ckpt_interval : 0;
+  p.ckpt = ckpt;
+  p.ckpt_capacity = ckpt_capacity;
   if (kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate,
+                           const int32_t* cu_seqlens, const float* initial_state, void* o,
+                           float* final_state, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
+                  nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, const void* k,
+                                const void* v, const void* a, const void* b, const void* gate,
+                                const int32_t* cu_seqlens, const float* initial_state, void* o,
+                                float* final_state, int32_t ckpt_interval, float* ckpt_states,
+                                int64_t ckpt_capacity, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!valid_interval(ckpt_interval) || ckpt_capacity < 0) {
+    const kda_status st = check_shape(shape);
+    return st != KDA_OK ? st : KDA_ERR_BAD_SHAPE;
+  }
+  if (ckpt_capacity > 0 && !ckpt_states) return KDA_ERR_NULL_POINTER;
+  if (!aligned16(ckpt_states)) return KDA_ERR_MISALIGNED;
+  return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state,
+                  ckpt_interval, ckpt_states, ckpt_capacity, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_ckpt_count(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                              int32_t ckpt_interval, int64_t* count) {
+  if (!count || (num_seqs > 0 && !cu_seqlens_host)) return KDA_ERR_NULL_POINTER;
+  if (num_seqs < 0 || !valid_interval(ckpt_interval)) return KDA_ERR_BAD_SHAPE;
+  int64_t total = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t len = int64_t(cu_seqlens_host[n + 1]) - int64_t(cu_seqlens_host[n]);
+    if (len < 0 || (n == 0 && cu_seqlens_host[0] != 0)) return KDA_ERR_BAD_SHAPE;
+    total += len / ckpt_interval;
+  }
+  *count = total;
   return KDA_OK;
 }
 

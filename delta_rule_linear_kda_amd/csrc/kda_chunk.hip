@@ -117,7 +117,8 @@ __global__ void __launch_bounds__(kThreads)
                      const TI* __restrict__ a, const TI* __restrict__ bl,
                      const TI* __restrict__ gate, const int32_t* __restrict__ cu_seqlens,
                      const float* __restrict__ s_init, float* __restrict__ o,
-                     float* __restrict__ s_final, int H, int DV) {
+                     float* __restrict__ s_final, int H, int DV, int ckpt_iv,
+                     float* __restrict__ ckpt, long long ckpt_cap) {
   using L = Layout<DK>;
   constexpr int LDK = L::LDK, L64 = L::L64, LDV = L::LDV;
   constexpr int NSEG = DK / 8;                 // 8-channel segments per row
@@ -158,6 +159,12 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
       S[ct][jj] = s_init ? s_init[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] : 0.f;
+
+  // First recorded-state slot of this sequence (the slots of the sequences
+  // before it come first).
+  int64_t ck_off = 0;
+  if (ckpt_iv > 0)
+    for (int m = 0; m < n; ++m) ck_off += (int64_t)(cu_seqlens[m + 1] - cu_seqlens[m]) / ckpt_iv;
 
   for (int64_t c0 = tok_beg; c0 < tok_end; c0 += kC) {
     const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
@@ -458,6 +465,20 @@ __global__ void __launch_bounds__(kThreads)
       }
       S[ct] = acc;
     }
+    // Record the state after the first `done` tokens when that is a multiple
+    // of the recording interval.
+    const int64_t done = c0 + kC - tok_beg;
+    if (ckpt_iv > 0 && done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
+      const int64_t slot = ck_off + done / ckpt_iv - 1;
+      if (slot < ckpt_cap) {
+        const int64_t cp = (slot * H + h) * (int64_t)DK * DV;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            ckpt[cp + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = S[ct][jj];
+      }
+    }
     // Epilogue: output gate and store.
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -499,7 +520,8 @@ hipError_t launch_t(const FwdArgs& p, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, (const TI*)p.q,
                      (const TI*)p.k, (const TI*)p.v, (const TI*)p.a, (const TI*)p.b,
                      (const TI*)p.gate, p.cu_seqlens, p.initial_state, (float*)p.o,
-                     p.final_state, p.num_heads, p.dv);
+                     p.final_state, p.num_heads, p.dv, p.ckpt_interval, p.ckpt,
+                     (long long)p.ckpt_capacity);
   return hipGetLastError();
 }
 

@@ -244,7 +244,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
                           const uint16_t* __restrict__ bl, const uint16_t* __restrict__ gate,
                           const int32_t* __restrict__ cu_seqlens, const float* __restrict__ s_init,
                           float* __restrict__ o, float* __restrict__ s_final, int H,
-                          int num_items, int dvt, int nsl) {
+                          int num_items, int dvt, int nsl, int ckpt_iv, float* __restrict__ ckpt,
+                          long long ckpt_cap) {
   using L = Cfg<DK, DV>;
   constexpr int NP = L::NP, CPL = L::CPL, RPW = L::RPW;
   constexpr int LB = L::LB, LT = L::LT, LX = L::LX, LA = L::LA;
@@ -596,6 +597,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     // ======================= state waves ======================================
     const int sw = wave - NP;  // owns state columns [16 sw, 16 sw + 16)
     const int64_t st_off = (int64_t)item * DK * dvt + col0;
+    // First recorded-state slot of this sequence: the slots of the sequences
+    // before it come first.
+    int64_t ck_off = 0;
+    if (ckpt_iv > 0)
+      for (int m = 0; m < n; ++m) ck_off += (int64_t)(cu_seqlens[m + 1] - cu_seqlens[m]) / ckpt_iv;
     f32x4_t S[NCT];
     {
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
@@ -805,6 +811,20 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           acc[2] = gv.z * S[ct][2]; acc[3] = gv.w * S[ct][3];
           S[ct] = mma_f16(lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g), uf, acc);
         }
+        // Record the state after the first `done` tokens when that is a
+        // multiple of the recording interval.
+        const int64_t done = (int64_t)kC * it;
+        if (ckpt_iv > 0 && done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
+          const int64_t slot = ck_off + done / ckpt_iv - 1;
+          if (slot < ckpt_cap) {
+            const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
+            const auto sp = sbase(ckpt + (slot * H + h) * DK * dvt + col0);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj];
+          }
+        }
       }
       lds_barrier();  // B2
 
@@ -845,7 +865,7 @@ hipError_t launch_cfg(const FwdArgs& p, int nsl, hipStream_t stream) {
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
                      (const uint16_t*)p.a, (const uint16_t*)p.b, (const uint16_t*)p.gate,
                      p.cu_seqlens, p.initial_state, (float*)p.o, p.final_state, p.num_heads,
-                     (int)items, p.dv, nsl);
+                     (int)items, p.dv, nsl, p.ckpt_interval, p.ckpt, (long long)p.ckpt_capacity);
   return hipGetLastError();
 }
 

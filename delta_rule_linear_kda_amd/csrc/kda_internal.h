@@ -24,6 +24,11 @@ struct FwdArgs {
   const float* initial_state;  // may be null (zero state)
   void* o;
   float* final_state;  // may be null
+  // Recorded states (kda_fwd_chunked_ckpt): every ckpt_interval tokens of a
+  // sequence; 0 = none.  Slot layout as final_state, ckpt_capacity slots.
+  int32_t ckpt_interval = 0;
+  float* ckpt = nullptr;
+  int64_t ckpt_capacity = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);

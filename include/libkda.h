@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1u
+#define KDA_ABI_VERSION 2u
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -92,9 +92,10 @@ KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes
  * Computes the recurrence above for every (sequence, head) with the
  * chunkwise-parallel form the pages name (page "[Paper Review] Kimi K3...",
  * section "Kimi Delta Attention (KDA)": recurrent but parallelisable per
- * chunk; 64-token chunks split into 16-token tiles whose pairwise decay
- * factors stay inside the bf16 range because g >= -5, "Lower-bounded decay"
- * paragraph).  The state is carried across chunks in fp32.
+ * chunk; chunks of 16-token tiles whose pairwise decay factors stay inside
+ * the bf16 range because g >= -5, "Lower-bounded decay" paragraph; 32-token
+ * chunks for bf16 inputs, 64-token chunks for fp32 inputs).  The state is
+ * carried across chunks in fp32.
  *
  *   q, k, a      [T, H, dk]   in_dtype
  *   v, gate      [T, H, dv]   in_dtype; gate may be NULL (no output gate)
@@ -115,6 +116,38 @@ KDA_API kda_status kda_fwd_chunked(const kda_shape* shape, const void* q, const 
                            const int32_t* cu_seqlens, const float* initial_state, void* o,
                            float* final_state, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* kda_fwd_chunked that also records the state at regular positions of every
+ * sequence: the hybrid cache of the serving stack keeps KDA states at fixed
+ * token intervals (every 512 tokens on page "atlas.lewiswon.me/...", cache
+ * paragraph), so a later request that shares a prefix resumes from the
+ * nearest recorded state instead of recomputing it.
+ *
+ *   ckpt_interval  tokens between recorded states: a positive multiple of 64
+ *   ckpt_states    [ckpt_capacity, H, dk, dv] fp32, device.  For sequence n of
+ *                  length L_n, slot ckpt_offset(n) + j, j = 0 ..
+ *                  floor(L_n / ckpt_interval) - 1, receives the state after the
+ *                  first (j + 1) * ckpt_interval tokens of the sequence, where
+ *                  ckpt_offset(n) = sum over m < n of floor(L_m / ckpt_interval)
+ *                  (kda_fwd_ckpt_count gives the total).  Slots at or beyond
+ *                  ckpt_capacity are not written.  May be NULL only when
+ *                  ckpt_capacity is 0.  Must not overlap any other argument.
+ * Everything else is as for kda_fwd_chunked (same results, bitwise).
+ * Errors: as kda_fwd_chunked; BAD_SHAPE also for a bad ckpt_interval or a
+ * negative ckpt_capacity. */
+KDA_API kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, const void* k,
+                                const void* v, const void* a, const void* b, const void* gate,
+                                const int32_t* cu_seqlens, const float* initial_state, void* o,
+                                float* final_state, int32_t ckpt_interval, float* ckpt_states,
+                                int64_t ckpt_capacity, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Number of state slots kda_fwd_chunked_ckpt fills for HOST-resident
+ * cu_seqlens [num_seqs + 1] (same validity rules as the device array).
+ * Errors: NULL_POINTER, BAD_SHAPE (num_seqs < 0, bad interval, decreasing
+ * offsets). */
+KDA_API kda_status kda_fwd_ckpt_count(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                              int32_t ckpt_interval, int64_t* count);
 
 /* One decode step: one new token for each of N independent sequences, the
  * recurrent update the pages' serving section runs with dedicated decode

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     for code in range(8):
         assert kda.status_str(code).startswith(kda.STATUS[code])
     assert kda.status_str(99) == "unknown kda_status"
@@ -135,3 +135,41 @@ def test_zero_sequences_is_a_no_op():
     # N = 0, T = 0: nothing to do, nothing launched.
     assert fwd(good_shape(num_seqs=0, total_tokens=0)) == OK
     assert dec(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+def fwd_ckpt(shape, interval=512, ckpt=None, capacity=4, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_fwd_chunked_ckpt(
+        ctypes.byref(shape), args["q"], args["k"], args["v"], args["a"], args["b"], args["gate"],
+        args["cu"], args["s0"], args["o"], args["sf"], interval,
+        BASE + 11 * (1 << 36) if ckpt is None else ckpt, capacity, None, 0, None)
+
+
+@pytest.mark.parametrize("interval,capacity,code", [(0, 4, SHAPE), (100, 4, SHAPE), (32, 4, SHAPE),
+                                                    (-512, 4, SHAPE), (512, -1, SHAPE)])
+def test_ckpt_rejects_bad_interval_or_capacity(interval, capacity, code):
+    assert fwd_ckpt(good_shape(), interval=interval, capacity=capacity) == code
+
+
+def test_ckpt_rejects_null_misaligned_and_aliasing():
+    s = good_shape()
+    assert fwd_ckpt(s, ckpt=0, capacity=4) == NULLP
+    assert fwd_ckpt(s, ckpt=BASE + 11 * (1 << 36) + 8) == MISAL
+    assert fwd_ckpt(s, ckpt=P["o"]) == ALIAS          # overlaps the output
+    assert fwd_ckpt(s, ckpt=P["k"]) == ALIAS          # overlaps an input
+    assert fwd_ckpt(s, ckpt=P["sf"]) == ALIAS         # overlaps the final state
+    assert fwd_ckpt(good_shape(dk=96)) == SHAPE       # the shape is still checked
+
+
+def test_ckpt_count():
+    cu = [0, 1100, 1612, 1912, 1912, 3448]
+    assert kda.ckpt_count(cu, 512) == 2 + 1 + 0 + 0 + 3
+    assert kda.ckpt_count(cu, 64) == sum((cu[i + 1] - cu[i]) // 64 for i in range(5))
+    assert kda.ckpt_count([0], 512) == 0
+    for bad_cu, iv in [(cu, 100), ([0, 10, 5], 512), ([3, 600], 512)]:
+        with pytest.raises(kda.KdaError) as e:
+            kda.ckpt_count(bad_cu, iv)
+        assert e.value.code == SHAPE
+    out = ctypes.c_int64(0)
+    assert kda.lib().kda_fwd_ckpt_count(2, None, 512, ctypes.byref(out)) == NULLP

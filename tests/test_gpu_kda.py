@@ -284,3 +284,45 @@ def test_device_generator_matches_host():
         h = kc.host_tokens(w, name, 64)
         dn = d.view(torch.int16).cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(dn.reshape(h.shape), h)
+
+
+# --- recorded states every 512 tokens (kda_fwd_chunked_ckpt) ----------------
+@pytest.mark.parametrize("base,heads,interval", [(1, 3, 512), (1, 136, 512), (0, 2, 128)])
+def test_fwd_checkpoints(base, heads, interval):
+    """States recorded every `interval` tokens equal the oracle's state after
+    that many tokens of each sequence (the oracle runs each sequence piecewise
+    over the same intervals, carrying its state); o and the final state equal
+    the plain forward bitwise."""
+    _require_gpu()
+    W = synth.WORKLOADS[base]
+    w = kc.custom_workload(W, heads=heads, dk=128 if base else 64, dv=128 if base else 64,
+                           s0_std=0.02 if base else 0.5)
+    lens = [1100, 512, 300, 0, 1536] if base else [300, 128, 64, 0, 257]
+    print(f"[case] checkpoints {w.name} H={heads} interval={interval} lens={lens}", flush=True)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    s0 = kc.host_state(w, len(lens))
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0_d = torch.from_numpy(s0).cuda()
+    o1, sf1 = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                              cu_d, s0_d)
+    o2, sf2, ck = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                                  cu_d, s0_d, checkpoint_interval=interval)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(sf1, sf2)
+    assert ck.shape[0] == sum(L // interval for L in lens)
+    ck = ck.cpu().numpy()
+    xr = {n: kc.f64(x[n]) for n in x}
+    slot, worst = 0, 0.0
+    for n, L in enumerate(lens):
+        state = s0[n:n + 1].astype(np.float64)
+        for j in range(L // interval):
+            t0, t1 = int(cu[n]) + j * interval, int(cu[n]) + (j + 1) * interval
+            _, state = oracle.fwd(*(xr[m][t0:t1] for m in ("q", "k", "v", "a", "b", "gate")),
+                                  [0, t1 - t0], state)
+            worst = max(worst, kc.rel_err(ck[slot], state[0]))
+            slot += 1
+    print(f"    worst recorded-state err={worst:.3e} over {slot} states", flush=True)
+    assert worst <= tol(w)
