@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
 CHUNK = 32                   # chunk length of the bf16 forward kernel
-FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 8>"
+FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 64>"  # d_v-sliced launch at 96 heads
 FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_chunk_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_T1048576_H96_d128.traffic.txt")
 COPY_PROBE_BYTES = 2 << 30
@@ -152,7 +152,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
     _, cfl = pick(fetch, "copyBuffer")
     _, cwl = pick(write, "copyBuffer")
     cf, cw = max(cfl), max(cwl)
-    kname, kfl = pick(fetch, FWD_KERNEL)
+    kname, kfl = pick(fetch, FWD_KERNEL.split("  ")[0])
     _, kwl = pick(write, FWD_KERNEL)
     kf, kw = sum(kfl) / len(kfl), sum(kwl) / len(kwl)
     f_scale = COPY_PROBE_BYTES / (cf * 1024.0)
