@@ -57,6 +57,10 @@ def _L():
         lib.kda_ref_fwd.argtypes = [ctypes.c_int32, dp, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                     ctypes.c_int]
+        lib.kda_ref_segment_transition.restype = ctypes.c_int
+        lib.kda_ref_segment_transition.argtypes = [ctypes.c_int32, dp, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, dp, dp, dp,
+                                                   dp, dp, ctypes.c_int]
         lib.kda_ref_decode_step.restype = ctypes.c_int
         lib.kda_ref_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, dp, dp, dp, dp, dp, dp, dp, dp,
@@ -120,3 +124,48 @@ def decode_step(q, k, v, a, b, gate, state, *, nthreads: Optional[int] = None):
     if rc != 0:
         raise ValueError("kda_ref_decode_step: bad argument")
     return o
+
+
+def segment_transition(k, v, a, b, cu_seqlens, *, nthreads: Optional[int] = None):
+    """Transition of every segment (one segment per sequence of cu_seqlens):
+    the recurrence maps a start state S0 to M S0 + S_loc.  Page "[Paper
+    Review] Kimi K3...", section "Infrastructure: how to actually run
+    trillion-scale", KDA co-design item (a cumulative transition plus a
+    locally generated state).  Returns fp64 [N, H, dk, dv + dk]: per row
+    S_loc then M."""
+    k, v, a, b = map(_f64, (k, v, a, b))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = len(cu) - 1
+    assert cu[-1] == T and a.shape == k.shape and b.shape == (T, H)
+    tr = np.zeros((N, H, dk, dv + dk))
+    rc = _L().kda_ref_segment_transition(N, cu.ctypes.data, H, dk, dv, _p(k), _p(v), _p(a),
+                                         _p(b), tr.ctypes.data, nthreads or threads())
+    if rc != 0:
+        raise ValueError("kda_ref_segment_transition: bad argument")
+    return tr
+
+
+def segment_compose(seg_offsets, trans, dv: int, s0=None):
+    """Chains segment transitions in token order, per sequence n and head h:
+    S = s0[n, h] (or 0), then S <- M_j S + S_loc_j for the segments
+    j = seg_offsets[n] .. seg_offsets[n+1]-1 (associative composition of the
+    same KDA co-design item).  Returns (seg_start [S, H, dk, dv]: the state
+    before each segment, final [N, H, dk, dv])."""
+    trans = np.asarray(trans, dtype=np.float64)
+    off = np.asarray(seg_offsets, dtype=np.int64)
+    S_, H, dk, w = trans.shape
+    assert w == dv + dk
+    N = len(off) - 1
+    starts = np.zeros((S_, H, dk, dv))
+    final = np.zeros((N, H, dk, dv))
+    for n in range(N):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if s0 is None else np.array(s0[n, h], dtype=np.float64)
+            for j in range(off[n], off[n + 1]):
+                starts[j, h] = S
+                S_loc, M = trans[j, h, :, :dv], trans[j, h, :, dv:]
+                S = M @ S + S_loc
+            final[n, h] = S
+    return starts, final

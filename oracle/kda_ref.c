@@ -170,3 +170,82 @@ int kda_ref_decode_step(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, con
   dec_job J = {num_seqs, H, dk, dv, q, k, v, a, b, gate, state, o, 0};
   return run_threads(dec_worker, &J, nthreads);
 }
+
+/* ---- Segment transitions ------------------------------------------------
+ * Page "[Paper Review] Kimi K3...", section "Infrastructure: how to actually
+ * run trillion-scale", KDA co-design item: a segment's effect on the state is
+ * a cumulative transition plus a locally generated state.  Written out from
+ * the recurrence: each token applies S -> F_t S + beta_t kh_t v_t^T with the
+ * dk x dk factor F_t = (I - beta_t kh_t kh_t^T) Diag(alpha_t), so a segment
+ * maps a start state S0 to M S0 + S_loc with M = F_last ... F_first and S_loc
+ * the state reached from S0 = 0.  Here F_t is formed as a dense matrix and
+ * multiplied in, the plainest form of that definition. */
+typedef struct {
+  int32_t num_seqs, H, dk, dv;
+  const int64_t* cu;
+  const double *k, *v, *a, *b;
+  double* trans;
+  atomic_long next;
+} trans_job;
+
+static void* trans_worker(void* p) {
+  trans_job* J = (trans_job*)p;
+  const int32_t H = J->H, dk = J->dk, dv = J->dv, w = dv + dk;
+  double* X = (double*)malloc(sizeof(double) * (size_t)dk * w);  /* [S_loc | M] */
+  double* Y = (double*)malloc(sizeof(double) * (size_t)dk * w);
+  double* F = (double*)malloc(sizeof(double) * (size_t)dk * dk);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+  if (!X || !Y || !F || !kh) abort();
+  const long total = (long)J->num_seqs * H;
+  for (;;) {
+    long item = atomic_fetch_add(&J->next, 1);
+    if (item >= total) break;
+    int32_t n = (int32_t)(item / H), h = (int32_t)(item % H);
+    /* S_loc = 0, M = I. */
+    for (int32_t r = 0; r < dk; ++r)
+      for (int32_t j = 0; j < w; ++j) X[(size_t)r * w + j] = (j - dv == r) ? 1.0 : 0.0;
+    for (int64_t t = J->cu[n]; t < J->cu[n + 1]; ++t) {
+      size_t th = (size_t)t * H + h;
+      const double* k = J->k + th * dk;
+      const double* v = J->v + th * dv;
+      const double* a = J->a + th * dk;
+      double sk = 0.0;
+      for (int32_t c = 0; c < dk; ++c) sk += k[c] * k[c];
+      double rk = 1.0 / sqrt(sk + KDA_REF_EPS);
+      for (int32_t c = 0; c < dk; ++c) kh[c] = k[c] * rk;
+      double beta = sigmoid(J->b[th]);
+      /* F = (I - beta kh kh^T) Diag(alpha), alpha = exp(g_min sigmoid(a)). */
+      for (int32_t r = 0; r < dk; ++r)
+        for (int32_t c = 0; c < dk; ++c)
+          F[(size_t)r * dk + c] = ((r == c ? 1.0 : 0.0) - beta * kh[r] * kh[c]) *
+                                  exp(KDA_REF_GMIN * sigmoid(a[c]));
+      /* [S_loc | M] <- F [S_loc | M] + [beta kh v^T | 0]. */
+      for (int32_t r = 0; r < dk; ++r)
+        for (int32_t j = 0; j < w; ++j) {
+          double acc = j < dv ? beta * kh[r] * v[j] : 0.0;
+          for (int32_t c = 0; c < dk; ++c) acc += F[(size_t)r * dk + c] * X[(size_t)c * w + j];
+          Y[(size_t)r * w + j] = acc;
+        }
+      memcpy(X, Y, sizeof(double) * (size_t)dk * w);
+    }
+    memcpy(J->trans + (size_t)item * dk * w, X, sizeof(double) * (size_t)dk * w);
+  }
+  free(X);
+  free(Y);
+  free(F);
+  free(kh);
+  return NULL;
+}
+
+int kda_ref_segment_transition(int32_t num_seqs, const int64_t* cu_seqlens, int32_t H,
+                               int32_t dk, int32_t dv, const double* k, const double* v,
+                               const double* a, const double* b, double* trans, int nthreads) {
+  if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return -1;
+  if (cu_seqlens[0] != 0) return -1;
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+  if (num_seqs > 0 && !trans) return -1;
+  if (cu_seqlens[num_seqs] > 0 && (!k || !v || !a || !b)) return -1;
+  trans_job J = {num_seqs, H, dk, dv, cu_seqlens, k, v, a, b, trans, 0};
+  return run_threads(trans_worker, &J, nthreads);
+}

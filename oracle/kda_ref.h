@@ -48,6 +48,15 @@ int kda_ref_decode_step(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, con
                         const double* k, const double* v, const double* a, const double* b,
                         const double* gate, double* state, double* o, int nthreads);
 
+/* Segment transitions: every sequence of cu_seqlens is one segment.  For
+ * segment n and head h, the recurrence maps a start state S0 to M S0 + S_loc;
+ * trans [num_seqs, H, dk, dv + dk] receives, per row r, S_loc[r, :] then
+ * M[r, :], with M = F_last ... F_first, F_t = (I - beta kh kh^T) Diag(alpha)
+ * formed densely, and S_loc the state from S0 = 0.  Returns 0 or -1. */
+int kda_ref_segment_transition(int32_t num_seqs, const int64_t* cu_seqlens, int32_t H,
+                               int32_t dk, int32_t dv, const double* k, const double* v,
+                               const double* a, const double* b, double* trans, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

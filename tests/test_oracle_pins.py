@@ -328,3 +328,86 @@ def test_planted_mistakes_are_caught(mutation):
     # and the correct copy of the same code agrees with the chunk model
     o0, s0_ = _mutant_fwd(q, k, v, a, b, gate, [0, T], s0, mutation="none")
     np.testing.assert_allclose(o0, oc, rtol=1e-9, atol=1e-12)
+
+
+# --- Segment transitions (KDA co-design item of the "Infrastructure" section):
+# the recurrence over a segment is affine in its start state, S0 -> M S0 + S_loc.
+def test_transition_reproduces_recurrence_from_any_start():
+    """The dense-factor transition against the rank-1 token recurrence: for
+    random start states, fwd's final state equals M S0 + S_loc."""
+    T, H, dk, dv = 37, 2, 8, 5
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=40)
+    a = a - 4.0  # alpha near 0.9, so M stays O(1) over the segment and is tested
+    cu = [0, 9, 9, 37]                                    # includes an empty segment
+    tr = oracle.segment_transition(k, v, a, b, cu)
+    s0 = np.random.default_rng(41).standard_normal((3, H, dk, dv))
+    _, sf = oracle.fwd(q, k, v, a, b, gate, cu, s0)
+    for n in range(3):
+        for h in range(H):
+            S_loc, M = tr[n, h, :, :dv], tr[n, h, :, dv:]
+            np.testing.assert_allclose(M @ s0[n, h] + S_loc, sf[n, h], rtol=1e-12, atol=1e-13)
+    # the empty segment: identity transition, zero local state
+    np.testing.assert_array_equal(tr[1, :, :, dv:], np.broadcast_to(np.eye(dk), (H, dk, dk)))
+    assert np.all(tr[1, :, :, :dv] == 0.0)
+
+
+def test_transition_single_token_closed_form():
+    """One token: M = (I - beta kh kh^T) Diag(alpha), S_loc = beta kh v^T."""
+    H, dk, dv = 1, 6, 4
+    _, k, v, a, b, _ = rand_inputs(1, H, dk, dv, seed=42)
+    tr = oracle.segment_transition(k, v, a, b, [0, 1])
+    kh = l2n(k)[0, 0]
+    beta = sig(b[0, 0])
+    alpha = np.exp(-5.0 * sig(a[0, 0]))
+    M = (np.eye(dk) - beta * np.outer(kh, kh)) @ np.diag(alpha)
+    np.testing.assert_allclose(tr[0, 0, :, dv:], M, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(tr[0, 0, :, :dv], beta * np.outer(kh, v[0, 0]), rtol=1e-13)
+
+
+def test_transition_beta_zero_is_decay_product():
+    """beta = 0: only retention acts, M = Diag(prod alpha) and S_loc = 0."""
+    T, H, dk, dv = 20, 2, 7, 3
+    _, k, v, a, _, _ = rand_inputs(T, H, dk, dv, seed=43)
+    b = np.full((T, H), -np.inf)
+    tr = oracle.segment_transition(k, v, a, b, [0, T])
+    for h in range(H):
+        lam = np.exp((-5.0 * sig(a[:, h])).sum(0))
+        np.testing.assert_allclose(tr[0, h, :, dv:], np.diag(lam), rtol=1e-12, atol=1e-300)
+        assert np.all(tr[0, h, :, :dv] == 0.0)
+
+
+@pytest.mark.parametrize("cuts", [[0, 64, 100], [0, 1, 2, 50, 100], [0, 100]])
+def test_compose_equals_whole_sequence(cuts):
+    """Chaining the transitions of consecutive segments reproduces the
+    recurrence over the whole sequence (start of every segment and the end)."""
+    T, H, dk, dv = 100, 2, 8, 6
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=44)
+    a = a - 5.0  # weak decay: start states carry across segments
+    s0 = np.random.default_rng(45).standard_normal((1, H, dk, dv))
+    tr = oracle.segment_transition(k, v, a, b, cuts)
+    starts, final = oracle.segment_compose([0, len(cuts) - 1], tr, dv, s0)
+    _, sf = oracle.fwd(q, k, v, a, b, gate, [0, T], s0)
+    np.testing.assert_allclose(final, sf, rtol=1e-11, atol=1e-12)
+    for j in range(len(cuts) - 1):  # state before segment j = fwd over the prefix
+        if cuts[j] == 0:
+            np.testing.assert_array_equal(starts[j], s0[0])
+            continue
+        _, sp = oracle.fwd(q[:cuts[j]], k[:cuts[j]], v[:cuts[j]], a[:cuts[j]], b[:cuts[j]],
+                           None, [0, cuts[j]], s0)
+        np.testing.assert_allclose(starts[j], sp[0], rtol=1e-11, atol=1e-12)
+
+
+def test_transition_catches_transposed_product():
+    """A plausible slip, the transposed product (factors multiplied in the
+    reverse order with Diag(alpha) on the wrong side), is caught by the affine
+    pin when the decay is weak enough for the start state to matter."""
+    T, H, dk, dv = 12, 1, 6, 3
+    q, k, v, a, b, gate = rand_inputs(T, H, dk, dv, seed=46)
+    a = a - 4.0
+    tr = oracle.segment_transition(k, v, a, b, [0, T])
+    s0 = np.random.default_rng(47).standard_normal((1, H, dk, dv))
+    _, sf = oracle.fwd(q, k, v, a, b, None, [0, T], s0)
+    M, S_loc = tr[0, 0, :, dv:], tr[0, 0, :, :dv]
+    assert np.abs(M @ s0[0, 0]).max() > 0.1       # the start state matters here
+    np.testing.assert_allclose(M @ s0[0, 0] + S_loc, sf[0, 0], rtol=1e-12, atol=1e-13)
+    assert np.abs(M.T @ s0[0, 0] + S_loc - sf[0, 0]).max() > 1e-2
