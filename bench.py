@@ -15,7 +15,14 @@ events recorded on the stream the kernels are launched on.
 Prints ONE JSON line.  ``value`` is the forward throughput (tokens/s, a token
 being one position across all 96 heads).
 
+After the timed steps (outside them), ``kcp_share`` reports one GPU's share of
+the same sequence under 8-way head sharding -- 12 heads, 1 x 1,048,576 tokens
+-- through kda_fwd_chunked (direct form: 24 workgroups) and through
+kda_fwd_chunked_kcp (segment-transition form with the automatic segment
+length), each the mean of 3 launches after one warm-up.
+
 Profiling helpers (not part of a timed run):
+  --no-kcp-share / --only-kcp-share   skip, or run only, the 12-head comparison;
   --copy-probe          after the timed steps, run a plain 2 GiB device copy so
                         that a hardware-counter run of this same command can
                         scale FETCH_SIZE / WRITE_SIZE against known bytes;
@@ -37,7 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
 CHUNK = 32                   # chunk length of the bf16 forward kernel
-FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 64>"  # d_v-sliced launch at 96 heads
+FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 64, false>"  # d_v-sliced launch at 96 heads
 FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_chunk_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_T1048576_H96_d128.traffic.txt")
 COPY_PROBE_BYTES = 2 << 30
@@ -96,11 +103,56 @@ def cpu_baseline(T: int = 65536, slice_tokens: int = 8192) -> dict:
                       f"the state carried, {threads} threads, {dt:.1f} s of oracle time"}
 
 
-def _sha256(path: str) -> str:
-    import hashlib
+def kcp_share(T: int, stream, reps: int = 3) -> dict:
+    """Direct vs segment-transition form on 12 heads x 1 x T tokens."""
+    import torch
 
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import delta_rule_linear_kda_amd as kda
+    import synth
+    from tests import kda_cases as kc
+
+    H = 12
+    w = kc.custom_workload(synth.WORKLOADS[3], heads=H)
+    x = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    args = tuple(x[n] for n in ("q", "k", "v", "a", "b", "gate"))
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    o = torch.empty((T, H, w.dv), dtype=torch.float32, device="cuda")
+    sf = torch.empty((1, H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws_bytes = kda.kcp_workspace_bytes(1, T, H, w.dk, w.dv, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def timed(fn) -> float:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    direct = timed(lambda: kda.fwd_chunked(*args, cu, None, out=o, final_state=sf, stream=stream))
+    seg = timed(lambda: kda.fwd_chunked_kcp(*args, cu, None, out=o, final_state=sf,
+                                            workspace=ws, stream=stream))
+    return {"workload": f"kda_fwd_bf16_T{T}_H{H}_d128 (one GPU's share under 8-way head "
+                        f"sharding)", "direct_ms": direct, "segment_form_ms": seg,
+            "segment_form_tokens_per_s": T / (seg * 1e-3), "speedup": direct / seg,
+            "workspace_bytes": ws_bytes}
+
+
+def _sha256(path: str) -> str:
+    """sha256 of a C/HIP source's code: comments removed and whitespace
+    collapsed, so that editing a comment does not invalidate counters taken
+    on unchanged code."""
+    import hashlib
+    import re
+
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def read_traffic() -> dict | None:
@@ -113,7 +165,7 @@ def read_traffic() -> dict | None:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256") != _sha256(FWD_SOURCE):
+        if kv.get("kernel_code_sha256") != _sha256(FWD_SOURCE):
             return None
         return {"fetch": float(kv["fetch_bytes_per_launch"]),
                 "write": float(kv["write_bytes_per_launch"])}
@@ -170,7 +222,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
         f"kernel_write_kib: {kw:.1f}",
         f"fetch_bytes_per_launch: {fb:.0f}",
         f"write_bytes_per_launch: {wb:.0f}",
-        f"kernel_source_sha256: {_sha256(FWD_SOURCE)}",
+        f"kernel_code_sha256: {_sha256(FWD_SOURCE)}",
     ]
     return "\n".join(lines) + "\n"
 
@@ -183,6 +235,9 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=1 << 20, help="forward sequence length")
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kcp-share", action="store_true")
+    ap.add_argument("--only-kcp-share", action="store_true",
+                    help="run only the 12-head direct vs segment-form comparison")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
@@ -206,6 +261,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.only_kcp_share:
+        print(json.dumps({"kcp_share": kcp_share(args.tokens, stream)}), flush=True)
+        return 0
 
     # ---- forward workload: 1 x T tokens, H=96, d=128, bf16 ----------------
     wf = synth.WORKLOADS[3]
@@ -305,6 +363,10 @@ def main() -> int:
         out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
         out["roofline"]["traffic_fetch"] = tr["fetch"]
         out["roofline"]["traffic_write"] = tr["write"]
+    if not args.no_kcp_share:
+        del xin, o, dec_in
+        torch.cuda.empty_cache()
+        out["kcp_share"] = kcp_share(T, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

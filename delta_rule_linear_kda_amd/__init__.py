@@ -8,8 +8,11 @@ import of any entry point raises -- there is no fallback path.
 Entry points (same names as the C ABI):
   * ``fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, ...)``
   * ``decode_step(q, k, v, a, b, gate, state, ...)``
-  * ``fwd_workspace_bytes(...)``, ``ckpt_count(...)``, ``status_str(code)``,
-    ``abi_version()``
+  * ``segment_transition(k, v, a, b, cu_seqlens, ...)``,
+    ``segment_compose(seg_offsets, trans, ...)``,
+    ``fwd_chunked_kcp(q, k, v, a, b, gate, cu_seqlens, ...)``
+  * ``fwd_workspace_bytes(...)``, ``kcp_workspace_bytes(...)``,
+    ``ckpt_count(...)``, ``status_str(code)``, ``abi_version()``
 """
 from __future__ import annotations
 
@@ -26,7 +29,9 @@ STATUS = {
     4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP",
 }
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
-           "kda_fwd_ckpt_count", "kda_decode_step", "kda_status_str", "kda_abi_version")
+           "kda_fwd_ckpt_count", "kda_segment_transition", "kda_segment_compose",
+           "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_decode_step",
+           "kda_status_str", "kda_abi_version")
 
 
 class KdaError(RuntimeError):
@@ -64,6 +69,16 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_ckpt_count.restype = ctypes.c_int
         L.kda_fwd_ckpt_count.argtypes = [ctypes.c_int32, vp, ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_int64)]
+        L.kda_segment_transition.restype = ctypes.c_int
+        L.kda_segment_transition.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+        i32 = ctypes.c_int32
+        L.kda_segment_compose.restype = ctypes.c_int
+        L.kda_segment_compose.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.kda_fwd_kcp_workspace_bytes.restype = ctypes.c_int
+        L.kda_fwd_kcp_workspace_bytes.argtypes = [sp, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kda_fwd_chunked_kcp.restype = ctypes.c_int
+        L.kda_fwd_chunked_kcp.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                          ctypes.c_size_t, vp]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_status_str.restype = ctypes.c_char_p
@@ -179,6 +194,104 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     if rc != 0:
         raise KdaError(rc, "kda_fwd_chunked_ckpt")
     return out, final_state, checkpoints
+
+
+def segment_transition(k, v, a, b, cu_seqlens, *, out=None, stream=None):
+    """Transitions of the segments given as packed sequences (C ABI
+    ``kda_segment_transition``): k, a [T, H, dk]; v [T, H, dv]; b [T, H];
+    cu_seqlens int32 [S+1] on the device (one segment per entry).  Returns
+    fp32 [S, H, dk, dv + dk]: per row, the segment's zero-start state S_loc
+    followed by its transition M."""
+    import torch
+
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    S = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if out is None:
+        out = torch.empty((S, H, dk, dv + dk), dtype=torch.float32, device=k.device)
+    shape = Shape(S, T, H, dk, dv, _dtype_code(k), KDA_F32)
+    rc = lib().kda_segment_transition(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                      _ptr(cu_seqlens), _ptr(out), _stream(k.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_segment_transition")
+    return out
+
+
+def segment_compose(seg_offsets, trans, dv: int, initial_state=None, *, seg_start=None,
+                    final_state=None, want_seg_start: bool = True, want_final: bool = True,
+                    stream=None):
+    """Composition of segment transitions in token order (C ABI
+    ``kda_segment_compose``): seg_offsets int32 [N+1] on the device; trans
+    fp32 [S, H, dk, dv + dk]; initial_state fp32 [N, H, dk, dv] or None.
+    Returns (seg_start [S, H, dk, dv] or None, final_state [N, H, dk, dv] or
+    None)."""
+    import torch
+
+    S, H, dk, w = trans.shape
+    if w != dv + dk:
+        raise ValueError("trans must be [S, H, dk, dv + dk]")
+    N = seg_offsets.numel() - 1
+    if seg_offsets.dtype != torch.int32:
+        raise TypeError("seg_offsets must be int32")
+    dev = trans.device
+    if seg_start is None and want_seg_start:
+        seg_start = torch.empty((S, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    rc = lib().kda_segment_compose(N, S, H, dk, dv, _ptr(seg_offsets), _ptr(trans),
+                                   _ptr(initial_state), _ptr(seg_start), _ptr(final_state),
+                                   _stream(dev, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_segment_compose")
+    return seg_start, final_state
+
+
+def kcp_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                        segment_len: int = 0, in_dtype: int = KDA_BF16) -> int:
+    shape = Shape(num_seqs, total_tokens, num_heads, dk, dv, in_dtype, KDA_F32)
+    out = ctypes.c_size_t(0)
+    rc = lib().kda_fwd_kcp_workspace_bytes(ctypes.byref(shape), int(segment_len),
+                                           ctypes.byref(out))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_kcp_workspace_bytes")
+    return int(out.value)
+
+
+def fwd_chunked_kcp(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
+                    segment_len: int = 0, output_final_state: bool = True, out=None,
+                    final_state=None, workspace=None, stream=None):
+    """Chunked forward in segment-transition form (C ABI
+    ``kda_fwd_chunked_kcp``); arguments and results as ``fwd_chunked``.
+    ``segment_len``: tokens per segment (a multiple of 64), 0 = automatic.
+    ``workspace``: a uint8 device tensor of at least ``kcp_workspace_bytes``
+    bytes, or None to allocate one."""
+    import torch
+
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.float32, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    ws_bytes = kcp_workspace_bytes(N, T, H, dk, dv, segment_len, dt)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
+    rc = lib().kda_fwd_chunked_kcp(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                   _ptr(b), _ptr(gate), _ptr(cu_seqlens), _ptr(initial_state),
+                                   _ptr(out), _ptr(final_state), int(segment_len),
+                                   _ptr(workspace),
+                                   int(workspace.numel()) if workspace is not None else 0,
+                                   _stream(q.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_chunked_kcp")
+    return out, final_state
 
 
 def decode_step(q, k, v, a, b, gate, state, *, out=None, stream=None):

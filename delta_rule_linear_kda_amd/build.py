@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_chunk_bf16.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_chunk_bf16.hip",
+           "kda_segments.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 FLAGS = [

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/libkda.h"
 #include "kda_internal.h"
 
@@ -96,17 +98,14 @@ namespace {
 
 bool valid_interval(int32_t iv) { return iv > 0 && iv % 64 == 0; }
 
-kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const void* v,
-                    const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
-                    const float* initial_state, void* o, float* final_state,
-                    int32_t ckpt_interval, float* ckpt, int64_t ckpt_capacity, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  kda_status st = check_shape(shape);
-  if (st != KDA_OK) return st;
+// Checks shared by the forward entry points, after check_shape.  Sets *empty
+// when there is nothing to do (no sequences).
+kda_status check_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                     const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
+                     const float* initial_state, void* o, float* final_state,
+                     int32_t ckpt_interval, float* ckpt, int64_t ckpt_capacity, bool* empty) {
   const kda_shape& s = *shape;
-  size_t need = 0;
-  kda_fwd_workspace_bytes(shape, &need);
-  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+  *empty = s.num_seqs == 0;
   if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
   if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
   if (s.total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return KDA_ERR_NULL_POINTER;
@@ -137,7 +136,12 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
       if (overlap(sc, x)) return KDA_ERR_ALIAS;
     if (overlap(sc, so) || overlap(sc, sf)) return KDA_ERR_ALIAS;
   }
+  return KDA_OK;
+}
 
+kda::FwdArgs fwd_args(const kda_shape& s, const void* q, const void* k, const void* v,
+                      const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
+                      const float* initial_state, void* o, float* final_state) {
   kda::FwdArgs p;
   p.num_seqs = s.num_seqs;
   p.num_heads = s.num_heads;
@@ -150,6 +154,26 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
   p.initial_state = initial_state;
   p.o = o;
   p.final_state = final_state;
+  return p;
+}
+
+kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const void* v,
+                    const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
+                    const float* initial_state, void* o, float* final_state,
+                    int32_t ckpt_interval, float* ckpt, int64_t ckpt_capacity, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  size_t need = 0;
+  kda_fwd_workspace_bytes(shape, &need);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+  bool empty = false;
+  st = check_fwd(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state,
+                 ckpt_interval, ckpt, ckpt_capacity, &empty);
+  if (st != KDA_OK || empty) return st;
+
+  kda::FwdArgs p = fwd_args(s, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state);
   p.ckpt_interval = ckpt_capacity > 0 ? ckpt_interval : 0;
   p.ckpt = ckpt;
   p.ckpt_capacity = ckpt_capacity;
@@ -231,6 +255,212 @@ kda_status kda_decode_step(const kda_shape* shape, const void* q, const void* k,
   p.state = state;
   p.o = o;
   if (kda::launch_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Segment-transition form (context parallelism on one GPU).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int32_t kSegQuantum = 64;        // segment lengths: multiples of both chunk sizes
+constexpr int64_t kMinAutoSegment = 4096;  // shorter automatic segments do not pay
+
+uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
+
+// Workspace of kda_fwd_chunked_kcp for segment length L: segment table,
+// per-sequence segment offsets, [S_loc | M] per (segment, head) and the start
+// state of every segment.  `cap` bounds the segment count:
+// sum_n ceil(L_n / L) <= floor(T / L) + N.
+struct KcpLayout {
+  int64_t cap;
+  uint64_t seg_cu, seg_off, trans, start, total;
+};
+
+KcpLayout kcp_layout(const kda_shape& s, int64_t L) {
+  KcpLayout w;
+  w.cap = s.total_tokens / L + s.num_seqs;
+  const uint64_t hk = uint64_t(s.num_heads) * uint64_t(s.dk);
+  w.seg_cu = 0;
+  w.seg_off = round_up(uint64_t(w.cap + 1) * 4, 256);
+  w.trans = w.seg_off + round_up(uint64_t(s.num_seqs + 1) * 4, 256);
+  w.start = w.trans + round_up(uint64_t(w.cap) * hk * uint64_t(s.dv + s.dk) * 4, 256);
+  w.total = w.start + round_up(uint64_t(w.cap) * hk * uint64_t(s.dv) * 4, 256);
+  return w;
+}
+
+// Segment length for `segment_len` (0 = automatic); *L = 0 selects the direct
+// form.  The segment form costs about three chunk passes per segment and head
+// (the transition over d_v + d_k columns, then the forward), spread over the
+// whole GPU, against one pass per (sequence, head) for the direct form, which
+// runs at most 2 workgroups per pair.  The automatic choice therefore
+// segments when there are at most cus / 4 (sequence, head) pairs, and aims at
+// about one segment per compute unit and head.
+kda_status kcp_resolve(const kda_shape& s, int32_t segment_len, int64_t* L) {
+  if (segment_len < 0 || segment_len % kSegQuantum != 0) return KDA_ERR_BAD_SHAPE;
+  *L = segment_len;
+  if (segment_len == 0) {
+    const int64_t items = int64_t(s.num_seqs) * s.num_heads;
+    const int cus = kda::device_cus();
+    if (items == 0 || 4 * items > cus) return KDA_OK;
+    const int64_t target = std::max<int64_t>(2, cus / s.num_heads);
+    const int64_t len = (int64_t)round_up((s.total_tokens + target - 1) / target, kSegQuantum);
+    if (len >= kMinAutoSegment && s.total_tokens >= 2 * len * s.num_seqs) *L = len;
+  }
+  if (*L == 0) return KDA_OK;
+  // The segment count must stay within the kernels' limits.
+  const KcpLayout w = kcp_layout(s, *L);
+  if (w.cap + 1 > INT32_MAX || w.cap * s.num_heads > (int64_t(1) << 31) / 4 ||
+      w.total > uint64_t(kMaxElems))
+    return KDA_ERR_BAD_SHAPE;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_segment_transition(const kda_shape* shape, const void* k, const void* v,
+                                  const void* a, const void* b, const int32_t* cu_seqlens,
+                                  float* trans, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
+  if (!cu_seqlens || !trans) return KDA_ERR_NULL_POINTER;
+  if (s.total_tokens > 0 && (!k || !v || !a || !b)) return KDA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+  for (const void* p : {k, v, a, (const void*)trans})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  if (!aligned_elem(b, s.in_dtype)) return KDA_ERR_MISALIGNED;
+  const Sizes z = byte_sizes(shape, s.total_tokens);
+  const uint64_t tb = uint64_t(s.num_seqs) * uint64_t(s.num_heads) * uint64_t(s.dk) *
+                      uint64_t(s.dv + s.dk) * 4;
+  const Span st_(trans, tb);
+  for (const Span& x : {Span(k, z.qk), Span(v, z.v), Span(a, z.qk), Span(b, z.b),
+                        Span(cu_seqlens, uint64_t(s.num_seqs + 1) * 4)})
+    if (overlap(st_, x)) return KDA_ERR_ALIAS;
+  kda::FwdArgs p = fwd_args(s, nullptr, k, v, a, b, nullptr, cu_seqlens, nullptr, nullptr, nullptr);
+  p.transition = trans;
+  if (kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_segment_compose(int32_t num_seqs, int32_t num_segments, int32_t num_heads,
+                               int32_t dk, int32_t dv, const int32_t* seg_offsets,
+                               const float* trans, const float* initial_state, float* seg_start,
+                               float* final_state, void* stream) {
+  if (num_seqs < 0 || num_segments < 0 || num_heads < 1 || !valid_dim(dk) || !valid_dim(dv))
+    return KDA_ERR_BAD_SHAPE;
+  if (int64_t(num_seqs) * num_heads > (int64_t(1) << 31) / 4 ||
+      int64_t(num_segments) * num_heads > (int64_t(1) << 31) / 4)
+    return KDA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return KDA_OK;
+  if (!seg_offsets || (num_segments > 0 && !trans)) return KDA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(seg_offsets) & 3u) != 0) return KDA_ERR_MISALIGNED;
+  for (const void* p : {(const void*)trans, (const void*)initial_state, (const void*)seg_start,
+                        (const void*)final_state})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  const uint64_t hk = uint64_t(num_heads) * uint64_t(dk);
+  const Span so(seg_offsets, uint64_t(num_seqs + 1) * 4);
+  const Span stt(trans, uint64_t(num_segments) * hk * uint64_t(dv + dk) * 4);
+  const Span si(initial_state, uint64_t(num_seqs) * hk * uint64_t(dv) * 4);
+  const Span ss(seg_start, uint64_t(num_segments) * hk * uint64_t(dv) * 4);
+  const Span sf(final_state, uint64_t(num_seqs) * hk * uint64_t(dv) * 4);
+  for (const Span& x : {so, stt, si, sf})
+    if (overlap(ss, x)) return KDA_ERR_ALIAS;
+  if (overlap(sf, so) || overlap(sf, stt)) return KDA_ERR_ALIAS;
+  if (overlap(sf, si) && (const void*)final_state != (const void*)initial_state)
+    return KDA_ERR_ALIAS;
+  kda::ComposeArgs p;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.seg_offsets = seg_offsets;
+  p.trans = trans;
+  p.initial_state = initial_state;
+  p.seg_start = seg_start;
+  p.final_state = final_state;
+  if (kda::launch_compose(p, static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_fwd_kcp_workspace_bytes(const kda_shape* shape, int32_t segment_len,
+                                       size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_POINTER;
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  int64_t L = 0;
+  st = kcp_resolve(*shape, segment_len, &L);
+  if (st != KDA_OK) return st;
+  *bytes = L == 0 ? 0 : size_t(kcp_layout(*shape, L).total);
+  return KDA_OK;
+}
+
+kda_status kda_fwd_chunked_kcp(const kda_shape* shape, const void* q, const void* k,
+                               const void* v, const void* a, const void* b, const void* gate,
+                               const int32_t* cu_seqlens, const float* initial_state, void* o,
+                               float* final_state, int32_t segment_len, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  int64_t L = 0;
+  st = kcp_resolve(s, segment_len, &L);
+  if (st != KDA_OK) return st;
+  if (L == 0)  // direct form
+    return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
+                    nullptr, 0, nullptr, 0, stream);
+  const KcpLayout w = kcp_layout(s, L);
+  if (workspace_bytes < w.total || !workspace) return KDA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+  bool empty = false;
+  st = check_fwd(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
+                 nullptr, 0, &empty);
+  if (st != KDA_OK || empty) return st;
+  {  // the workspace is disjoint from every argument
+    const Sizes z = byte_sizes(shape, s.total_tokens);
+    const Span ws(workspace, w.total);
+    for (const Span& x : {Span(q, z.qk), Span(k, z.qk), Span(v, z.v), Span(a, z.qk),
+                          Span(b, z.b), Span(gate, z.v),
+                          Span(cu_seqlens, uint64_t(s.num_seqs + 1) * 4),
+                          Span(initial_state, z.st), Span(o, z.o), Span(final_state, z.st)})
+      if (overlap(ws, x)) return KDA_ERR_ALIAS;
+  }
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  int32_t* seg_cu = reinterpret_cast<int32_t*>(base + w.seg_cu);
+  int32_t* seg_off = reinterpret_cast<int32_t*>(base + w.seg_off);
+  float* trans = reinterpret_cast<float*>(base + w.trans);
+  float* start = reinterpret_cast<float*>(base + w.start);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // 1. segments  2. their transitions  3. composition (start states and the
+  // final state)  4. the chunked forward of every segment from its start state.
+  if (kda::launch_segment_table(cu_seqlens, s.num_seqs, (int32_t)L, (int32_t)w.cap, seg_cu,
+                                seg_off, hs) != hipSuccess)
+    return KDA_ERR_HIP;
+  kda::FwdArgs pa = fwd_args(s, nullptr, k, v, a, b, nullptr, seg_cu, nullptr, nullptr, nullptr);
+  pa.num_seqs = (int32_t)w.cap;
+  pa.transition = trans;
+  if (kda::launch_fwd_chunked(pa, hs) != hipSuccess) return KDA_ERR_HIP;
+  kda::ComposeArgs pc;
+  pc.num_seqs = s.num_seqs;
+  pc.num_heads = s.num_heads;
+  pc.dk = s.dk;
+  pc.dv = s.dv;
+  pc.seg_offsets = seg_off;
+  pc.trans = trans;
+  pc.initial_state = initial_state;
+  pc.seg_start = start;
+  pc.final_state = final_state;
+  if (kda::launch_compose(pc, hs) != hipSuccess) return KDA_ERR_HIP;
+  kda::FwdArgs pb = fwd_args(s, q, k, v, a, b, gate, seg_cu, start, o, nullptr);
+  pb.num_seqs = (int32_t)w.cap;
+  if (kda::launch_fwd_chunked(pb, hs) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 

@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(kThreads)
                      const TI* __restrict__ a, const TI* __restrict__ bl,
                      const TI* __restrict__ gate, const int32_t* __restrict__ cu_seqlens,
                      const float* __restrict__ s_init, float* __restrict__ o,
-                     float* __restrict__ s_final, int H, int DV, int ckpt_iv,
+                     float* __restrict__ s_final, int H, int DV, int SDV, int ckpt_iv,
                      float* __restrict__ ckpt, long long ckpt_cap) {
   using L = Layout<DK>;
   constexpr int LDK = L::LDK, L64 = L::L64, LDV = L::LDV;
@@ -142,23 +142,30 @@ __global__ void __launch_bounds__(kThreads)
   float* sGe = smem + L::oGe;
   float* sBeta = smem + L::oBeta;
 
-  const int nslices = DV / kDvs;
+  // State rows hold SDV columns: d_v, or d_v + d_k for the transition form,
+  // whose columns [d_v, d_v + d_k) carry the transition matrix (value rows
+  // zero, start state the identity; no outputs are written).
+  const int nslices = SDV / kDvs;
   const int slice = blockIdx.x % nslices;
   const int item = blockIdx.x / nslices;  // sequence * H + head
   const int n = item / H, h = item % H;
   const int j0 = slice * kDvs;
   const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
   const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
-  const int64_t st_off = (int64_t)item * DK * DV;
+  const int64_t st_off = (int64_t)item * DK * SDV;
   const int jcol = j0 + 16 * wave + li;  // this lane's state / output column
+  const bool tslice = j0 >= DV;          // a slice of transition columns
 
   // State slice in accumulator layout: S[ct] holds rows 16ct + 4g + jj, column jcol.
   f32x4_t S[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      S[ct][jj] = s_init ? s_init[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] : 0.f;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * ct + 4 * g + jj;
+      S[ct][jj] = tslice ? (r == jcol - DV ? 1.f : 0.f)
+                  : s_init ? s_init[st_off + (int64_t)r * SDV + jcol] : 0.f;
+    }
 
   // First recorded-state slot of this sequence (the slots of the sequences
   // before it come first).
@@ -178,7 +185,12 @@ __global__ void __launch_bounds__(kThreads)
       const bool valid = row < nrows;
       if (valid) {
         const int64_t off = ((c0 + row) * H + h) * (int64_t)DK + seg * 8;
-        ld8(q + off, qx);
+        if (q) {  // the transition form reads no queries
+          ld8(q + off, qx);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qx[j] = 0.f;
+        }
         ld8(k + off, kx);
         ld8(a + off, ax);
       } else {
@@ -206,7 +218,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int it = 0; it < kC * (kDvs / 8) / kThreads; ++it) {
       const int idx = t + kThreads * it, row = idx / (kDvs / 8), seg = idx % (kDvs / 8);
       float vx[8];
-      if (row < nrows)
+      if (row < nrows && !tslice)
         ld8(v + ((c0 + row) * H + h) * (int64_t)DV + j0 + seg * 8, vx);
       else
 #pragma unroll
@@ -485,7 +497,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj;
-        if (r < nrows) {
+        if (o && r < nrows) {
           const int64_t off = ((c0 + r) * H + h) * (int64_t)DV + jcol;
           float y = O[tt][jj];
           if (gate) y *= sigmoidf(ld_elem(gate, off));
@@ -501,7 +513,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        s_final[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = S[ct][jj];
+        s_final[st_off + (int64_t)(16 * ct + 4 * g + jj) * SDV + jcol] = S[ct][jj];
   }
 }
 
@@ -516,12 +528,15 @@ hipError_t launch_t(const FwdArgs& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int64_t grid = (int64_t)p.num_seqs * p.num_heads * (p.dv / kDvs);
+  const bool tr = p.transition != nullptr;
+  const int sdv = tr ? p.dv + p.dk : p.dv;
+  const int64_t grid = (int64_t)p.num_seqs * p.num_heads * (sdv / kDvs);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, (const TI*)p.q,
                      (const TI*)p.k, (const TI*)p.v, (const TI*)p.a, (const TI*)p.b,
-                     (const TI*)p.gate, p.cu_seqlens, p.initial_state, (float*)p.o,
-                     p.final_state, p.num_heads, p.dv, p.ckpt_interval, p.ckpt,
-                     (long long)p.ckpt_capacity);
+                     tr ? nullptr : (const TI*)p.gate, p.cu_seqlens,
+                     tr ? nullptr : p.initial_state, tr ? nullptr : (float*)p.o,
+                     tr ? p.transition : p.final_state, p.num_heads, p.dv, sdv,
+                     tr ? 0 : p.ckpt_interval, p.ckpt, (long long)p.ckpt_capacity);
   return hipGetLastError();
 }
 

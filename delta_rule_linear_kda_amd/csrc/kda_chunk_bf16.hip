@@ -44,6 +44,16 @@
 // Every barrier orders LDS only (s_waitcnt lgkmcnt(0); s_barrier), so global
 // prefetches and output stores stay in flight across it.  Both groups run
 // loops of identical trip count with three barriers per iteration.
+//
+// TRANS = true is the segment-transition form of context parallelism (page
+// "[Paper Review] Kimi K3...", section "Infrastructure: how to actually run
+// trillion-scale", KDA co-design item): each sequence is a segment and the
+// state has d_v + d_k columns, the first d_v from a zero start with the real
+// values (the segment's local state S_loc), the last d_k from the identity
+// with value rows zero (U0 = 0, so each chunk applies
+// diag(Gamma_end) - Kend^T W: the product is the segment's transition M).
+// No queries, gate or outputs: Qt, Qbar, P, Qbar S, P U and the stores drop
+// out, and the final state [S_loc | M] is the result.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -237,7 +247,7 @@ struct Cfg {
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool TRANS>
 __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     chunk_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                           const uint16_t* __restrict__ v, const uint16_t* __restrict__ a,
@@ -309,7 +319,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         const int r = 16 * tau + li;
         const int rr = r < nr ? r : nr - 1;
         const uint32_t off = (uint32_t)(rr * H * DK) + 16 * wave + 4 * g;
-        rq[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(qb_ + off);
+        if constexpr (!TRANS)
+          rq[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(qb_ + off);
         rk[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(kb_ + off);
         ra[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(ab_ + off);
         rb[tau] = bb_[(uint32_t)(rr * H)];
@@ -337,8 +348,10 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         float qf[2][4], kf[2][4], cum[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-          qf[tau][0] = bf16lo(rq[tau][0]); qf[tau][1] = bf16hi(rq[tau][0]);
-          qf[tau][2] = bf16lo(rq[tau][1]); qf[tau][3] = bf16hi(rq[tau][1]);
+          if constexpr (!TRANS) {
+            qf[tau][0] = bf16lo(rq[tau][0]); qf[tau][1] = bf16hi(rq[tau][0]);
+            qf[tau][2] = bf16lo(rq[tau][1]); qf[tau][3] = bf16hi(rq[tau][1]);
+          }
           kf[tau][0] = bf16lo(rk[tau][0]); kf[tau][1] = bf16hi(rk[tau][0]);
           kf[tau][2] = bf16lo(rk[tau][1]); kf[tau][3] = bf16hi(rk[tau][1]);
           const float av[4] = {bf16lo(ra[tau][0]), bf16hi(ra[tau][0]), bf16lo(ra[tau][1]),
@@ -395,16 +408,19 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           for (int j = 0; j < 4; ++j) {
             const float x = cum[tau][j];  // log2(e) (b - p) <= 0
             const float er = exp2f_fast(x), ir = exp2f_fast(-x);
-            const float kt = kf[tau][j] * er, qt = qf[tau][j] * er, kh = kf[tau][j] * ir;
-            const float qbar = tau ? qt * e0[j] : qt;
+            const float kt = kf[tau][j] * er, kh = kf[tau][j] * ir;
+            if constexpr (!TRANS) {
+              const float qt = qf[tau][j] * er;
+              const float qbar = tau ? qt * e0[j] : qt;
+              qhb[j] = (__bf16)qt;
+              qlb[j] = (__bf16)(qt - (float)qhb[j]);
+              qbf[j] = (_Float16)qbar;
+            }
             const float kbar = tau ? kt * e0[j] : kt;
             const float kend = kh * fend[tau][j];
             ktb[j] = (__bf16)kt;
-            qhb[j] = (__bf16)qt;
-            qlb[j] = (__bf16)(qt - (float)qhb[j]);
             khh[j] = (__bf16)kh;
             khl[j] = (__bf16)(kh - (float)khh[j]);
-            qbf[j] = (_Float16)qbar;
             kbt[j * LT + 16 * tau] = f16_bits(kbar);
             ket[j * LT + 16 * tau] = f16_bits(kend);
             if (tau == 0) {  // column operand of the off-diagonal tile: Kh exp(p_1) <= 1
@@ -414,11 +430,13 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             }
           }
           *reinterpret_cast<bf16x4_t*>(sKT + r * LB + cb) = ktb;
-          *reinterpret_cast<bf16x4_t*>(sQH + r * LB + cb) = qhb;
-          *reinterpret_cast<bf16x4_t*>(sQL + r * LB + cb) = qlb;
           *reinterpret_cast<bf16x4_t*>(sKHH + r * LB + cb) = khh;
           *reinterpret_cast<bf16x4_t*>(sKHL + r * LB + cb) = khl;
-          *reinterpret_cast<f16x4_t*>(qbp + r * LB + cb) = qbf;
+          if constexpr (!TRANS) {
+            *reinterpret_cast<bf16x4_t*>(sQH + r * LB + cb) = qhb;
+            *reinterpret_cast<bf16x4_t*>(sQL + r * LB + cb) = qlb;
+            *reinterpret_cast<f16x4_t*>(qbp + r * LB + cb) = qbf;
+          }
           if (tau == 0) {
             *reinterpret_cast<bf16x4_t*>(sK1H + li * LB + cb) = k1h;
             *reinterpret_cast<bf16x4_t*>(sK1L + li * LB + cb) = k1l;
@@ -524,7 +542,9 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sA10[(4 * g + jj) * LA + li] = acc[jj];
           }
-          if constexpr (NP >= 6) {
+          if constexpr (TRANS) {
+            // no outputs: P is not needed
+          } else if constexpr (NP >= 6) {
             if (wave >= 3 && wave < 6) p_job(wave - 3);
           } else {
             if (wave == 2) {
@@ -596,7 +616,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
   } else {
     // ======================= state waves ======================================
     const int sw = wave - NP;  // owns state columns [16 sw, 16 sw + 16)
-    const int64_t st_off = (int64_t)item * DK * dvt + col0;
+    // State row length: d_v, or d_v + d_k for the transition form, whose
+    // columns [d_v, d_v + d_k) carry the transition matrix (value rows zero).
+    const int sdv = TRANS ? dvt + DK : dvt;
+    const bool tslice = TRANS && col0 >= dvt;  // a slice of transition columns
+    const int64_t st_off = (int64_t)item * DK * sdv + col0;
     // First recorded-state slot of this sequence: the slots of the sequences
     // before it come first.
     int64_t ck_off = 0;
@@ -605,8 +629,14 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     f32x4_t S[NCT];
     {
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-      const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;  // state element (row 4g, column)
-      if (s_init) {
+      const uint32_t st_lane = 4 * g * sdv + 16 * sw + li;  // state element (row 4g, column)
+      if (tslice) {  // transition columns start from the identity
+        const int mc = col0 - dvt + 16 * sw + li;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) S[ct][jj] = 16 * ct + 4 * g + jj == mc ? 1.f : 0.f;
+      } else if (s_init && !TRANS) {
         const auto sp = sbase(s_init + st_off);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -638,7 +668,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         const int r = RPW * sw + 4 * ps + g;
         const int rr = r < nr ? r : nr - 1;
         const uint32_t off = (uint32_t)(rr * H * DK) + CPL * li;
-        nq_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(qb_ + off);
+        if constexpr (!TRANS)
+          nq_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(qb_ + off);
         nk_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(kb_ + off);
       }
     };
@@ -710,7 +741,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       };
 
       // ---- E: sigmoid(gate) of c; norms of chunk it; U0, U = U0 - W S, O = Qbar S
-      if (act && gate) {
+      if (!TRANS && act && gate) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           rg[j] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
@@ -723,16 +754,17 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           float sq = 0.f, sk = 0.f;
 #pragma unroll
           for (int e = 0; e < CPL / 2; ++e) {
-            const float q0 = bf16lo(nq_[ps][e]), q1 = bf16hi(nq_[ps][e]);
+            const float q0 = TRANS ? 0.f : bf16lo(nq_[ps][e]);
+            const float q1 = TRANS ? 0.f : bf16hi(nq_[ps][e]);
             const float k0 = bf16lo(nk_[ps][e]), k1 = bf16hi(nk_[ps][e]);
-            sq += q0 * q0 + q1 * q1;
+            if constexpr (!TRANS) sq += q0 * q0 + q1 * q1;
             sk += k0 * k0 + k1 * k1;
           }
-          sq = row_sum16(sq);
+          if constexpr (!TRANS) sq = row_sum16(sq);
           sk = row_sum16(sk);
           if (li == 0) {
             const int r = RPW * sw + 4 * ps + g;
-            nqo[r] = rsqrtf(sq + kNormEps);
+            if constexpr (!TRANS) nqo[r] = rsqrtf(sq + kNormEps);
             nko[r] = rsqrtf(sk + kNormEps);
           }
         }
@@ -740,7 +772,10 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       if (act) {
         const float* xb = bX(p);
         const float* be = bBeta(p);
-        {
+        if (tslice) {  // no value rows: U0 = 0
+          U[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          U[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
           float rr[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -766,14 +801,18 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
             U[rt] = mma_f16(lds4x2<f16x8_t>(wp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk, U[rt]);
-            O[rt] = mma_f16(lds4x2<f16x8_t>(qbp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk, O[rt]);
+            if constexpr (!TRANS)
+              O[rt] = mma_f16(lds4x2<f16x8_t>(qbp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk,
+                              O[rt]);
           }
         }
-        const float* nq = bNQ(p);
+        if constexpr (!TRANS) {
+          const float* nq = bNQ(p);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float4 nr = *reinterpret_cast<const float4*>(nq + 16 * rt + 4 * g);
-          O[rt][0] *= nr.x; O[rt][1] *= nr.y; O[rt][2] *= nr.z; O[rt][3] *= nr.w;
+          for (int rt = 0; rt < 2; ++rt) {
+            const float4 nr = *reinterpret_cast<const float4*>(nq + 16 * rt + 4 * g);
+            O[rt][0] *= nr.x; O[rt][1] *= nr.y; O[rt][2] *= nr.z; O[rt][3] *= nr.w;
+          }
         }
       }
       lds_barrier();  // B1
@@ -792,14 +831,16 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           us[0] = uu[0] * n0.x; us[1] = uu[1] * n0.y; us[2] = uu[2] * n0.z; us[3] = uu[3] * n0.w;
           us[4] = uu[4] * n1.x; us[5] = uu[5] * n1.y; us[6] = uu[6] * n1.z; us[7] = uu[7] * n1.w;
           uf = pack_f16x8(us);
-          split_bf16x8(uu, uh, ul);
+          if constexpr (!TRANS) split_bf16x8(uu, uh, ul);
         }
-        const uint16_t* ph = bPH(p);
-        const uint16_t* pl = bPL(p);
+        if constexpr (!TRANS) {
+          const uint16_t* ph = bPH(p);
+          const uint16_t* pl = bPL(p);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const int off = (16 * rt + li) * LT + 4 * g;
-          O[rt] = mma_x3(lds4x2<bf16x8_t>(ph + off), lds4x2<bf16x8_t>(pl + off), uh, ul, O[rt]);
+          for (int rt = 0; rt < 2; ++rt) {
+            const int off = (16 * rt + li) * LT + 4 * g;
+            O[rt] = mma_x3(lds4x2<bf16x8_t>(ph + off), lds4x2<bf16x8_t>(pl + off), uh, ul, O[rt]);
+          }
         }
         const float* ge = bGE(p);
         const uint16_t* kep = bKE(p);
@@ -814,7 +855,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         // Record the state after the first `done` tokens when that is a
         // multiple of the recording interval.
         const int64_t done = (int64_t)kC * it;
-        if (ckpt_iv > 0 && done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
+        if (!TRANS && ckpt_iv > 0 && done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
           const int64_t slot = ck_off + done / ckpt_iv - 1;
           if (slot < ckpt_cap) {
             const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
@@ -836,52 +877,39 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       {
         const int64_t c_this = tok_beg + (int64_t)kC * (it < nch ? it : nch - 1);
         const int64_t c_next = tok_beg + (int64_t)kC * (it + 1 < nch ? it + 1 : nch - 1);
-        load_g(c_this, g, jcol);  // chunk it's gate and v, for the chain at it+1
-        load_v(c_this, g, jcol);
-        load_qk(c_next, g, li);   // norms at it+1
+        if constexpr (!TRANS) load_g(c_this, g, jcol);  // chunk it's gate and v, for it+1
+        if (!tslice) load_v(c_this, g, jcol);
+        load_qk(c_next, g, li);  // norms at it+1
       }
-      if (act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
+      if (!TRANS && act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
       lds_barrier();  // B3
     }
 
     if (s_final) {
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-      const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
+      const uint32_t st_lane = 4 * g * sdv + 16 * sw + li;
       const auto sp = sbase(s_final + st_off);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj];
+        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * sdv] = S[ct][jj];
     }
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool TRANS>
 hipError_t launch_cfg(const FwdArgs& p, int nsl, hipStream_t stream) {
-  auto kern = chunk_fwd_bf16_kernel<DK, DV>;  // LDS is static (Cfg<DK, DV>::bytes)
+  auto kern = chunk_fwd_bf16_kernel<DK, DV, TRANS>;  // LDS is static (Cfg<DK, DV>::bytes)
   const int64_t items = (int64_t)p.num_seqs * p.num_heads;
   const int64_t grid = (items + 7) / 8 * 8 * nsl;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg<DK, DV>::NT), 0, stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
-                     (const uint16_t*)p.a, (const uint16_t*)p.b, (const uint16_t*)p.gate,
-                     p.cu_seqlens, p.initial_state, (float*)p.o, p.final_state, p.num_heads,
-                     (int)items, p.dv, nsl, p.ckpt_interval, p.ckpt, (long long)p.ckpt_capacity);
+                     (const uint16_t*)p.a, (const uint16_t*)p.b,
+                     TRANS ? nullptr : (const uint16_t*)p.gate, p.cu_seqlens,
+                     TRANS ? nullptr : p.initial_state, TRANS ? nullptr : (float*)p.o,
+                     TRANS ? p.transition : p.final_state, p.num_heads, (int)items, p.dv, nsl,
+                     TRANS ? 0 : p.ckpt_interval, p.ckpt, (long long)p.ckpt_capacity);
   return hipGetLastError();
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
 }
 
 }  // namespace
@@ -889,16 +917,28 @@ int device_cus() {
 // One workgroup per (sequence, head) when that fills the GPU; with fewer
 // items than half the compute units, d_v = 128 is split into two 64-column
 // slices per item (the key-side work is repeated, the state work halves).
+//
+// The transition form has state rows of d_v + d_k columns: 64-column slices
+// while they fit the GPU in one round, otherwise (d_k = d_v = 128) two
+// 128-column slices per item.
 hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream) {
   const int64_t items = (int64_t)p.num_seqs * p.num_heads;
   if (items == 0) return hipSuccess;
+  if (p.transition) {
+    const int nsl64 = (p.dv + p.dk) / 64;
+    if (p.dk == 128) {
+      if (p.dv == 128 && nsl64 * items > device_cus()) return launch_cfg<128, 128, true>(p, 2, stream);
+      return launch_cfg<128, 64, true>(p, nsl64, stream);
+    }
+    return launch_cfg<64, 64, true>(p, nsl64, stream);
+  }
   const bool split = p.dv == 128 && 2 * items <= device_cus();
   if (p.dk == 128) {
-    if (p.dv == 128 && !split) return launch_cfg<128, 128>(p, 1, stream);
-    return launch_cfg<128, 64>(p, p.dv / 64, stream);
+    if (p.dv == 128 && !split) return launch_cfg<128, 128, false>(p, 1, stream);
+    return launch_cfg<128, 64, false>(p, p.dv / 64, stream);
   }
-  if (p.dv == 128 && !split) return launch_cfg<64, 128>(p, 1, stream);
-  return launch_cfg<64, 64>(p, p.dv / 64, stream);
+  if (p.dv == 128 && !split) return launch_cfg<64, 128, false>(p, 1, stream);
+  return launch_cfg<64, 64, false>(p, p.dv / 64, stream);
 }
 
 }  // namespace kda

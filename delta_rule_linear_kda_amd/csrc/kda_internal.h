@@ -29,9 +29,31 @@ struct FwdArgs {
   int32_t ckpt_interval = 0;
   float* ckpt = nullptr;
   int64_t ckpt_capacity = 0;
+  // Transition form (kda_segment_transition): when set, each sequence is a
+  // segment and [S_loc | M] rows of d_v + d_k columns are written here,
+  // [N, H, dk, dv + dk]; gate, initial_state, o, final_state and the
+  // recorded states are not used.
+  float* transition = nullptr;
 };
 
+struct ComposeArgs {
+  int32_t num_seqs, num_heads, dk, dv;
+  const int32_t* seg_offsets;   // [N + 1], device
+  const float* trans;           // [segments, H, dk, dv + dk]
+  const float* initial_state;   // [N, H, dk, dv] or null (zero)
+  float* seg_start;             // [segments, H, dk, dv] or null
+  float* final_state;           // [N, H, dk, dv] or null
+};
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
+// kda_segments.hip
+hipError_t launch_segment_table(const int32_t* cu_seqlens, int32_t num_seqs, int32_t seg_len,
+                                int32_t cap, int32_t* seg_cu, int32_t* seg_off,
+                                hipStream_t stream);
+hipError_t launch_compose(const ComposeArgs& p, hipStream_t stream);
 hipError_t launch_fwd_chunked(const FwdArgs& p, hipStream_t stream);
 // bf16-input kernel (kda_chunk_bf16.hip); launch_fwd_chunked dispatches to it.
 hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream);

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2u
+#define KDA_ABI_VERSION 3u
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -148,6 +148,76 @@ KDA_API kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, c
  * offsets). */
 KDA_API kda_status kda_fwd_ckpt_count(int32_t num_seqs, const int32_t* cu_seqlens_host,
                               int32_t ckpt_interval, int64_t* count);
+
+/* ---- Segment-transition form (context parallelism) -----------------------
+ * KDA context parallelism (page "[Paper Review] Kimi K3...", section
+ * "Infrastructure: how to actually run trillion-scale", KDA co-design item)
+ * computes the state transition of every segment of a sequence on its own and
+ * composes the transitions associatively, so segments proceed in parallel and
+ * only fixed-size states cross segment boundaries.  For one segment and head,
+ * the recurrence is affine in its start state S0:
+ *     S_end = M S0 + S_loc
+ * with M (dk x dk) the product of the per-token factors
+ * (I - beta kh kh^T) Diag(alpha) over the segment, latest on the left, and
+ * S_loc (dk x dv) the state the segment reaches from S0 = 0.
+ */
+
+/* Transitions of segments given as packed sequences (each sequence of
+ * cu_seqlens is one segment; shape as for kda_fwd_chunked; gate, q and the
+ * initial state play no part).
+ *   k, a [T, H, dk]; v [T, H, dv]; b [T, H]   in_dtype
+ *   trans [N, H, dk, dv + dk] fp32 out: row r of (n, h) holds S_loc[r, 0..dv)
+ *         followed by M[r, 0..dk).  An empty segment gives S_loc = 0, M = I.
+ * trans must not overlap any input.
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, HIP. */
+KDA_API kda_status kda_segment_transition(const kda_shape* shape, const void* k, const void* v,
+                                          const void* a, const void* b,
+                                          const int32_t* cu_seqlens, float* trans, void* stream);
+
+/* Composition of segment transitions, in token order, for every sequence n
+ * and head h.  Sequence n owns segments seg_offsets[n] .. seg_offsets[n+1]-1:
+ *     S = initial_state[n, h] (or 0);  for each segment j:  S <- M_j S + S_loc_j
+ *   seg_offsets [num_seqs + 1] int32, device; 0 = seg_offsets[0] <=
+ *               ... <= seg_offsets[num_seqs] <= num_segments (caller's duty)
+ *   trans       [num_segments, H, dk, dv + dk] fp32 (kda_segment_transition)
+ *   initial_state [num_seqs, H, dk, dv] fp32 or NULL (zero)
+ *   seg_start   [num_segments, H, dk, dv] fp32 out or NULL: S before segment j
+ *   final_state [num_seqs, H, dk, dv] fp32 out or NULL: S after the last
+ *               segment; may be exactly initial_state (in place).
+ * Outputs must not overlap inputs or each other otherwise.
+ * Errors: NULL_POINTER, BAD_SHAPE, MISALIGNED, ALIAS, HIP. */
+KDA_API kda_status kda_segment_compose(int32_t num_seqs, int32_t num_segments, int32_t num_heads,
+                                       int32_t dk, int32_t dv, const int32_t* seg_offsets,
+                                       const float* trans, const float* initial_state,
+                                       float* seg_start, float* final_state, void* stream);
+
+/* Bytes of workspace kda_fwd_chunked_kcp needs for `shape` and segment_len
+ * (0 when the automatic choice is the direct form).
+ * Errors: NULL_POINTER, BAD_SHAPE (bad segment_len, too many segments),
+ * BAD_DTYPE. */
+KDA_API kda_status kda_fwd_kcp_workspace_bytes(const kda_shape* shape, int32_t segment_len,
+                                               size_t* bytes);
+
+/* kda_fwd_chunked evaluated in segment-transition form on one GPU: every
+ * sequence is cut into segments of segment_len tokens (the last may be
+ * shorter); the transitions of all segments are formed in parallel, composed
+ * in order, and every segment is then run through the chunked forward from its
+ * true start state.  For few (sequence, head) pairs and long sequences this
+ * keeps many more compute units busy than the direct form.  Results equal
+ * kda_fwd_chunked up to rounding (not bitwise).
+ *   segment_len  a positive multiple of 64, or 0: chosen from the shape and
+ *                the current device (the direct form when segmenting would
+ *                not pay; then no workspace is used)
+ *   workspace    kda_fwd_kcp_workspace_bytes(shape, segment_len) bytes,
+ *                16-byte aligned, disjoint from every other argument
+ * Everything else as for kda_fwd_chunked.
+ * Errors: as kda_fwd_chunked; BAD_SHAPE also for a bad segment_len. */
+KDA_API kda_status kda_fwd_chunked_kcp(const kda_shape* shape, const void* q, const void* k,
+                                       const void* v, const void* a, const void* b,
+                                       const void* gate, const int32_t* cu_seqlens,
+                                       const float* initial_state, void* o, float* final_state,
+                                       int32_t segment_len, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* One decode step: one new token for each of N independent sequences, the
  * recurrent update the pages' serving section runs with dedicated decode

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     for code in range(8):
         assert kda.status_str(code).startswith(kda.STATUS[code])
     assert kda.status_str(99) == "unknown kda_status"
@@ -173,3 +173,105 @@ def test_ckpt_count():
         assert e.value.code == SHAPE
     out = ctypes.c_int64(0)
     assert kda.lib().kda_fwd_ckpt_count(2, None, 512, ctypes.byref(out)) == NULLP
+
+
+# --- segment-transition form -------------------------------------------------
+def _kcp_layout_bytes(N, T, H, dk, dv, L):
+    up = lambda x: (x + 255) // 256 * 256
+    cap = T // L + N
+    return (up((cap + 1) * 4) + up((N + 1) * 4) + up(cap * H * dk * (dv + dk) * 4)
+            + up(cap * H * dk * dv * 4))
+
+
+def test_kcp_workspace_query():
+    # explicit segment length: table, offsets, [S_loc | M] and start states
+    assert kda.kcp_workspace_bytes(1, 1 << 20, 12, 128, 128, 4096) == \
+        _kcp_layout_bytes(1, 1 << 20, 12, 128, 128, 4096)
+    assert kda.kcp_workspace_bytes(3, 1000, 2, 64, 128, 128) == \
+        _kcp_layout_bytes(3, 1000, 2, 64, 128, 128)
+    # automatic: many (sequence, head) pairs keep the direct form (no workspace)
+    assert kda.kcp_workspace_bytes(1, 1 << 20, 96, 128, 128, 0) == 0
+    assert kda.kcp_workspace_bytes(4, 4096, 2, 128, 128, 0) == 0      # too short to segment
+    for bad in (-64, 100, 32):
+        with pytest.raises(kda.KdaError) as e:
+            kda.kcp_workspace_bytes(1, 1 << 20, 12, 128, 128, bad)
+        assert e.value.code == SHAPE
+    with pytest.raises(kda.KdaError) as e:  # more segments than the kernels index
+        kda.kcp_workspace_bytes(1, 1 << 30, 64, 128, 128, 64)
+    assert e.value.code == SHAPE
+    out = ctypes.c_size_t(0)
+    assert kda.lib().kda_fwd_kcp_workspace_bytes(None, 0, ctypes.byref(out)) == NULLP
+    s = good_shape()
+    assert kda.lib().kda_fwd_kcp_workspace_bytes(ctypes.byref(s), 0, None) == NULLP
+
+
+WSP = BASE + 12 * (1 << 36)
+
+
+def fwd_kcp(shape, seg=128, ws=WSP, ws_bytes=1 << 34, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_fwd_chunked_kcp(
+        ctypes.byref(shape), args["q"], args["k"], args["v"], args["a"], args["b"], args["gate"],
+        args["cu"], args["s0"], args["o"], args["sf"], seg, ws, ws_bytes, None)
+
+
+def test_kcp_rejects():
+    s = good_shape()
+    need = _kcp_layout_bytes(2, 300, 4, 128, 128, 128)
+    assert fwd_kcp(good_shape(dk=96)) == SHAPE
+    assert fwd_kcp(s, seg=96) == SHAPE
+    assert fwd_kcp(s, seg=-128) == SHAPE
+    assert fwd_kcp(s, ws=None) == WS
+    assert fwd_kcp(s, ws_bytes=need - 1) == WS
+    assert fwd_kcp(s, ws=WSP + 8) == MISAL
+    assert fwd_kcp(s, ws=P["q"]) == ALIAS             # workspace over an input
+    assert fwd_kcp(s, ws=P["o"] - 64) == ALIAS        # workspace runs into the output
+    assert fwd_kcp(s, q=None) == NULLP                # the forward's own checks apply
+    assert fwd_kcp(s, o=P["k"]) == ALIAS
+    assert fwd_kcp(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+TRP = BASE + 13 * (1 << 36)
+
+
+def seg_trans(shape, trans=TRP, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_segment_transition(ctypes.byref(shape), args["k"], args["v"], args["a"],
+                                            args["b"], args["cu"], trans, None)
+
+
+def test_segment_transition_rejects():
+    s = good_shape()
+    assert seg_trans(good_shape(dv=48)) == SHAPE
+    assert seg_trans(good_shape(in_dtype=3)) == DTYPE
+    assert seg_trans(s, trans=None) == NULLP
+    for name in ["k", "v", "a", "b", "cu"]:
+        assert seg_trans(s, **{name: None}) == NULLP, name
+    assert seg_trans(s, trans=TRP + 4) == MISAL
+    assert seg_trans(s, k=P["k"] + 8) == MISAL
+    assert seg_trans(s, trans=P["v"]) == ALIAS
+    assert seg_trans(s, trans=P["cu"] - 64) == ALIAS
+    assert seg_trans(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+def compose(N=2, S=5, H=4, dk=128, dv=128, off=P["cu"], trans=TRP, s0=P["s0"],
+            start=BASE + 14 * (1 << 36), sf=P["sf"]):
+    return kda.lib().kda_segment_compose(N, S, H, dk, dv, off, trans, s0, start, sf, None)
+
+
+def test_segment_compose_rejects():
+    assert compose(dk=32) == SHAPE
+    assert compose(N=-1) == SHAPE
+    assert compose(S=-1) == SHAPE
+    assert compose(H=0) == SHAPE
+    assert compose(off=None) == NULLP
+    assert compose(trans=None) == NULLP
+    assert compose(off=P["cu"] + 2) == MISAL
+    assert compose(trans=TRP + 8) == MISAL
+    assert compose(start=TRP) == ALIAS                 # start states over the transitions
+    assert compose(start=P["sf"]) == ALIAS             # over the final states
+    assert compose(sf=TRP + 1024) == ALIAS
+    assert compose(sf=P["s0"] + 16) == ALIAS           # partial overlap with the start
+    assert compose(N=0) == OK

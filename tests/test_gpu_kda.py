@@ -384,3 +384,199 @@ def test_fwd_config3_full_size():
     es = kc.rel_err(s_b.cpu().numpy(), sf.cpu().numpy())
     print(f"    split at {half}: err o={eo:.3e} state={es:.3e}", flush=True)
     assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
+
+
+# --- segment-transition form (context parallelism on one GPU) ---------------
+def _shift_logits(arr, delta):
+    """Decay logits a + delta, as the generator's storage type (fp32, or bf16
+    bits rounded to nearest even).  Weak decay (delta << 0) keeps the
+    transition M of a long segment O(1), so start states matter."""
+    if arr.dtype == np.float32:
+        return (arr + np.float32(delta)).astype(np.float32)
+    f = (synth.to_f64(arr) + delta).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+SEG_LENS = [300, 17, 0, 129, 64, 1]
+
+
+@pytest.mark.parametrize("base,dk,dv,heads", [
+    (1, 128, 128, 3), (1, 128, 128, 20), (1, 128, 64, 3), (1, 64, 128, 3), (1, 64, 64, 3),
+    (0, 64, 64, 2), (0, 128, 128, 2)])
+def test_segment_transition(base, dk, dv, heads):
+    """[S_loc | M] of every segment against the oracle's dense-factor product,
+    with weak decay so that M is O(1).  heads=20 at d=128 takes the
+    128-column-slice launch, heads=3 the 64-column one."""
+    _require_gpu()
+    w = kc.custom_workload(synth.WORKLOADS[base], dk=dk, dv=dv, heads=heads)
+    print(f"[case] transition {w.name} dk={dk} dv={dv} H={heads} lens={SEG_LENS}", flush=True)
+    T = sum(SEG_LENS)
+    cu = np.concatenate([[0], np.cumsum(SEG_LENS)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    x["a"] = _shift_logits(x["a"], -10.0)
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    tr = kda.segment_transition(dev["k"], dev["v"], dev["a"], dev["b"],
+                                torch.from_numpy(cu.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    tr = tr.cpu().numpy()
+    xr = {n: kc.f64(x[n]) for n in x}
+    ref = oracle.segment_transition(xr["k"], xr["v"], xr["a"], xr["b"], cu)
+    el = kc.rel_err(tr[..., :dv], ref[..., :dv])
+    em = kc.rel_err(tr[..., dv:], ref[..., dv:])
+    print(f"    err S_loc={el:.3e} M={em:.3e} (M rms {np.sqrt(np.mean(ref[..., dv:] ** 2)):.2f})",
+          flush=True)
+    assert np.all(np.isfinite(tr))
+    assert el <= tol(w) and em <= tol(w)
+    # the empty segment is exact: S_loc = 0, M = I
+    assert np.all(tr[2, :, :, :dv] == 0.0)
+    assert np.array_equal(tr[2, :, :, dv:], np.broadcast_to(np.eye(dk, dtype=np.float32),
+                                                            (heads, dk, dk)))
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+def test_segment_compose(dk, dv):
+    """Composition of given transitions (the oracle's, rounded to fp32: the
+    same bits on both sides) against the oracle's composition, per sequence
+    in order, including a sequence without segments."""
+    _require_gpu()
+    print(f"[case] compose dk={dk} dv={dv}", flush=True)
+    H = 3
+    rng = np.random.default_rng(7)
+    cuts = [0, 40, 41, 200, 330, 480, 600]  # 6 segments; sequences own [0,2), [2,2), [2,6)
+    T = cuts[-1]
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    a = rng.standard_normal((T, H, dk)) - 9.0
+    b = rng.standard_normal((T, H))
+    tr = oracle.segment_transition(k, v, a, b, cuts).astype(np.float32)
+    off = np.array([0, 2, 2, 6])
+    s0 = (0.3 * rng.standard_normal((3, H, dk, dv))).astype(np.float32)
+    st_ref, fin_ref = oracle.segment_compose(off, tr, dv, s0)
+    st, fin = kda.segment_compose(torch.from_numpy(off.astype(np.int32)).cuda(),
+                                  torch.from_numpy(tr).cuda(), dv, torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    es = kc.rel_err(st.cpu().numpy(), st_ref)
+    ef = kc.rel_err(fin.cpu().numpy(), fin_ref)
+    print(f"    err starts={es:.3e} final={ef:.3e}", flush=True)
+    assert es <= 1e-5 and ef <= 1e-5
+    assert np.array_equal(fin.cpu().numpy()[1], s0[1])  # no segments: final = initial
+
+
+@pytest.mark.parametrize("base,weak,seg", [(1, True, 128), (1, False, 64), (0, True, 128),
+                                           (1, True, 4096)])
+def test_fwd_kcp(base, weak, seg):
+    """kda_fwd_chunked_kcp against the oracle's token recurrence: o and the
+    final state, ragged sequences (one empty, one shorter than a segment),
+    initial states and the output gate."""
+    _require_gpu()
+    W = synth.WORKLOADS[base]
+    w = kc.custom_workload(W, heads=3, dk=128 if base else 64, dv=128 if base else 64,
+                           s0_std=0.5)
+    lens = [1000, 17, 0, 300, 129]
+    print(f"[case] kcp {w.name} weak={weak} seg={seg} lens={lens}", flush=True)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    if weak:
+        x["a"] = _shift_logits(x["a"], -10.0)
+    s0 = kc.host_state(w, len(lens))
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    o, sf = kda.fwd_chunked_kcp(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                                torch.from_numpy(cu.astype(np.int32)).cuda(),
+                                torch.from_numpy(s0).cuda(), segment_len=seg)
+    torch.cuda.synchronize()
+    xr = {n: kc.f64(x[n]) for n in x}
+    o_ref, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], xr["gate"], cu, s0)
+    eo, es = kc.rel_err(o.cpu().numpy(), o_ref), kc.rel_err(sf.cpu().numpy(), sf_ref)
+    print(f"    err o={eo:.3e} state={es:.3e} (tol {tol(w):.0e})", flush=True)
+    assert eo <= tol(w) and es <= tol(w)
+
+
+def test_fwd_kcp_in_place_state():
+    """final_state may be the initial_state tensor itself."""
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=2, s0_std=0.5)
+    lens = [700, 0, 260]
+    print(f"[case] kcp in place lens={lens}", flush=True)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    x["a"] = _shift_logits(x["a"], -10.0)
+    s0 = kc.host_state(w, len(lens))
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    st = torch.from_numpy(s0).cuda()
+    kda.fwd_chunked_kcp(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                        torch.from_numpy(cu.astype(np.int32)).cuda(), st, final_state=st,
+                        segment_len=192)
+    torch.cuda.synchronize()
+    xr = {n: kc.f64(x[n]) for n in x}
+    _, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], xr["gate"], cu, s0)
+    es = kc.rel_err(st.cpu().numpy(), sf_ref)
+    print(f"    err state={es:.3e}", flush=True)
+    assert es <= kc.TOL_BF16
+
+
+def test_fwd_kcp_auto_segments():
+    """The automatic segment length at a shape where it segments (12 heads,
+    one 131,072-token sequence: the direct form would run 24 workgroups).
+    Heads 0, 5 and 11 against the oracle over the whole sequence."""
+    _require_gpu()
+    w = kc.custom_workload(W1, heads=12, s0_std=0.02)
+    T = 131072
+    ws = kda.kcp_workspace_bytes(1, T, 12, 128, 128, 0)
+    print(f"[case] kcp auto T={T} H=12 workspace={ws}", flush=True)
+    assert ws > 0  # the automatic choice segments here
+    dev = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    s0 = kc.device_state(w, 1)
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    o, sf = kda.fwd_chunked_kcp(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                                cu, s0)
+    torch.cuda.synchronize()
+    for h in (0, 5, 11):
+        x = {nm: kc.host_head_slice(w, nm, 0, T, h) for nm in synth.TOKEN_TENSORS}
+        xr = {nm: kc.f64(x[nm])[:, None] for nm in x}
+        xr["b"] = kc.f64(x["b"])[:, None]
+        s0h = kc.host_state_item(w, 0, h)[None, None].astype(np.float64)
+        o_ref, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], xr["gate"],
+                                   [0, T], s0h)
+        eo = kc.rel_err(o[:, h].cpu().numpy(), o_ref[:, 0])
+        es = kc.rel_err(sf[0, h].cpu().numpy(), sf_ref[0, 0])
+        print(f"    head {h}: err o={eo:.3e} state={es:.3e}", flush=True)
+        assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
+
+
+def test_fwd_kcp_long_context_share():
+    """One GPU's share of the 1,048,576-token workload under 8-way head
+    sharding (12 heads) in segment form, at full size: the first 4096 output
+    rows of heads 0 and 11 against the oracle, and the whole output and final
+    state against the direct form (both are the same recurrence; to the bf16
+    bound).  With this workload's decay logits (std 3, mean decay e^-2.5 per
+    token) a start state's effect underflows fp32 within a few hundred
+    tokens, so the transitions of these long segments are exactly zero and
+    the two forms agree bitwise; the weak-decay cases above exercise the
+    composition itself."""
+    _require_gpu()
+    w = kc.custom_workload(W3, heads=12)
+    T = w.seq_lens()[0]
+    print(f"[case] kcp long-context share T={T} H=12", flush=True)
+    dev = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    args = tuple(dev[n] for n in ("q", "k", "v", "a", "b", "gate"))
+    o, sf = kda.fwd_chunked_kcp(*args, cu)
+    torch.cuda.synchronize()
+    t_s = 4096
+    for h in (0, 11):
+        x = {nm: kc.host_head_slice(w, nm, 0, t_s, h) for nm in synth.TOKEN_TENSORS}
+        xr = {nm: kc.f64(x[nm])[:, None] for nm in x}
+        xr["b"] = kc.f64(x["b"])[:, None]
+        o_ref, _ = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], xr["gate"], [0, t_s])
+        eo = kc.rel_err(o[:t_s, h].cpu().numpy(), o_ref[:, 0])
+        print(f"    head {h}, tokens [0, {t_s}): err o={eo:.3e}", flush=True)
+        assert eo <= kc.TOL_BF16
+    o_d, sf_d = kda.fwd_chunked(*args, cu)
+    torch.cuda.synchronize()
+    eo = _rel_err_device(o, o_d)
+    es = kc.rel_err(sf.cpu().numpy(), sf_d.cpu().numpy())
+    print(f"    segment form vs direct form: err o={eo:.3e} state={es:.3e}", flush=True)
+    assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
