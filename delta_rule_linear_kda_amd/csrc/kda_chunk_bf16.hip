@@ -646,10 +646,6 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      // Let the initial state arrive now: otherwise every use of S inside the
-      // loop carries a wait on the memory counter that also covers the
-      // loop's own stores.
-      __builtin_amdgcn_s_waitcnt(0);
     }
     typedef __attribute__((ext_vector_type(CPL / 2))) uint32_t uvec_t;
     constexpr int NPASS = RPW / 4;
@@ -702,11 +698,12 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     };
     // Gated output of chunk c (its O accumulators), stored fp32 through a
     // buffer resource whose range ends after the chunk's last valid row: all
-    // eight stores always issue (so the in-order count of outstanding memory
-    // operations is exact for the waits that follow), and the hardware drops
-    // the padding rows of a partial chunk.
-    auto epilogue = [&](int64_t c0, int g, int jcol) {
-      const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+    // eight stores always issue, on every iteration (so the in-order count of
+    // outstanding memory operations is the same on every path and the waits
+    // that follow never have to cover them), and the hardware drops the
+    // padding rows of a partial chunk, or every row when there is no chunk to
+    // store yet (nrows = 0, first iteration).
+    auto epilogue = [&](int64_t c0, int nrows, int g, int jcol) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           o + (c0 * H + h) * dvt + col0, 0, nrows * H * dvt * 4, kBufferRsrcFlags);
       const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
@@ -723,6 +720,13 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       const int lane = threadIdx.x % 64;
       load_qk(tok_beg, lane / 16, lane % 16);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rv[j] = rgr[j] = 0u;  // first read before their first load
+    // Let the initial state and chunk 0's rows arrive before the loop: the
+    // memory counter completes in order, so a load still pending on entry
+    // would make the compiler's loop-invariant waits count the loop's own
+    // output stores as well (every iteration would wait for them).
+    __builtin_amdgcn_s_waitcnt(0);
     // Iteration it: the chain works on chunk c = it - 1.
     for (int it = 0; nch > 0 && it <= nch; ++it) {
       const bool act = it >= 1;
@@ -741,12 +745,18 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       };
 
       // ---- E: sigmoid(gate) of c; norms of chunk it; U0, U = U0 - W S, O = Qbar S
-      if (!TRANS && act && gate) {
+      // The consumers of the registers loaded in the previous W stage run on
+      // every iteration (at it = 0 the gate words are unused, at it = nch the
+      // norms of the clamped chunk go to the LDS buffer no one reads then), so
+      // every path waits for those loads at the same place and no later
+      // reuse of their registers needs a drain of the memory counter, which
+      // would also wait for the output stores.
+      if (!TRANS) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           rg[j] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
       }
-      if (it < nch) {
+      {
         float* nqo = bNQ(it & 1);
         float* nko = bNK(it & 1);
 #pragma unroll
@@ -869,11 +879,19 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       }
       lds_barrier();  // B2
 
-      // ---- W: requests for the next iteration, then chunk c's gated output ----
-      // The requests are unconditional (chunk index clamped to the last
-      // chunk), so they land directly in the carried registers, and they are
-      // issued before the stores, so the next stage's waits for them never
-      // cover the stores.
+      // ---- W: chunk c's gated output, then the requests for the next iteration
+      // The stores issue first and the loads last, so no instruction after a
+      // load can touch its destination registers (which would make it wait
+      // for the load, and, the memory counter being in order, for everything
+      // before it).  The requests are unconditional (chunk index clamped to
+      // the last chunk), so they land directly in the carried registers; the
+      // next stage's waits for them also cover these stores, issued just
+      // before and no slower to complete.
+      if constexpr (!TRANS) {
+        const int64_t c_out = tok_beg + (int64_t)kC * (act ? it - 1 : 0);
+        const int n_out = act ? (int)(tok_end - c_out < kC ? tok_end - c_out : kC) : 0;
+        epilogue(c_out, n_out, g, jcol);
+      }
       {
         const int64_t c_this = tok_beg + (int64_t)kC * (it < nch ? it : nch - 1);
         const int64_t c_next = tok_beg + (int64_t)kC * (it + 1 < nch ? it + 1 : nch - 1);
@@ -881,7 +899,6 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         if (!tslice) load_v(c_this, g, jcol);
         load_qk(c_next, g, li);  // norms at it+1
       }
-      if (!TRANS && act) epilogue(tok_beg + (int64_t)kC * (it - 1), g, jcol);
       lds_barrier();  // B3
     }
 
