@@ -19,10 +19,13 @@ After the timed steps (outside them), ``kcp_share`` reports one GPU's share of
 the same sequence under 8-way head sharding -- 12 heads, 1 x 1,048,576 tokens
 -- through kda_fwd_chunked (direct form: 24 workgroups) and through
 kda_fwd_chunked_kcp (segment-transition form with the automatic segment
-length), each the mean of 3 launches after one warm-up.
+length), each the mean of 3 launches after one warm-up, and ``layer`` times
+the layer operations around the core (short convolution -> Swish -> L2 on q,
+RMSNorm -> sigmoid gate on o) on the same resident tensors.
 
 Profiling helpers (not part of a timed run):
   --no-kcp-share / --only-kcp-share   skip, or run only, the 12-head comparison;
+  --no-layer / --only-layer           skip, or run only, the layer operations;
   --copy-probe          after the timed steps, run a plain 2 GiB device copy so
                         that a hardware-counter run of this same command can
                         scale FETCH_SIZE / WRITE_SIZE against known bytes;
@@ -140,6 +143,42 @@ def kcp_share(T: int, stream, reps: int = 3) -> dict:
             "workspace_bytes": ws_bytes}
 
 
+def layer_ops(q, gate, o, stream, reps: int = 5) -> dict:
+    """The layer operations around the core on the resident long-context
+    tensors: the short convolution -> Swish -> L2 front on q (width 4,
+    synthetic weights) and the RMSNorm -> sigmoid gate back on o (in place).
+    Algorithmic bytes: front 2 x 2 B per element (bf16 in and out), back
+    4 + 2 + 4 B per element (fp32 o read and written, bf16 gate read)."""
+    import torch
+
+    import delta_rule_linear_kda_amd as kda
+
+    T, H, d = q.shape
+    wt = torch.full((H, d, 4), 0.25, dtype=torch.float32, device=q.device)
+    nw = torch.ones(o.shape[2], dtype=torch.float32, device=q.device)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=q.device)
+    y = torch.empty_like(q)
+
+    def timed(fn) -> float:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_f = timed(lambda: kda.shortconv_swish_l2(q, wt, cu, out=y, stream=stream))
+    ms_b = timed(lambda: kda.rmsnorm_gate(o, gate, nw, 1e-6, out=o, stream=stream))
+    bf, bb = 4.0 * q.numel(), 10.0 * o.numel()
+    return {"workload": f"{T} tokens x {H} heads x d={d}, bf16 q and gate, fp32 o",
+            "shortconv_swish_l2": {"ms": ms_f, "GB_per_s": bf / ms_f / 1e6,
+                                   "frac_hbm": bf / ms_f / 1e6 / HBM_PEAK_GBS},
+            "rmsnorm_gate": {"ms": ms_b, "GB_per_s": bb / ms_b / 1e6,
+                             "frac_hbm": bb / ms_b / 1e6 / HBM_PEAK_GBS}}
+
+
 def _sha256(path: str) -> str:
     """sha256 of a C/HIP source's code: comments removed and whitespace
     collapsed, so that editing a comment does not invalidate counters taken
@@ -236,6 +275,10 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kcp-share", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip timing the layer operations around the core")
+    ap.add_argument("--only-layer", action="store_true",
+                    help="time only the layer operations around the core")
     ap.add_argument("--only-kcp-share", action="store_true",
                     help="run only the 12-head direct vs segment-form comparison")
     ap.add_argument("--copy-probe", action="store_true")
@@ -263,6 +306,14 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.only_kcp_share:
         print(json.dumps({"kcp_share": kcp_share(args.tokens, stream)}), flush=True)
+        return 0
+    if args.only_layer:
+        wl = synth.WORKLOADS[3]
+        q = kc.device_tokens(wl, "q", args.tokens)
+        g = kc.device_tokens(wl, "gate", args.tokens)
+        o = torch.empty((args.tokens, wl.heads, wl.dv), dtype=torch.float32, device=dev)
+        synth.device_normal(o.view(-1, wl.dv), synth.key(wl.seed, "o"))
+        print(json.dumps({"layer": layer_ops(q, g, o, stream)}), flush=True)
         return 0
 
     # ---- forward workload: 1 x T tokens, H=96, d=128, bf16 ----------------
@@ -363,6 +414,8 @@ def main() -> int:
         out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
         out["roofline"]["traffic_fetch"] = tr["fetch"]
         out["roofline"]["traffic_write"] = tr["write"]
+    if not args.no_layer:
+        out["layer"] = layer_ops(xin["q"], xin["gate"], o, stream)
     if not args.no_kcp_share:
         del xin, o, dec_in
         torch.cuda.empty_cache()

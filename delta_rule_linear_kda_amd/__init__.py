@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   * ``segment_transition(k, v, a, b, cu_seqlens, ...)``,
     ``segment_compose(seg_offsets, trans, ...)``,
     ``fwd_chunked_kcp(q, k, v, a, b, gate, cu_seqlens, ...)``
+  * ``shortconv_swish_l2(x, weight, cu_seqlens, ...)``,
+    ``rmsnorm_gate(o, gate, weight, eps, ...)``
   * ``fwd_workspace_bytes(...)``, ``kcp_workspace_bytes(...)``,
     ``ckpt_count(...)``, ``status_str(code)``, ``abi_version()``
 """
@@ -30,8 +32,8 @@ STATUS = {
 }
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
            "kda_fwd_ckpt_count", "kda_segment_transition", "kda_segment_compose",
-           "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_decode_step",
-           "kda_status_str", "kda_abi_version")
+           "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_shortconv_swish_l2",
+           "kda_rmsnorm_gate", "kda_decode_step", "kda_status_str", "kda_abi_version")
 
 
 class KdaError(RuntimeError):
@@ -79,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_kcp.restype = ctypes.c_int
         L.kda_fwd_chunked_kcp.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                           ctypes.c_size_t, vp]
+        L.kda_shortconv_swish_l2.restype = ctypes.c_int
+        L.kda_shortconv_swish_l2.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.kda_rmsnorm_gate.restype = ctypes.c_int
+        L.kda_rmsnorm_gate.argtypes = [sp, vp, vp, vp, ctypes.c_float, vp, vp]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_status_str.restype = ctypes.c_char_p
@@ -292,6 +298,51 @@ def fwd_chunked_kcp(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     if rc != 0:
         raise KdaError(rc, "kda_fwd_chunked_kcp")
     return out, final_state
+
+
+def shortconv_swish_l2(x, weight, cu_seqlens, state_in=None, *, out=None, state_out=None,
+                       want_state: bool = False, stream=None):
+    """Short convolution -> Swish -> L2 of one projection (C ABI
+    ``kda_shortconv_swish_l2``): x [T, H, d] (float32 or bfloat16); weight fp32
+    [H, d, W]; cu_seqlens int32 [N+1] on the device; state_in [N, H, d, W-1]
+    (x's dtype) or None.  Returns y (x's dtype), plus the carried state when
+    ``want_state`` or ``state_out`` is given."""
+    import torch
+
+    T, H, d = x.shape
+    W = weight.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if out is None:
+        out = torch.empty_like(x)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, H, d, W - 1), dtype=x.dtype, device=x.device)
+    shape = Shape(N, T, H, d, d, _dtype_code(x), KDA_F32)
+    rc = lib().kda_shortconv_swish_l2(ctypes.byref(shape), int(W), _ptr(x), _ptr(weight),
+                                      _ptr(cu_seqlens), _ptr(state_in), _ptr(state_out),
+                                      _ptr(out), _stream(x.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_shortconv_swish_l2")
+    return (out, state_out) if (want_state or state_out is not None) else out
+
+
+def rmsnorm_gate(o, gate, weight=None, eps: float = 1e-6, *, out=None, stream=None):
+    """Head-wise RMSNorm then sigmoid gate (C ABI ``kda_rmsnorm_gate``):
+    o fp32 [T, H, dv]; gate [T, H, dv] (float32 or bfloat16) or None; weight
+    fp32 [dv] or None.  ``out`` may be ``o`` (in place).  Returns y fp32."""
+    import torch
+
+    T, H, dv = o.shape
+    if out is None:
+        out = torch.empty_like(o)
+    shape = Shape(1, T, H, dv, dv, _dtype_code(gate) if gate is not None else KDA_BF16,
+                  KDA_F32)
+    rc = lib().kda_rmsnorm_gate(ctypes.byref(shape), _ptr(o), _ptr(gate), _ptr(weight),
+                                float(eps), _ptr(out), _stream(o.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_rmsnorm_gate")
+    return out
 
 
 def decode_step(q, k, v, a, b, gate, state, *, out=None, stream=None):

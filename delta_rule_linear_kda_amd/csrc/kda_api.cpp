@@ -465,3 +465,88 @@ kda_status kda_fwd_chunked_kcp(const kda_shape* shape, const void* q, const void
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Layer operations around the core: short convolution -> Swish -> L2 front,
+// head-wise RMSNorm -> sigmoid gate back.
+// ---------------------------------------------------------------------------
+extern "C" {
+
+kda_status kda_shortconv_swish_l2(const kda_shape* shape, int32_t width, const void* x,
+                                  const float* weight, const int32_t* cu_seqlens,
+                                  const void* state_in, void* state_out, void* y,
+                                  void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  if (width < 1 || width > 4) return KDA_ERR_BAD_SHAPE;
+  if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
+  if (!cu_seqlens || !weight) return KDA_ERR_NULL_POINTER;
+  if (s.total_tokens > 0 && (!x || !y)) return KDA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+  for (const void* p : {x, (const void*)weight, (const void*)y})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  for (const void* p : {state_in, (const void*)state_out})
+    if (!aligned_elem(p, s.in_dtype)) return KDA_ERR_MISALIGNED;
+  const uint64_t es = s.in_dtype == KDA_BF16 ? 2 : 4;
+  const uint64_t hk = uint64_t(s.num_heads) * uint64_t(s.dk);
+  const Span sx(x, uint64_t(s.total_tokens) * hk * es), sy(y, uint64_t(s.total_tokens) * hk * es);
+  const Span sw(weight, hk * uint64_t(width) * 4);
+  const Span sc(cu_seqlens, uint64_t(s.num_seqs + 1) * 4);
+  const uint64_t stb = uint64_t(s.num_seqs) * hk * uint64_t(width - 1) * es;
+  const Span si(state_in, stb), so(state_out, stb);
+  for (const Span& in : {sx, sw, sc, si})
+    if (overlap(sy, in)) return KDA_ERR_ALIAS;
+  if (overlap(sy, so)) return KDA_ERR_ALIAS;
+  for (const Span& in : {sx, sw, sc})
+    if (overlap(so, in)) return KDA_ERR_ALIAS;
+  if (overlap(so, si) && state_out != state_in) return KDA_ERR_ALIAS;
+  kda::ConvArgs p;
+  p.num_seqs = s.num_seqs;
+  p.num_heads = s.num_heads;
+  p.dim = s.dk;
+  p.width = width;
+  p.total_tokens = s.total_tokens;
+  p.in_bf16 = s.in_dtype == KDA_BF16;
+  p.x = x;
+  p.weight = weight;
+  p.cu_seqlens = cu_seqlens;
+  p.state_in = state_in;
+  p.state_out = state_out;
+  p.y = y;
+  if (kda::launch_conv_swish_l2(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, const void* gate,
+                            const float* weight, float eps, float* y, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  if (!(eps >= 0.f) || eps > 1.f) return KDA_ERR_BAD_SHAPE;
+  if (s.total_tokens == 0) return KDA_OK;
+  if (!o || !y) return KDA_ERR_NULL_POINTER;
+  for (const void* p : {(const void*)o, gate, (const void*)weight, (const void*)y})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  const uint64_t rowsb = uint64_t(s.total_tokens) * uint64_t(s.num_heads) * uint64_t(s.dv);
+  const Span so(o, rowsb * 4), sy(y, rowsb * 4);
+  const Span sg(gate, rowsb * (s.in_dtype == KDA_BF16 ? 2 : 4)), sw(weight, uint64_t(s.dv) * 4);
+  if (overlap(sy, sg) || overlap(sy, sw)) return KDA_ERR_ALIAS;
+  if (overlap(sy, so) && (const void*)y != (const void*)o) return KDA_ERR_ALIAS;
+  kda::RmsGateArgs p;
+  p.num_heads = s.num_heads;
+  p.dv = s.dv;
+  p.total_tokens = s.total_tokens;
+  p.in_bf16 = s.in_dtype == KDA_BF16;
+  p.o = o;
+  p.gate = gate;
+  p.weight = weight;
+  p.eps = eps;
+  p.y = y;
+  if (kda::launch_rmsnorm_gate(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

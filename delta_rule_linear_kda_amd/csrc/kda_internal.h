@@ -45,6 +45,31 @@ struct ComposeArgs {
   float* final_state;           // [N, H, dk, dv] or null
 };
 
+// Short convolution -> Swish -> L2 over [T, H, dim] rows (kda_layer.hip).
+struct ConvArgs {
+  int32_t num_seqs, num_heads, dim, width;
+  int64_t total_tokens;
+  bool in_bf16;
+  const void* x;
+  const float* weight;          // [H, dim, width]
+  const int32_t* cu_seqlens;
+  const void* state_in;         // [N, H, dim, width - 1] or null (zero)
+  void* state_out;              // same layout or null; may equal state_in
+  void* y;
+};
+
+// Head-wise RMSNorm then sigmoid gate over [T, H, dv] rows (kda_layer.hip).
+struct RmsGateArgs {
+  int32_t num_heads, dv;
+  int64_t total_tokens;
+  bool in_bf16;                 // dtype of gate
+  const float* o;
+  const void* gate;             // or null
+  const float* weight;          // [dv] or null (ones)
+  float eps;
+  float* y;                     // may equal o
+};
+
 // Compute units of the current device (cached per device).
 int device_cus();
 
@@ -54,6 +79,9 @@ hipError_t launch_segment_table(const int32_t* cu_seqlens, int32_t num_seqs, int
                                 int32_t cap, int32_t* seg_cu, int32_t* seg_off,
                                 hipStream_t stream);
 hipError_t launch_compose(const ComposeArgs& p, hipStream_t stream);
+// kda_layer.hip
+hipError_t launch_conv_swish_l2(const ConvArgs& p, hipStream_t stream);
+hipError_t launch_rmsnorm_gate(const RmsGateArgs& p, hipStream_t stream);
 hipError_t launch_fwd_chunked(const FwdArgs& p, hipStream_t stream);
 // bf16-input kernel (kda_chunk_bf16.hip); launch_fwd_chunked dispatches to it.
 hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream);

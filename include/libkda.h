@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3u
+#define KDA_ABI_VERSION 4u
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -218,6 +218,50 @@ KDA_API kda_status kda_fwd_chunked_kcp(const kda_shape* shape, const void* q, co
                                        const float* initial_state, void* o, float* final_state,
                                        int32_t segment_len, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/* ---- Layer operations around the core ------------------------------------
+ * Page "[Paper Review] Kimi K3...", section "Kimi Delta Attention (KDA)": the
+ * query and key pass through a short convolution, then Swish, and are
+ * L2-normalised (projections paragraph); the sigmoid output gate follows a
+ * head-wise RMSNorm of the head's output ("Full-rank gate" paragraph).  The
+ * pages print neither operation's details; the readings are stated below.
+ */
+
+/* Short convolution -> Swish -> L2 normalisation of one projection (q or k),
+ * over packed sequences.  For sequence n, head h, channel c and token t:
+ *     c_t = sum_{i < width} weight[h, c, width-1-i] * x_{t-i}
+ *     s_t = c_t * sigmoid(c_t),   y_t = s_t / sqrt(|s_t|^2 + 1e-6)
+ * (|.| over the head's dk channels) -- a causal depthwise convolution within
+ * each sequence, no bias; positions before the sequence's first token are
+ * taken from state_in, else zero.
+ *   shape        num_seqs, total_tokens, num_heads, dk (= the channel count),
+ *                in_dtype (of x, y and the states); dv and out_dtype unused
+ *   width        1..4
+ *   x, y         [T, H, dk] in_dtype; y must not overlap x
+ *   weight       [H, dk, width] fp32
+ *   cu_seqlens   [N + 1] int32, device, as for kda_fwd_chunked
+ *   state_in     [N, H, dk, width-1] in_dtype (oldest position first), or NULL
+ *   state_out    same layout, or NULL: the last width-1 inputs of
+ *                [state_in, sequence] (the state a following call continues
+ *                from; for decode, one token per sequence); may be state_in
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, HIP. */
+KDA_API kda_status kda_shortconv_swish_l2(const kda_shape* shape, int32_t width, const void* x,
+                                          const float* weight, const int32_t* cu_seqlens,
+                                          const void* state_in, void* state_out, void* y,
+                                          void* stream);
+
+/* Head-wise RMSNorm, then the sigmoid output gate, per (token, head) row:
+ *     y = sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps)
+ * (mean over the head's dv channels).  o is the core's output computed
+ * without a gate (kda_fwd_chunked with gate = NULL).
+ *   shape   total_tokens, num_heads, dv, in_dtype (of gate); others unused
+ *   o, y    [T, H, dv] fp32; y may be o (in place), no other overlap
+ *   gate    [T, H, dv] in_dtype, or NULL (no gate)
+ *   weight  [dv] fp32 shared by the heads, or NULL (ones)
+ *   eps     0 <= eps <= 1
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, HIP. */
+KDA_API kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, const void* gate,
+                                    const float* weight, float eps, float* y, void* stream);
 
 /* One decode step: one new token for each of N independent sequences, the
  * recurrent update the pages' serving section runs with dedicated decode

@@ -26,7 +26,8 @@ HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
 DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
 
 # Tensor ids in the stream key.
-TENSOR = {"q": 1, "k": 2, "v": 3, "a": 4, "b": 5, "gate": 6, "s0": 7, "lengths": 8}
+TENSOR = {"q": 1, "k": 2, "v": 3, "a": 4, "b": 5, "gate": 6, "s0": 7, "lengths": 8,
+          "conv_w": 9, "conv_state": 10, "norm_w": 11, "o": 12}
 
 F32, BF16 = 0, 1
 

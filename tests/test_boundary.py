@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     for code in range(8):
         assert kda.status_str(code).startswith(kda.STATUS[code])
     assert kda.status_str(99) == "unknown kda_status"
@@ -275,3 +275,49 @@ def test_segment_compose_rejects():
     assert compose(sf=TRP + 1024) == ALIAS
     assert compose(sf=P["s0"] + 16) == ALIAS           # partial overlap with the start
     assert compose(N=0) == OK
+
+
+# --- layer operations: short convolution front, RMSNorm gate back ------------
+XP, WP, YP, SIP, SOP = (BASE + (20 + i) * (1 << 36) for i in range(5))
+
+
+def conv(shape, width=4, x=XP, w=WP, cu=P["cu"], si=SIP, so=SOP, y=YP):
+    return kda.lib().kda_shortconv_swish_l2(ctypes.byref(shape), width, x, w, cu, si, so, y, None)
+
+
+def test_shortconv_rejects():
+    s = good_shape()
+    assert conv(good_shape(dk=48)) == SHAPE
+    assert conv(good_shape(in_dtype=9)) == DTYPE
+    for wd in (0, 5, -1):
+        assert conv(s, width=wd) == SHAPE
+    assert conv(s, x=None) == NULLP
+    assert conv(s, y=None) == NULLP
+    assert conv(s, w=None) == NULLP
+    assert conv(s, cu=None) == NULLP
+    assert conv(s, x=XP + 8) == MISAL
+    assert conv(s, w=WP + 4) == MISAL
+    assert conv(s, si=SIP + 1) == MISAL            # bf16 state: 2-byte alignment
+    assert conv(s, y=XP) == ALIAS                  # output over the input
+    assert conv(s, so=WP) == ALIAS                 # state over the weights
+    assert conv(s, so=YP) == ALIAS                 # state over the output
+    assert conv(s, so=SIP + 2) == ALIAS            # partial overlap with the state in
+    assert conv(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+def rms(shape, o=XP, gate=WP, w=SIP, eps=1e-6, y=YP):
+    return kda.lib().kda_rmsnorm_gate(ctypes.byref(shape), o, gate, w, eps, y, None)
+
+
+def test_rmsnorm_gate_rejects():
+    s = good_shape()
+    assert rms(good_shape(dv=100)) == SHAPE
+    assert rms(s, eps=-1.0) == SHAPE
+    assert rms(s, eps=float("nan")) == SHAPE
+    assert rms(s, o=None) == NULLP
+    assert rms(s, y=None) == NULLP
+    assert rms(s, o=XP + 4) == MISAL
+    assert rms(s, gate=WP + 2) == MISAL
+    assert rms(s, y=WP) == ALIAS                   # output over the gate
+    assert rms(s, y=XP + 16) == ALIAS              # partial overlap with o
+    assert rms(good_shape(num_seqs=0, total_tokens=0)) == OK
