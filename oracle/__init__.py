@@ -61,6 +61,9 @@ def _L():
         lib.kda_ref_segment_transition.argtypes = [ctypes.c_int32, dp, ctypes.c_int32,
                                                    ctypes.c_int32, ctypes.c_int32, dp, dp, dp,
                                                    dp, dp, ctypes.c_int]
+        lib.kda_ref_bwd.restype = ctypes.c_int
+        lib.kda_ref_bwd.argtypes = [ctypes.c_int32, dp, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32] + [dp] * 16 + [ctypes.c_int]
         lib.kda_ref_decode_step.restype = ctypes.c_int
         lib.kda_ref_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, dp, dp, dp, dp, dp, dp, dp, dp,
@@ -169,3 +172,27 @@ def segment_compose(seg_offsets, trans, dv: int, s0=None):
                 S = M @ S + S_loc
             final[n, h] = S
     return starts, final
+
+
+def bwd(q, k, v, a, b, gate, cu_seqlens, s0, dy, d_sfinal=None, *,
+        nthreads: Optional[int] = None):
+    """Gradients of sum_t <dy_t, y_t> + <d_sfinal, S_final> (the outputs of
+    ``fwd``) with respect to q, k, v, a, b, gate, s0, by reverse-mode chain
+    rule through the token recurrence (``kda_ref_bwd``).  Returns a dict of
+    fp64 arrays: dq, dk, dv, da, db, dgate (None without gate), ds0."""
+    q, k, v, a, b, gate, s0, dy, d_sfinal = map(_f64, (q, k, v, a, b, gate, s0, dy, d_sfinal))
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = len(cu) - 1
+    out = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+           "da": np.zeros((T, H, dk)), "db": np.zeros((T, H)),
+           "dgate": np.zeros((T, H, dv)) if gate is not None else None,
+           "ds0": np.zeros((N, H, dk, dv))}
+    rc = _L().kda_ref_bwd(N, cu.ctypes.data, H, dk, dv, _p(q), _p(k), _p(v), _p(a), _p(b),
+                          _p(gate), _p(s0), _p(dy), _p(d_sfinal), _p(out["dq"]), _p(out["dk"]),
+                          _p(out["dv"]), _p(out["da"]), _p(out["db"]), _p(out["dgate"]),
+                          _p(out["ds0"]), nthreads or threads())
+    if rc != 0:
+        raise ValueError("kda_ref_bwd: bad argument")
+    return out

@@ -57,6 +57,18 @@ int kda_ref_segment_transition(int32_t num_seqs, const int64_t* cu_seqlens, int3
                                int32_t dk, int32_t dv, const double* k, const double* v,
                                const double* a, const double* b, double* trans, int nthreads);
 
+/* Backward: gradients of L = sum_t <dy_t, y_t> + <d_sfinal, S_final> with
+ * respect to q, k, v, a, b, gate and s0, by the chain rule through the same
+ * token recurrence in reverse.  dy [T, H, dv]; d_sfinal [N, H, dk, dv] or
+ * NULL; outputs dq, dk, da [T, H, dk], dv [T, H, dv], db [T, H], dgate
+ * [T, H, dv] (may be NULL; zero where gate is NULL), ds0 [N, H, dk, dv] or
+ * NULL.  Returns 0 or -1. */
+int kda_ref_bwd(int32_t num_seqs, const int64_t* cu_seqlens, int32_t H, int32_t dk, int32_t dv,
+                const double* q, const double* k, const double* v, const double* a,
+                const double* b, const double* gate, const double* s0, const double* dy,
+                const double* d_sfinal, double* dq, double* dk_out, double* dv_out, double* da,
+                double* db, double* dgate, double* ds0, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
