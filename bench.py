@@ -21,11 +21,13 @@ the same sequence under 8-way head sharding -- 12 heads, 1 x 1,048,576 tokens
 kda_fwd_chunked_kcp (segment-transition form with the automatic segment
 length), each the mean of 3 launches after one warm-up, and ``layer`` times
 the layer operations around the core (short convolution -> Swish -> L2 on q,
-RMSNorm -> sigmoid gate on o) on the same resident tensors.
+RMSNorm -> sigmoid gate on o) on the same resident tensors, and ``bwd`` times
+the backward on the 4 x 4096-token, 32-head prefill workload.
 
 Profiling helpers (not part of a timed run):
   --no-kcp-share / --only-kcp-share   skip, or run only, the 12-head comparison;
   --no-layer / --only-layer           skip, or run only, the layer operations;
+  --no-bwd / --only-bwd               skip, or run only, the backward;
   --copy-probe          after the timed steps, run a plain 2 GiB device copy so
                         that a hardware-counter run of this same command can
                         scale FETCH_SIZE / WRITE_SIZE against known bytes;
@@ -179,6 +181,45 @@ def layer_ops(q, gate, o, stream, reps: int = 5) -> dict:
                              "frac_hbm": bb / ms_b / 1e6 / HBM_PEAK_GBS}}
 
 
+def backward(stream, reps: int = 3) -> dict:
+    """kda_bwd_chunked on the training-shaped prefill workload (4 x 4096
+    tokens, 32 heads, d = 128, bf16 inputs, zero initial state, fp32 dy):
+    the forward recomputation with states every 64 tokens, the adjoint
+    recurrence and the reduction over column slices, one call each."""
+    import torch
+
+    import delta_rule_linear_kda_amd as kda
+    import synth
+    from tests import kda_cases as kc
+
+    w = synth.WORKLOADS[1]
+    T, H = sum(w.seq_lens()), w.heads
+    x = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    args = tuple(x[n] for n in ("q", "k", "v", "a", "b", "gate"))
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32, device="cuda")
+    dy = torch.empty((T, H, w.dv), dtype=torch.float32, device="cuda")
+    synth.device_normal(dy.view(-1, w.dv), synth.key(w.seed, "o", 1))
+    ws = torch.empty(kda.bwd_workspace_bytes(w.num_seqs, T, H, w.dk, w.dv), dtype=torch.uint8,
+                     device="cuda")
+
+    def timed(fn) -> float:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fwd_ms = timed(lambda: kda.fwd_chunked(*args, cu, None, stream=stream))
+    bwd_ms = timed(lambda: kda.bwd_chunked(*args, cu, None, dy, None, workspace=ws,
+                                           stream=stream))
+    return {"workload": f"kda_bwd_bf16_{w.num_seqs}x{T // w.num_seqs}_H{H}_d{w.dk}",
+            "ms": bwd_ms, "tokens_per_s": T / (bwd_ms * 1e-3), "fwd_ms": fwd_ms,
+            "bwd_over_fwd": bwd_ms / fwd_ms, "workspace_bytes": ws.numel()}
+
+
 def _sha256(path: str) -> str:
     """sha256 of a C/HIP source's code: comments removed and whitespace
     collapsed, so that editing a comment does not invalidate counters taken
@@ -279,6 +320,8 @@ def main() -> int:
                     help="skip timing the layer operations around the core")
     ap.add_argument("--only-layer", action="store_true",
                     help="time only the layer operations around the core")
+    ap.add_argument("--no-bwd", action="store_true", help="skip timing the backward")
+    ap.add_argument("--only-bwd", action="store_true", help="time only the backward")
     ap.add_argument("--only-kcp-share", action="store_true",
                     help="run only the 12-head direct vs segment-form comparison")
     ap.add_argument("--copy-probe", action="store_true")
@@ -306,6 +349,9 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.only_kcp_share:
         print(json.dumps({"kcp_share": kcp_share(args.tokens, stream)}), flush=True)
+        return 0
+    if args.only_bwd:
+        print(json.dumps({"bwd": backward(stream)}), flush=True)
         return 0
     if args.only_layer:
         wl = synth.WORKLOADS[3]
@@ -416,8 +462,12 @@ def main() -> int:
         out["roofline"]["traffic_write"] = tr["write"]
     if not args.no_layer:
         out["layer"] = layer_ops(xin["q"], xin["gate"], o, stream)
-    if not args.no_kcp_share:
+    if not args.no_kcp_share or not args.no_bwd:
         del xin, o, dec_in
+        torch.cuda.empty_cache()
+    if not args.no_bwd:
+        out["bwd"] = backward(stream)
+    if not args.no_kcp_share:
         torch.cuda.empty_cache()
         out["kcp_share"] = kcp_share(T, stream)
     if not args.no_cpu_baseline:

@@ -13,7 +13,8 @@ Entry points (same names as the C ABI):
     ``fwd_chunked_kcp(q, k, v, a, b, gate, cu_seqlens, ...)``
   * ``shortconv_swish_l2(x, weight, cu_seqlens, ...)``,
     ``rmsnorm_gate(o, gate, weight, eps, ...)``
-  * ``fwd_workspace_bytes(...)``, ``kcp_workspace_bytes(...)``,
+  * ``bwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state, dy, ...)``
+  * ``fwd_workspace_bytes(...)``, ``kcp_workspace_bytes(...)``, ``bwd_workspace_bytes(...)``,
     ``ckpt_count(...)``, ``status_str(code)``, ``abi_version()``
 """
 from __future__ import annotations
@@ -33,7 +34,8 @@ STATUS = {
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
            "kda_fwd_ckpt_count", "kda_segment_transition", "kda_segment_compose",
            "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_shortconv_swish_l2",
-           "kda_rmsnorm_gate", "kda_decode_step", "kda_status_str", "kda_abi_version")
+           "kda_rmsnorm_gate", "kda_bwd_workspace_bytes", "kda_bwd_chunked", "kda_decode_step",
+           "kda_status_str", "kda_abi_version")
 
 
 class KdaError(RuntimeError):
@@ -85,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.kda_shortconv_swish_l2.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.kda_rmsnorm_gate.restype = ctypes.c_int
         L.kda_rmsnorm_gate.argtypes = [sp, vp, vp, vp, ctypes.c_float, vp, vp]
+        L.kda_bwd_workspace_bytes.restype = ctypes.c_int
+        L.kda_bwd_workspace_bytes.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+        L.kda_bwd_chunked.restype = ctypes.c_int
+        L.kda_bwd_chunked.argtypes = [sp] + [vp] * 18 + [ctypes.c_size_t, vp]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_status_str.restype = ctypes.c_char_p
@@ -343,6 +349,52 @@ def rmsnorm_gate(o, gate, weight=None, eps: float = 1e-6, *, out=None, stream=No
     if rc != 0:
         raise KdaError(rc, "kda_rmsnorm_gate")
     return out
+
+
+def bwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                        in_dtype: int = KDA_BF16) -> int:
+    shape = Shape(num_seqs, total_tokens, num_heads, dk, dv, in_dtype, KDA_F32)
+    out = ctypes.c_size_t(0)
+    rc = lib().kda_bwd_workspace_bytes(ctypes.byref(shape), ctypes.byref(out))
+    if rc != 0:
+        raise KdaError(rc, "kda_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def bwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state, dy, d_final_state=None, *,
+                want_d_initial_state: bool = True, workspace=None, stream=None):
+    """Gradients of sum <dy, y> + <d_final_state, S_final> for the forward of
+    ``fwd_chunked`` on the same inputs (C ABI ``kda_bwd_chunked``).  dy fp32
+    [T, H, dv]; d_final_state fp32 [N, H, dk, dv] or None.  Returns a dict of
+    fp32 tensors: dq, dk, dv, da, db, dgate (None without gate), ds0 (None
+    unless wanted)."""
+    import torch
+
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dt = _dtype_code(q)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty((T, H, dk), **f32), "dk": torch.empty((T, H, dk), **f32),
+         "dv": torch.empty((T, H, dv), **f32), "da": torch.empty((T, H, dk), **f32),
+         "db": torch.empty((T, H), **f32),
+         "dgate": torch.empty((T, H, dv), **f32) if gate is not None else None,
+         "ds0": torch.empty((N, H, dk, dv), **f32) if want_d_initial_state else None}
+    ws_bytes = bwd_workspace_bytes(N, T, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
+    rc = lib().kda_bwd_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                               _ptr(gate), _ptr(cu_seqlens), _ptr(initial_state), _ptr(dy),
+                               _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                               _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dgate"]), _ptr(g["ds0"]),
+                               _ptr(workspace), int(workspace.numel()),
+                               _stream(q.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_bwd_chunked")
+    return g
 
 
 def decode_step(q, k, v, a, b, gate, state, *, out=None, stream=None):

@@ -550,3 +550,128 @@ kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, const void* 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int32_t kBwdCkpt = 64;  // tokens between the forward states the backward restarts from
+constexpr int32_t kBwdSlice = 8;  // state columns per backward wavefront
+
+struct BwdLayout {
+  uint64_t ckpt, o_raw, p_dqh, p_dkh, p_dal, p_dbeta, sub, total;
+  int64_t slots;
+};
+
+BwdLayout bwd_layout(const kda_shape& s) {
+  BwdLayout w;
+  const uint64_t th = uint64_t(s.total_tokens) * uint64_t(s.num_heads);
+  const uint64_t nsl = uint64_t(s.dv / kBwdSlice);
+  w.slots = s.total_tokens / kBwdCkpt;  // >= sum over sequences of floor(L_n / 64)
+  w.ckpt = 0;
+  w.o_raw = round_up(uint64_t(w.slots) * uint64_t(s.num_heads) * s.dk * s.dv * 4, 256);
+  w.p_dqh = w.o_raw + round_up(th * s.dv * 4, 256);
+  w.p_dkh = w.p_dqh + round_up(nsl * th * s.dk * 4, 256);
+  w.p_dal = w.p_dkh + round_up(nsl * th * s.dk * 4, 256);
+  w.p_dbeta = w.p_dal + round_up(nsl * th * s.dk * 4, 256);
+  w.sub = w.p_dbeta + round_up(nsl * th * 4, 256);
+  // per (sequence, head, 8-column slice): the 8 sub-chunk start states of a
+  // 64-token chunk, dk x 8 fp32 each
+  w.total = w.sub + round_up(uint64_t(s.num_seqs) * uint64_t(s.num_heads) * nsl * 8 * s.dk * 8 * 4,
+                             256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_bwd_workspace_bytes(const kda_shape* shape, size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_POINTER;
+  const kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const BwdLayout w = bwd_layout(*shape);
+  if (w.total > uint64_t(kMaxElems)) return KDA_ERR_BAD_SHAPE;
+  *bytes = size_t(w.total);
+  return KDA_OK;
+}
+
+kda_status kda_bwd_chunked(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const void* gate,
+                           const int32_t* cu_seqlens, const float* initial_state,
+                           const float* dy, const float* d_final_state, float* dq, float* dk,
+                           float* dv, float* da, float* db, float* dgate, float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
+  const BwdLayout w = bwd_layout(s);
+  if (w.total > uint64_t(kMaxElems)) return KDA_ERR_BAD_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
+  if (s.total_tokens > 0 &&
+      (!q || !k || !v || !a || !b || !dy || !dq || !dk || !dv || !da || !db))
+    return KDA_ERR_NULL_POINTER;
+  if (gate && s.total_tokens > 0 && !dgate) return KDA_ERR_NULL_POINTER;
+  if (workspace_bytes < w.total || !workspace) return KDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return KDA_ERR_MISALIGNED;
+  for (const void* p : {q, k, v, a, gate, (const void*)initial_state, (const void*)dy,
+                        (const void*)d_final_state, (const void*)dq, (const void*)dk,
+                        (const void*)dv, (const void*)da, (const void*)db, (const void*)dgate,
+                        (const void*)d_initial_state, (const void*)workspace})
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  if (!aligned_elem(b, s.in_dtype)) return KDA_ERR_MISALIGNED;
+  {  // outputs and workspace: disjoint from every input and from each other
+    const Sizes z = byte_sizes(shape, s.total_tokens);
+    const uint64_t th = uint64_t(s.total_tokens) * uint64_t(s.num_heads);
+    const Span in[] = {Span(q, z.qk), Span(k, z.qk), Span(v, z.v), Span(a, z.qk), Span(b, z.b),
+                       Span(gate, z.v), Span(cu_seqlens, uint64_t(s.num_seqs + 1) * 4),
+                       Span(initial_state, z.st), Span(dy, z.o), Span(d_final_state, z.st)};
+    const Span out[] = {Span(dq, th * s.dk * 4), Span(dk, th * s.dk * 4), Span(dv, z.o),
+                        Span(da, th * s.dk * 4), Span(db, th * 4), Span(dgate, z.o),
+                        Span(d_initial_state, z.st), Span(workspace, w.total)};
+    for (const Span& o : out)
+      for (const Span& i : in)
+        if (overlap(o, i)) return KDA_ERR_ALIAS;
+    for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i)
+      for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
+        if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
+  }
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // 1. the forward with states recorded every 64 tokens and the ungated output
+  kda::FwdArgs f = fwd_args(s, q, k, v, a, b, nullptr, cu_seqlens, initial_state,
+                            base + w.o_raw, nullptr);
+  f.ckpt_interval = kBwdCkpt;
+  f.ckpt = reinterpret_cast<float*>(base + w.ckpt);
+  f.ckpt_capacity = w.slots;
+  if (kda::launch_fwd_chunked(f, hs) != hipSuccess) return KDA_ERR_HIP;
+  // 2. the adjoint recurrence and the reduction over column slices
+  kda::BwdArgs p;
+  p.num_seqs = s.num_seqs;
+  p.num_heads = s.num_heads;
+  p.dk = s.dk;
+  p.dv = s.dv;
+  p.total_tokens = s.total_tokens;
+  p.in_bf16 = s.in_dtype == KDA_BF16;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.gate = gate;
+  p.cu_seqlens = cu_seqlens;
+  p.initial_state = initial_state;
+  p.dy = dy;
+  p.d_final_state = d_final_state;
+  p.o_raw = reinterpret_cast<const float*>(base + w.o_raw);
+  p.ckpt = reinterpret_cast<const float*>(base + w.ckpt);
+  p.dq_out = dq; p.dk_out = dk; p.dv_out = dv; p.da_out = da; p.db_out = db;
+  p.dgate_out = gate ? dgate : nullptr;
+  p.d_s0 = d_initial_state;
+  p.p_dqh = reinterpret_cast<float*>(base + w.p_dqh);
+  p.p_dkh = reinterpret_cast<float*>(base + w.p_dkh);
+  p.p_dal = reinterpret_cast<float*>(base + w.p_dal);
+  p.p_dbeta = reinterpret_cast<float*>(base + w.p_dbeta);
+  p.sub_ws = reinterpret_cast<float*>(base + w.sub);
+  if (kda::launch_bwd(p, hs) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -70,6 +70,25 @@ struct RmsGateArgs {
   float* y;                     // may equal o
 };
 
+// Backward (kda_bwd.hip).  The forward's recorded states and ungated output
+// are computed by the caller (kda_api.cpp) into the workspace first.
+struct BwdArgs {
+  int32_t num_seqs, num_heads, dk, dv;
+  int64_t total_tokens;
+  bool in_bf16;
+  const void *q, *k, *v, *a, *b, *gate;  // gate may be null
+  const int32_t* cu_seqlens;
+  const float* initial_state;   // may be null
+  const float* dy;              // [T, H, dv]
+  const float* d_final_state;   // may be null
+  const float* o_raw;           // [T, H, dv] ungated forward output
+  const float* ckpt;            // states after every 64 tokens of each sequence
+  float *dq_out, *dk_out, *dv_out, *da_out, *db_out, *dgate_out, *d_s0;  // dgate, d_s0 may be null
+  float *p_dqh, *p_dkh, *p_dal, *p_dbeta;  // per-slice partial sums
+  float* sub_ws;  // per-wavefront sub-chunk start states [N H dv/8][8][dk x 8]
+};
+hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4u
+#define KDA_ABI_VERSION 5u
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -262,6 +262,35 @@ KDA_API kda_status kda_shortconv_swish_l2(const kda_shape* shape, int32_t width,
  * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, HIP. */
 KDA_API kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, const void* gate,
                                     const float* weight, float eps, float* y, void* stream);
+
+/* ---- Backward -------------------------------------------------------------
+ * Training through the KDA mixer (the method page trains it at scale and
+ * splits it over devices for training -- section "Infrastructure: how to
+ * actually run trillion-scale", KDA co-design item -- but describes no
+ * backward).  kda_bwd_chunked computes the gradients of
+ *     L = sum_t <dy_t, y_t> + <d_final_state, S_final>
+ * (y, S_final the outputs of kda_fwd_chunked on the same inputs) with respect
+ * to q, k, v, a, b, gate and initial_state, by the chain rule through the
+ * recurrence stated at the top of this header, in reverse token order.
+ *   q, k, v, a, b, gate, cu_seqlens, initial_state: as for kda_fwd_chunked
+ *   dy             [T, H, dv] fp32
+ *   d_final_state  [N, H, dk, dv] fp32, or NULL (zero)
+ *   dq, dk, da     [T, H, dk] fp32 out;  dv [T, H, dv] fp32 out;  db [T, H] fp32 out
+ *   dgate          [T, H, dv] fp32 out (required when gate is given; unused otherwise)
+ *   d_initial_state [N, H, dk, dv] fp32 out, or NULL
+ *   workspace      kda_bwd_workspace_bytes(shape) bytes, 16-byte aligned
+ * Outputs and workspace must not overlap any input or each other.  The
+ * forward is recomputed inside (states recorded every 64 tokens); results are
+ * deterministic (no atomics).
+ * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, WORKSPACE, ALIAS, HIP. */
+KDA_API kda_status kda_bwd_workspace_bytes(const kda_shape* shape, size_t* bytes);
+KDA_API kda_status kda_bwd_chunked(const kda_shape* shape, const void* q, const void* k,
+                                   const void* v, const void* a, const void* b,
+                                   const void* gate, const int32_t* cu_seqlens,
+                                   const float* initial_state, const float* dy,
+                                   const float* d_final_state, float* dq, float* dk, float* dv,
+                                   float* da, float* db, float* dgate, float* d_initial_state,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* One decode step: one new token for each of N independent sequences, the
  * recurrent update the pages' serving section runs with dedicated decode

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     for code in range(8):
         assert kda.status_str(code).startswith(kda.STATUS[code])
     assert kda.status_str(99) == "unknown kda_status"
@@ -321,3 +321,47 @@ def test_rmsnorm_gate_rejects():
     assert rms(s, y=WP) == ALIAS                   # output over the gate
     assert rms(s, y=XP + 16) == ALIAS              # partial overlap with o
     assert rms(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+# --- backward ----------------------------------------------------------------
+GP = {name: BASE + (30 + i) * (1 << 36) for i, name in enumerate(
+    ["dy", "dsf", "dq", "dk", "dv", "da", "db", "dgate", "ds0", "ws"])}
+
+
+def bwd(shape, ws_bytes=1 << 40, **over):
+    args = dict(P)
+    args.update(GP)
+    args.update(over)
+    return kda.lib().kda_bwd_chunked(
+        ctypes.byref(shape), args["q"], args["k"], args["v"], args["a"], args["b"], args["gate"],
+        args["cu"], args["s0"], args["dy"], args["dsf"], args["dq"], args["dk"], args["dv"],
+        args["da"], args["db"], args["dgate"], args["ds0"], args["ws"], ws_bytes, None)
+
+
+def test_bwd_workspace_query():
+    up = lambda x: (x + 255) // 256 * 256
+    N, T, H, dk, dv = 2, 300, 4, 128, 128
+    th, nsl = T * H, dv // 8
+    exp = (up((T // 64) * H * dk * dv * 4) + up(th * dv * 4) + 3 * up(nsl * th * dk * 4)
+           + up(nsl * th * 4) + up(N * H * nsl * 8 * dk * 8 * 4))
+    assert kda.bwd_workspace_bytes(N, T, H, dk, dv) == exp
+    out = ctypes.c_size_t(0)
+    assert kda.lib().kda_bwd_workspace_bytes(None, ctypes.byref(out)) == NULLP
+
+
+def test_bwd_rejects():
+    s = good_shape()
+    assert bwd(good_shape(dk=80)) == SHAPE
+    assert bwd(good_shape(in_dtype=4)) == DTYPE
+    for name in ["q", "k", "v", "a", "b", "cu", "dy", "dq", "dk", "dv", "da", "db"]:
+        assert bwd(s, **{name: None}) == NULLP, name
+    assert bwd(s, dgate=None) == NULLP                # a gate needs its gradient
+    assert bwd(s, ws=None) == WS
+    assert bwd(s, ws_bytes=16) == WS
+    for name in ["q", "dy", "dq", "dgate", "ds0", "ws"]:
+        assert bwd(s, **{name: GP.get(name, P.get(name)) + 8}) == MISAL, name
+    assert bwd(s, dq=P["k"]) == ALIAS                 # gradient over an input
+    assert bwd(s, dv=GP["dy"]) == ALIAS               # over the cotangent
+    assert bwd(s, dk=GP["dq"] + 64) == ALIAS          # two gradients overlap
+    assert bwd(s, ws=GP["ds0"]) == ALIAS              # workspace over an output
+    assert bwd(good_shape(num_seqs=0, total_tokens=0)) == OK
