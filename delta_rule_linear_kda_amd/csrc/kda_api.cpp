@@ -88,7 +88,12 @@ kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes) {
   if (!bytes) return KDA_ERR_NULL_POINTER;
   const kda_status st = check_shape(shape);
   if (st != KDA_OK) return st;
-  *bytes = 0;
+  const kda_shape& s = *shape;
+  // bf16 inputs run the two-pass form, whose chunk records live here
+  *bytes = s.in_dtype == KDA_BF16 && s.num_seqs > 0
+               ? size_t(kda::split_layout(s.num_seqs, s.total_tokens, s.num_heads, s.dk, s.dv)
+                            .total)
+               : 0;
   return KDA_OK;
 }
 
@@ -168,17 +173,33 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
   size_t need = 0;
   kda_fwd_workspace_bytes(shape, &need);
   if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return KDA_ERR_MISALIGNED;
   bool empty = false;
   st = check_fwd(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state,
                  ckpt_interval, ckpt, ckpt_capacity, &empty);
   if (st != KDA_OK || empty) return st;
+  if (need > 0) {  // the workspace is disjoint from every argument
+    const Sizes z = byte_sizes(shape, s.total_tokens);
+    const Span ws(workspace, need);
+    for (const Span& x : {Span(q, z.qk), Span(k, z.qk), Span(v, z.v), Span(a, z.qk),
+                          Span(b, z.b), Span(gate, z.v),
+                          Span(cu_seqlens, uint64_t(s.num_seqs + 1) * 4),
+                          Span(initial_state, z.st), Span(o, z.o), Span(final_state, z.st)})
+      if (overlap(ws, x)) return KDA_ERR_ALIAS;
+    if (ckpt_interval != 0 &&
+        overlap(ws, Span(ckpt, uint64_t(ckpt_capacity) * uint64_t(s.num_heads) *
+                                   uint64_t(s.dk) * uint64_t(s.dv) * 4)))
+      return KDA_ERR_ALIAS;
+  }
 
   kda::FwdArgs p = fwd_args(s, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state);
   p.ckpt_interval = ckpt_capacity > 0 ? ckpt_interval : 0;
   p.ckpt = ckpt;
   p.ckpt_capacity = ckpt_capacity;
-  if (kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return KDA_ERR_HIP;
+  const hipError_t e = s.in_dtype == KDA_BF16
+                           ? kda::launch_fwd_split_bf16(p, workspace, static_cast<hipStream_t>(stream))
+                           : kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 
@@ -397,7 +418,8 @@ kda_status kda_fwd_kcp_workspace_bytes(const kda_shape* shape, int32_t segment_l
   int64_t L = 0;
   st = kcp_resolve(*shape, segment_len, &L);
   if (st != KDA_OK) return st;
-  *bytes = L == 0 ? 0 : size_t(kcp_layout(*shape, L).total);
+  if (L == 0) return kda_fwd_workspace_bytes(shape, bytes);  // direct form
+  *bytes = size_t(kcp_layout(*shape, L).total);
   return KDA_OK;
 }
 
@@ -414,7 +436,7 @@ kda_status kda_fwd_chunked_kcp(const kda_shape* shape, const void* q, const void
   if (st != KDA_OK) return st;
   if (L == 0)  // direct form
     return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
-                    nullptr, 0, nullptr, 0, stream);
+                    nullptr, 0, workspace, workspace_bytes, stream);
   const KcpLayout w = kcp_layout(s, L);
   if (workspace_bytes < w.total || !workspace) return KDA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;

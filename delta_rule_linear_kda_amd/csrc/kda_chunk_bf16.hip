@@ -54,155 +54,11 @@
 // diag(Gamma_end) - Kend^T W: the product is the segment's transition M).
 // No queries, gate or outputs: Qt, Qbar, P, Qbar S, P U and the stores drop
 // out, and the final state [S_loc | M] is the result.
-#include "kda_device.h"
+#include "kda_chunk_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
-
-constexpr int kC = 32;          // chunk length (tokens)
-// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx950.
-constexpr int kBufferRsrcFlags = 0x00020000;
-constexpr float kLog2e = 1.4426950408889634f;
-
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-
-__device__ __forceinline__ f32x4_t mma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma_f32(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// (ah + al)(bh + bl) ~ ah bh + ah bl + al bh
-__device__ __forceinline__ f32x4_t mma_x3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl,
-                                          f32x4_t c) {
-  c = mma_bf16(al, bh, c);
-  c = mma_bf16(ah, bl, c);
-  return mma_bf16(ah, bh, c);
-}
-
-__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float rcpf_fast(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// Data-parallel primitives within a row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp0(float x) {  // lanes whose source is outside the row read 0
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
-}
-template <int CTRL>
-__device__ __forceinline__ void scan_step_x8(float (&x)[2][4]) {
-  float y[2][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) y[t][j] = dpp0<CTRL>(x[t][j]);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[t][j] += y[t][j];
-}
-// Inclusive prefix sums over the 16 lanes of each row, for eight independent
-// values, step by step (row_shr 1, 2, 4, 8; lanes whose source is outside the
-// row add 0).
-__device__ __forceinline__ void scan16_x8(float (&x)[2][4]) {
-  scan_step_x8<0x111>(x);
-  scan_step_x8<0x112>(x);
-  scan_step_x8<0x114>(x);
-  scan_step_x8<0x118>(x);
-}
-// Sum over the 16 lanes of each row, in every lane of the row.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp0<0x128>(x);  // row_ror:8
-  x += dpp0<0x124>(x);  // row_ror:4
-  x += dpp0<0x122>(x);  // row_ror:2
-  x += dpp0<0x121>(x);  // row_ror:1
-  return x;
-}
-// Value held by lane S of each quad of lanes, in all four lanes of the quad.
-template <int S>
-__device__ __forceinline__ float quad_bcast_t(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                            S | (S << 2) | (S << 4) | (S << 6), 0xf,
-                                                            0xf, false));
-}
-__device__ __forceinline__ float quad_bcast(float x, int s) {  // s: compile-time after unrolling
-  return s == 0 ? quad_bcast_t<0>(x) : s == 1 ? quad_bcast_t<1>(x) : s == 2 ? quad_bcast_t<2>(x)
-                                                                            : quad_bcast_t<3>(x);
-}
-// Value of lane 15 of each row of 16 lanes, in every lane of the row.
-__device__ __forceinline__ float row_last16(float x) {
-  // ds_swizzle bit-mask mode: lane = (lane & 0x10) | 0x0f within 32 lanes.
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x01F0));
-}
-
-__device__ __forceinline__ f16x8_t pack_f16x8(const float (&x)[8]) {
-  f16x8_t r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (_Float16)x[j];
-  return r;
-}
-__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 hv = (__bf16)x[j];
-    hi[j] = hv;
-    lo[j] = (__bf16)(x[j] - (float)hv);
-  }
-}
-
-// 8 consecutive 16-bit values from LDS (16-byte aligned).
-template <typename V>
-__device__ __forceinline__ V lds8(const uint16_t* p) {
-  return __builtin_bit_cast(V, *reinterpret_cast<const u32x4_t*>(p));
-}
-// 4 + 4 16-bit values at p and p + 16 (8-byte aligned each): the permuted k
-// order that matches a B operand made of two stacked accumulator tiles.
-template <typename V>
-__device__ __forceinline__ V lds4x2(const uint16_t* p) {
-  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(p);
-  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(p + 16);
-  const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(V, v);
-}
-__device__ __forceinline__ void lds_f32x8(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-// 4 + 4 floats at p and p + 16 (permuted k order).
-__device__ __forceinline__ void lds_f32x4x2(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 16);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-// Pins a wave-uniform pointer in scalar registers and hides its provenance
-// from the optimiser, so `p + lane_offset` is addressed as SGPR base + 32-bit
-// VGPR offset instead of a hoisted 64-bit address per access.
-template <typename T>
-using gptr = __attribute__((address_space(1))) T*;  // global memory
-template <typename T>
-__device__ __forceinline__ gptr<T> sbase(T* p) {
-  gptr<T> gp = (gptr<T>)p;
-  __asm__ volatile("" : "+s"(gp));
-  return gp;
-}
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-__device__ __forceinline__ uint16_t f16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
 
 template <int DK, int DV>
 struct Cfg {

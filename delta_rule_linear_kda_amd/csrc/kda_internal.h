@@ -36,6 +36,19 @@ struct FwdArgs {
   float* transition = nullptr;
 };
 
+// Two-pass bf16 forward (kda_split_bf16.hip): workspace layout.  Chunks are
+// processed in `blocks` blocks of `bc` chunks per sequence; per block the
+// chunk records occupy [rec, slot), the per-sequence record offsets [slot,
+// carry) and, with more than one block, the carried states [carry, total).
+struct SplitLayout {
+  int bc, blocks;
+  uint64_t rec, slot, carry, total;
+};
+constexpr uint64_t kSplitRecordBudget = 4ull << 30;  // bytes of chunk records per block
+SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk,
+                         int dv);
+hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream);
+
 struct ComposeArgs {
   int32_t num_seqs, num_heads, dk, dv;
   const int32_t* seg_offsets;   // [N + 1], device

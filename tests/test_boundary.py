@@ -39,8 +39,34 @@ def test_version_and_status_strings():
     assert kda.status_str(99) == "unknown kda_status"
 
 
+def _split_bytes(N, T, H, dk, dv):
+    """Host mirror of the two-pass forward's workspace: one block of chunk
+    records (33,664 / 21,120 bytes per 32-token chunk at d_k = 128 / 64,
+    at most 4 GiB unless 8 chunks per sequence need more), the per-sequence
+    record offsets, and the carried states when there is more than one block."""
+    rb = 33664 if dk == 128 else 21120
+    nch_max = max(1, -(-T // 32))
+    every = H * (nch_max + N)
+    budget = (4 << 30) // rb
+    if every <= budget:
+        bc, recs = nch_max, every
+    else:
+        bc = max(8, budget // max(1, H * N))
+        recs = min(every, H * N * bc)
+    bc = min(bc, 0x7FFFFFFF // rb, nch_max)
+    recs = min(recs, H * N * bc)
+    blocks = -(-nch_max // bc)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return up(recs * rb) + up((N + 1) * 4) + (up(N * H * dk * dv * 4) if blocks > 1 else 0)
+
+
 def test_workspace_query():
-    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == 0
+    for args in [(4, 16384, 32, 128, 128), (1, 1 << 20, 96, 128, 128), (16, 131072, 96, 128, 128),
+                 (3, 1000, 2, 64, 128), (1, 0, 4, 128, 64), (5000, 5000, 8, 128, 128)]:
+        assert kda.fwd_workspace_bytes(*args) == _split_bytes(*args), args
+    # the 1M-token, 96-head workload runs in blocks within about 4 GiB
+    assert kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128) < (4 << 30) + (64 << 20)
+    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128, in_dtype=0) == 0   # fp32: none
     L = kda.lib()
     out = ctypes.c_size_t(0)
     assert L.kda_fwd_workspace_bytes(None, ctypes.byref(out)) == NULLP
@@ -53,7 +79,8 @@ def test_workspace_query():
 # Fake, distinct, 16-byte aligned addresses, far apart (never dereferenced).
 BASE = 1 << 40
 P = {name: BASE + i * (1 << 36) for i, name in enumerate(
-    ["q", "k", "v", "a", "b", "gate", "cu", "s0", "o", "sf"])}
+    ["q", "k", "v", "a", "b", "gate", "cu", "s0", "o", "sf", "ws"])}
+P["ws_bytes"] = 1 << 34
 
 
 def fwd(shape, **over):
@@ -62,7 +89,7 @@ def fwd(shape, **over):
     return kda.lib().kda_fwd_chunked(
         ctypes.byref(shape) if shape is not None else None, args["q"], args["k"], args["v"],
         args["a"], args["b"], args["gate"], args["cu"], args["s0"], args["o"], args["sf"],
-        args.get("ws"), args.get("ws_bytes", 0), None)
+        args["ws"], args["ws_bytes"], None)
 
 
 def dec(shape, **over):
@@ -110,10 +137,14 @@ def test_fwd_rejects_aliasing():
     assert fwd(good_shape(), o=P["cu"] - 16) == ALIAS            # o runs into cu_seqlens
 
 
-def test_fwd_rejects_small_workspace_never():
-    # zero workspace is required; a NULL workspace is accepted by the check,
-    # so only verify the query path (a passing call would launch).
-    assert kda.fwd_workspace_bytes(2, 300, 4, 128, 128) == 0
+def test_fwd_rejects_bad_workspace():
+    need = kda.fwd_workspace_bytes(2, 300, 4, 128, 128)
+    assert need > 0
+    assert fwd(good_shape(), ws_bytes=need - 1) == WS
+    assert fwd(good_shape(), ws=None) == WS
+    assert fwd(good_shape(), ws=P["ws"] + 8) == MISAL
+    assert fwd(good_shape(), ws=P["q"]) == ALIAS                  # workspace over an input
+    assert fwd(good_shape(), ws=P["o"] - 64) == ALIAS             # workspace runs into o
 
 
 def test_decode_rejects():
@@ -143,7 +174,8 @@ def fwd_ckpt(shape, interval=512, ckpt=None, capacity=4, **over):
     return kda.lib().kda_fwd_chunked_ckpt(
         ctypes.byref(shape), args["q"], args["k"], args["v"], args["a"], args["b"], args["gate"],
         args["cu"], args["s0"], args["o"], args["sf"], interval,
-        BASE + 11 * (1 << 36) if ckpt is None else ckpt, capacity, None, 0, None)
+        BASE + 11 * (1 << 36) if ckpt is None else ckpt, capacity, args["ws"], args["ws_bytes"],
+        None)
 
 
 @pytest.mark.parametrize("interval,capacity,code", [(0, 4, SHAPE), (100, 4, SHAPE), (32, 4, SHAPE),
@@ -159,6 +191,7 @@ def test_ckpt_rejects_null_misaligned_and_aliasing():
     assert fwd_ckpt(s, ckpt=P["o"]) == ALIAS          # overlaps the output
     assert fwd_ckpt(s, ckpt=P["k"]) == ALIAS          # overlaps an input
     assert fwd_ckpt(s, ckpt=P["sf"]) == ALIAS         # overlaps the final state
+    assert fwd_ckpt(s, ckpt=P["ws"] + 256) == ALIAS   # overlaps the workspace
     assert fwd_ckpt(good_shape(dk=96)) == SHAPE       # the shape is still checked
 
 
@@ -189,9 +222,11 @@ def test_kcp_workspace_query():
         _kcp_layout_bytes(1, 1 << 20, 12, 128, 128, 4096)
     assert kda.kcp_workspace_bytes(3, 1000, 2, 64, 128, 128) == \
         _kcp_layout_bytes(3, 1000, 2, 64, 128, 128)
-    # automatic: many (sequence, head) pairs keep the direct form (no workspace)
-    assert kda.kcp_workspace_bytes(1, 1 << 20, 96, 128, 128, 0) == 0
-    assert kda.kcp_workspace_bytes(4, 4096, 2, 128, 128, 0) == 0      # too short to segment
+    # automatic: many (sequence, head) pairs keep the direct form (its workspace)
+    assert kda.kcp_workspace_bytes(1, 1 << 20, 96, 128, 128, 0) == \
+        kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128)
+    assert kda.kcp_workspace_bytes(4, 4096, 2, 128, 128, 0) == \
+        kda.fwd_workspace_bytes(4, 4096, 2, 128, 128)                  # too short to segment
     for bad in (-64, 100, 32):
         with pytest.raises(kda.KdaError) as e:
             kda.kcp_workspace_bytes(1, 1 << 20, 12, 128, 128, bad)
