@@ -82,8 +82,13 @@ typedef struct kda_shape {
   kda_dtype out_dtype;  /* dtype of o: KDA_F32 (fp32 output only)               */
 } kda_shape;
 
-/* Bytes of device workspace kda_fwd_chunked needs for `shape` (currently 0:
- * the chunked kernel keeps everything in registers and LDS).
+/* Bytes of device workspace kda_fwd_chunked (and kda_fwd_chunked_ckpt) need
+ * for `shape`.  fp32 inputs: 0.  bf16 inputs run in two passes over 32-token
+ * chunks (the chunk operands of every chunk first, in parallel; then the
+ * state chain over them), and the workspace holds one block of those chunk
+ * records: at most about 4 GiB (more only when 8 chunks of every (sequence,
+ * head) pair need more), plus the state carried between blocks.  The size
+ * depends on the shape only.
  * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_DTYPE. */
 KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes);
 
@@ -107,7 +112,9 @@ KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes
  *   final_state  [N, H, dk, dv] fp32, or NULL (= not written); it may be the
  *                same pointer as initial_state (in-place update), but may not
  *                overlap it partially.
- *   workspace    workspace_bytes bytes (may be NULL when 0 are required)
+ *   workspace    at least kda_fwd_workspace_bytes(shape) bytes, 16-byte
+ *                aligned, overlapping no argument (may be NULL when 0 are
+ *                required); its contents are scratch
  * A zero-length sequence produces no rows and final_state = initial_state
  * (or zeros).  o must not overlap any input.
  * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, WORKSPACE, ALIAS, HIP. */
