@@ -8,13 +8,14 @@
 //
 //   pass 1  chunk_prep_bf16_kernel   for every (sequence, head, 32-token
 //           chunk), independently: the decay-scaled operands, A, P, the
-//           inverse X = (I + A)^-1 and W, written as one "chunk record"
-//           (X fp32, P bf16 hi/lo, Gamma_end, beta, 1/|q|, 1/|k|, Qbar fp16,
-//           -W fp16, Kend^T fp16: 33,664 bytes at d_k = 128);
+//           inverse X = (I + A)^-1 and W, written as one "chunk record" with
+//           every row scale folded in: X diag(beta) (bf16 hi/lo), P (bf16
+//           hi/lo), Gamma_end, diag(nq) Qbar, -W and (Kend diag(nk))^T
+//           (fp16), 33,280 bytes at d_k = 128 (nq, nk: 1/|q|, 1/|k|);
 //   pass 2  chunk_state_bf16_kernel  per (sequence, head, d_v slice), the
 //           sequential chain over the records: U0 = X diag(beta) V,
-//           U = U0 - W S, O = diag(nq) Qbar S + P U, S <- diag(Gamma_end) S
-//           + Kend^T diag(nk) U, y = sigmoid(gate) O.
+//           U = U0 - W S, O = Qbar' S + P U, S <- diag(Gamma_end) S
+//           + Kend'^T U, y = sigmoid(gate) O.
 //
 // Why two passes: the fused kernel runs the key-side work once per d_v slice
 // and ties it to the state chain's pace; here it runs once per head with no
@@ -43,37 +44,47 @@ struct Rec {
   static constexpr int LT = kC + 8;   // 16-bit [DK][32] and [32][32] rows
   static constexpr int LX = kC + 4;   // fp32 [32][32] rows
   static constexpr int LA = 20;       // fp32 [16][16] scratch rows
-  static constexpr int dX = 0;                       // X fp32 [32][LX]
-  static constexpr int dPH = dX + kC * LX * 4;       // P hi bf16 [32][LT]
-  static constexpr int dPL = dPH + kC * LT * 2;      // P lo bf16 [32][LT]
-  static constexpr int dGE = dPL + kC * LT * 2;      // Gamma_end fp32 [DK]
-  static constexpr int dBeta = dGE + DK * 4;         // beta fp32 [32]
-  static constexpr int dNQ = dBeta + kC * 4;         // 1/|q| fp32 [32]
-  static constexpr int dNK = dNQ + kC * 4;           // 1/|k| fp32 [32]
-  static constexpr int dQB = dNK + kC * 4;           // Qbar fp16 [32][LB]
-  static constexpr int dW = dQB + kC * LB * 2;       // -W fp16 [32][LB]
-  static constexpr int dKE = dW + kC * LB * 2;       // Kend^T fp16 [DK][LT]
-  static constexpr int dSize = dKE + DK * LT * 2;
-  static constexpr int kSegs = (kC * 128 + 2 * kC * 64 + DK * 4 + 3 * kC * 4 +
-                                2 * kC * DK * 2 + DK * 64) / 16;
-  static constexpr int kBytes = 16 * kSegs;
-  static_assert(dSize % 16 == 0, "alignment");
+  // LDS rows of the record in pass 2, whose reads are 8-byte MFMA operand
+  // pieces from 16 consecutive rows: a row stride of 2 (mod 32) dwords puts
+  // the 16 rows' pieces on distinct banks.
+  static constexpr int RB = DK + 4;   // 16-bit [32][DK] rows
+  static constexpr int RT = kC + 4;   // 16-bit [DK][32] and [32][32] rows
+  static constexpr int dXH = 0;                      // X diag(beta) hi bf16 [32][RT]
+  static constexpr int dXL = dXH + kC * RT * 2;      // X diag(beta) lo bf16 [32][RT]
+  static constexpr int dPH = dXL + kC * RT * 2;      // P hi bf16 [32][RT]
+  static constexpr int dPL = dPH + kC * RT * 2;      // P lo bf16 [32][RT]
+  static constexpr int dGE = dPL + kC * RT * 2;      // Gamma_end fp32 [DK]
+  static constexpr int dQB = dGE + DK * 4;           // diag(nq) Qbar fp16 [32][RB]
+  static constexpr int dW = dQB + kC * RB * 2;       // -W fp16 [32][RB]
+  static constexpr int dKE = dW + kC * RB * 2;       // (Kend diag(nk))^T fp16 [DK][RT]
+  // (globally Kend diag(nk) is stored token-major [32][DK], transposed into
+  // LDS by pass 2)
+  static constexpr int dSize = dKE + DK * RT * 2;
+  // compact (global) byte offsets, same regions in the same order
+  static constexpr int cXH = 0;
+  static constexpr int cXL = cXH + kC * kC * 2;
+  static constexpr int cPH = cXL + kC * kC * 2;
+  static constexpr int cPL = cPH + kC * kC * 2;
+  static constexpr int cGE = cPL + kC * kC * 2;
+  static constexpr int cQB = cGE + DK * 4;
+  static constexpr int cW = cQB + kC * DK * 2;
+  static constexpr int cKE = cW + kC * DK * 2;
+  static constexpr int kBytes = cKE + DK * kC * 2;
+  static constexpr int kSegs = cKE / 16;  // segments copied as they are (all but Kend)
+  static_assert(dSize % 16 == 0 && (RB * 2) % 8 == 0 && (RT * 2) % 8 == 0, "alignment");
 };
 
 // LDS byte offset of compact segment s of a record (0 past the end).
 template <int DK>
 __device__ __forceinline__ int rec_lds_offset(int s) {
   using R = Rec<DK>;
-  constexpr int rows[10] = {kC, kC, kC, 1, 1, 1, 1, kC, kC, DK};
-  constexpr int rowb[10] = {kC * 4, kC * 2, kC * 2, DK * 4, kC * 4, kC * 4, kC * 4,
-                            DK * 2, DK * 2, kC * 2};
-  constexpr int off[10] = {R::dX, R::dPH, R::dPL, R::dGE, R::dBeta, R::dNQ, R::dNK,
-                           R::dQB, R::dW, R::dKE};
-  constexpr int stride[10] = {R::LX * 4, R::LT * 2, R::LT * 2, 0, 0, 0, 0,
-                              R::LB * 2, R::LB * 2, R::LT * 2};
+  constexpr int rows[7] = {kC, kC, kC, kC, 1, kC, kC};
+  constexpr int rowb[7] = {kC * 2, kC * 2, kC * 2, kC * 2, DK * 4, DK * 2, DK * 2};
+  constexpr int off[7] = {R::dXH, R::dXL, R::dPH, R::dPL, R::dGE, R::dQB, R::dW};
+  constexpr int stride[7] = {R::RT * 2, R::RT * 2, R::RT * 2, R::RT * 2, 0, R::RB * 2, R::RB * 2};
   int base = 0, out = 0;
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
+  for (int r = 0; r < 7; ++r) {
     const int per = rowb[r] / 16, nseg = rows[r] * per;
     if (s >= base && s < base + nseg) {
       const int i = s - base;
@@ -126,9 +137,9 @@ __global__ void __launch_bounds__(kPlanThreads)
 //   N   (one wave) 1/|q|, 1/|k| of the 32 rows
 //   AP  A diagonal blocks and their inverses (waves 0, 1), A10 (wave 2), P
 //   W   X10 = -X11 A10 X00 and the W^T tiles
-// then every thread copies its segments of the record to global memory.  The
-// record buffer is double-buffered in LDS, so the copy of chunk c overlaps the
-// E stage of chunk c + 1.
+// Each lane writes its parts of the record straight to global memory (small
+// stores that the L2 merges into whole lines), so the LDS holds only the
+// stage operands (73 KB at d_k = 128: two workgroups per CU).
 template <int DK>
 __global__ void __launch_bounds__(64 * (DK / 16))
     chunk_prep_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -140,12 +151,14 @@ __global__ void __launch_bounds__(64 * (DK / 16))
   constexpr int NP = R::NP, NT = 64 * NP;
   constexpr int LB = R::LB, LT = R::LT, LX = R::LX, LA = R::LA;
   constexpr int NKB = DK / 32;
-  constexpr int NSEG = (R::kSegs + NT - 1) / NT;
   constexpr int oAT = 0;                          // A diagonal blocks^T fp32 [2][16][LA]
   constexpr int oA10 = oAT + 2 * 16 * LA * 4;     // A10 fp32 [16][LA]
   constexpr int oPart = oA10 + 16 * LA * 4;       // squared-norm partials fp32 [NP][64]
-  constexpr int oRec = oPart + NP * 64 * 4;       // two record buffers
-  constexpr int oKT = oRec + 2 * R::dSize;        // Kt bf16 [32][LB]
+  constexpr int oX = oPart + NP * 64 * 4;         // X fp32 [32][LX]
+  constexpr int oBeta = oX + kC * LX * 4;         // beta fp32 [32]
+  constexpr int oNQ = oBeta + kC * 4;             // 1/|q| fp32 [32]
+  constexpr int oNK = oNQ + kC * 4;               // 1/|k| fp32 [32]
+  constexpr int oKT = oNK + kC * 4;               // Kt bf16 [32][LB]
   constexpr int oQH = oKT + kC * LB * 2;          // Qt hi
   constexpr int oQL = oQH + kC * LB * 2;          // Qt lo
   constexpr int oKHH = oQL + kC * LB * 2;         // Kh hi
@@ -154,12 +167,16 @@ __global__ void __launch_bounds__(64 * (DK / 16))
   constexpr int oK1L = oK1H + 16 * LB * 2;        // Kh exp(p_1) lo
   constexpr int oKBT = oK1L + 16 * LB * 2;        // Kbar^T fp16 [DK][LT]
   constexpr int kLds = oKBT + DK * LT * 2;
-  static_assert(oRec % 16 == 0 && kLds <= 160 * 1024, "LDS budget");
+  static_assert(oKT % 16 == 0 && kLds <= 80 * 1024, "LDS budget: two workgroups per CU");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   float* sAT = reinterpret_cast<float*>(smem + oAT);
   float* sA10 = reinterpret_cast<float*>(smem + oA10);
   float* sPart = reinterpret_cast<float*>(smem + oPart);
+  float* rX = reinterpret_cast<float*>(smem + oX);
+  float* rBeta = reinterpret_cast<float*>(smem + oBeta);
+  float* rNQ = reinterpret_cast<float*>(smem + oNQ);
+  float* rNK = reinterpret_cast<float*>(smem + oNK);
   uint16_t* sKT = reinterpret_cast<uint16_t*>(smem + oKT);
   uint16_t* sQH = reinterpret_cast<uint16_t*>(smem + oQH);
   uint16_t* sQL = reinterpret_cast<uint16_t*>(smem + oQL);
@@ -182,9 +199,6 @@ __global__ void __launch_bounds__(64 * (DK / 16))
   unsigned char* rec_item = rec + ((int64_t)H * slot_base[n] + (int64_t)h * cnt) * R::kBytes;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
 
-  int segl[NSEG];  // LDS offsets of this thread's record segments
-#pragma unroll
-  for (int i = 0; i < NSEG; ++i) segl[i] = rec_lds_offset<DK>((int)threadIdx.x + NT * i);
 
   // Lane (li, g): rows li (tile 0) and 16 + li (tile 1), key channels
   // 16 * wave + 4g .. +3; the tokens of a tile run along a 16-lane DPP row.
@@ -218,21 +232,19 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 
   for (int c = c_lo; c < c_hi; ++c) {
     const int64_t c0 = tok_beg + (int64_t)kC * c;
-    unsigned char* rbuf = smem + oRec + ((c - c_lo) & 1) * R::dSize;
-    float* rX = reinterpret_cast<float*>(rbuf + R::dX);
-    uint16_t* rPH = reinterpret_cast<uint16_t*>(rbuf + R::dPH);
-    uint16_t* rPL = reinterpret_cast<uint16_t*>(rbuf + R::dPL);
-    float* rGE = reinterpret_cast<float*>(rbuf + R::dGE);
-    float* rBeta = reinterpret_cast<float*>(rbuf + R::dBeta);
-    float* rNQ = reinterpret_cast<float*>(rbuf + R::dNQ);
-    float* rNK = reinterpret_cast<float*>(rbuf + R::dNK);
-    uint16_t* rQB = reinterpret_cast<uint16_t*>(rbuf + R::dQB);
-    uint16_t* rW = reinterpret_cast<uint16_t*>(rbuf + R::dW);
-    uint16_t* rKE = reinterpret_cast<uint16_t*>(rbuf + R::dKE);
+    // this chunk's record (compact layout), written straight from registers
+    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+        rec_item + (int64_t)(c - c_begin) * R::kBytes, 0, R::kBytes, kBufferRsrcFlags);
+    auto st64 = [&](int off, auto x) __attribute__((always_inline)) {  // 8 bytes
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, x), dst, off, 0, 0);
+    };
     int t_ = threadIdx.x;
     __asm__ volatile("" : "+v"(t_));
     const int lane = t_ % 64, li = lane % 16, g = lane / 16;
 
+    // Qbar and Kend of rows li, 16 + li at channels cb..cb+3, kept until the
+    // norms are known and folded in (AP stage).
+    float qbr[2][4], ker[2][4];
     // ---- E: elementwise ----------------------------------------------------
     {
       const int nrows = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
@@ -299,36 +311,33 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         fend[0][j] = e0[j] * fend[1][j];     // exp(b_end - p_0) = Gamma_end
       }
       if (li == 0)
-        *reinterpret_cast<float4*>(rGE + cb) =
-            make_float4(fend[0][0], fend[0][1], fend[0][2], fend[0][3]);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, f32x4_t{fend[0][0], fend[0][1], fend[0][2], fend[0][3]}),
+            dst, R::cGE + 4 * cb, 0, 0);
       if (wave == 0 && g == 0) {
         rBeta[li] = beta[0];
         rBeta[16 + li] = beta[1];
       }
       uint16_t* kbt = sKBT + cb * LT + li;  // [channel cb + j][token 16 tau + li]
-      uint16_t* ket = rKE + cb * LT + li;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         const int r = 16 * tau + li;
         bf16x4_t ktb, qhb, qlb, khh, khl, k1h, k1l;
-        f16x4_t qbf;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float x = cum[tau][j];  // log2(e) (b - p) <= 0
           const float er = exp2f_fast(x), ir = exp2f_fast(-x);
           const float kt = kf[tau][j] * er, kh = kf[tau][j] * ir;
           const float qt = qf[tau][j] * er;
-          const float qbar = tau ? qt * e0[j] : qt;
           qhb[j] = (__bf16)qt;
           qlb[j] = (__bf16)(qt - (float)qhb[j]);
-          qbf[j] = (_Float16)qbar;
+          qbr[tau][j] = tau ? qt * e0[j] : qt;
           const float kbar = tau ? kt * e0[j] : kt;
-          const float kend = kh * fend[tau][j];
+          ker[tau][j] = kh * fend[tau][j];
           ktb[j] = (__bf16)kt;
           khh[j] = (__bf16)kh;
           khl[j] = (__bf16)(kh - (float)khh[j]);
           kbt[j * LT + 16 * tau] = f16_bits(kbar);
-          ket[j * LT + 16 * tau] = f16_bits(kend);
           if (tau == 0) {  // column operand of the off-diagonal tile: Kh exp(p_1) <= 1
             const float y = kh * e0[j];
             k1h[j] = (__bf16)y;
@@ -340,7 +349,6 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         *reinterpret_cast<bf16x4_t*>(sKHL + r * LB + cb) = khl;
         *reinterpret_cast<bf16x4_t*>(sQH + r * LB + cb) = qhb;
         *reinterpret_cast<bf16x4_t*>(sQL + r * LB + cb) = qlb;
-        *reinterpret_cast<f16x4_t*>(rQB + r * LB + cb) = qbf;
         if (tau == 0) {
           *reinterpret_cast<bf16x4_t*>(sK1H + li * LB + cb) = k1h;
           *reinterpret_cast<bf16x4_t*>(sK1L + li * LB + cb) = k1l;
@@ -363,6 +371,22 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 
     // ---- AP: A and X (waves 0, 1) | A10 (wave 2) | P tiles --------------------
     {
+      {  // diag(nq) Qbar and Kend diag(nk) of this lane's rows into the record
+        const int cb = 16 * wave + 4 * g;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const int r = 16 * tau + li;
+          const float nqr = rNQ[r], nkr = rNK[r];
+          f16x4_t qv, kv;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            qv[j] = (_Float16)(qbr[tau][j] * nqr);
+            kv[j] = (_Float16)(ker[tau][j] * nkr);
+          }
+          st64(R::cQB + 2 * (r * DK + cb), qv);
+          st64(R::cKE + 2 * (r * DK + cb), kv);
+        }
+      }
       // Row scale beta_r nk_r and column scale nk_i of the A tiles.
       auto a_tile = [&](int tr, int ti, const uint16_t* col) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -379,6 +403,9 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         acc[2] *= ber.z * nkr.z * nkc; acc[3] *= ber.w * nkr.w * nkc;
         return acc;
       };
+      // P tile (tr, ti) formed transposed (the key operand on the matrix
+      // cores' A side), so that lane (li, g) ends with row 16 tr + li, columns
+      // 16 ti + 4g .. +3: one 8-byte store each for the hi and lo parts.
       auto p_job = [&](int job) {  // 0 = (0,0), 1 = (1,0), 2 = (1,1)
         const int tr = job == 0 ? 0 : 1, ti = job == 2 ? 1 : 0;
         const uint16_t* colh = job == 1 ? sK1H + li * LB : sKHH + (16 * ti + li) * LB;
@@ -387,27 +414,27 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int cc = 32 * kb + 8 * g;
-          acc = mma_x3(lds8<bf16x8_t>(sQH + (16 * tr + li) * LB + cc),
-                       lds8<bf16x8_t>(sQL + (16 * tr + li) * LB + cc),
-                       lds8<bf16x8_t>(colh + cc), lds8<bf16x8_t>(coll + cc), acc);
+          acc = mma_x3(lds8<bf16x8_t>(colh + cc), lds8<bf16x8_t>(coll + cc),
+                       lds8<bf16x8_t>(sQH + (16 * tr + li) * LB + cc),
+                       lds8<bf16x8_t>(sQL + (16 * tr + li) * LB + cc), acc);
         }
-        const float nki = rNK[16 * ti + li];
-        const float4 nqr = *reinterpret_cast<const float4*>(rNQ + 16 * tr + 4 * g);
-        const float nqv[4] = {nqr.x, nqr.y, nqr.z, nqr.w};
+        const int r = 16 * tr + li;
+        const float nqr = rNQ[r];
+        const float4 nki = *reinterpret_cast<const float4*>(rNK + 16 * ti + 4 * g);
+        const float nkv[4] = {nki.x, nki.y, nki.z, nki.w};
+        bf16x4_t hv, lv;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
-          const float pv = i <= r ? acc[jj] * nqv[jj] * nki : 0.f;
-          const __bf16 hv = (__bf16)pv;
-          rPH[r * LT + i] = __builtin_bit_cast(uint16_t, hv);
-          rPL[r * LT + i] = bf16_bits(pv - (float)hv);
+          const int i = 16 * ti + 4 * g + jj;
+          const float pv = i <= r ? acc[jj] * nqr * nkv[jj] : 0.f;
+          hv[jj] = (__bf16)pv;
+          lv[jj] = (__bf16)(pv - (float)hv[jj]);
         }
+        st64(R::cPH + 2 * (r * kC + 16 * ti + 4 * g), hv);
+        st64(R::cPL + 2 * (r * kC + 16 * ti + 4 * g), lv);
         if (job == 0) {  // the upper tile (0, 1) of P is zero
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            rPH[(4 * g + jj) * LT + 16 + li] = 0;
-            rPL[(4 * g + jj) * LT + 16 + li] = 0;
-          }
+          st64(R::cPH + 2 * (li * kC + 16 + 4 * g), u32x2_t{0u, 0u});
+          st64(R::cPL + 2 * (li * kC + 16 + 4 * g), u32x2_t{0u, 0u});
         }
       };
       if (wave < 2) {
@@ -491,10 +518,25 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         xx[1][0] = x10[0]; xx[1][1] = x10[1]; xx[1][2] = x10[2]; xx[1][3] = x10[3];
         xx[1][4] = x11.x; xx[1][5] = x11.y; xx[1][6] = x11.z; xx[1][7] = x11.w;
       }
-      if (wave == 0) {  // complete X for pass 2: X10, and X01 = 0 (blocks no wave reads here)
-        *reinterpret_cast<float4*>(rX + (16 + li) * LX + 4 * g) =
-            make_float4(x10[0], x10[1], x10[2], x10[3]);
-        *reinterpret_cast<float4*>(rX + li * LX + 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (wave == 0) {  // X diag(beta) as bf16 hi + lo: blocks X00, X01 = 0, X10, X11
+        const float bt[8] = {rBeta[4 * g], rBeta[4 * g + 1], rBeta[4 * g + 2], rBeta[4 * g + 3],
+                             rBeta[16 + 4 * g], rBeta[17 + 4 * g], rBeta[18 + 4 * g],
+                             rBeta[19 + 4 * g]};
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x4_t hv, lv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float xv = xx[rt][4 * half + j] * bt[4 * half + j];
+              hv[j] = (__bf16)xv;
+              lv[j] = (__bf16)(xv - (float)hv[j]);
+            }
+            const int off = 2 * ((16 * rt + li) * kC + 16 * half + 4 * g);
+            st64(R::cXH + off, hv);
+            st64(R::cXL + off, lv);
+          }
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -504,36 +546,31 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         // acc[jj] = W[16 rt + li][16 wave + 4 g + jj]
         const f16x4_t wv = {(_Float16)(-acc[0]), (_Float16)(-acc[1]), (_Float16)(-acc[2]),
                             (_Float16)(-acc[3])};
-        *reinterpret_cast<f16x4_t*>(rW + (16 * rt + li) * LB + 16 * wave + 4 * g) = wv;
+        st64(R::cW + 2 * ((16 * rt + li) * DK + 16 * wave + 4 * g), wv);
       }
     }
-    lds_barrier();  // B3: the record is complete in LDS
-
-    // ---- copy the record out (overlaps the next chunk's E stage) -------------
-    {
-      const auto dst = sbase(rec_item + (int64_t)(c - c_begin) * R::kBytes);
-#pragma unroll
-      for (int i = 0; i < NSEG; ++i) {
-        const int s = (int)threadIdx.x + NT * i;
-        if (s < R::kSegs)
-          *reinterpret_cast<gptr<u32x4_t>>(dst + 16 * s) =
-              *reinterpret_cast<const u32x4_t*>(rbuf + segl[i]);
-      }
-    }
+    lds_barrier();  // B3: scratch free for the next chunk
   }
 }
 
 // ============================ pass 2 ==========================================
-// One workgroup of DV/16 waves per (sequence, head, d_v slice of DV columns);
-// wave s owns state columns [16 s, 16 s + 16) of the slice in MFMA
-// accumulator registers for the block.  Records stream global -> registers ->
-// LDS (two LDS buffers, two register sets): the record of chunk c + 2 is
-// requested while chunk c is computed and written to LDS one chunk later, so
-// one workgroup barrier per chunk orders everything.  Every global request
-// and store issues on every iteration (indices clamped, store ranges emptied
-// when inactive), so the in-order memory counter never needs a full drain.
-template <int DK, int DV, bool CKPT>
-__global__ void __launch_bounds__(64 * (DV / 16))
+// One workgroup per (sequence, head, 64-column d_v slice) with two wave groups:
+//   state waves (4)   wave s owns state columns [16 s, 16 s + 16) of the slice
+//                     in MFMA accumulator registers for the whole block and
+//                     runs the chain of chunk c from LDS;
+//   stream waves (4)  move the record and the v and gate tiles of chunk c + 1
+//                     from global memory into the other LDS buffer, with the
+//                     requests for the next kAhead chunks in flight in their
+//                     own registers.
+// One workgroup barrier per chunk orders the two LDS buffers.  The state
+// waves' only global accesses are the output stores (no waits on memory); the
+// stream waves' only global accesses are loads, consumed in request order.
+constexpr int kStateWaves = 4;   // 64 columns
+constexpr int kStreamWaves = 4;
+constexpr int kAhead = 3;        // chunks requested ahead of the one written to LDS
+
+template <int DK, bool CKPT>
+__global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
                             const int32_t* __restrict__ cu_seqlens,
                             const int32_t* __restrict__ slot_base,
@@ -543,10 +580,20 @@ __global__ void __launch_bounds__(64 * (DV / 16))
                             int num_items, int dvt, int nsl, int c_begin, int bc, int ckpt_iv,
                             float* __restrict__ ckpt, long long ckpt_cap) {
   using R = Rec<DK>;
-  constexpr int NS = DV / 16, NT = 64 * NS, NCT = DK / 16, NKB = DK / 32;
-  constexpr int LB = R::LB, LT = R::LT, LX = R::LX;
-  constexpr int NSEG = (R::kSegs + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * R::dSize];
+  constexpr int DV = 16 * kStateWaves;
+  constexpr int NCT = DK / 16, NKB = DK / 32;
+  constexpr int LB = R::RB, LT = R::RT;
+  // LDS buffer: record, then the v and gate tiles [32][VS] (16-bit); the
+  // 8-byte row padding puts the four rows a state-wave read touches on
+  // distinct banks.
+  constexpr int VS = DV + 4;
+  constexpr int dV = R::dSize, dG = dV + kC * VS * 2, dBuf = dG + kC * VS * 2;
+  constexpr int NTS = 64 * kStreamWaves;            // stream threads
+  constexpr int NSEG = (R::kSegs + NTS - 1) / NTS;  // record segments per stream thread
+  constexpr int VPR = DV * 2 / 16;                  // 16-byte segments per tile row
+  constexpr int VSEG = kC * VPR / NTS;              // tile segments per stream thread
+  static_assert(dBuf % 16 == 0 && (kC * VPR) % NTS == 0 && VSEG >= 1, "layout");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf];
 
   // Block -> (item, slice): the nsl slices of an item sit 8 blocks apart, on
   // the same XCD, so the second slice's record reads hit that XCD's L2.
@@ -560,125 +607,224 @@ __global__ void __launch_bounds__(64 * (DV / 16))
   if (c_begin > 0 && c_begin >= nch) return;  // finished in an earlier block
   const int c_end = min(c_begin + bc, nch);
   const int cnt = c_end - c_begin;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const unsigned char* rec_item = rec + ((int64_t)H * slot_base[n] + (int64_t)h * max(cnt, 0)) * R::kBytes;
+
+  if (wave >= kStateWaves) {
+    // ======================= stream waves =====================================
+    if (cnt == 0) return;  // the state waves then run no barrier either
+    const int st = (int)threadIdx.x - 64 * kStateWaves;
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(rec_item), 0, cnt * R::kBytes, kBufferRsrcFlags);
+    int segl[NSEG];       // LDS offsets of this thread's record segments
+    uint32_t segg[NSEG];  // their byte offsets in a record
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      const int sg = st + NTS * i;
+      segl[i] = rec_lds_offset<DK>(sg);
+      segg[i] = 16u * (uint32_t)(sg < R::kSegs ? sg : R::kSegs - 1);
+    }
+    int vl[VSEG];       // LDS offsets (within a tile) of this thread's v / gate segments
+    uint32_t vgo[VSEG];  // their byte offsets from the chunk's first row
+#pragma unroll
+    for (int i = 0; i < VSEG; ++i) {
+      const int sv = st + NTS * i, row = sv / VPR, c8 = sv % VPR;
+      vl[i] = row * VS * 2 + c8 * 16;
+      vgo[i] = 2u * (uint32_t)(row * H * dvt + 8 * c8);
+    }
+    // Kend' arrives token-major; thread st < KJOBS transposes tokens 2 kp and
+    // 2 kp + 1 of channels 8 kg .. 8 kg + 7 (consecutive lanes: consecutive
+    // token pairs, so the 32-bit LDS writes fall on distinct banks).
+    constexpr int KJOBS = 16 * (DK / 8);
+    const int kp = st % 16, kg = st / 16;
+    const uint32_t kgo = 2u * (uint32_t)(R::cKE / 2 + 2 * kp * DK + 8 * kg);
+    u32x4_t Rr[kAhead][NSEG], Rv[kAhead][VSEG], Rq[kAhead][VSEG], Rk[kAhead][2];
+    // Requests for chunk c_begin + min(s, cnt - 1) into register set K; rows
+    // past the sequence's end read as zero (their range is empty).
+    auto fetch = [&](int s, auto Kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(Kc)::value;
+      const int cs = min(s, cnt - 1);
+      const int soff = cs * R::kBytes;
+#pragma unroll
+      for (int i = 0; i < NSEG; ++i)
+        Rr[K][i] = __builtin_bit_cast(u32x4_t,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rrs, segg[i], soff, 0));
+      if (st < KJOBS) {
+        Rk[K][0] = __builtin_bit_cast(u32x4_t,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo, soff, 0));
+        Rk[K][1] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo + 2 * DK, soff, 0));
+      }
+      const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + cs);
+      const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+      const uint32_t range = (uint32_t)nr * (uint32_t)(H * dvt) * 2u;
+      const int64_t eoff = (c0 * H + h) * dvt + col0;
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(v + eoff), 0, range, kBufferRsrcFlags);
+#pragma unroll
+      for (int i = 0; i < VSEG; ++i)
+        Rv[K][i] = __builtin_bit_cast(u32x4_t,
+                                      __builtin_amdgcn_raw_buffer_load_b128(vr, vgo[i], 0, 0));
+      if (gate) {
+        const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(gate + eoff), 0, range, kBufferRsrcFlags);
+#pragma unroll
+        for (int i = 0; i < VSEG; ++i)
+          Rq[K][i] = __builtin_bit_cast(u32x4_t,
+                                        __builtin_amdgcn_raw_buffer_load_b128(gr, vgo[i], 0, 0));
+      }
+    };
+    // Register set K into LDS buffer b (8-byte writes: padded rows).
+    auto put = [&](int b, auto Kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(Kc)::value;
+      unsigned char* base = smem + b * dBuf;
+#pragma unroll
+      for (int i = 0; i < NSEG; ++i)
+        if (st + NTS * i < R::kSegs) {
+          u32x2_t* d = reinterpret_cast<u32x2_t*>(base + segl[i]);
+          d[0] = u32x2_t{Rr[K][i][0], Rr[K][i][1]};
+          d[1] = u32x2_t{Rr[K][i][2], Rr[K][i][3]};
+        }
+      if (st < KJOBS) {
+        // channel 8 kg + e: (token 2 kp, token 2 kp + 1) as one 32-bit word
+        uint32_t* d = reinterpret_cast<uint32_t*>(base + R::dKE) + ((8 * kg) * LT + 2 * kp) / 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          d[e * LT / 2] = __builtin_amdgcn_perm(Rk[K][1][e / 2], Rk[K][0][e / 2],
+                                                (e & 1) ? 0x07060302u : 0x05040100u);
+      }
+#pragma unroll
+      for (int i = 0; i < VSEG; ++i) {
+        u32x2_t* d = reinterpret_cast<u32x2_t*>(base + dV + vl[i]);
+        d[0] = u32x2_t{Rv[K][i][0], Rv[K][i][1]};
+        d[1] = u32x2_t{Rv[K][i][2], Rv[K][i][3]};
+        if (gate) {
+          u32x2_t* e = reinterpret_cast<u32x2_t*>(base + dG + vl[i]);
+          e[0] = u32x2_t{Rq[K][i][0], Rq[K][i][1]};
+          e[1] = u32x2_t{Rq[K][i][2], Rq[K][i][3]};
+        }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    static_assert(kAhead == 3, "the unrolled loop below rotates three register sets");
+    fetch(0, I0());
+    fetch(1, I1());
+    fetch(2, I2());
+    put(0, I0());
+    fetch(3, I0());
+    lds_barrier();
+    // step s: chunk s + 1 (set (s + 1) % 3) into buffer (s + 1) & 1, then
+    // chunk s + 4 requested into that set
+    for (int s0 = 0; s0 < cnt; s0 += 3) {
+      if (s0 < cnt) {
+        put((s0 + 1) & 1, I1());
+        fetch(s0 + 4, I1());
+        lds_barrier();
+      }
+      if (s0 + 1 < cnt) {
+        put((s0 + 2) & 1, I2());
+        fetch(s0 + 5, I2());
+        lds_barrier();
+      }
+      if (s0 + 2 < cnt) {
+        put((s0 + 3) & 1, I0());
+        fetch(s0 + 6, I0());
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ======================= state waves ========================================
   const float* s_src = c_begin == 0 ? s_init : carry;
   float* s_dst = c_begin + bc >= nch ? s_final : carry;
-  const int sw = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int sw = wave;
   const int64_t st_off = (int64_t)item * DK * dvt + col0;
-
+  int t0_ = threadIdx.x;
+  __asm__ volatile("" : "+v"(t0_));
+  const int lane = t0_ % 64, g = lane / 16, li = lane % 16;
+  const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
   f32x4_t S[NCT];
-  {
-    const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-    const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
-    if (s_src) {
-      const auto sp = sbase(s_src + st_off);
+  if (s_src) {
+    const auto sp = sbase(s_src + st_off);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * dvt];
-    } else {
+      for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * dvt];
+  } else {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   if (cnt > 0) {
     int64_t ck_off = 0;  // first recorded-state slot of this sequence
     if (CKPT)
       for (int m = 0; m < n; ++m) ck_off += (int64_t)(cu_seqlens[m + 1] - cu_seqlens[m]) / ckpt_iv;
-    const unsigned char* rec_item =
-        rec + ((int64_t)H * slot_base[n] + (int64_t)h * cnt) * R::kBytes;
-    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(rec_item), 0, cnt * R::kBytes, kBufferRsrcFlags);
-    int segl[NSEG];      // LDS offsets of this thread's record segments
-    uint32_t segg[NSEG];  // their byte offsets in a record
-#pragma unroll
-    for (int i = 0; i < NSEG; ++i) {
-      const int s = (int)threadIdx.x + NT * i;
-      segl[i] = rec_lds_offset<DK>(s);
-      segg[i] = 16u * (uint32_t)(s < R::kSegs ? s : R::kSegs - 1);
-    }
-    u32x4_t Rg[2][NSEG];
-    auto rec_load = [&](int cc, u32x4_t(&dst)[NSEG]) __attribute__((always_inline)) {
-      const int soff = (cc - c_begin) * R::kBytes;
-#pragma unroll
-      for (int i = 0; i < NSEG; ++i)
-        dst[i] = __builtin_bit_cast(u32x4_t,
-                                    __builtin_amdgcn_raw_buffer_load_b128(rrs, segg[i], soff, 0));
-    };
-    auto rec_to_lds = [&](int b, const u32x4_t(&src)[NSEG]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < NSEG; ++i)
-        if ((int)threadIdx.x + NT * i < R::kSegs)
-          *reinterpret_cast<u32x4_t*>(smem + b * R::dSize + segl[i]) = src[i];
-    };
-
-    int t0_ = threadIdx.x;
-    __asm__ volatile("" : "+v"(t0_));
-    const int lane = t0_ % 64, g = lane / 16, li = lane % 16;
     const int jcol = 16 * sw + li;
-    const uint32_t hsh = 16u * (li & 1);  // which half of a loaded word is this lane's
-    // v and gate of a chunk: lane (li, g) reads rows 16 (i / 4) + 4 g + i % 4,
-    // as the aligned 32-bit word holding its bf16 (the lane pair (jcol & ~1,
-    // jcol | 1) shares it); rows past the sequence's end read as zero.
-    // Every offset a range check must see is in the lane offset (the
-    // wave-uniform offset is kept out of it).
-    uint32_t vgo[8];
+    // v / gate words of rows 16 (i / 4) + 4 g + i % 4 at the lane's column
+    // (the aligned 32-bit word holding its bf16), and the perm selector of
+    // the lane's half
+    int vwo[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      vgo[i] = 2u * (uint32_t)((16 * (i / 4) + 4 * g + (i % 4)) * H * dvt + (jcol & ~1));
-    uint32_t rv[8], rgr[8];
-    float rg[8];
-    auto load_vg = [&](int cc) __attribute__((always_inline)) {
-      const int64_t c0 = tok_beg + (int64_t)kC * cc;
-      const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
-      const uint32_t range = (uint32_t)nr * (uint32_t)(H * dvt) * 2u;
-      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(v + (c0 * H + h) * dvt + col0), 0, range, kBufferRsrcFlags);
-      // Without a gate the same rows of v are read (and ignored), so the
-      // number of requests never depends on the gate.
-      const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>((gate ? gate : v) + (c0 * H + h) * dvt + col0), 0, range,
-          kBufferRsrcFlags);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        rv[i] = __builtin_amdgcn_raw_buffer_load_b32(vr, vgo[i], 0, 0);
-        rgr[i] = __builtin_amdgcn_raw_buffer_load_b32(gr, vgo[i], 0, 0);
-      }
-    };
+    for (int i = 0; i < 8; ++i) vwo[i] = ((16 * (i / 4) + 4 * g + (i % 4)) * VS + (jcol & ~1)) * 2;
+    const uint32_t hsh = 16u * (li & 1);
+    const uint32_t vsel = (li & 1) ? 0x07060302u : 0x05040100u;
     f32x4_t O[2], U[2];
-    // Chunk cc from LDS buffer b: U0, U = U0 - W S, O = diag(nq) Qbar S + P U,
-    // then (when act) S <- diag(Gamma_end) S + Kend^T diag(nk) U.
-    auto compute = [&](int b, int cc, bool act) __attribute__((always_inline)) {
-      const unsigned char* rb = smem + b * R::dSize;
-      const float* xb = reinterpret_cast<const float*>(rb + R::dX);
-      const float* be = reinterpret_cast<const float*>(rb + R::dBeta);
-      const float* nq = reinterpret_cast<const float*>(rb + R::dNQ);
-      const float* nk = reinterpret_cast<const float*>(rb + R::dNK);
-      const float* ge = reinterpret_cast<const float*>(rb + R::dGE);
-      const uint16_t* wp = reinterpret_cast<const uint16_t*>(rb + R::dW);
-      const uint16_t* qbp = reinterpret_cast<const uint16_t*>(rb + R::dQB);
+    float rg[8];
+    lds_barrier();  // the first buffer is in LDS
+    for (int s = 0; s < cnt; ++s) {
+      const int cc = c_begin + s;
+      const unsigned char* rb = smem + (s & 1) * dBuf;
+      const uint16_t* xh = reinterpret_cast<const uint16_t*>(rb + R::dXH);
+      const uint16_t* xl = reinterpret_cast<const uint16_t*>(rb + R::dXL);
       const uint16_t* ph = reinterpret_cast<const uint16_t*>(rb + R::dPH);
       const uint16_t* pl = reinterpret_cast<const uint16_t*>(rb + R::dPL);
+      const float* ge = reinterpret_cast<const float*>(rb + R::dGE);
+      const uint16_t* qbp = reinterpret_cast<const uint16_t*>(rb + R::dQB);
+      const uint16_t* wp = reinterpret_cast<const uint16_t*>(rb + R::dW);
       const uint16_t* kep = reinterpret_cast<const uint16_t*>(rb + R::dKE);
+      // operands of the chunk, requested first
+      bf16x8_t aXH[2], aXL[2], aPH[2], aPL[2];
+      f16x8_t aW[2][NKB], aQ[2][NKB];
+      uint32_t rv[8], rgr[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        rg[j] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
-      {
-        float rr[8];
+      for (int i = 0; i < 8; ++i) {
+        rv[i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i]);
+        rgr[i] = gate ? *reinterpret_cast<const uint32_t*>(rb + dG + vwo[i]) : 0u;
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          rr[j] = be[16 * (j >> 2) + 4 * g + (j & 3)] * __uint_as_float((rv[j] >> hsh) << 16);
-        bf16x8_t rh, rl;
-        split_bf16x8(rr, rh, rl);
+      for (int rt = 0; rt < 2; ++rt) {
+        const int off = (16 * rt + li) * LT + 4 * g;
+        aXH[rt] = lds4x2<bf16x8_t>(xh + off);
+        aXL[rt] = lds4x2<bf16x8_t>(xl + off);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          float xx[8];
-          lds_f32x4x2(xb + (16 * rt + li) * LX + 4 * g, xx);
-          bf16x8_t xh, xl;
-          split_bf16x8(xx, xh, xl);
-          U[rt] = mma_x3(xh, xl, rh, rl, f32x4_t{0.f, 0.f, 0.f, 0.f});
+          aW[rt][kb] = lds4x2<f16x8_t>(wp + (16 * rt + li) * LB + 32 * kb + 4 * g);
+          aQ[rt][kb] = lds4x2<f16x8_t>(qbp + (16 * rt + li) * LB + 32 * kb + 4 * g);
         }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int off = (16 * rt + li) * LT + 4 * g;
+        aPH[rt] = lds4x2<bf16x8_t>(ph + off);
+        aPL[rt] = lds4x2<bf16x8_t>(pl + off);
       }
+      // U0 = (X diag(beta))_hi V + (X diag(beta))_lo V; v is exact in bf16
+      bf16x8_t vb;
+      {
+        u32x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(rv[2 * i + 1], rv[2 * i], vsel);
+        vb = __builtin_bit_cast(bf16x8_t, w);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        U[rt] = mma_bf16(aXH[rt], vb, mma_bf16(aXL[rt], vb, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      // U += (-W) S, O = Qbar' S
       O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       O[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -688,110 +834,71 @@ __global__ void __launch_bounds__(64 * (DV / 16))
         for (int j = 0; j < 8; ++j) sbk[j] = (_Float16)S[2 * kb + (j >> 2)][j & 3];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          U[rt] = mma_f16(lds4x2<f16x8_t>(wp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk, U[rt]);
-          O[rt] = mma_f16(lds4x2<f16x8_t>(qbp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk, O[rt]);
+          U[rt] = mma_f16(aW[rt][kb], sbk, U[rt]);
+          O[rt] = mma_f16(aQ[rt][kb], sbk, O[rt]);
         }
       }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const float4 nr = *reinterpret_cast<const float4*>(nq + 16 * rt + 4 * g);
-        O[rt][0] *= nr.x; O[rt][1] *= nr.y; O[rt][2] *= nr.z; O[rt][3] *= nr.w;
-      }
+      // O += P U (U as bf16 hi + lo); Kend'^T U takes U in fp16
       f16x8_t uf;
       bf16x8_t uh, ul;
       {
-        float uu[8], us[8];
+        float uu[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) uu[j] = U[j >> 2][j & 3];
-        const float4 n0 = *reinterpret_cast<const float4*>(nk + 4 * g);
-        const float4 n1 = *reinterpret_cast<const float4*>(nk + 16 + 4 * g);
-        us[0] = uu[0] * n0.x; us[1] = uu[1] * n0.y; us[2] = uu[2] * n0.z; us[3] = uu[3] * n0.w;
-        us[4] = uu[4] * n1.x; us[5] = uu[5] * n1.y; us[6] = uu[6] * n1.z; us[7] = uu[7] * n1.w;
-        uf = pack_f16x8(us);
+        uf = pack_f16x8(uu);
         split_bf16x8(uu, uh, ul);
       }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int off = (16 * rt + li) * LT + 4 * g;
-        O[rt] = mma_x3(lds4x2<bf16x8_t>(ph + off), lds4x2<bf16x8_t>(pl + off), uh, ul, O[rt]);
-      }
-      if (act) {
+      for (int rt = 0; rt < 2; ++rt) O[rt] = mma_x3(aPH[rt], aPL[rt], uh, ul, O[rt]);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const float4 gv = *reinterpret_cast<const float4*>(ge + 16 * ct + 4 * g);
-          f32x4_t acc;
-          acc[0] = gv.x * S[ct][0]; acc[1] = gv.y * S[ct][1];
-          acc[2] = gv.z * S[ct][2]; acc[3] = gv.w * S[ct][3];
-          S[ct] = mma_f16(lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g), uf, acc);
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 gv = *reinterpret_cast<const float4*>(ge + 16 * ct + 4 * g);
+        f32x4_t acc;
+        acc[0] = gv.x * S[ct][0]; acc[1] = gv.y * S[ct][1];
+        acc[2] = gv.z * S[ct][2]; acc[3] = gv.w * S[ct][3];
+        S[ct] = mma_f16(lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g), uf, acc);
+      }
+      if constexpr (CKPT) {
+        // the state after the first `done` tokens, when that is a multiple of
+        // the recording interval
+        const int64_t done = (int64_t)kC * (cc + 1);
+        if (done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
+          const int64_t slot = ck_off + done / ckpt_iv - 1;
+          if (slot < ckpt_cap) {
+            // lane address held in vector registers (no scalar base)
+            uint64_t ad = reinterpret_cast<uint64_t>(ckpt + (slot * H + h) * DK * dvt + col0 + st_lane);
+            __asm__ volatile("" : "+v"(ad));
+            float* sp = reinterpret_cast<float*>(ad);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) sp[(16 * ct + jj) * dvt] = S[ct][jj];
+          }
         }
       }
-    };
-    auto record = [&](int cc) __attribute__((always_inline)) {
-      const int64_t done = (int64_t)kC * (cc + 1);
-      if (done % ckpt_iv == 0 && done <= tok_end - tok_beg) {
-        const int64_t slot = ck_off + done / ckpt_iv - 1;
-        if (slot < ckpt_cap) {
-          const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
-          // lane address held in vector registers (no scalar base)
-          uint64_t ad = reinterpret_cast<uint64_t>(ckpt + (slot * H + h) * DK * dvt + col0 + st_lane);
-          __asm__ volatile("" : "+v"(ad));
-          float* sp = reinterpret_cast<float*>(ad);
+      // gated output through a buffer resource whose range ends after the
+      // chunk's last valid row
+      {
+        const int64_t c0 = tok_beg + (int64_t)kC * cc;
+        const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
+        const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sp[(16 * ct + jj) * dvt] = S[ct][jj];
+        for (int j = 0; j < 8; ++j) {
+          float y = O[j >> 2][j & 3];
+          if (gate)
+            y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __float_as_uint(y), rs,
+              4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
         }
       }
-    };
-    // Gated output of chunk cc through a buffer resource whose range ends
-    // after the chunk's last valid row (0 when inactive): the eight stores
-    // always issue and the hardware drops the rest.
-    auto epilogue = [&](int cc, bool act) __attribute__((always_inline)) {
-      const int64_t c0 = tok_beg + (int64_t)kC * (act ? cc : c_begin);
-      const int nr = act ? (int)(tok_end - c0 < kC ? tok_end - c0 : kC) : 0;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
-      const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float y = O[j >> 2][j & 3];
-        if (gate) y *= rg[j];
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __float_as_uint(y), rs, 4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)),
-            0, 0);
-      }
-    };
-    // Iteration for chunk cc, LDS buffer and register set B = (cc - c_begin) & 1.
-    auto step = [&](int cc, auto Bc) __attribute__((always_inline)) {
-      constexpr int B = decltype(Bc)::value;
-      const bool act = cc < c_end;
-      rec_load(min(cc + 2, c_end - 1), Rg[B]);
-      compute(B, cc, act);
-      if constexpr (CKPT)
-        if (act) record(cc);
-      load_vg(min(cc + 1, c_end - 1));
-      epilogue(cc, act);
-      rec_to_lds(B ^ 1, Rg[B ^ 1]);
       lds_barrier();
-    };
-
-    rec_load(c_begin, Rg[0]);
-    rec_load(min(c_begin + 1, c_end - 1), Rg[1]);
-    load_vg(c_begin);
-    // Let everything requested so far arrive before the loop: a request still
-    // pending on entry would make the loop's waits count its own stores too.
-    __builtin_amdgcn_s_waitcnt(0);
-    rec_to_lds(0, Rg[0]);
-    lds_barrier();
-    for (int cc = c_begin; cc < c_end; cc += 2) {
-      step(cc, std::integral_constant<int, 0>());
-      step(cc + 1, std::integral_constant<int, 1>());
     }
   }
 
   if (s_dst) {
-    const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
-    const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
     const auto sp = sbase(s_dst + st_off);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -845,8 +952,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
   const int H = p.num_heads, N = p.num_seqs;
-  const int nsl = p.dv == 128 && 2 * items <= device_cus() ? 2 : 1;
-  const int dvs = p.dv / nsl;  // columns per pass-2 workgroup
+  const int nsl = p.dv / 64;  // pass-2 workgroups per item (64 columns each)
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;
   // chunks per pass-1 workgroup: enough workgroups to fill the GPU several
@@ -869,28 +975,19 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                          (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
                          (int)items, c_begin, w.bc, cpw, rec);
-    auto launch_state = [&](auto kern, int threads) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(threads), 0, stream,
-                         (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
-                         (const unsigned char*)rec, p.initial_state, carry, p.final_state,
+    auto launch_state = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (kStateWaves + kStreamWaves)), 0,
+                         stream, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens,
+                         slot, (const unsigned char*)rec, p.initial_state, carry, p.final_state,
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
-    if (p.dk == 128) {
-      if (dvs == 128)
-        ck ? launch_state(chunk_state_bf16_kernel<128, 128, true>, 512)
-           : launch_state(chunk_state_bf16_kernel<128, 128, false>, 512);
-      else
-        ck ? launch_state(chunk_state_bf16_kernel<128, 64, true>, 256)
-           : launch_state(chunk_state_bf16_kernel<128, 64, false>, 256);
-    } else {
-      if (dvs == 128)
-        ck ? launch_state(chunk_state_bf16_kernel<64, 128, true>, 512)
-           : launch_state(chunk_state_bf16_kernel<64, 128, false>, 512);
-      else
-        ck ? launch_state(chunk_state_bf16_kernel<64, 64, true>, 256)
-           : launch_state(chunk_state_bf16_kernel<64, 64, false>, 256);
-    }
+    if (p.dk == 128)
+      ck ? launch_state(chunk_state_bf16_kernel<128, true>)
+         : launch_state(chunk_state_bf16_kernel<128, false>);
+    else
+      ck ? launch_state(chunk_state_bf16_kernel<64, true>)
+         : launch_state(chunk_state_bf16_kernel<64, false>);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
