@@ -48,10 +48,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
-CHUNK = 32                   # chunk length of the bf16 forward kernel
-FWD_KERNEL = "chunk_fwd_bf16_kernel<128, 64, false>"  # d_v-sliced launch at 96 heads
-FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_chunk_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_T1048576_H96_d128.traffic.txt")
+CHUNK = 32                   # chunk length of the bf16 forward kernels
+# The bf16 forward runs in blocks of chunks, each block a plan kernel, the
+# chunk-record pass and the state pass; the roofline is taken over the whole
+# forward call (every launch of these kernels).
+FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, false>",
+               "split_plan_kernel")
+FWD_KERNEL = "split forward: " + " + ".join(FWD_KERNELS[:2]) + " (per block of chunks)"
+FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_split_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_fwd_bf16_T1048576_H96_d128.traffic.txt")
 COPY_PROBE_BYTES = 2 << 30
 
 
@@ -254,10 +259,11 @@ def read_traffic() -> dict | None:
 
 
 def pmc_summary(fetch_csv: str, write_csv: str) -> str:
-    """Summarise a FETCH_SIZE run and a WRITE_SIZE run of
-    ``bench.py --copy-probe`` (rocprofv3 --pmc, csv output).  Each counter is
+    """Summarise a FETCH_SIZE run and a WRITE_SIZE run of ``bench.py --steps 1
+    --warmup 0 --copy-probe`` (rocprofv3 --pmc, csv output).  Each counter is
     calibrated on the plain copy of COPY_PROBE_BYTES (it reads and writes
-    exactly that many bytes), then applied to the forward kernel's dispatches."""
+    exactly that many bytes), then summed over every dispatch of the forward's
+    kernels: the run makes exactly one forward call."""
     import csv
 
     def per_dispatch(path: str, counter: str) -> dict:
@@ -284,22 +290,26 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
     _, cfl = pick(fetch, "copyBuffer")
     _, cwl = pick(write, "copyBuffer")
     cf, cw = max(cfl), max(cwl)
-    kname, kfl = pick(fetch, FWD_KERNEL.split("  ")[0])
-    _, kwl = pick(write, FWD_KERNEL)
-    kf, kw = sum(kfl) / len(kfl), sum(kwl) / len(kwl)
     f_scale = COPY_PROBE_BYTES / (cf * 1024.0)
     w_scale = COPY_PROBE_BYTES / (cw * 1024.0)
-    fb, wb = kf * 1024.0 * f_scale, kw * 1024.0 * w_scale
     lines = [
-        f"# HBM traffic of {kname}",
+        "# HBM traffic of one forward call (every dispatch of its kernels)",
         "# workload: 1 x 1048576 tokens, H=96, dk=dv=128, bf16 inputs, fp32 o, final state",
         f"copy_probe_bytes: {COPY_PROBE_BYTES}",
         f"copy_fetch_kib: {cf:.1f}",
         f"copy_write_kib: {cw:.1f}",
         f"fetch_scale: {f_scale:.4f}",
         f"write_scale: {w_scale:.4f}",
-        f"kernel_fetch_kib: {kf:.1f}",
-        f"kernel_write_kib: {kw:.1f}",
+    ]
+    fb = wb = 0.0
+    for kn in FWD_KERNELS:
+        name, kfl = pick(fetch, kn)
+        _, kwl = pick(write, kn)
+        kf, kw = sum(kfl) * 1024.0 * f_scale, sum(kwl) * 1024.0 * w_scale
+        fb, wb = fb + kf, wb + kw
+        lines += [f"# {name[:100]}: {len(kfl)} dispatches",
+                  f"fetch_bytes[{kn}]: {kf:.0f}", f"write_bytes[{kn}]: {kw:.0f}"]
+    lines += [
         f"fetch_bytes_per_launch: {fb:.0f}",
         f"write_bytes_per_launch: {wb:.0f}",
         f"kernel_code_sha256: {_sha256(FWD_SOURCE)}",
