@@ -84,13 +84,32 @@ const char* kda_status_str(kda_status st) {
   return "unknown kda_status";
 }
 
+}  // extern "C"
+
+namespace {
+
+// bf16 inputs take the two-pass form when the fused kernel's workgroups
+// ((sequence, head) pairs, times two d_v slices when that still fits in one
+// round) would leave compute units of the current device idle; otherwise the
+// fused kernel, which then has no idle units and no record round trip.
+bool fwd_uses_split(const kda_shape& s) {
+  if (s.in_dtype != KDA_BF16 || s.num_seqs <= 0) return false;
+  const int64_t items = int64_t(s.num_seqs) * s.num_heads, cus = kda::device_cus();
+  const int64_t fused_wgs = s.dv == 128 && 2 * items <= cus ? 2 * items : items;
+  return fused_wgs < cus;
+}
+
+}  // namespace
+
+extern "C" {
+
 kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes) {
   if (!bytes) return KDA_ERR_NULL_POINTER;
   const kda_status st = check_shape(shape);
   if (st != KDA_OK) return st;
   const kda_shape& s = *shape;
-  // bf16 inputs run the two-pass form, whose chunk records live here
-  *bytes = s.in_dtype == KDA_BF16 && s.num_seqs > 0
+  // the two-pass form's chunk records live here
+  *bytes = fwd_uses_split(s)
                ? size_t(kda::split_layout(s.num_seqs, s.total_tokens, s.num_heads, s.dk, s.dv)
                             .total)
                : 0;
@@ -196,7 +215,7 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
   p.ckpt_interval = ckpt_capacity > 0 ? ckpt_interval : 0;
   p.ckpt = ckpt;
   p.ckpt_capacity = ckpt_capacity;
-  const hipError_t e = s.in_dtype == KDA_BF16
+  const hipError_t e = fwd_uses_split(s)
                            ? kda::launch_fwd_split_bf16(p, workspace, static_cast<hipStream_t>(stream))
                            : kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KDA_ERR_HIP;

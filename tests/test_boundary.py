@@ -63,10 +63,23 @@ def _split_bytes(N, T, H, dk, dv):
     return up(recs * rb) + up((N + 1) * 4) + (up(N * H * dk * dv * 4) if blocks > 1 else 0)
 
 
+def _uses_split(N, H, dv, cus=256):
+    """The two-pass form runs when the fused kernel's workgroups ((sequence,
+    head) pairs, two d_v slices each when that fits one round) would leave
+    compute units idle (no GPU here: the library assumes 256)."""
+    items = N * H
+    fused = 2 * items if dv == 128 and 2 * items <= cus else items
+    return fused < cus
+
+
 def test_workspace_query():
     for args in [(4, 16384, 32, 128, 128), (1, 1 << 20, 96, 128, 128), (16, 131072, 96, 128, 128),
-                 (3, 1000, 2, 64, 128), (1, 0, 4, 128, 64), (5000, 5000, 8, 128, 128)]:
-        assert kda.fwd_workspace_bytes(*args) == _split_bytes(*args), args
+                 (3, 1000, 2, 64, 128), (1, 0, 4, 128, 64), (5000, 5000, 8, 128, 128),
+                 (2, 4096, 12, 64, 64), (1, 1 << 20, 12, 128, 128)]:
+        N, T, H, dk, dv = args
+        exp = _split_bytes(*args) if _uses_split(N, H, dv) else 0
+        assert kda.fwd_workspace_bytes(*args) == exp, args
+    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == 0        # 256 workgroups: fused
     # the 1M-token, 96-head workload runs in blocks within about 4 GiB
     assert kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128) < (4 << 30) + (64 << 20)
     assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128, in_dtype=0) == 0   # fp32: none
