@@ -37,12 +37,13 @@ struct FwdArgs {
 };
 
 // Two-pass bf16 forward (kda_split_bf16.hip): workspace layout.  Chunks are
-// processed in `blocks` blocks of `bc` chunks per sequence; per block the
-// chunk records occupy [rec, slot), the per-sequence record offsets [slot,
-// carry) and, with more than one block, the carried states [carry, total).
+// processed in `blocks` blocks of `bc` chunks per sequence, alternating over
+// `nbuf` (1 or 2) buffers of chunk records at rec[i] and per-sequence record
+// offsets at slot[i]; with more than one block the carried states sit at
+// [carry, total).
 struct SplitLayout {
-  int bc, blocks;
-  uint64_t rec, slot, carry, total;
+  int bc, blocks, nbuf;
+  uint64_t rec[2], slot[2], carry, total;
 };
 constexpr uint64_t kSplitRecordBudget = 4ull << 30;  // bytes of chunk records per block
 SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk,

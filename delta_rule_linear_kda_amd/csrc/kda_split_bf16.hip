@@ -26,6 +26,7 @@
 // records densely in the workspace, pass 1 fills them and pass 2 consumes
 // them, carrying the state from block to block through the workspace.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_chunk_common.h"
@@ -923,11 +924,12 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
   const uint64_t all = H * (nch_max + N);  // records of every chunk (upper bound)
   const uint64_t budget = kSplitRecordBudget / rb;
   uint64_t bc, recs;
-  if (all <= budget) {
+  if (all <= budget) {  // one block
     bc = nch_max;
     recs = all;
-  } else {
-    bc = std::max<uint64_t>(8, budget / std::max<uint64_t>(1, H * N));
+  } else {  // blocks in two record buffers, so that a block's records are
+            // built while the previous block's are consumed
+    bc = std::max<uint64_t>(8, budget / 2 / std::max<uint64_t>(1, H * N));
     recs = std::min(all, H * N * bc);
   }
   bc = std::min<uint64_t>(bc, 0x7fffffffull / rb);  // a sequence's block stays under 2 GiB
@@ -936,20 +938,61 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
   auto up = [](uint64_t x) { return (x + 255) / 256 * 256; };
   w.bc = (int)bc;
   w.blocks = (int)((nch_max + bc - 1) / bc);
-  w.rec = 0;
-  w.slot = up(recs * rb);
-  w.carry = w.slot + up((N + 1) * 4);
+  w.nbuf = w.blocks > 1 ? 2 : 1;
+  uint64_t off = 0;
+  for (int i = 0; i < w.nbuf; ++i) {
+    w.rec[i] = off;
+    off += up(recs * rb);
+  }
+  for (int i = 0; i < w.nbuf; ++i) {
+    w.slot[i] = off;
+    off += up((N + 1) * 4);
+  }
+  w.carry = off;
   w.total = w.carry + (w.blocks > 1 ? up(N * H * (uint64_t)dk * (uint64_t)dv * 4) : 0);
   return w;
 }
 
+namespace {
+
+// Per device: a second stream (default priority) for the state pass, and
+// the events that order it against the chunk-record pass on the caller's
+// stream.  Created on first use and kept for the process; one mutex
+// serialises the enqueueing (not the GPU work) of concurrent calls.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t start = nullptr, built[2] = {nullptr, nullptr}, used[2] = {nullptr, nullptr};
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    hipEvent_t* evs[5] = {&ss.start, &ss.built[0], &ss.built[1], &ss.used[0], &ss.used[1]};
+    for (hipEvent_t* ev : evs)
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
+}  // namespace
+
+// Block b's plan and record pass run on the caller's stream into buffer
+// b % 2; its state pass runs on the side stream once they are done, while
+// block b + 1's records are built.  Block b + 2 reuses buffer b % 2 after
+// block b's state pass; the caller's stream waits for the last state pass.
 hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream) {
   const int64_t items = (int64_t)p.num_seqs * p.num_heads;
   if (items == 0) return hipSuccess;
   const SplitLayout w = split_layout(p.num_seqs, p.total_tokens, p.num_heads, p.dk, p.dv);
   unsigned char* base = static_cast<unsigned char*>(workspace);
-  unsigned char* rec = base + w.rec;
-  int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
   const int H = p.num_heads, N = p.num_seqs;
   const int nsl = p.dv / 64;  // pass-2 workgroups per item (64 columns each)
@@ -961,8 +1004,23 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   int cpw = 16;
   while (cpw > 1 && items * ((w.bc + cpw - 1) / cpw) < want) cpw /= 2;
   const int64_t pgrid = items * ((w.bc + cpw - 1) / cpw);
+
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  hipStream_t s2 = stream;  // one block: everything on the caller's stream
+  hipError_t e;
+  if (w.blocks > 1) {
+    if ((e = side_stream(&side)) != hipSuccess) return e;
+    s2 = side->s;
+    if ((e = hipEventRecord(side->start, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s2, side->start, 0)) != hipSuccess) return e;
+  }
   for (int blk = 0; blk < w.blocks; ++blk) {
-    const int c_begin = blk * w.bc;
+    const int c_begin = blk * w.bc, bi = blk % w.nbuf;
+    unsigned char* rec = base + w.rec[bi];
+    int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot[bi]);
+    if (side && blk >= 2 && (e = hipStreamWaitEvent(stream, side->used[bi], 0)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_seqlens,
                        N, c_begin, w.bc, slot);
     if (p.dk == 128)
@@ -975,10 +1033,15 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                          (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
                          (int)items, c_begin, w.bc, cpw, rec);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (side) {
+      if ((e = hipEventRecord(side->built[bi], stream)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(s2, side->built[bi], 0)) != hipSuccess) return e;
+    }
     auto launch_state = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (kStateWaves + kStreamWaves)), 0,
-                         stream, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens,
-                         slot, (const unsigned char*)rec, p.initial_state, carry, p.final_state,
+                         s2, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
+                         (const unsigned char*)rec, p.initial_state, carry, p.final_state,
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
@@ -988,9 +1051,12 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     else
       ck ? launch_state(chunk_state_bf16_kernel<64, true>)
          : launch_state(chunk_state_bf16_kernel<64, false>);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (side && (e = hipEventRecord(side->used[bi], s2)) != hipSuccess) return e;
   }
+  if (side && (e = hipStreamWaitEvent(stream, side->used[(w.blocks - 1) % w.nbuf], 0)) !=
+                  hipSuccess)
+    return e;
   return hipSuccess;
 }
 

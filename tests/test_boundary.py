@@ -44,8 +44,9 @@ def _split_bytes(N, T, H, dk, dv):
     records (per 32-token chunk: X diag(beta) and P as bf16 hi/lo 32 x 32
     each, Gamma_end fp32 [dk], Qbar', -W and Kend' fp16 32 x dk each;
     33,280 / 20,736 bytes at d_k = 128 / 64), at most 4 GiB unless 8 chunks
-    per sequence need more, the per-sequence record offsets, and the carried
-    states when there is more than one block."""
+    per sequence need more (two half-size buffers when the input needs more
+    than one block), the per-sequence record offsets, and the carried states
+    when there is more than one block."""
     rb = 4 * 32 * 32 * 2 + dk * 4 + 3 * 32 * dk * 2
     assert rb == {128: 33280, 64: 20736}[dk]
     nch_max = max(1, -(-T // 32))
@@ -53,14 +54,16 @@ def _split_bytes(N, T, H, dk, dv):
     budget = (4 << 30) // rb
     if every <= budget:
         bc, recs = nch_max, every
-    else:
-        bc = max(8, budget // max(1, H * N))
+    else:  # two record buffers (one block built while the previous is consumed)
+        bc = max(8, budget // 2 // max(1, H * N))
         recs = min(every, H * N * bc)
     bc = min(bc, 0x7FFFFFFF // rb, nch_max)
     recs = min(recs, H * N * bc)
     blocks = -(-nch_max // bc)
+    nbuf = 2 if blocks > 1 else 1
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    return up(recs * rb) + up((N + 1) * 4) + (up(N * H * dk * dv * 4) if blocks > 1 else 0)
+    return (nbuf * (up(recs * rb) + up((N + 1) * 4)) +
+            (up(N * H * dk * dv * 4) if blocks > 1 else 0))
 
 
 def _uses_split(N, H, dv, cus=256):
