@@ -33,7 +33,10 @@ Profiling helpers (not part of a timed run):
                         scale FETCH_SIZE / WRITE_SIZE against known bytes;
   --pmc-summary F W     turn two rocprofv3 --pmc CSV files (FETCH_SIZE run,
                         WRITE_SIZE run) into the traffic summary text that the
-                        forward line's roofline.traffic is read from.
+                        forward line's roofline.traffic is read from;
+  --trace-spans CSV     from a rocprofv3 --kernel-trace CSV, the wall-clock span
+                        of each forward call (first start to last end of its
+                        kernels, which overlap across two streams).
 """
 from __future__ import annotations
 
@@ -317,6 +320,32 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def trace_spans(trace_csv: str) -> str:
+    """Per forward call: first start to last end of its kernels' dispatches
+    (calls are separated by the decode launches that follow each forward)."""
+    import csv
+
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    calls, cur = [], None
+    for st, en, name in rows:
+        if any(k in name for k in FWD_KERNELS):
+            if cur is None:
+                cur = [st, en, 0]
+            cur[0], cur[1], cur[2] = min(cur[0], st), max(cur[1], en), cur[2] + 1
+        elif "decode_kernel" in name and cur is not None:
+            calls.append(cur)
+            cur = None
+    if cur is not None:
+        calls.append(cur)
+    lines = [f"forward call {i}: {c[2]} dispatches, span {(c[1] - c[0]) / 1e6:.3f} ms"
+             for i, c in enumerate(calls)]
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,8 +365,12 @@ def main() -> int:
                     help="run only the 12-head direct vs segment-form comparison")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--trace-spans", metavar="TRACE_CSV")
     args = ap.parse_args()
 
+    if args.trace_spans:
+        sys.stdout.write(trace_spans(args.trace_spans))
+        return 0
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(*args.pmc_summary))
         return 0
