@@ -617,9 +617,10 @@ BwdLayout bwd_layout(const kda_shape& s) {
   w.p_dal = w.p_dkh + round_up(nsl * th * s.dk * 4, 256);
   w.p_dbeta = w.p_dal + round_up(nsl * th * s.dk * 4, 256);
   w.sub = w.p_dbeta + round_up(nsl * th * 4, 256);
-  // per (sequence, head, 8-column slice): the 8 sub-chunk start states of a
+  // per (sequence, head, 8-column slice): the sub-chunk start states of a
   // 64-token chunk, dk x 8 fp32 each
-  w.total = w.sub + round_up(uint64_t(s.num_seqs) * uint64_t(s.num_heads) * nsl * 8 * s.dk * 8 * 4,
+  w.total = w.sub + round_up(uint64_t(s.num_seqs) * uint64_t(s.num_heads) * nsl *
+                                 kda::kBwdSubStarts * s.dk * 8 * 4,
                              256);
   return w;
 }

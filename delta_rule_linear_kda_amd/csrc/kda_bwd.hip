@@ -19,12 +19,14 @@
 // RPT l .. RPT l + RPT - 1 (RPT = dk / 64) of the state slice and of its
 // adjoint in registers.  The sequence is walked backwards in 64-token chunks;
 // each chunk's start state is the forward's recorded state (states every 64
-// tokens), the chunk is replayed once to record the starts of its 8-token
-// sub-chunks in LDS, and each sub-chunk, last first, is replayed again to
-// record the state before each of its tokens, then the adjoint runs through
-// it token by token.  The sub-chunk starts live in a per-wavefront global
-// scratch and the per-token states in LDS (32 KB at d_k = 128), so four
-// single-wave workgroups share a CU, one per SIMD.  The per-row partial sums over the wavefront's columns
+// tokens), the chunk is replayed once to record the starts of its 4-token
+// sub-chunks, and each sub-chunk, last first, is replayed again to record
+// the state before each of its tokens, then the adjoint runs through it
+// token by token.  The sub-chunk starts live in a per-wavefront global
+// scratch and the per-token states in LDS (16 KB at d_k = 128), so about
+// nine single-wave workgroups share a CU: the per-token chains are short
+// dependent reductions, and other waves on the SIMD hide their latency.
+// The per-row partial sums over the wavefront's columns
 // (dqh, dkh, dalpha, and the scalar dbeta) go to per-slice buffers, which the
 // reduction kernel adds in a fixed order (no atomics: bitwise repeatable).
 #include "kda_device.h"
@@ -35,8 +37,9 @@ namespace {
 
 constexpr int kSC = 8;        // state columns per wavefront
 constexpr int kChunk = 64;    // tokens between recorded forward states
-constexpr int kSub = 8;       // tokens per replayed sub-chunk
+constexpr int kSub = 4;       // tokens per replayed sub-chunk
 constexpr int kNSub = kChunk / kSub;
+static_assert(kNSub == kBwdSubStarts && kSub * kSC <= 64, "sub-chunk layout");
 
 __device__ __forceinline__ float sigm(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(64)
       load_rows<TI, RPT>(a + th * DK + RPT * lane, AL[i]);
       if (adj) load_rows<TI, RPT>(q + th * DK + RPT * lane, qr[i]);
     }
-    {
+    if (lane < kSub * kSC) {
       const int ti = lane / kSC, j = lane % kSC;
       const int64_t th = (t0 + (ti < ls ? ti : ls - 1)) * H + h;
       const int64_t e = th * DV + col0 + j;
@@ -186,12 +189,13 @@ __global__ void __launch_bounds__(64)
         sDO[ti][j] = dyj * sg;
       }
     }
-    float part[kSub], tot[kSub];
+    float part[8], tot[8];  // (reduce8 sums eight values; the rest are zero)
 #pragma unroll
-    for (int i = 0; i < kSub; ++i) {
+    for (int i = 0; i < 8; ++i) {
       part[i] = 0.f;
+      if (i < kSub)
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) part[i] += kr[i][r] * kr[i][r];
+        for (int r = 0; r < RPT; ++r) part[i] += kr[i < kSub ? i : 0][r] * kr[i < kSub ? i : 0][r];
     }
     reduce8(part, tot, lane);
 #pragma unroll
@@ -205,10 +209,11 @@ __global__ void __launch_bounds__(64)
     }
     if (adj) {
 #pragma unroll
-      for (int i = 0; i < kSub; ++i) {
+      for (int i = 0; i < 8; ++i) {
         part[i] = 0.f;
+        if (i < kSub)
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) part[i] += qr[i][r] * qr[i][r];
+          for (int r = 0; r < RPT; ++r) part[i] += qr[i < kSub ? i : 0][r] * qr[i < kSub ? i : 0][r];
       }
       reduce8(part, tot, lane);
 #pragma unroll

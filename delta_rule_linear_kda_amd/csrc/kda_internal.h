@@ -50,6 +50,10 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
                          int dv);
 hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream);
 
+// Backward: sub-chunks per 64-token chunk whose start states each
+// wavefront keeps in global scratch (kda_bwd.hip).
+constexpr int kBwdSubStarts = 16;
+
 struct ComposeArgs {
   int32_t num_seqs, num_heads, dk, dv;
   const int32_t* seg_offsets;   // [N + 1], device
@@ -99,7 +103,7 @@ struct BwdArgs {
   const float* ckpt;            // states after every 64 tokens of each sequence
   float *dq_out, *dk_out, *dv_out, *da_out, *db_out, *dgate_out, *d_s0;  // dgate, d_s0 may be null
   float *p_dqh, *p_dkh, *p_dal, *p_dbeta;  // per-slice partial sums
-  float* sub_ws;  // per-wavefront sub-chunk start states [N H dv/8][8][dk x 8]
+  float* sub_ws;  // per-wavefront sub-chunk start states [N H dv/8][kBwdSubStarts][dk x 8]
 };
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
 

@@ -397,7 +397,7 @@ def test_bwd_workspace_query():
     N, T, H, dk, dv = 2, 300, 4, 128, 128
     th, nsl = T * H, dv // 8
     exp = (up((T // 64) * H * dk * dv * 4) + up(th * dv * 4) + 3 * up(nsl * th * dk * 4)
-           + up(nsl * th * 4) + up(N * H * nsl * 8 * dk * 8 * 4))
+           + up(nsl * th * 4) + up(N * H * nsl * 16 * dk * 8 * 4))
     assert kda.bwd_workspace_bytes(N, T, H, dk, dv) == exp
     out = ctypes.c_size_t(0)
     assert kda.lib().kda_bwd_workspace_bytes(None, ctypes.byref(out)) == NULLP
