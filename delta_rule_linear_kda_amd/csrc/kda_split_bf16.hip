@@ -570,7 +570,7 @@ constexpr int kStateWaves = 4;   // 64 columns
 constexpr int kStreamWaves = 4;
 constexpr int kAhead = 3;        // chunks requested ahead of the one written to LDS
 
-template <int DK, bool CKPT>
+template <int DK, bool CKPT, bool GATE>
 __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
                             const int32_t* __restrict__ cu_seqlens,
@@ -637,7 +637,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     // 2 kp + 1 of channels 8 kg .. 8 kg + 7 (consecutive lanes: consecutive
     // token pairs, so the 32-bit LDS writes fall on distinct banks).
     constexpr int KJOBS = 16 * (DK / 8);
-    const int kp = st % 16, kg = st / 16;
+    const int kp = st % 16, kg = (st % KJOBS) / 16;
     const uint32_t kgo = 2u * (uint32_t)(R::cKE / 2 + 2 * kp * DK + 8 * kg);
     u32x4_t Rr[kAhead][NSEG], Rv[kAhead][VSEG], Rq[kAhead][VSEG], Rk[kAhead][2];
     // Requests for chunk c_begin + min(s, cnt - 1) into register set K; rows
@@ -650,12 +650,12 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
       for (int i = 0; i < NSEG; ++i)
         Rr[K][i] = __builtin_bit_cast(u32x4_t,
                                       __builtin_amdgcn_raw_buffer_load_b128(rrs, segg[i], soff, 0));
-      if (st < KJOBS) {
-        Rk[K][0] = __builtin_bit_cast(u32x4_t,
-                                      __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo, soff, 0));
-        Rk[K][1] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo + 2 * DK, soff, 0));
-      }
+      // (every thread requests, so the count of requests in flight is the
+      // same on every path; threads past KJOBS repeat a job)
+      Rk[K][0] = __builtin_bit_cast(u32x4_t,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo, soff, 0));
+      Rk[K][1] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rrs, kgo + 2 * DK, soff, 0));
       const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + cs);
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
       const uint32_t range = (uint32_t)nr * (uint32_t)(H * dvt) * 2u;
@@ -666,7 +666,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
       for (int i = 0; i < VSEG; ++i)
         Rv[K][i] = __builtin_bit_cast(u32x4_t,
                                       __builtin_amdgcn_raw_buffer_load_b128(vr, vgo[i], 0, 0));
-      if (gate) {
+      if constexpr (GATE) {
         const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(gate + eoff), 0, range, kBufferRsrcFlags);
 #pragma unroll
@@ -699,7 +699,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
         u32x2_t* d = reinterpret_cast<u32x2_t*>(base + dV + vl[i]);
         d[0] = u32x2_t{Rv[K][i][0], Rv[K][i][1]};
         d[1] = u32x2_t{Rv[K][i][2], Rv[K][i][3]};
-        if (gate) {
+        if constexpr (GATE) {
           u32x2_t* e = reinterpret_cast<u32x2_t*>(base + dG + vl[i]);
           e[0] = u32x2_t{Rq[K][i][0], Rq[K][i][1]};
           e[1] = u32x2_t{Rq[K][i][2], Rq[K][i][3]};
@@ -716,24 +716,18 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     put(0, I0());
     fetch(3, I0());
     lds_barrier();
-    // step s: chunk s + 1 (set (s + 1) % 3) into buffer (s + 1) & 1, then
-    // chunk s + 4 requested into that set
-    for (int s0 = 0; s0 < cnt; s0 += 3) {
-      if (s0 < cnt) {
-        put((s0 + 1) & 1, I1());
-        fetch(s0 + 4, I1());
-        lds_barrier();
-      }
-      if (s0 + 1 < cnt) {
-        put((s0 + 2) & 1, I2());
-        fetch(s0 + 5, I2());
-        lds_barrier();
-      }
-      if (s0 + 2 < cnt) {
-        put((s0 + 3) & 1, I0());
-        fetch(s0 + 6, I0());
-        lds_barrier();
-      }
+    // Step s: chunk s + 1 (register set (s + 1) % 3) into buffer (s + 1) & 1,
+    // then chunk s + 4 requested into that set.  Six steps per iteration make
+    // both indices static; steps past the last chunk repeat it (the state
+    // waves run the same number of barriers), so every request is issued on
+    // every path and each wait covers exactly one set.
+    for (int s0 = 0; s0 < cnt; s0 += 6) {
+      put(1, I1()); fetch(s0 + 4, I1()); lds_barrier();
+      put(0, I2()); fetch(s0 + 5, I2()); lds_barrier();
+      put(1, I0()); fetch(s0 + 6, I0()); lds_barrier();
+      put(0, I1()); fetch(s0 + 7, I1()); lds_barrier();
+      put(1, I2()); fetch(s0 + 8, I2()); lds_barrier();
+      put(0, I0()); fetch(s0 + 9, I0()); lds_barrier();
     }
     return;
   }
@@ -774,10 +768,11 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     const uint32_t vsel = (li & 1) ? 0x07060302u : 0x05040100u;
     f32x4_t O[2], U[2];
     float rg[8];
-    lds_barrier();  // the first buffer is in LDS
-    for (int s = 0; s < cnt; ++s) {
+    // Chunk c_begin + s from LDS buffer B.
+    auto chunk_step = [&](int s, auto Bc) __attribute__((always_inline)) {
+      constexpr int B = decltype(Bc)::value;
       const int cc = c_begin + s;
-      const unsigned char* rb = smem + (s & 1) * dBuf;
+      const unsigned char* rb = smem + B * dBuf;
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(rb + R::dXH);
       const uint16_t* xl = reinterpret_cast<const uint16_t*>(rb + R::dXL);
       const uint16_t* ph = reinterpret_cast<const uint16_t*>(rb + R::dPH);
@@ -793,7 +788,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         rv[i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i]);
-        rgr[i] = gate ? *reinterpret_cast<const uint32_t*>(rb + dG + vwo[i]) : 0u;
+        if constexpr (GATE) rgr[i] = *reinterpret_cast<const uint32_t*>(rb + dG + vwo[i]);
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -888,7 +883,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float y = O[j >> 2][j & 3];
-          if (gate)
+          if constexpr (GATE)
             y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
           __builtin_amdgcn_raw_buffer_store_b32(
               __float_as_uint(y), rs,
@@ -896,6 +891,18 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
         }
       }
       lds_barrier();
+    };
+    lds_barrier();  // the first buffer is in LDS
+    const int steps = (cnt + 5) / 6 * 6;  // as many barriers as the stream waves
+    for (int s = 0; s < steps; s += 2) {
+      if (s < cnt)
+        chunk_step(s, std::integral_constant<int, 0>());
+      else
+        lds_barrier();
+      if (s + 1 < cnt)
+        chunk_step(s + 1, std::integral_constant<int, 1>());
+      else
+        lds_barrier();
     }
   }
 
@@ -1045,12 +1052,22 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
-    if (p.dk == 128)
-      ck ? launch_state(chunk_state_bf16_kernel<128, true>)
-         : launch_state(chunk_state_bf16_kernel<128, false>);
-    else
-      ck ? launch_state(chunk_state_bf16_kernel<64, true>)
-         : launch_state(chunk_state_bf16_kernel<64, false>);
+    const bool gt = p.gate != nullptr;
+    if (p.dk == 128) {
+      if (ck)
+        gt ? launch_state(chunk_state_bf16_kernel<128, true, true>)
+           : launch_state(chunk_state_bf16_kernel<128, true, false>);
+      else
+        gt ? launch_state(chunk_state_bf16_kernel<128, false, true>)
+           : launch_state(chunk_state_bf16_kernel<128, false, false>);
+    } else {
+      if (ck)
+        gt ? launch_state(chunk_state_bf16_kernel<64, true, true>)
+           : launch_state(chunk_state_bf16_kernel<64, true, false>);
+      else
+        gt ? launch_state(chunk_state_bf16_kernel<64, false, true>)
+           : launch_state(chunk_state_bf16_kernel<64, false, false>);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side && (e = hipEventRecord(side->used[bi], s2)) != hipSuccess) return e;
   }
