@@ -153,6 +153,42 @@ def kcp_share(T: int, stream, reps: int = 3) -> dict:
             "workspace_bytes": ws_bytes}
 
 
+def cp_share(xin: dict, stream, T: int = 1 << 17, reps: int = 3) -> dict:
+    """One GPU's share of the long-context workload under 8-way sequence
+    splitting (context parallelism): the first T/8 = 131,072 tokens x 96
+    heads of the resident tensors, as the segment it would own.  Times the
+    two per-GPU kernels of that split: the segment's [S_loc | M] transition
+    and the forward from the composed start state (here zero)."""
+    import torch
+
+    import delta_rule_linear_kda_amd as kda
+
+    x = {n: xin[n][:T] for n in ("q", "k", "v", "a", "b", "gate")}
+    H, dk, dv = x["q"].shape[1], x["q"].shape[2], x["v"].shape[2]
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    o = torch.empty((T, H, dv), dtype=torch.float32, device="cuda")
+    sf = torch.empty((1, H, dk, dv), dtype=torch.float32, device="cuda")
+    tr = torch.empty((1, H, dk, dv + dk), dtype=torch.float32, device="cuda")
+
+    def timed(fn) -> float:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fwd = timed(lambda: kda.fwd_chunked(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"], cu,
+                                        None, out=o, final_state=sf, stream=stream))
+    trans = timed(lambda: kda.segment_transition(x["k"], x["v"], x["a"], x["b"], cu, out=tr,
+                                                 stream=stream))
+    return {"workload": f"kda_fwd_bf16_T{T}_H{H}_d128 (one GPU's segment under 8-way sequence "
+                        f"splitting)", "forward_ms": fwd, "transition_ms": trans,
+            "forward_tokens_per_s": T / (fwd * 1e-3)}
+
+
 def layer_ops(q, gate, o, stream, reps: int = 5) -> dict:
     """The layer operations around the core on the resident long-context
     tensors: the short convolution -> Swish -> L2 front on q (width 4,
@@ -505,6 +541,8 @@ def main() -> int:
         out["roofline"]["traffic_write"] = tr["write"]
     if not args.no_layer:
         out["layer"] = layer_ops(xin["q"], xin["gate"], o, stream)
+    if not args.no_kcp_share:
+        out["cp_share"] = cp_share(xin, stream)
     if not args.no_kcp_share or not args.no_bwd:
         del xin, o, dec_in
         torch.cuda.empty_cache()
