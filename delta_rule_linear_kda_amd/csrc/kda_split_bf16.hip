@@ -559,16 +559,22 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 //   state waves (4)   wave s owns state columns [16 s, 16 s + 16) of the slice
 //                     in MFMA accumulator registers for the whole block and
 //                     runs the chain of chunk c from LDS;
-//   stream waves (4)  move the record and the v and gate tiles of chunk c + 1
-//                     from global memory into the other LDS buffer, with the
+//   stream waves (4)  move the record and the v tile of chunk c + 1 from
+//                     global memory into the other LDS buffer, with the
 //                     requests for the next kAhead chunks in flight in their
 //                     own registers.
 // One workgroup barrier per chunk orders the two LDS buffers.  The state
-// waves' only global accesses are the output stores (no waits on memory); the
-// stream waves' only global accesses are loads, consumed in request order.
+// waves read their gate values straight from global memory one chunk ahead
+// and store the outputs; every step (idle tail steps included) issues the same
+// loads and stores in the same order, so a wait for the gate values never has
+// to cover the previous chunk's stores.  The stream waves' only global
+// accesses are loads, consumed in request order.  The LDS stays under 80 KB:
+// a workgroup above that shares its compute unit with no other large
+// workgroup, and this pass runs beside the record pass of the next block.
 constexpr int kStateWaves = 4;   // 64 columns
 constexpr int kStreamWaves = 4;
-constexpr int kAhead = 3;        // chunks requested ahead of the one written to LDS
+constexpr int kAhead = 2;        // chunks requested ahead of the one written to LDS
+constexpr int kStepPeriod = 2;   // chunks per iteration of the stream waves' unrolled loop
 
 template <int DK, bool CKPT, bool GATE>
 __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
@@ -584,16 +590,16 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
   constexpr int DV = 16 * kStateWaves;
   constexpr int NCT = DK / 16, NKB = DK / 32;
   constexpr int LB = R::RB, LT = R::RT;
-  // LDS buffer: record, then the v and gate tiles [32][VS] (16-bit); the
-  // 8-byte row padding puts the four rows a state-wave read touches on
-  // distinct banks.
+  // LDS buffer: record, then the v tile [32][VS] (16-bit); the 8-byte row
+  // padding puts the four rows a state-wave read touches on distinct banks.
   constexpr int VS = DV + 4;
-  constexpr int dV = R::dSize, dG = dV + kC * VS * 2, dBuf = dG + kC * VS * 2;
+  constexpr int dV = R::dSize, dBuf = dV + kC * VS * 2;
   constexpr int NTS = 64 * kStreamWaves;            // stream threads
   constexpr int NSEG = (R::kSegs + NTS - 1) / NTS;  // record segments per stream thread
   constexpr int VPR = DV * 2 / 16;                  // 16-byte segments per tile row
   constexpr int VSEG = kC * VPR / NTS;              // tile segments per stream thread
   static_assert(dBuf % 16 == 0 && (kC * VPR) % NTS == 0 && VSEG >= 1, "layout");
+  static_assert(2 * dBuf <= 80 * 1024, "LDS budget: room for a record-pass workgroup beside");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf];
 
   // Block -> (item, slice): the nsl slices of an item sit 8 blocks apart, on
@@ -639,7 +645,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     constexpr int KJOBS = 16 * (DK / 8);
     const int kp = st % 16, kg = (st % KJOBS) / 16;
     const uint32_t kgo = 2u * (uint32_t)(R::cKE / 2 + 2 * kp * DK + 8 * kg);
-    u32x4_t Rr[kAhead][NSEG], Rv[kAhead][VSEG], Rq[kAhead][VSEG], Rk[kAhead][2];
+    u32x4_t Rr[kAhead][NSEG], Rv[kAhead][VSEG], Rk[kAhead][2];
     // Requests for chunk c_begin + min(s, cnt - 1) into register set K; rows
     // past the sequence's end read as zero (their range is empty).
     auto fetch = [&](int s, auto Kc) __attribute__((always_inline)) {
@@ -666,14 +672,6 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
       for (int i = 0; i < VSEG; ++i)
         Rv[K][i] = __builtin_bit_cast(u32x4_t,
                                       __builtin_amdgcn_raw_buffer_load_b128(vr, vgo[i], 0, 0));
-      if constexpr (GATE) {
-        const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(gate + eoff), 0, range, kBufferRsrcFlags);
-#pragma unroll
-        for (int i = 0; i < VSEG; ++i)
-          Rq[K][i] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(gr, vgo[i], 0, 0));
-      }
     };
     // Register set K into LDS buffer b (8-byte writes: padded rows).
     auto put = [&](int b, auto Kc) __attribute__((always_inline)) {
@@ -699,35 +697,24 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
         u32x2_t* d = reinterpret_cast<u32x2_t*>(base + dV + vl[i]);
         d[0] = u32x2_t{Rv[K][i][0], Rv[K][i][1]};
         d[1] = u32x2_t{Rv[K][i][2], Rv[K][i][3]};
-        if constexpr (GATE) {
-          u32x2_t* e = reinterpret_cast<u32x2_t*>(base + dG + vl[i]);
-          e[0] = u32x2_t{Rq[K][i][0], Rq[K][i][1]};
-          e[1] = u32x2_t{Rq[K][i][2], Rq[K][i][3]};
-        }
       }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    static_assert(kAhead == 3, "the unrolled loop below rotates three register sets");
+    static_assert(kAhead == 2, "the unrolled loop below rotates two register sets");
     fetch(0, I0());
     fetch(1, I1());
-    fetch(2, I2());
     put(0, I0());
-    fetch(3, I0());
+    fetch(2, I0());
     lds_barrier();
-    // Step s: chunk s + 1 (register set (s + 1) % 3) into buffer (s + 1) & 1,
-    // then chunk s + 4 requested into that set.  Six steps per iteration make
-    // both indices static; steps past the last chunk repeat it (the state
+    // Step s: chunk s + 1 (register set (s + 1) % 2) into buffer (s + 1) & 1,
+    // then chunk s + 3 requested into that set.  Two steps per iteration make
+    // both indices static; a step past the last chunk repeats it (the state
     // waves run the same number of barriers), so every request is issued on
     // every path and each wait covers exactly one set.
-    for (int s0 = 0; s0 < cnt; s0 += 6) {
-      put(1, I1()); fetch(s0 + 4, I1()); lds_barrier();
-      put(0, I2()); fetch(s0 + 5, I2()); lds_barrier();
-      put(1, I0()); fetch(s0 + 6, I0()); lds_barrier();
-      put(0, I1()); fetch(s0 + 7, I1()); lds_barrier();
-      put(1, I2()); fetch(s0 + 8, I2()); lds_barrier();
-      put(0, I0()); fetch(s0 + 9, I0()); lds_barrier();
+    for (int s0 = 0; s0 < cnt; s0 += kStepPeriod) {
+      put(1, I1()); fetch(s0 + 3, I1()); lds_barrier();
+      put(0, I0()); fetch(s0 + 4, I0()); lds_barrier();
     }
     return;
   }
@@ -766,12 +753,43 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
     for (int i = 0; i < 8; ++i) vwo[i] = ((16 * (i / 4) + 4 * g + (i % 4)) * VS + (jcol & ~1)) * 2;
     const uint32_t hsh = 16u * (li & 1);
     const uint32_t vsel = (li & 1) ? 0x07060302u : 0x05040100u;
+    // gate words of those rows (byte offsets from the chunk's first row), in
+    // two sets: set s & 1 holds chunk c_begin + s, requested one step ahead
+    uint32_t gwo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      gwo[i] = 2u * (uint32_t)((16 * (i / 4) + 4 * g + (i % 4)) * H * dvt + (jcol & ~1));
+    uint32_t gw[2][8];
+    // Requests for the gate words of chunk c_begin + min(s, cnt - 1) into set
+    // K; rows past the sequence's end read as zero (their range is empty).
+    auto gate_fetch = [&](int s, auto Kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(Kc)::value;
+      if constexpr (GATE) {
+        const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + min(s, cnt - 1));
+        const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+        const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(gate + (c0 * H + h) * dvt + col0), 0,
+            (uint32_t)nr * (uint32_t)(H * dvt) * 2u, kBufferRsrcFlags);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gw[K][i] = __builtin_amdgcn_raw_buffer_load_b32(gr, gwo[i], 0, 0);
+      }
+    };
+    // The eight output stores of a step past the last chunk: empty range, so
+    // nothing is written, but the count of memory operations per step stays
+    // the same on every path.
+    auto idle_stores = [&]() __attribute__((always_inline)) {
+      if constexpr (GATE) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, kBufferRsrcFlags);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, rs, 4 * j, 0, 0);
+      }
+    };
     f32x4_t O[2], U[2];
-    float rg[8];
-    // Chunk c_begin + s from LDS buffer B.
+    // Chunk c_begin + s from LDS buffer B (gate words in set B).
     auto chunk_step = [&](int s, auto Bc) __attribute__((always_inline)) {
       constexpr int B = decltype(Bc)::value;
       const int cc = c_begin + s;
+      gate_fetch(s + 1, std::integral_constant<int, B ^ 1>());
       const unsigned char* rb = smem + B * dBuf;
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(rb + R::dXH);
       const uint16_t* xl = reinterpret_cast<const uint16_t*>(rb + R::dXL);
@@ -784,12 +802,9 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
       // operands of the chunk, requested first
       bf16x8_t aXH[2], aXL[2], aPH[2], aPL[2];
       f16x8_t aW[2][NKB], aQ[2][NKB];
-      uint32_t rv[8], rgr[8];
+      uint32_t rv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        rv[i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i]);
-        if constexpr (GATE) rgr[i] = *reinterpret_cast<const uint32_t*>(rb + dG + vwo[i]);
-      }
+      for (int i = 0; i < 8; ++i) rv[i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int off = (16 * rt + li) * LT + 4 * g;
@@ -884,7 +899,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
         for (int j = 0; j < 8; ++j) {
           float y = O[j >> 2][j & 3];
           if constexpr (GATE)
-            y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
+            y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][j] >> hsh) << 16)));
           __builtin_amdgcn_raw_buffer_store_b32(
               __float_as_uint(y), rs,
               4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
@@ -892,17 +907,27 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
       }
       lds_barrier();
     };
+    // the first chunk's gate words, followed by the same stores as a step
+    gate_fetch(0, std::integral_constant<int, 0>());
+    idle_stores();
     lds_barrier();  // the first buffer is in LDS
-    const int steps = (cnt + 5) / 6 * 6;  // as many barriers as the stream waves
+    const int steps = (cnt + kStepPeriod - 1) / kStepPeriod * kStepPeriod;  // as many barriers as the stream waves
+    static_assert(kStepPeriod == 2, "two LDS buffers and gate sets per iteration");
     for (int s = 0; s < steps; s += 2) {
-      if (s < cnt)
+      if (s < cnt) {
         chunk_step(s, std::integral_constant<int, 0>());
-      else
+      } else {
+        gate_fetch(s + 1, std::integral_constant<int, 1>());
+        idle_stores();
         lds_barrier();
-      if (s + 1 < cnt)
+      }
+      if (s + 1 < cnt) {
         chunk_step(s + 1, std::integral_constant<int, 1>());
-      else
+      } else {
+        gate_fetch(s + 2, std::integral_constant<int, 0>());
+        idle_stores();
         lds_barrier();
+      }
     }
   }
 
