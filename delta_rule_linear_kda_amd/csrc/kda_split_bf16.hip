@@ -555,10 +555,10 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 }
 
 // ============================ pass 2 ==========================================
-// One workgroup per (sequence, head, 64-column d_v slice) with two wave groups:
-//   state waves (4)   wave s owns state columns [16 s, 16 s + 16) of the slice
-//                     in MFMA accumulator registers for the whole block and
-//                     runs the chain of chunk c from LDS;
+// One workgroup per (sequence, head) with two wave groups:
+//   state waves (SW)  wave s owns state columns [16 s, 16 s + 16) in MFMA
+//                     accumulator registers for the whole block and runs the
+//                     chain of chunk c from LDS (SW = d_v / 16);
 //   stream waves (4)  move the record and the v tile of chunk c + 1 from
 //                     global memory into the other LDS buffer, with the
 //                     requests for the next kAhead chunks in flight in their
@@ -568,16 +568,18 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 // and store the outputs; every step (idle tail steps included) issues the same
 // loads and stores in the same order, so a wait for the gate values never has
 // to cover the previous chunk's stores.  The stream waves' only global
-// accesses are loads, consumed in request order.  The LDS stays under 80 KB:
-// a workgroup above that shares its compute unit with no other large
-// workgroup, and this pass runs beside the record pass of the next block.
-constexpr int kStateWaves = 4;   // 64 columns
+// accesses are loads, consumed in request order.
+// At d_v = 128 a workgroup is 12 waves (two state waves and one stream wave
+// per SIMD, 152 VGPRs each) with 87 KB of LDS, so it has its compute unit to
+// itself (a CU holds 16 waves, and a workgroup above 80 KB of LDS shares it
+// with no other large one): the state pass of a block takes one CU per head
+// and the record pass of the next block runs at full rate on the others.
 constexpr int kStreamWaves = 4;
 constexpr int kAhead = 2;        // chunks requested ahead of the one written to LDS
 constexpr int kStepPeriod = 2;   // chunks per iteration of the stream waves' unrolled loop
 
-template <int DK, bool CKPT, bool GATE>
-__global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
+template <int DK, int SW, bool CKPT, bool GATE>
+__global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
                             const int32_t* __restrict__ cu_seqlens,
                             const int32_t* __restrict__ slot_base,
@@ -587,7 +589,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
                             int num_items, int dvt, int nsl, int c_begin, int bc, int ckpt_iv,
                             float* __restrict__ ckpt, long long ckpt_cap) {
   using R = Rec<DK>;
-  constexpr int DV = 16 * kStateWaves;
+  constexpr int DV = 16 * SW;
   constexpr int NCT = DK / 16, NKB = DK / 32;
   constexpr int LB = R::RB, LT = R::RT;
   // LDS buffer: record, then the v tile [32][VS] (16-bit); the 8-byte row
@@ -599,7 +601,7 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
   constexpr int VPR = DV * 2 / 16;                  // 16-byte segments per tile row
   constexpr int VSEG = kC * VPR / NTS;              // tile segments per stream thread
   static_assert(dBuf % 16 == 0 && (kC * VPR) % NTS == 0 && VSEG >= 1, "layout");
-  static_assert(2 * dBuf <= 80 * 1024, "LDS budget: room for a record-pass workgroup beside");
+  static_assert(2 * dBuf <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf];
 
   // Block -> (item, slice): the nsl slices of an item sit 8 blocks apart, on
@@ -617,10 +619,10 @@ __global__ void __launch_bounds__(64 * (kStateWaves + kStreamWaves))
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
   const unsigned char* rec_item = rec + ((int64_t)H * slot_base[n] + (int64_t)h * max(cnt, 0)) * R::kBytes;
 
-  if (wave >= kStateWaves) {
+  if (wave >= SW) {
     // ======================= stream waves =====================================
     if (cnt == 0) return;  // the state waves then run no barrier either
-    const int st = (int)threadIdx.x - 64 * kStateWaves;
+    const int st = (int)threadIdx.x - 64 * SW;
     const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(rec_item), 0, cnt * R::kBytes, kBufferRsrcFlags);
     int segl[NSEG];       // LDS offsets of this thread's record segments
@@ -1027,7 +1029,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   unsigned char* base = static_cast<unsigned char*>(workspace);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
   const int H = p.num_heads, N = p.num_seqs;
-  const int nsl = p.dv / 64;  // pass-2 workgroups per item (64 columns each)
+  const int nsl = 1;  // pass-2 workgroups per item (all d_v columns each)
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;
   // chunks per pass-1 workgroup: enough workgroups to fill the GPU several
@@ -1071,28 +1073,30 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
       if ((e = hipStreamWaitEvent(s2, side->built[bi], 0)) != hipSuccess) return e;
     }
     auto launch_state = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (kStateWaves + kStreamWaves)), 0,
+      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (p.dv / 16 + kStreamWaves)), 0,
                          s2, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
                          (const unsigned char*)rec, p.initial_state, carry, p.final_state,
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
     const bool gt = p.gate != nullptr;
-    if (p.dk == 128) {
+    auto pick = [&](auto dkc, auto swc) {
+      constexpr int K = decltype(dkc)::value, W = decltype(swc)::value;
       if (ck)
-        gt ? launch_state(chunk_state_bf16_kernel<128, true, true>)
-           : launch_state(chunk_state_bf16_kernel<128, true, false>);
+        gt ? launch_state(chunk_state_bf16_kernel<K, W, true, true>)
+           : launch_state(chunk_state_bf16_kernel<K, W, true, false>);
       else
-        gt ? launch_state(chunk_state_bf16_kernel<128, false, true>)
-           : launch_state(chunk_state_bf16_kernel<128, false, false>);
-    } else {
-      if (ck)
-        gt ? launch_state(chunk_state_bf16_kernel<64, true, true>)
-           : launch_state(chunk_state_bf16_kernel<64, true, false>);
-      else
-        gt ? launch_state(chunk_state_bf16_kernel<64, false, true>)
-           : launch_state(chunk_state_bf16_kernel<64, false, false>);
-    }
+        gt ? launch_state(chunk_state_bf16_kernel<K, W, false, true>)
+           : launch_state(chunk_state_bf16_kernel<K, W, false, false>);
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    using W8 = std::integral_constant<int, 8>;
+    using W4 = std::integral_constant<int, 4>;
+    if (p.dk == 128)
+      p.dv == 128 ? pick(D128(), W8()) : pick(D128(), W4());
+    else
+      p.dv == 128 ? pick(D64(), W8()) : pick(D64(), W4());
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side && (e = hipEventRecord(side->used[bi], s2)) != hipSuccess) return e;
   }
