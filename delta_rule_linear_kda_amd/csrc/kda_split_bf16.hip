@@ -556,9 +556,10 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 
 // ============================ pass 2 ==========================================
 // One workgroup per (sequence, head) with two wave groups:
-//   state waves (SW)  wave s owns state columns [16 s, 16 s + 16) in MFMA
-//                     accumulator registers for the whole block and runs the
-//                     chain of chunk c from LDS (SW = d_v / 16);
+//   state waves (SW)  wave s owns state columns [16 CT s, 16 CT (s + 1)) as CT
+//                     tiles of 16 in MFMA accumulator registers for the whole
+//                     block and runs the chain of chunk c from LDS; its
+//                     column tiles share each operand read (SW CT = d_v / 16);
 //   stream waves (4)  move the record and the v tile of chunk c + 1 from
 //                     global memory into the other LDS buffer, with the
 //                     requests for the next kAhead chunks in flight in their
@@ -569,16 +570,21 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 // loads and stores in the same order, so a wait for the gate values never has
 // to cover the previous chunk's stores.  The stream waves' only global
 // accesses are loads, consumed in request order.
-// At d_v = 128 a workgroup is 12 waves (two state waves and one stream wave
-// per SIMD, 152 VGPRs each) with 87 KB of LDS, so it has its compute unit to
-// itself (a CU holds 16 waves, and a workgroup above 80 KB of LDS shares it
-// with no other large one): the state pass of a block takes one CU per head
-// and the record pass of the next block runs at full rate on the others.
+// With many (sequence, head) items at d_v = 128 a workgroup covers a whole
+// head: four state waves of two column tiles (one state and one stream wave
+// per SIMD) and 87 KB of LDS, so it has its compute unit to itself (a
+// workgroup above 80 KB of LDS shares it with no other large one): the state
+// pass of a block takes one CU per head and the record pass of the next block
+// runs at full rate on the others; two column tiles per state wave halve the
+// LDS operand reads.  With few items, 64-column slices (one tile per state
+// wave, 80 KB) halve the state chain's work per step instead.
+constexpr int kStateWaves = 4;
 constexpr int kStreamWaves = 4;
+constexpr int kWideItems = 32;   // above this many items, one workgroup per item at d_v = 128
 constexpr int kAhead = 2;        // chunks requested ahead of the one written to LDS
 constexpr int kStepPeriod = 2;   // chunks per iteration of the stream waves' unrolled loop
 
-template <int DK, int SW, bool CKPT, bool GATE>
+template <int DK, int SW, int CT, bool CKPT, bool GATE>
 __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
                             const int32_t* __restrict__ cu_seqlens,
@@ -589,7 +595,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
                             int num_items, int dvt, int nsl, int c_begin, int bc, int ckpt_iv,
                             float* __restrict__ ckpt, long long ckpt_cap) {
   using R = Rec<DK>;
-  constexpr int DV = 16 * SW;
+  constexpr int DV = 16 * CT * SW;
   constexpr int NCT = DK / 16, NKB = DK / 32;
   constexpr int LB = R::RB, LT = R::RT;
   // LDS buffer: record, then the v tile [32][VS] (16-bit); the 8-byte row
@@ -729,24 +735,29 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
   int t0_ = threadIdx.x;
   __asm__ volatile("" : "+v"(t0_));
   const int lane = t0_ % 64, g = lane / 16, li = lane % 16;
-  const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
-  f32x4_t S[NCT];
+  // column tile t of this wave: columns 16 (CT sw + t) .. + 15 of the slice
+  const uint32_t st_lane = 4 * g * dvt + 16 * CT * sw + li;
+  f32x4_t S[CT][NCT];
   if (s_src) {
     const auto sp = sbase(s_src + st_off);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int t = 0; t < CT; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * dvt];
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[t][ct][jj] = sp[st_lane + 16 * t + (16 * ct + jj) * dvt];
   } else {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) S[t][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   if (cnt > 0) {
     int64_t ck_off = 0;  // first recorded-state slot of this sequence
     if (CKPT)
       for (int m = 0; m < n; ++m) ck_off += (int64_t)(cu_seqlens[m + 1] - cu_seqlens[m]) / ckpt_iv;
-    const int jcol = 16 * sw + li;
+    const int jcol = 16 * CT * sw + li;  // the lane's column in tile 0 (tile t: + 16 t)
     // v / gate words of rows 16 (i / 4) + 4 g + i % 4 at the lane's column
     // (the aligned 32-bit word holding its bf16), and the perm selector of
     // the lane's half
@@ -761,7 +772,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       gwo[i] = 2u * (uint32_t)((16 * (i / 4) + 4 * g + (i % 4)) * H * dvt + (jcol & ~1));
-    uint32_t gw[2][8];
+    uint32_t gw[2][CT][8];
     // Requests for the gate words of chunk c_begin + min(s, cnt - 1) into set
     // K; rows past the sequence's end read as zero (their range is empty).
     auto gate_fetch = [&](int s, auto Kc) __attribute__((always_inline)) {
@@ -773,20 +784,23 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             const_cast<uint16_t*>(gate + (c0 * H + h) * dvt + col0), 0,
             (uint32_t)nr * (uint32_t)(H * dvt) * 2u, kBufferRsrcFlags);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gw[K][i] = __builtin_amdgcn_raw_buffer_load_b32(gr, gwo[i], 0, 0);
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            gw[K][t][i] = __builtin_amdgcn_raw_buffer_load_b32(gr, gwo[i] + 32u * t, 0, 0);
       }
     };
-    // The eight output stores of a step past the last chunk: empty range, so
+    // The output stores of a step past the last chunk: empty range, so
     // nothing is written, but the count of memory operations per step stays
     // the same on every path.
     auto idle_stores = [&]() __attribute__((always_inline)) {
       if constexpr (GATE) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, kBufferRsrcFlags);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, rs, 4 * j, 0, 0);
+        for (int j = 0; j < 8 * CT; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, rs, 4 * j, 0, 0);
       }
     };
-    f32x4_t O[2], U[2];
+    f32x4_t O[CT][2], U[CT][2];
     // Chunk c_begin + s from LDS buffer B (gate words in set B).
     auto chunk_step = [&](int s, auto Bc) __attribute__((always_inline)) {
       constexpr int B = decltype(Bc)::value;
@@ -801,12 +815,15 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       const uint16_t* qbp = reinterpret_cast<const uint16_t*>(rb + R::dQB);
       const uint16_t* wp = reinterpret_cast<const uint16_t*>(rb + R::dW);
       const uint16_t* kep = reinterpret_cast<const uint16_t*>(rb + R::dKE);
-      // operands of the chunk, requested first
+      // operands of the chunk (shared by the wave's column tiles), requested first
       bf16x8_t aXH[2], aXL[2], aPH[2], aPL[2];
       f16x8_t aW[2][NKB], aQ[2][NKB];
-      uint32_t rv[8];
+      uint32_t rv[CT][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rv[i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i]);
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rv[t][i] = *reinterpret_cast<const uint32_t*>(rb + dV + vwo[i] + 32 * t);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int off = (16 * rt + li) * LT + 4 * g;
@@ -826,50 +843,61 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
         aPH[rt] = lds4x2<bf16x8_t>(ph + off);
         aPL[rt] = lds4x2<bf16x8_t>(pl + off);
       }
-      // U0 = (X diag(beta))_hi V + (X diag(beta))_lo V; v is exact in bf16
-      bf16x8_t vb;
-      {
-        u32x4_t w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(rv[2 * i + 1], rv[2 * i], vsel);
-        vb = __builtin_bit_cast(bf16x8_t, w);
-      }
+      for (int t = 0; t < CT; ++t) {
+        // U0 = (X diag(beta))_hi V + (X diag(beta))_lo V; v is exact in bf16
+        bf16x8_t vb;
+        {
+          u32x4_t w;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        U[rt] = mma_bf16(aXH[rt], vb, mma_bf16(aXL[rt], vb, f32x4_t{0.f, 0.f, 0.f, 0.f}));
-      // U += (-W) S, O = Qbar' S
-      O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      O[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        f16x8_t sbk;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sbk[j] = (_Float16)S[2 * kb + (j >> 2)][j & 3];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          U[rt] = mma_f16(aW[rt][kb], sbk, U[rt]);
-          O[rt] = mma_f16(aQ[rt][kb], sbk, O[rt]);
+          for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_amdgcn_perm(rv[t][2 * i + 1], rv[t][2 * i], vsel);
+          vb = __builtin_bit_cast(bf16x8_t, w);
         }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          U[t][rt] = mma_bf16(aXH[rt], vb, mma_bf16(aXL[rt], vb, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        O[t][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        O[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+      // U += (-W) S, O = Qbar' S
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          f16x8_t sbk;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sbk[j] = (_Float16)S[t][2 * kb + (j >> 2)][j & 3];
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            U[t][rt] = mma_f16(aW[rt][kb], sbk, U[t][rt]);
+            O[t][rt] = mma_f16(aQ[rt][kb], sbk, O[t][rt]);
+          }
+        }
       // O += P U (U as bf16 hi + lo); Kend'^T U takes U in fp16
-      f16x8_t uf;
-      bf16x8_t uh, ul;
-      {
+      f16x8_t uf[CT];
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        bf16x8_t uh, ul;
         float uu[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) uu[j] = U[j >> 2][j & 3];
-        uf = pack_f16x8(uu);
+        for (int j = 0; j < 8; ++j) uu[j] = U[t][j >> 2][j & 3];
+        uf[t] = pack_f16x8(uu);
         split_bf16x8(uu, uh, ul);
-      }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) O[rt] = mma_x3(aPH[rt], aPL[rt], uh, ul, O[rt]);
+        for (int rt = 0; rt < 2; ++rt) O[t][rt] = mma_x3(aPH[rt], aPL[rt], uh, ul, O[t][rt]);
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const float4 gv = *reinterpret_cast<const float4*>(ge + 16 * ct + 4 * g);
-        f32x4_t acc;
-        acc[0] = gv.x * S[ct][0]; acc[1] = gv.y * S[ct][1];
-        acc[2] = gv.z * S[ct][2]; acc[3] = gv.w * S[ct][3];
-        S[ct] = mma_f16(lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g), uf, acc);
+        const f16x8_t ke = lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g);
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          f32x4_t acc;
+          acc[0] = gv.x * S[t][ct][0]; acc[1] = gv.y * S[t][ct][1];
+          acc[2] = gv.z * S[t][ct][2]; acc[3] = gv.w * S[t][ct][3];
+          S[t][ct] = mma_f16(ke, uf[t], acc);
+        }
       }
       if constexpr (CKPT) {
         // the state after the first `done` tokens, when that is a multiple of
@@ -883,9 +911,11 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             __asm__ volatile("" : "+v"(ad));
             float* sp = reinterpret_cast<float*>(ad);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int t = 0; t < CT; ++t)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) sp[(16 * ct + jj) * dvt] = S[ct][jj];
+              for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) sp[16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj];
           }
         }
       }
@@ -898,14 +928,16 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
         const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float y = O[j >> 2][j & 3];
-          if constexpr (GATE)
-            y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][j] >> hsh) << 16)));
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __float_as_uint(y), rs,
-              4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
-        }
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float y = O[t][j >> 2][j & 3];
+            if constexpr (GATE)
+              y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][t][j] >> hsh) << 16)));
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(y), rs,
+                4 * (vo_lane + 16 * t + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
+          }
       }
       lds_barrier();
     };
@@ -936,9 +968,11 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
   if (s_dst) {
     const auto sp = sbase(s_dst + st_off);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int t = 0; t < CT; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj];
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sp[st_lane + 16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj];
   }
 }
 
@@ -1029,7 +1063,12 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   unsigned char* base = static_cast<unsigned char*>(workspace);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
   const int H = p.num_heads, N = p.num_seqs;
-  const int nsl = 1;  // pass-2 workgroups per item (all d_v columns each)
+  // Pass-2 workgroups: one per item with two 16-column tiles per state wave
+  // (128 columns) when there are enough items to fill the GPU with both
+  // passes; with few items the state chain is the whole cost, and 64-column
+  // slices (one tile per state wave, two workgroups per item) shorten it.
+  const bool wide = p.dv == 128 && items > kWideItems;
+  const int nsl = wide ? 1 : p.dv / 64;
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;
   // chunks per pass-1 workgroup: enough workgroups to fill the GPU several
@@ -1073,30 +1112,30 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
       if ((e = hipStreamWaitEvent(s2, side->built[bi], 0)) != hipSuccess) return e;
     }
     auto launch_state = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (p.dv / 16 + kStreamWaves)), 0,
+      hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (kStateWaves + kStreamWaves)), 0,
                          s2, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
                          (const unsigned char*)rec, p.initial_state, carry, p.final_state,
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
     const bool gt = p.gate != nullptr;
-    auto pick = [&](auto dkc, auto swc) {
-      constexpr int K = decltype(dkc)::value, W = decltype(swc)::value;
+    auto pick = [&](auto dkc, auto ctc) {
+      constexpr int K = decltype(dkc)::value, T = decltype(ctc)::value;
       if (ck)
-        gt ? launch_state(chunk_state_bf16_kernel<K, W, true, true>)
-           : launch_state(chunk_state_bf16_kernel<K, W, true, false>);
+        gt ? launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, true, true>)
+           : launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, true, false>);
       else
-        gt ? launch_state(chunk_state_bf16_kernel<K, W, false, true>)
-           : launch_state(chunk_state_bf16_kernel<K, W, false, false>);
+        gt ? launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, false, true>)
+           : launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, false, false>);
     };
     using D128 = std::integral_constant<int, 128>;
     using D64 = std::integral_constant<int, 64>;
-    using W8 = std::integral_constant<int, 8>;
-    using W4 = std::integral_constant<int, 4>;
+    using T2 = std::integral_constant<int, 2>;
+    using T1 = std::integral_constant<int, 1>;
     if (p.dk == 128)
-      p.dv == 128 ? pick(D128(), W8()) : pick(D128(), W4());
+      wide ? pick(D128(), T2()) : pick(D128(), T1());
     else
-      p.dv == 128 ? pick(D64(), W8()) : pick(D64(), W4());
+      wide ? pick(D64(), T2()) : pick(D64(), T1());
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side && (e = hipEventRecord(side->used[bi], s2)) != hipSuccess) return e;
   }

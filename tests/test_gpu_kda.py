@@ -84,6 +84,15 @@ def test_fwd_bf16_dv_slicing(heads):
     run_case(w, [70, 33], label=f"bf16 H={heads}")
 
 
+@pytest.mark.parametrize("dk", [64, 128])
+def test_fwd_bf16_whole_head_state_pass(dk):
+    """Enough (sequence, head) items for the two-pass form to give each item
+    one state-pass workgroup (two 16-column tiles per state wave); ragged
+    lengths and an empty sequence, against the oracle."""
+    w = kc.custom_workload(W1, dk=dk, dv=128, heads=40, s0_std=0.02)
+    run_case(w, [300, 17, 0, 129], label=f"bf16 {dk}x128 H=40")
+
+
 def test_fwd_bf16_no_gate():
     w = kc.custom_workload(W1, heads=2, s0_std=0.02)
     run_case(w, [190, 64], gate=False, label="no gate")
