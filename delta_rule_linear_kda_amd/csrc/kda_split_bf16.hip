@@ -150,6 +150,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
                            int c_begin, int bc, int cpw, unsigned char* __restrict__ rec) {
   using R = Rec<DK>;
   constexpr int NP = R::NP, NT = 64 * NP;
+  constexpr int kXbWave = NP >= 8 ? 6 : 0;
   constexpr int LB = R::LB, LT = R::LT, LX = R::LX, LA = R::LA;
   constexpr int NKB = DK / 32;
   constexpr int oAT = 0;                          // A diagonal blocks^T fp32 [2][16][LA]
@@ -262,10 +263,12 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         for (int j = 0; j < 4; ++j)  // g in log2 units: -5 log2(e) sigmoid(a)
           cum[tau][j] = (kGMin * kLog2e) * rcpf_fast(1.f + exp2f_fast(-kLog2e * av[j]));
       }
-      float beta[2];
+      float beta[2] = {0.f, 0.f};  // only wave 0 publishes them
+      if (wave == 0) {
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-        beta[tau] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((uint32_t)rb[tau] << 16)));
+        for (int tau = 0; tau < 2; ++tau)
+          beta[tau] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((uint32_t)rb[tau] << 16)));
+      }
       // squared norms of rows li and 16 + li over this lane's four channels,
       // summed over the four lanes (g) that share the rows
       float pq[2], pk[2];
@@ -519,7 +522,9 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         xx[1][0] = x10[0]; xx[1][1] = x10[1]; xx[1][2] = x10[2]; xx[1][3] = x10[3];
         xx[1][4] = x11.x; xx[1][5] = x11.y; xx[1][6] = x11.z; xx[1][7] = x11.w;
       }
-      if (wave == 0) {  // X diag(beta) as bf16 hi + lo: blocks X00, X01 = 0, X10, X11
+      // X diag(beta) as bf16 hi + lo (blocks X00, X01 = 0, X10, X11), on a
+      // wave that is idle in the AP stage
+      if (wave == kXbWave) {
         const float bt[8] = {rBeta[4 * g], rBeta[4 * g + 1], rBeta[4 * g + 2], rBeta[4 * g + 3],
                              rBeta[16 + 4 * g], rBeta[17 + 4 * g], rBeta[18 + 4 * g],
                              rBeta[19 + 4 * g]};
