@@ -55,7 +55,7 @@ CHUNK = 32                   # chunk length of the bf16 forward kernels
 # The bf16 forward runs in blocks of chunks, each block a plan kernel, the
 # chunk-record pass and the state pass; the roofline is taken over the whole
 # forward call (every launch of these kernels).
-FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, false, true>",
+FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, 4, 2, false, true>",
                "split_plan_kernel")
 FWD_KERNEL = "split forward: " + " + ".join(FWD_KERNELS[:2]) + " (per block of chunks)"
 FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_split_bf16.hip")
