@@ -12,15 +12,15 @@
 // reductions over key channels are taken before the state is modified.
 //
 // The kernel is HBM-bound (128 KiB of state traffic per (sequence, head) at
-// DK = DV = 128 against ~1.3 KiB of token inputs).  A workgroup of 1024
-// threads updates two consecutive (sequence, head) items, 512 threads each:
-// their states are adjacent, so a workgroup streams one contiguous 128 KiB
-// block in and out, the shape that sustains the most HBM bandwidth for an
-// in-place update on gfx950 (measured ~6.1-6.2 TB/s against ~5.4 TB/s for one
-// 64 KiB item per 256-thread workgroup).  Each thread holds DK*DV/512 floats of
-// its item's state in registers as float4 columns, so every byte of S is read
-// and written exactly once with 16-byte nontemporal accesses, consecutive
-// lanes covering consecutive addresses.
+// DK = DV = 128 against ~1.3 KiB of token inputs).  A workgroup of 512
+// threads (8 waves) updates one (sequence, head) item, and two workgroups
+// share a compute unit (it holds 16 waves), so one workgroup's reductions
+// and stores overlap the other's state loads: measured 5.8-5.9 TB/s against
+// 5.6-5.8 TB/s for two items per 1024-thread workgroup (one per CU) and
+// ~5.4 TB/s for one item per 256-thread workgroup.  Each thread holds
+// DK*DV/512 floats of its item's state in registers as float4 columns, so
+// every byte of S is read and written exactly once with 16-byte nontemporal
+// accesses, consecutive lanes covering consecutive addresses.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -28,7 +28,7 @@ namespace kda {
 namespace {
 
 constexpr int kTPI = 512;    // threads per (sequence, head) item
-constexpr int kItems = 2;    // items per workgroup
+constexpr int kItems = 1;    // items per workgroup
 
 template <typename TI, int DK, int DV>
 __global__ void __launch_bounds__(kTPI * kItems)
