@@ -206,30 +206,36 @@ __global__ void __launch_bounds__(64 * (DK / 16))
   // 16 * wave + 4g .. +3; the tokens of a tile run along a 16-lane DPP row.
   u32x2_t rq[2], rk[2], ra[2];
   uint16_t rb[2];
-  auto load = [&](int64_t c0, int li, int g) {
-    const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+  // Requests for the rows of the chunk starting at token c0 through buffer
+  // resources whose range ends at the sequence's last row (rows past it read
+  // as zero; they also get g = 0 and beta = 0, which removes every
+  // contribution they could make); an empty range (`live` false) issues the
+  // same requests without touching memory.
+  auto load = [&](int64_t c0, bool live, int li, int g) {
+    const int nr = live ? (int)(tok_end - c0 < kC ? tok_end - c0 : kC) : 0;
     const int64_t tb = c0 * H + h;
-    const auto qb_ = sbase(q + tb * DK);
-    const auto kb_ = sbase(k + tb * DK);
-    const auto ab_ = sbase(a + tb * DK);
-    const auto bb_ = sbase(bl + tb);
-    // Rows past the end of the sequence re-load its last row (in bounds,
-    // finite); they get g = 0 and beta = 0, which removes every contribution
-    // they could make.
+    const uint32_t rows = (uint32_t)nr * (uint32_t)H;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q + tb * DK), 0, rows * DK * 2u, kBufferRsrcFlags);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(k + tb * DK), 0, rows * DK * 2u, kBufferRsrcFlags);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a + tb * DK), 0, rows * DK * 2u, kBufferRsrcFlags);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(bl + tb), 0, rows * 2u, kBufferRsrcFlags);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int r = 16 * tau + li;
-      const int rr = r < nr ? r : nr - 1;
-      const uint32_t off = (uint32_t)(rr * H * DK) + 16 * wave + 4 * g;
-      rq[tau] = *reinterpret_cast<const gptr<const u32x2_t>>(qb_ + off);
-      rk[tau] = *reinterpret_cast<const gptr<const u32x2_t>>(kb_ + off);
-      ra[tau] = *reinterpret_cast<const gptr<const u32x2_t>>(ab_ + off);
-      rb[tau] = bb_[(uint32_t)(rr * H)];
+      const uint32_t r = 16 * tau + li;
+      const uint32_t off = 2u * (r * (uint32_t)(H * DK) + 16 * wave + 4 * g);
+      rq[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(qr, off, 0, 0));
+      rk[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(kr, off, 0, 0));
+      ra[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ar, off, 0, 0));
+      rb[tau] = __builtin_amdgcn_raw_buffer_load_b16(br, 2u * r * (uint32_t)H, 0, 0);
     }
   };
   {
     const int lane = threadIdx.x % 64;
-    load(tok_beg + (int64_t)kC * c_lo, lane % 16, lane / 16);
+    load(tok_beg + (int64_t)kC * c_lo, true, lane % 16, lane / 16);
   }
 
   for (int c = c_lo; c < c_hi; ++c) {
@@ -358,9 +364,9 @@ __global__ void __launch_bounds__(64 * (DK / 16))
           *reinterpret_cast<bf16x4_t*>(sK1L + li * LB + cb) = k1l;
         }
       }
-      // next chunk's inputs (this chunk's again after the last), requested
+      // next chunk's inputs (an empty request after the last), requested
       // when this chunk's raw registers are dead
-      load(c + 1 < c_hi ? c0 + kC : c0, li, g);
+      load(c0 + kC, c + 1 < c_hi, li, g);
     }
     lds_barrier();  // B0: operands and norm partials in LDS
 

@@ -93,6 +93,12 @@ def test_fwd_bf16_whole_head_state_pass(dk):
     run_case(w, [300, 17, 0, 129], label=f"bf16 {dk}x128 H=40")
 
 
+def test_fwd_bf16_whole_head_state_pass_no_gate():
+    """The whole-head state pass without an output gate."""
+    w = kc.custom_workload(W1, heads=40, s0_std=0.02)
+    run_case(w, [190, 64], gate=False, label="no gate H=40")
+
+
 def test_fwd_bf16_no_gate():
     w = kc.custom_workload(W1, heads=2, s0_std=0.02)
     run_case(w, [190, 64], gate=False, label="no gate")
