@@ -1082,12 +1082,16 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   const int nsl = wide ? 1 : p.dv / 64;
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;
+  // Block schedule: with several blocks the first is a quarter of the
+  // others (its record pass runs alone, before any state pass) and the last
+  // takes the remainder (its state pass runs alone); block b covers chunks
+  // [b0, b0 + nb) of every sequence.
+  const int64_t nch_max = std::max<int64_t>(1, (p.total_tokens + kC - 1) / kC);
+  const int first = w.blocks > 1 ? std::max(8, w.bc / 4) : w.bc;
+  const int nblocks = w.blocks > 1 ? 1 + (int)((nch_max - first + w.bc - 1) / w.bc) : 1;
   // chunks per pass-1 workgroup: enough workgroups to fill the GPU several
   // times over, at most 16 chunks each
   const int64_t want = 8LL * device_cus();
-  int cpw = 16;
-  while (cpw > 1 && items * ((w.bc + cpw - 1) / cpw) < want) cpw /= 2;
-  const int64_t pgrid = items * ((w.bc + cpw - 1) / cpw);
 
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream* side = nullptr;
@@ -1099,24 +1103,29 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     if ((e = hipEventRecord(side->start, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, side->start, 0)) != hipSuccess) return e;
   }
-  for (int blk = 0; blk < w.blocks; ++blk) {
-    const int c_begin = blk * w.bc, bi = blk % w.nbuf;
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int c_begin = blk == 0 ? 0 : first + (blk - 1) * w.bc;
+    const int nb = blk == 0 ? first : w.bc;
+    const int bi = blk % w.nbuf;
+    int cpw = 16;
+    while (cpw > 1 && items * ((nb + cpw - 1) / cpw) < want) cpw /= 2;
+    const int64_t pgrid = items * ((nb + cpw - 1) / cpw);
     unsigned char* rec = base + w.rec[bi];
     int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot[bi]);
     if (side && blk >= 2 && (e = hipStreamWaitEvent(stream, side->used[bi], 0)) != hipSuccess)
       return e;
     hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_seqlens,
-                       N, c_begin, w.bc, slot);
+                       N, c_begin, nb, slot);
     if (p.dk == 128)
       hipLaunchKernelGGL(chunk_prep_bf16_kernel<128>, dim3((unsigned)pgrid), dim3(64 * 8), 0,
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                          (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
-                         (int)items, c_begin, w.bc, cpw, rec);
+                         (int)items, c_begin, nb, cpw, rec);
     else
       hipLaunchKernelGGL(chunk_prep_bf16_kernel<64>, dim3((unsigned)pgrid), dim3(64 * 4), 0,
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                          (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
-                         (int)items, c_begin, w.bc, cpw, rec);
+                         (int)items, c_begin, nb, cpw, rec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side) {
       if ((e = hipEventRecord(side->built[bi], stream)) != hipSuccess) return e;
@@ -1126,7 +1135,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
       hipLaunchKernelGGL(kern, dim3((unsigned)sgrid), dim3(64 * (kStateWaves + kStreamWaves)), 0,
                          s2, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
                          (const unsigned char*)rec, p.initial_state, carry, p.final_state,
-                         (float*)p.o, H, (int)items, p.dv, nsl, c_begin, w.bc, p.ckpt_interval,
+                         (float*)p.o, H, (int)items, p.dv, nsl, c_begin, nb, p.ckpt_interval,
                          p.ckpt, (long long)p.ckpt_capacity);
     };
     const bool gt = p.gate != nullptr;
@@ -1150,7 +1159,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side && (e = hipEventRecord(side->used[bi], s2)) != hipSuccess) return e;
   }
-  if (side && (e = hipStreamWaitEvent(stream, side->used[(w.blocks - 1) % w.nbuf], 0)) !=
+  if (side && (e = hipStreamWaitEvent(stream, side->used[(nblocks - 1) % w.nbuf], 0)) !=
                   hipSuccess)
     return e;
   return hipSuccess;
