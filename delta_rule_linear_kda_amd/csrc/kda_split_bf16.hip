@@ -12,8 +12,9 @@
 //           every row scale folded in: X diag(beta) (bf16 hi/lo), P (bf16
 //           hi/lo), Gamma_end, diag(nq) Qbar, -W and (Kend diag(nk))^T
 //           (fp16), 33,280 bytes at d_k = 128 (nq, nk: 1/|q|, 1/|k|);
-//   pass 2  chunk_state_bf16_kernel  per (sequence, head, d_v slice), the
-//           sequential chain over the records: U0 = X diag(beta) V,
+//   pass 2  chunk_state_bf16_kernel  per (sequence, head) -- or per
+//           (sequence, head, 64-column d_v slice) when there are few items --
+//           the sequential chain over the records: U0 = X diag(beta) V,
 //           U = U0 - W S, O = Qbar' S + P U, S <- diag(Gamma_end) S
 //           + Kend'^T U, y = sigmoid(gate) O.
 //
@@ -25,6 +26,9 @@
 // in blocks of chunks: for each block, a plan kernel places the block's
 // records densely in the workspace, pass 1 fills them and pass 2 consumes
 // them, carrying the state from block to block through the workspace.
+// Pass 2 of a block runs on a second stream beside pass 1 of the next; with
+// whole-head state workgroups (87 KB of LDS, alone on their compute units)
+// the two passes split the GPU between them.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
