@@ -561,6 +561,64 @@ def test_fwd_kcp_auto_segments():
         assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
 
 
+def test_fwd_split_blocks_varlen():
+    """The two-pass form over many blocks of chunks with sequences of very
+    different lengths: 12 heads x [1000, 120000, 17, 0, 300000] tokens (60
+    items: one state-pass workgroup per item; 13 blocks of up to 1075 chunks
+    after a quarter-size first block of 268).  Two sequences end inside the
+    first block, one is empty, two cross many block boundaries.  The decay
+    logits are shifted by -10 (weak decay), so states carried across blocks
+    shape the outputs long after each boundary.  Against the oracle: the two
+    short sequences whole (all heads, outputs and final states), the empty
+    one's final state (its initial state, exactly), and the first 45,056
+    tokens of each long sequence (the first two block boundaries are at 8,576
+    and 42,976 tokens) for one head each."""
+    _require_gpu()
+    w = kc.custom_workload(W3, heads=12, s0_std=0.02)
+    lens = [1000, 120_000, 17, 0, 300_000]
+    H = w.heads
+    T = sum(lens)
+    print(f"[case] split blocks varlen lens={lens} H={H}", flush=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    dev = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    dev["a"] = (dev["a"].float() - 10.0).to(torch.bfloat16)  # weak decay (RNE)
+    s0 = kc.device_state(w, len(lens))
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    o, sf = kda.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["gate"],
+                            cu_d, s0)
+    torch.cuda.synchronize()
+    s0_h = s0.cpu().numpy()
+    sf_h = sf.cpu().numpy()
+    assert np.all(np.isfinite(sf_h))
+    assert np.array_equal(sf_h[3], s0_h[3])  # the empty sequence
+
+    def ref(n, t_len, heads):
+        t0 = int(cu[n])
+        x = {}
+        for nm in ("q", "k", "v", "gate", "b"):
+            x[nm] = np.stack([kc.f64(kc.host_head_slice(w, nm, t0, t0 + t_len, h))
+                              for h in heads], axis=1)
+        x["a"] = dev["a"][t0:t0 + t_len, heads].float().cpu().numpy().astype(np.float64)
+        st = s0_h[n][heads][None].astype(np.float64)
+        return oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"], [0, t_len], st)
+
+    all_h = list(range(H))
+    for n in (0, 2):
+        o_ref, s_ref = ref(n, lens[n], all_h)
+        t0 = int(cu[n])
+        eo = kc.rel_err(o[t0:t0 + lens[n]].cpu().numpy(), o_ref)
+        es = kc.rel_err(sf_h[n], s_ref[0])
+        print(f"    seq {n} (len {lens[n]}): err o={eo:.3e} state={es:.3e}", flush=True)
+        assert eo <= kc.TOL_BF16 and es <= kc.TOL_BF16
+    t_s = 45_056
+    for n, h in ((1, 0), (4, 11)):
+        o_ref, _ = ref(n, t_s, [h])
+        t0 = int(cu[n])
+        eo = kc.rel_err(o[t0:t0 + t_s, h].cpu().numpy(), o_ref[:, 0])
+        print(f"    seq {n} head {h}, tokens [0, {t_s}): err o={eo:.3e}", flush=True)
+        assert eo <= kc.TOL_BF16
+
+
 def test_fwd_kcp_long_context_share():
     """One GPU's share of the 1,048,576-token workload under 8-way head
     sharding (12 heads) in segment form, at full size: the first 4096 output
