@@ -570,7 +570,8 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 }
 
 // ============================ pass 2 ==========================================
-// One workgroup per (sequence, head) with two wave groups:
+// One workgroup per (sequence, head), or per (sequence, head, 64-column d_v
+// slice) when there are few items, with two wave groups:
 //   state waves (SW)  wave s owns state columns [16 CT s, 16 CT (s + 1)) as CT
 //                     tiles of 16 in MFMA accumulator registers for the whole
 //                     block and runs the chain of chunk c from LDS; its
