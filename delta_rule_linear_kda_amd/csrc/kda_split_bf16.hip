@@ -65,12 +65,15 @@ struct Rec {
   // (globally Kend diag(nk) is stored token-major [32][DK], transposed into
   // LDS by pass 2)
   static constexpr int dSize = dKE + DK * RT * 2;
-  // compact (global) byte offsets, same regions in the same order
+  // compact (global) byte offsets, same regions in the same order; the 32x32
+  // matrices X diag(beta) and P keep their three nonzero 16x16 blocks only
+  // (rows 0-15: columns 0-15; rows 16-31: columns 0-31), see tri_off
+  static constexpr int kTri = 3 * 16 * 16 * 2;  // bytes of one such matrix
   static constexpr int cXH = 0;
-  static constexpr int cXL = cXH + kC * kC * 2;
-  static constexpr int cPH = cXL + kC * kC * 2;
-  static constexpr int cPL = cPH + kC * kC * 2;
-  static constexpr int cGE = cPL + kC * kC * 2;
+  static constexpr int cXL = cXH + kTri;
+  static constexpr int cPH = cXL + kTri;
+  static constexpr int cPL = cPH + kTri;
+  static constexpr int cGE = cPL + kTri;
   static constexpr int cQB = cGE + DK * 4;
   static constexpr int cW = cQB + kC * DK * 2;
   static constexpr int cKE = cW + kC * DK * 2;
@@ -79,17 +82,35 @@ struct Rec {
   static_assert(dSize % 16 == 0 && (RB * 2) % 8 == 0 && (RT * 2) % 8 == 0, "alignment");
 };
 
+// Element offset of (r, c) in the compact form of a 32x32 matrix whose upper
+// right 16x16 block is zero (c < 16 when r < 16).
+__device__ __forceinline__ int tri_off(int r, int c) {
+  return r < 16 ? r * 16 + c : 256 + (r - 16) * 32 + c;
+}
+
 // LDS byte offset of compact segment s of a record (0 past the end).
 template <int DK>
 __device__ __forceinline__ int rec_lds_offset(int s) {
   using R = Rec<DK>;
-  constexpr int rows[7] = {kC, kC, kC, kC, 1, kC, kC};
-  constexpr int rowb[7] = {kC * 2, kC * 2, kC * 2, kC * 2, DK * 4, DK * 2, DK * 2};
-  constexpr int off[7] = {R::dXH, R::dXL, R::dPH, R::dPL, R::dGE, R::dQB, R::dW};
-  constexpr int stride[7] = {R::RT * 2, R::RT * 2, R::RT * 2, R::RT * 2, 0, R::RB * 2, R::RB * 2};
-  int base = 0, out = 0;
+  int out = 0;
+  // X diag(beta) hi, lo, P hi, lo: 16 rows of 2 segments, then 16 rows of 4
+  constexpr int tri[4] = {R::dXH, R::dXL, R::dPH, R::dPL};
 #pragma unroll
-  for (int r = 0; r < 7; ++r) {
+  for (int m = 0; m < 4; ++m) {
+    const int i = s - 96 * m;
+    if (i >= 0 && i < 96) {
+      const int row = i < 32 ? i / 2 : 16 + (i - 32) / 4;
+      const int sr = i < 32 ? i % 2 : (i - 32) % 4;
+      out = tri[m] + row * R::RT * 2 + sr * 16;
+    }
+  }
+  constexpr int rows[3] = {1, kC, kC};
+  constexpr int rowb[3] = {DK * 4, DK * 2, DK * 2};
+  constexpr int off[3] = {R::dGE, R::dQB, R::dW};
+  constexpr int stride[3] = {0, R::RB * 2, R::RB * 2};
+  int base = 4 * 96;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
     const int per = rowb[r] / 16, nseg = rows[r] * per;
     if (s >= base && s < base + nseg) {
       const int i = s - base;
@@ -444,12 +465,9 @@ __global__ void __launch_bounds__(64 * (DK / 16))
           hv[jj] = (__bf16)pv;
           lv[jj] = (__bf16)(pv - (float)hv[jj]);
         }
-        st64(R::cPH + 2 * (r * kC + 16 * ti + 4 * g), hv);
-        st64(R::cPL + 2 * (r * kC + 16 * ti + 4 * g), lv);
-        if (job == 0) {  // the upper tile (0, 1) of P is zero
-          st64(R::cPH + 2 * (li * kC + 16 + 4 * g), u32x2_t{0u, 0u});
-          st64(R::cPL + 2 * (li * kC + 16 + 4 * g), u32x2_t{0u, 0u});
-        }
+        // (the upper tile (0, 1) of P is zero and not stored)
+        st64(R::cPH + 2 * tri_off(r, 16 * ti + 4 * g), hv);
+        st64(R::cPL + 2 * tri_off(r, 16 * ti + 4 * g), lv);
       };
       if (wave < 2) {
         // Diagonal block tau = wave: A_tt, then X_tt = (I + A_tt)^-1.
@@ -541,7 +559,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
+          for (int half = 0; half <= rt; ++half) {  // block X01 is zero and not stored
             bf16x4_t hv, lv;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -549,7 +567,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
               hv[j] = (__bf16)xv;
               lv[j] = (__bf16)(xv - (float)hv[j]);
             }
-            const int off = 2 * ((16 * rt + li) * kC + 16 * half + 4 * g);
+            const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
             st64(R::cXH + off, hv);
             st64(R::cXL + off, lv);
           }
@@ -728,6 +746,17 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     static_assert(kAhead == 2, "the unrolled loop below rotates two register sets");
     fetch(0, I0());
     fetch(1, I1());
+    // The zero upper-right 16x16 blocks of X diag(beta) and P are not in the
+    // record: write them into both LDS buffers once (nothing overwrites them).
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp) {
+      const int idx = st + NTS * rp;  // 0 .. 511: buffer, matrix, row, 8-byte piece
+      const int b = idx / 256, m = (idx / 64) % 4, row = (idx / 4) % 16, q8 = idx % 4;
+      const int mb = m == 0 ? R::dXH : m == 1 ? R::dXL : m == 2 ? R::dPH : R::dPL;
+      *reinterpret_cast<u32x2_t*>(smem + b * dBuf + mb + row * LT * 2 + 32 + 8 * q8) =
+          u32x2_t{0u, 0u};
+    }
+    static_assert(NTS * 2 == 2 * 4 * 16 * 4, "one pass of 8-byte zero writes per thread and rep");
     put(0, I0());
     fetch(2, I0());
     lds_barrier();

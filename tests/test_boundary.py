@@ -41,14 +41,15 @@ def test_version_and_status_strings():
 
 def _split_bytes(N, T, H, dk, dv):
     """Host mirror of the two-pass forward's workspace: one block of chunk
-    records (per 32-token chunk: X diag(beta) and P as bf16 hi/lo 32 x 32
-    each, Gamma_end fp32 [dk], Qbar', -W and Kend' fp16 32 x dk each;
-    33,280 / 20,736 bytes at d_k = 128 / 64), at most 4 GiB unless 8 chunks
-    per sequence need more (two half-size buffers when the input needs more
-    than one block), the per-sequence record offsets, and the carried states
-    when there is more than one block."""
-    rb = 4 * 32 * 32 * 2 + dk * 4 + 3 * 32 * dk * 2
-    assert rb == {128: 33280, 64: 20736}[dk]
+    records (per 32-token chunk: X diag(beta) and P as bf16 hi/lo, each 32 x
+    32 lower block-triangular, stored as its three nonzero 16 x 16 blocks;
+    Gamma_end fp32 [dk]; Qbar', -W and Kend' fp16 32 x dk each; 31,232 /
+    18,688 bytes at d_k = 128 / 64), at most 4 GiB unless 8 chunks per
+    sequence need more (two half-size buffers when the input needs more than
+    one block), the per-sequence record offsets, and the carried states when
+    there is more than one block."""
+    rb = 4 * 3 * 16 * 16 * 2 + dk * 4 + 3 * 32 * dk * 2
+    assert rb == {128: 31232, 64: 18688}[dk]
     nch_max = max(1, -(-T // 32))
     every = H * (nch_max + N)
     budget = (4 << 30) // rb
