@@ -43,7 +43,7 @@ struct FwdArgs {
 // [carry, total).
 struct SplitLayout {
   int bc, blocks, nbuf;
-  uint64_t rec[2], slot[2], carry, total;
+  uint64_t rec[2], slot[2], carry, bt, total;  // bt: b transposed to [H, T] bf16
 };
 constexpr uint64_t kSplitRecordBudget = 4ull << 30;  // bytes of chunk records per block
 SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk,

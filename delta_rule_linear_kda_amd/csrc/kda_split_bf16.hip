@@ -155,6 +155,31 @@ __global__ void __launch_bounds__(kPlanThreads)
   if (t == 0) slot_base[N] = scan[kPlanThreads - 1];
 }
 
+// b [T, H] -> bt [H, T] (16-bit), so that the record pass reads a head's
+// write-strength logits as contiguous runs instead of one 2-byte value per
+// H-element row.  64 tokens x 64 heads per workgroup through LDS.
+constexpr int kBtTile = 64;
+__global__ void __launch_bounds__(256)
+    b_transpose_kernel(const uint16_t* __restrict__ b, uint16_t* __restrict__ bt, long long T,
+                       int H) {
+  __shared__ uint16_t tile[kBtTile][kBtTile + 2];
+  const int64_t t0 = (int64_t)blockIdx.x * kBtTile;
+  const int h0 = blockIdx.y * kBtTile;
+  for (int i = threadIdx.x; i < kBtTile * kBtTile; i += 256) {
+    const int r = i / kBtTile, c = i % kBtTile;  // token r, head c of the tile
+    const int64_t t = t0 + r;
+    const int hh = h0 + c;
+    tile[r][c] = (t < T && hh < H) ? b[t * H + hh] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBtTile * kBtTile; i += 256) {
+    const int r = i / kBtTile, c = i % kBtTile;  // head r, token c of the tile
+    const int64_t t = t0 + c;
+    const int hh = h0 + r;
+    if (t < T && hh < H) bt[(int64_t)hh * T + t] = tile[c][r];
+  }
+}
+
 // ============================ pass 1 ==========================================
 // One workgroup of DK/16 waves per (sequence, head, group of `cpw` chunks of
 // the block).  Per chunk the stages of the fused kernel's prep waves:
@@ -169,7 +194,8 @@ __global__ void __launch_bounds__(kPlanThreads)
 template <int DK>
 __global__ void __launch_bounds__(64 * (DK / 16))
     chunk_prep_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                           const uint16_t* __restrict__ a, const uint16_t* __restrict__ bl,
+                           const uint16_t* __restrict__ a, const uint16_t* __restrict__ bt,
+                           long long T,
                            const int32_t* __restrict__ cu_seqlens,
                            const int32_t* __restrict__ slot_base, int H, int num_items,
                            int c_begin, int bc, int cpw, unsigned char* __restrict__ rec) {
@@ -247,7 +273,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a + tb * DK), 0, rows * DK * 2u, kBufferRsrcFlags);
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(bl + tb), 0, rows * 2u, kBufferRsrcFlags);
+        const_cast<uint16_t*>(bt + (int64_t)h * T + c0), 0, (uint32_t)nr * 2u, kBufferRsrcFlags);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const uint32_t r = 16 * tau + li;
@@ -255,7 +281,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
       rq[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(qr, off, 0, 0));
       rk[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(kr, off, 0, 0));
       ra[tau] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ar, off, 0, 0));
-      rb[tau] = __builtin_amdgcn_raw_buffer_load_b16(br, 2u * r * (uint32_t)H, 0, 0);
+      rb[tau] = __builtin_amdgcn_raw_buffer_load_b16(br, 2u * r, 0, 0);
     }
   };
   {
@@ -1062,7 +1088,8 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
     off += up((N + 1) * 4);
   }
   w.carry = off;
-  w.total = w.carry + (w.blocks > 1 ? up(N * H * (uint64_t)dk * (uint64_t)dv * 4) : 0);
+  w.bt = w.carry + (w.blocks > 1 ? up(N * H * (uint64_t)dk * (uint64_t)dv * 4) : 0);
+  w.total = w.bt + up(H * (uint64_t)std::max<int64_t>(total_tokens, 0) * 2);
   return w;
 }
 
@@ -1107,6 +1134,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   const SplitLayout w = split_layout(p.num_seqs, p.total_tokens, p.num_heads, p.dk, p.dv);
   unsigned char* base = static_cast<unsigned char*>(workspace);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
+  uint16_t* bt = reinterpret_cast<uint16_t*>(base + w.bt);
   const int H = p.num_heads, N = p.num_seqs;
   // Pass-2 workgroups: one per item with two 16-column tiles per state wave
   // (128 columns) when there are enough items to fill the GPU with both
@@ -1131,6 +1159,13 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   SideStream* side = nullptr;
   hipStream_t s2 = stream;  // one block: everything on the caller's stream
   hipError_t e;
+  if (p.total_tokens > 0) {  // the record pass reads b as [H, T]
+    const dim3 grid((unsigned)((p.total_tokens + kBtTile - 1) / kBtTile),
+                    (unsigned)((H + kBtTile - 1) / kBtTile));
+    hipLaunchKernelGGL(b_transpose_kernel, grid, dim3(256), 0, stream, (const uint16_t*)p.b, bt,
+                       (long long)p.total_tokens, H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (w.blocks > 1) {
     if ((e = side_stream(&side)) != hipSuccess) return e;
     s2 = side->s;
@@ -1153,13 +1188,13 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     if (p.dk == 128)
       hipLaunchKernelGGL(chunk_prep_bf16_kernel<128>, dim3((unsigned)pgrid), dim3(64 * 8), 0,
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
-                         (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
-                         (int)items, c_begin, nb, cpw, rec);
+                         (const uint16_t*)p.a, bt, (long long)p.total_tokens, p.cu_seqlens,
+                         slot, H, (int)items, c_begin, nb, cpw, rec);
     else
       hipLaunchKernelGGL(chunk_prep_bf16_kernel<64>, dim3((unsigned)pgrid), dim3(64 * 4), 0,
                          stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
-                         (const uint16_t*)p.a, (const uint16_t*)p.b, p.cu_seqlens, slot, H,
-                         (int)items, c_begin, nb, cpw, rec);
+                         (const uint16_t*)p.a, bt, (long long)p.total_tokens, p.cu_seqlens,
+                         slot, H, (int)items, c_begin, nb, cpw, rec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (side) {
       if ((e = hipEventRecord(side->built[bi], stream)) != hipSuccess) return e;

@@ -88,8 +88,9 @@ typedef struct kda_shape {
  * passes over 32-token chunks (the chunk operands of every chunk first, in
  * parallel; then the state chain over them), and the workspace holds one
  * block of those chunk records: at most about 4 GiB (more only when 8 chunks
- * of every pair need more), plus the state carried between blocks; with
- * more pairs the single fused kernel runs and the size is 0.  The size
+ * of every pair need more), plus the state carried between blocks and b
+ * transposed to [H, T] (2 H T bytes); with more pairs the single fused
+ * kernel runs and the size is 0.  The size
  * depends on the shape and the current device's compute-unit count.
  * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_DTYPE. */
 KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes);

@@ -46,8 +46,8 @@ def _split_bytes(N, T, H, dk, dv):
     Gamma_end fp32 [dk]; Qbar', -W and Kend' fp16 32 x dk each; 31,232 /
     18,688 bytes at d_k = 128 / 64), at most 4 GiB unless 8 chunks per
     sequence need more (two half-size buffers when the input needs more than
-    one block), the per-sequence record offsets, and the carried states when
-    there is more than one block."""
+    one block), the per-sequence record offsets, the carried states when
+    there is more than one block, and b transposed to [H, T] (bf16)."""
     rb = 4 * 3 * 16 * 16 * 2 + dk * 4 + 3 * 32 * dk * 2
     assert rb == {128: 31232, 64: 18688}[dk]
     nch_max = max(1, -(-T // 32))
@@ -64,7 +64,7 @@ def _split_bytes(N, T, H, dk, dv):
     nbuf = 2 if blocks > 1 else 1
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     return (nbuf * (up(recs * rb) + up((N + 1) * 4)) +
-            (up(N * H * dk * dv * 4) if blocks > 1 else 0))
+            (up(N * H * dk * dv * 4) if blocks > 1 else 0) + up(H * T * 2))
 
 
 def _uses_split(N, H, dv, cus=256):
@@ -84,8 +84,9 @@ def test_workspace_query():
         exp = _split_bytes(*args) if _uses_split(N, H, dv) else 0
         assert kda.fwd_workspace_bytes(*args) == exp, args
     assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == 0        # 256 workgroups: fused
-    # the 1M-token, 96-head workload runs in blocks within about 4 GiB
-    assert kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128) < (4 << 30) + (64 << 20)
+    # the 1M-token, 96-head workload runs in blocks of records within about
+    # 4 GiB, plus b transposed (2 H T bytes: 192 MiB)
+    assert kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128) < (4 << 30) + (256 << 20)
     assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128, in_dtype=0) == 0   # fp32: none
     L = kda.lib()
     out = ctypes.c_size_t(0)
