@@ -52,11 +52,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
 CHUNK = 32                   # chunk length of the bf16 forward kernels
-# The bf16 forward runs in blocks of chunks, each block a plan kernel, the
-# chunk-record pass and the state pass; the roofline is taken over the whole
-# forward call (every launch of these kernels).
+# The bf16 forward transposes b, then runs in blocks of chunks, each block a
+# plan kernel, the chunk-record pass and the state pass; the roofline is taken
+# over the whole forward call (every launch of these kernels).
 FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, 4, 2, false, true>",
-               "split_plan_kernel")
+               "split_plan_kernel", "b_transpose_kernel")
 FWD_KERNEL = "split forward: " + " + ".join(FWD_KERNELS[:2]) + " (per block of chunks)"
 FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_split_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_fwd_bf16_T1048576_H96_d128.traffic.txt")
