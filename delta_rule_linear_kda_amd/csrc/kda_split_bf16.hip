@@ -66,9 +66,10 @@ struct Rec {
   // LDS by pass 2)
   static constexpr int dSize = dKE + DK * RT * 2;
   // compact (global) byte offsets, same regions in the same order; the 32x32
-  // matrices X diag(beta) and P keep their three nonzero 16x16 blocks only
-  // (rows 0-15: columns 0-15; rows 16-31: columns 0-31), see tri_off
-  static constexpr int kTri = 3 * 16 * 16 * 2;  // bytes of one such matrix
+  // matrices X diag(beta) and P are lower block-triangular with lower
+  // triangular diagonal blocks, and keep rows 0-7: columns 0-7, rows 8-15:
+  // 0-15, rows 16-23: 0-23, rows 24-31: 0-31 (see tri_off)
+  static constexpr int kTri = (8 * 8 + 8 * 16 + 8 * 24 + 8 * 32) * 2;  // bytes of one
   static constexpr int cXH = 0;
   static constexpr int cXL = cXH + kTri;
   static constexpr int cPH = cXL + kTri;
@@ -82,25 +83,31 @@ struct Rec {
   static_assert(dSize % 16 == 0 && (RB * 2) % 8 == 0 && (RT * 2) % 8 == 0, "alignment");
 };
 
-// Element offset of (r, c) in the compact form of a 32x32 matrix whose upper
-// right 16x16 block is zero (c < 16 when r < 16).
+// Element offset of (r, c) in the compact form of a 32x32 lower
+// block-triangular matrix with lower triangular 16x16 diagonal blocks: row r
+// keeps columns 0 .. 8 (r / 8) + 7 (c must be within them).
 __device__ __forceinline__ int tri_off(int r, int c) {
-  return r < 16 ? r * 16 + c : 256 + (r - 16) * 32 + c;
+  const int q = r / 8;  // row group: 8 (q + 1) columns kept
+  return 8 * 8 * q * (q + 1) / 2 + (r % 8) * 8 * (q + 1) + c;
 }
+// Whether column c of row r is kept (the columns beyond are zero).
+__device__ __forceinline__ bool tri_kept(int r, int c) { return c < 8 * (r / 8 + 1); }
 
 // LDS byte offset of compact segment s of a record (0 past the end).
 template <int DK>
 __device__ __forceinline__ int rec_lds_offset(int s) {
   using R = Rec<DK>;
   int out = 0;
-  // X diag(beta) hi, lo, P hi, lo: 16 rows of 2 segments, then 16 rows of 4
+  // X diag(beta) hi, lo, P hi, lo: 80 segments each (row group q: 8 rows of
+  // q + 1 segments)
   constexpr int tri[4] = {R::dXH, R::dXL, R::dPH, R::dPL};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int i = s - 96 * m;
-    if (i >= 0 && i < 96) {
-      const int row = i < 32 ? i / 2 : 16 + (i - 32) / 4;
-      const int sr = i < 32 ? i % 2 : (i - 32) % 4;
+    const int i = s - 80 * m;
+    if (i >= 0 && i < 80) {
+      const int q = i < 8 ? 0 : i < 24 ? 1 : i < 48 ? 2 : 3;
+      const int j = i - 4 * q * (q + 1);  // segment within the row group
+      const int row = 8 * q + j / (q + 1), sr = j % (q + 1);
       out = tri[m] + row * R::RT * 2 + sr * 16;
     }
   }
@@ -108,7 +115,7 @@ __device__ __forceinline__ int rec_lds_offset(int s) {
   constexpr int rowb[3] = {DK * 4, DK * 2, DK * 2};
   constexpr int off[3] = {R::dGE, R::dQB, R::dW};
   constexpr int stride[3] = {0, R::RB * 2, R::RB * 2};
-  int base = 4 * 96;
+  int base = 4 * 80;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int per = rowb[r] / 16, nseg = rows[r] * per;
@@ -491,9 +498,12 @@ __global__ void __launch_bounds__(64 * (DK / 16))
           hv[jj] = (__bf16)pv;
           lv[jj] = (__bf16)(pv - (float)hv[jj]);
         }
-        // (the upper tile (0, 1) of P is zero and not stored)
-        st64(R::cPH + 2 * tri_off(r, 16 * ti + 4 * g), hv);
-        st64(R::cPL + 2 * tri_off(r, 16 * ti + 4 * g), lv);
+        // (the upper tile (0, 1) of P and the upper parts of the diagonal
+        // tiles beyond the kept columns are zero and not stored)
+        if (tri_kept(r, 16 * ti + 4 * g)) {
+          st64(R::cPH + 2 * tri_off(r, 16 * ti + 4 * g), hv);
+          st64(R::cPL + 2 * tri_off(r, 16 * ti + 4 * g), lv);
+        }
       };
       if (wave < 2) {
         // Diagonal block tau = wave: A_tt, then X_tt = (I + A_tt)^-1.
@@ -593,9 +603,11 @@ __global__ void __launch_bounds__(64 * (DK / 16))
               hv[j] = (__bf16)xv;
               lv[j] = (__bf16)(xv - (float)hv[j]);
             }
-            const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
-            st64(R::cXH + off, hv);
-            st64(R::cXL + off, lv);
+            if (tri_kept(16 * rt + li, 16 * half + 4 * g)) {
+              const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
+              st64(R::cXH + off, hv);
+              st64(R::cXL + off, lv);
+            }
           }
       }
 #pragma unroll
@@ -772,17 +784,19 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     static_assert(kAhead == 2, "the unrolled loop below rotates two register sets");
     fetch(0, I0());
     fetch(1, I1());
-    // The zero upper-right 16x16 blocks of X diag(beta) and P are not in the
-    // record: write them into both LDS buffers once (nothing overwrites them).
+    // The zero parts of X diag(beta) and P beyond each row's kept columns are
+    // not in the record: write them into both LDS buffers once (nothing
+    // overwrites them).
 #pragma unroll
-    for (int rp = 0; rp < 2; ++rp) {
-      const int idx = st + NTS * rp;  // 0 .. 511: buffer, matrix, row, 8-byte piece
-      const int b = idx / 256, m = (idx / 64) % 4, row = (idx / 4) % 16, q8 = idx % 4;
+    for (int rp = 0; rp < 8; ++rp) {
+      const int idx = st + NTS * rp;  // 0 .. 2047: buffer, matrix, row, 4-column piece
+      const int b = idx / 1024, m = (idx / 256) % 4, row = (idx / 8) % 32, q4 = idx % 8;
       const int mb = m == 0 ? R::dXH : m == 1 ? R::dXL : m == 2 ? R::dPH : R::dPL;
-      *reinterpret_cast<u32x2_t*>(smem + b * dBuf + mb + row * LT * 2 + 32 + 8 * q8) =
-          u32x2_t{0u, 0u};
+      if (!tri_kept(row, 4 * q4))
+        *reinterpret_cast<u32x2_t*>(smem + b * dBuf + mb + row * LT * 2 + 8 * q4) =
+            u32x2_t{0u, 0u};
     }
-    static_assert(NTS * 2 == 2 * 4 * 16 * 4, "one pass of 8-byte zero writes per thread and rep");
+    static_assert(NTS * 8 == 2 * 4 * 32 * 8, "8-byte zero pieces: eight per thread");
     put(0, I0());
     fetch(2, I0());
     lds_barrier();

@@ -42,14 +42,15 @@ def test_version_and_status_strings():
 def _split_bytes(N, T, H, dk, dv):
     """Host mirror of the two-pass forward's workspace: one block of chunk
     records (per 32-token chunk: X diag(beta) and P as bf16 hi/lo, each 32 x
-    32 lower block-triangular, stored as its three nonzero 16 x 16 blocks;
-    Gamma_end fp32 [dk]; Qbar', -W and Kend' fp16 32 x dk each; 31,232 /
-    18,688 bytes at d_k = 128 / 64), at most 4 GiB unless 8 chunks per
+    32 lower block-triangular with lower triangular diagonal blocks, stored
+    as rows 8q .. 8q + 7 up to column 8q + 7 for q = 0 .. 3; Gamma_end fp32
+    [dk]; Qbar', -W and Kend' fp16 32 x dk each; 30,208 / 17,664 bytes at
+    d_k = 128 / 64), at most 4 GiB unless 8 chunks per
     sequence need more (two half-size buffers when the input needs more than
     one block), the per-sequence record offsets, the carried states when
     there is more than one block, and b transposed to [H, T] (bf16)."""
-    rb = 4 * 3 * 16 * 16 * 2 + dk * 4 + 3 * 32 * dk * 2
-    assert rb == {128: 31232, 64: 18688}[dk]
+    rb = 4 * (8 * 8 + 8 * 16 + 8 * 24 + 8 * 32) * 2 + dk * 4 + 3 * 32 * dk * 2
+    assert rb == {128: 30208, 64: 17664}[dk]
     nch_max = max(1, -(-T // 32))
     every = H * (nch_max + N)
     budget = (4 << 30) // rb
