@@ -256,7 +256,10 @@ __global__ void __launch_bounds__(256)
 // y = sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps) per (token, head)
 // row.  Each 16-lane row of a wave owns one row; lane li holds the channels
 // 64 k + 4 li .. + 3 (k < DV / 64), so every load instruction of the wave
-// reads whole contiguous segments of the rows.  A workgroup walks 64 rows.
+// reads whole contiguous segments of the rows.  A workgroup walks 64 rows;
+// each thread issues the loads of all four of its rows before the first
+// store (y may be o: every element is read and then written by the same
+// thread, so the order is safe, and four rows' loads are in flight at once).
 template <typename TG, int DV>
 __global__ void __launch_bounds__(kLayerThreads)
     rmsnorm_gate_kernel(const float* o, const TG* __restrict__ gate,
@@ -270,39 +273,63 @@ __global__ void __launch_bounds__(kLayerThreads)
   for (int k = 0; k < NCH; ++k)
 #pragma unroll
     for (int j = 0; j < 4; ++j) wt[k][j] = weight ? weight[64 * k + 4 * li + j] : 1.f;
+  constexpr int GW = sizeof(TG);  // 32-bit gate words per lane and 4 channels
+  float v[4][NCH][4];
+  uint32_t gr[4][NCH][GW];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int64_t row = (int64_t)blockIdx.x * 64 + it * 16 + 4 * wave + r;
     if (row >= rows) break;  // uniform within each 16-lane row
-    float v[NCH][4], ss = 0.f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const float4 q = *reinterpret_cast<const float4*>(o + row * DV + 64 * k + 4 * li);
-      v[k][0] = q.x; v[k][1] = q.y; v[k][2] = q.z; v[k][3] = q.w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ss += v[k][j] * v[k][j];
+      const f32x4_t q =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(o + row * DV + 64 * k + 4 * li));
+      v[it][k][0] = q[0]; v[it][k][1] = q[1]; v[it][k][2] = q[2]; v[it][k][3] = q[3];
+      if (gate) {
+        if constexpr (GW == 2) {
+          typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+          const f32x2_t u = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x2_t*>(gate + row * DV + 64 * k + 4 * li));
+          gr[it][k][0] = __float_as_uint(u[0]); gr[it][k][1] = __float_as_uint(u[1]);
+        } else {
+          const uint4 u = *reinterpret_cast<const uint4*>(gate + row * DV + 64 * k + 4 * li);
+          gr[it][k][0] = u.x; gr[it][k][1] = u.y; gr[it][k][2] = u.z; gr[it][k][3] = u.w;
+        }
+      }
     }
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int64_t row = (int64_t)blockIdx.x * 64 + it * 16 + 4 * wave + r;
+    if (row >= rows) break;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss += v[it][k][j] * v[it][k][j];
     const float rn = rsqrtf(row16_sum(ss) * (1.f / DV) + eps);
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       float gv[4] = {0.f, 0.f, 0.f, 0.f};
       if (gate) {
-        if constexpr (sizeof(TG) == 2) {
-          const uint2 u = *reinterpret_cast<const uint2*>(gate + row * DV + 64 * k + 4 * li);
-          gv[0] = __uint_as_float(u.x << 16); gv[1] = __uint_as_float(u.x & 0xFFFF0000u);
-          gv[2] = __uint_as_float(u.y << 16); gv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+        if constexpr (GW == 2) {
+          gv[0] = __uint_as_float(gr[it][k][0] << 16);
+          gv[1] = __uint_as_float(gr[it][k][0] & 0xFFFF0000u);
+          gv[2] = __uint_as_float(gr[it][k][1] << 16);
+          gv[3] = __uint_as_float(gr[it][k][1] & 0xFFFF0000u);
         } else {
-          const float4 q = *reinterpret_cast<const float4*>(gate + row * DV + 64 * k + 4 * li);
-          gv[0] = q.x; gv[1] = q.y; gv[2] = q.z; gv[3] = q.w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) gv[j] = __uint_as_float(gr[it][k][j]);
         }
       }
+      float* vv = v[it][k];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[k][j] *= rn * wt[k][j];
-        if (gate) v[k][j] *= sigmoid_fast(gv[j]);
+        vv[j] *= rn * wt[k][j];
+        if (gate) vv[j] *= sigmoid_fast(gv[j]);
       }
-      *reinterpret_cast<float4*>(y + row * DV + 64 * k + 4 * li) =
-          make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
+      __builtin_nontemporal_store(f32x4_t{vv[0], vv[1], vv[2], vv[3]},
+                                  reinterpret_cast<f32x4_t*>(y + row * DV + 64 * k + 4 * li));
     }
   }
 }
