@@ -68,8 +68,9 @@ struct Rec {
   // compact (global) byte offsets, same regions in the same order; the 32x32
   // matrices X diag(beta) and P are lower block-triangular with lower
   // triangular diagonal blocks, and keep rows 0-7: columns 0-7, rows 8-15:
-  // 0-15, rows 16-23: 0-23, rows 24-31: 0-31 (see tri_off)
-  static constexpr int kTri = (8 * 8 + 8 * 16 + 8 * 24 + 8 * 32) * 2;  // bytes of one
+  // 0-15, rows 16-23: 0-23, rows 24-31: 0-31 (see tri_off); kTri is the
+  // bytes of one such matrix (80 segments of 16 bytes)
+  static constexpr int kTri = (8 * 8 + 8 * 16 + 8 * 24 + 8 * 32) * 2;
   static constexpr int cXH = 0;
   static constexpr int cXL = cXH + kTri;
   static constexpr int cPH = cXL + kTri;
