@@ -122,11 +122,10 @@ def kcp_share(T: int, stream, reps: int = 3) -> dict:
 
     import delta_rule_linear_kda_amd as kda
     import synth
-    from tests import kda_cases as kc
 
     H = 12
-    w = kc.custom_workload(synth.WORKLOADS[3], heads=H)
-    x = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    w = synth.custom_workload(synth.WORKLOADS[3], heads=H)
+    x = {n: synth.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
     args = tuple(x[n] for n in ("q", "k", "v", "a", "b", "gate"))
     cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
     o = torch.empty((T, H, w.dv), dtype=torch.float32, device="cuda")
@@ -234,11 +233,10 @@ def backward(stream, reps: int = 3) -> dict:
 
     import delta_rule_linear_kda_amd as kda
     import synth
-    from tests import kda_cases as kc
 
     w = synth.WORKLOADS[1]
     T, H = sum(w.seq_lens()), w.heads
-    x = {n: kc.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    x = {n: synth.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
     args = tuple(x[n] for n in ("q", "k", "v", "a", "b", "gate"))
     cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32, device="cuda")
     dy = torch.empty((T, H, w.dv), dtype=torch.float32, device="cuda")
@@ -421,7 +419,6 @@ def main() -> int:
 
     import delta_rule_linear_kda_amd as kda
     import synth
-    from tests import kda_cases as kc
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -434,8 +431,8 @@ def main() -> int:
         return 0
     if args.only_layer:
         wl = synth.WORKLOADS[3]
-        q = kc.device_tokens(wl, "q", args.tokens)
-        g = kc.device_tokens(wl, "gate", args.tokens)
+        q = synth.device_tokens(wl, "q", args.tokens)
+        g = synth.device_tokens(wl, "gate", args.tokens)
         o = torch.empty((args.tokens, wl.heads, wl.dv), dtype=torch.float32, device=dev)
         synth.device_normal(o.view(-1, wl.dv), synth.key(wl.seed, "o"))
         print(json.dumps({"layer": layer_ops(q, g, o, stream)}), flush=True)
@@ -444,7 +441,7 @@ def main() -> int:
     # ---- forward workload: 1 x T tokens, H=96, d=128, bf16 ----------------
     wf = synth.WORKLOADS[3]
     T, H, dk, dv = args.tokens, wf.heads, wf.dk, wf.dv
-    xin = {n: kc.device_tokens(wf, n, T) for n in synth.TOKEN_TENSORS}
+    xin = {n: synth.device_tokens(wf, n, T) for n in synth.TOKEN_TENSORS}
     cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     sf = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
@@ -452,8 +449,8 @@ def main() -> int:
     # ---- decode workload: 256 x 96 heads, 64 steps of pre-staged tokens -----
     wd = synth.WORKLOADS[4]
     N, D = wd.num_seqs, args.decode_steps
-    state = kc.device_state(wd, N)
-    dec_in = [{n: kc.device_tokens(wd, n, N, step=s) for n in synth.TOKEN_TENSORS}
+    state = synth.device_state(wd, N)
+    dec_in = [{n: synth.device_tokens(wd, n, N, step=s) for n in synth.TOKEN_TENSORS}
               for s in range(D)]
     o_dec = torch.empty((N, wd.heads, wd.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()

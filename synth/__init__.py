@@ -208,3 +208,88 @@ TOKEN_TENSORS = ("q", "k", "v", "a", "b", "gate")
 def token_row_len(w: Workload, name: str) -> int:
     """Per-token, per-head element count of a token tensor."""
     return {"q": w.dk, "k": w.dk, "a": w.dk, "v": w.dv, "gate": w.dv, "b": 1}[name]
+
+
+# ---------------------------------------------------------------------------
+# Whole tensors of a workload, on the host (generator output: fp32 arrays or
+# bf16 bit patterns as uint16) or on the device (torch tensors, same values).
+# ---------------------------------------------------------------------------
+
+def custom_workload(base: Workload, **kw) -> Workload:
+    """A copy of a workload recipe with some fields changed."""
+    return dataclasses.replace(base, **kw)
+
+
+def host_tokens(w: Workload, name: str, T: int, step: int = 0) -> np.ndarray:
+    """Token tensor [T, H, L] (b: [T, H]) of workload w."""
+    L = token_row_len(w, name)
+    arr = host_normal(key(w.seed, name, step), T * w.heads, L, dtype=w.dtype, std=w.std_of(name))
+    return arr.reshape(T, w.heads) if name == "b" else arr.reshape(T, w.heads, L)
+
+
+def host_head_slice(w: Workload, name: str, t0: int, t1: int, h: int,
+                    step: int = 0) -> np.ndarray:
+    """Tokens [t0, t1) of head h only: [t1 - t0, L] (b: [t1 - t0])."""
+    L = token_row_len(w, name)
+    arr = host_normal(key(w.seed, name, step), t1 - t0, L, dtype=w.dtype, std=w.std_of(name),
+                      row_stride=w.heads * L, base=(t0 * w.heads + h) * L)
+    return arr[:, 0] if name == "b" else arr
+
+
+def host_state(w: Workload, num_seqs: int) -> Optional[np.ndarray]:
+    """Initial states [N, H, dk, dv] fp32, or None for a zero start."""
+    if w.s0_std is None:
+        return None
+    n = num_seqs * w.heads * w.dk
+    return host_normal(key(w.seed, "s0"), n, w.dv, dtype=F32,
+                       std=w.s0_std).reshape(num_seqs, w.heads, w.dk, w.dv)
+
+
+def host_state_item(w: Workload, n: int, h: int) -> np.ndarray:
+    """Initial state [dk, dv] of sequence n, head h."""
+    base = (n * w.heads + h) * w.dk * w.dv
+    return host_normal(key(w.seed, "s0"), w.dk, w.dv, dtype=F32, std=w.s0_std, base=base)
+
+
+def host_inputs(w: Workload, T: int, step: int = 0):
+    return {name: host_tokens(w, name, T, step) for name in TOKEN_TENSORS}
+
+
+def to_torch(arr: np.ndarray, device="cuda"):
+    """Host generator output as a torch tensor (bf16 bit patterns -> bfloat16)."""
+    import torch
+
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(arr)
+    return t.to(device)
+
+
+def torch_dtype(w: Workload):
+    import torch
+
+    return torch.float32 if w.dtype == F32 else torch.bfloat16
+
+
+def device_tokens(w: Workload, name: str, T: int, step: int = 0, device="cuda"):
+    """Token tensor generated directly on the device (same values as host_tokens)."""
+    import torch
+
+    L = token_row_len(w, name)
+    shape = (T, w.heads) if name == "b" else (T, w.heads, L)
+    t = torch.empty(shape, dtype=torch_dtype(w), device=device)
+    if t.numel():
+        device_normal(t.view(-1, L), key(w.seed, name, step), std=w.std_of(name))
+    return t
+
+
+def device_state(w: Workload, num_seqs: int, device="cuda"):
+    """Initial states generated on the device (same values as host_state)."""
+    import torch
+
+    if w.s0_std is None:
+        return None
+    t = torch.empty((num_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device=device)
+    device_normal(t.view(-1, w.dv), key(w.seed, "s0"), std=w.s0_std)
+    return t

@@ -24,85 +24,84 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) / rms
 
 
-def host_tokens(w: synth.Workload, name: str, T: int, step: int = 0) -> np.ndarray:
-    """Whole token tensor [T, H, L] (b: [T, H]) as generator output (fp32 or
-    bf16 bit patterns)."""
-    L = synth.token_row_len(w, name)
-    arr = synth.host_normal(synth.key(w.seed, name, step), T * w.heads, L, dtype=w.dtype,
-                            std=w.std_of(name))
-    return arr.reshape(T, w.heads) if name == "b" else arr.reshape(T, w.heads, L)
-
-
-def host_head_slice(w: synth.Workload, name: str, t0: int, t1: int, h: int,
-                    step: int = 0) -> np.ndarray:
-    """Tokens [t0, t1) of head h only: [t1 - t0, L] (b: [t1 - t0])."""
-    L = synth.token_row_len(w, name)
-    arr = synth.host_normal(synth.key(w.seed, name, step), t1 - t0, L, dtype=w.dtype,
-                            std=w.std_of(name), row_stride=w.heads * L, base=(t0 * w.heads + h) * L)
-    return arr[:, 0] if name == "b" else arr
-
-
-def host_state(w: synth.Workload, num_seqs: int) -> Optional[np.ndarray]:
-    if w.s0_std is None:
-        return None
-    n = num_seqs * w.heads * w.dk
-    return synth.host_normal(synth.key(w.seed, "s0"), n, w.dv, dtype=synth.F32,
-                             std=w.s0_std).reshape(num_seqs, w.heads, w.dk, w.dv)
-
-
-def host_state_item(w: synth.Workload, n: int, h: int) -> np.ndarray:
-    base = (n * w.heads + h) * w.dk * w.dv
-    return synth.host_normal(synth.key(w.seed, "s0"), w.dk, w.dv, dtype=synth.F32,
-                             std=w.s0_std, base=base)
-
-
-def to_torch(arr: np.ndarray, device="cuda"):
-    import torch
-
-    if arr.dtype == np.uint16:
-        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(arr)
-    return t.to(device)
-
-
-def torch_dtype(w: synth.Workload):
-    import torch
-
-    return torch.float32 if w.dtype == synth.F32 else torch.bfloat16
-
-
-def device_tokens(w: synth.Workload, name: str, T: int, step: int = 0, device="cuda"):
-    """Token tensor generated directly on the device (same values as host_tokens)."""
-    import torch
-
-    L = synth.token_row_len(w, name)
-    shape = (T, w.heads) if name == "b" else (T, w.heads, L)
-    t = torch.empty(shape, dtype=torch_dtype(w), device=device)
-    if t.numel():
-        synth.device_normal(t.view(-1, L), synth.key(w.seed, name, step), std=w.std_of(name))
-    return t
-
-
-def device_state(w: synth.Workload, num_seqs: int, device="cuda"):
-    import torch
-
-    if w.s0_std is None:
-        return None
-    t = torch.empty((num_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device=device)
-    synth.device_normal(t.view(-1, w.dv), synth.key(w.seed, "s0"), std=w.s0_std)
-    return t
-
-
-def host_inputs(w: synth.Workload, T: int, step: int = 0) -> Dict[str, np.ndarray]:
-    return {name: host_tokens(w, name, T, step) for name in synth.TOKEN_TENSORS}
+# The seeded generators' whole-tensor helpers live in synth/; re-exported
+# here for the tests.
+host_tokens = synth.host_tokens
+host_head_slice = synth.host_head_slice
+host_state = synth.host_state
+host_state_item = synth.host_state_item
+host_inputs = synth.host_inputs
+to_torch = synth.to_torch
+torch_dtype = synth.torch_dtype
+device_tokens = synth.device_tokens
+device_state = synth.device_state
+custom_workload = synth.custom_workload
 
 
 def f64(x: Optional[np.ndarray]) -> Optional[np.ndarray]:
     return None if x is None else synth.to_f64(x)
 
 
-def custom_workload(base: synth.Workload, **kw) -> synth.Workload:
-    import dataclasses
 
-    return dataclasses.replace(base, **kw)
+class ErrAcc:
+    """max |got - ref| and sum ref^2 accumulated over pieces of a tensor, so
+    that rel_err of a tensor too large to hold can be formed slice by slice."""
+
+    def __init__(self):
+        self.mx, self.ss, self.n = 0.0, 0.0, 0
+
+    def add(self, got: np.ndarray, ref: np.ndarray) -> None:
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        if ref.size:
+            self.mx = max(self.mx, float(np.max(np.abs(got - ref))))
+            self.ss += float(np.sum(ref * ref))
+            self.n += ref.size
+
+    def err(self) -> float:
+        rms = (self.ss / self.n) ** 0.5 if self.n else 0.0
+        return self.mx / rms if rms > 0 else self.mx
+
+
+def oracle_stream(fetch, n_tokens: int, s0, gate: bool = True, slice_tokens: int = 65536,
+                  on_slice=None):
+    """The oracle over tokens [0, n_tokens) of some heads of one sequence, in
+    slices with the state carried (the same recurrence as one run; bounded
+    host memory).  fetch(t0, t1) -> dict of f64 arrays q, k, v, a, gate
+    [n, Hs, L] and b [n, Hs]; on_slice(t0, t1, o_ref) receives each slice's
+    outputs.  Returns the final state [1, Hs, dk, dv]."""
+    import oracle
+
+    state = s0
+    for t0 in range(0, n_tokens, slice_tokens):
+        t1 = min(n_tokens, t0 + slice_tokens)
+        x = fetch(t0, t1)
+        o_ref, state = oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"],
+                                  x["gate"] if gate else None, [0, t1 - t0], state)
+        if on_slice is not None:
+            on_slice(t0, t1, o_ref)
+    return state
+
+
+def device_rows_f64(t, t0: int, t1: int, heads) -> np.ndarray:
+    """Rows [t0, t1) of heads `heads` of a device token tensor, widened exactly
+    to fp64 on the host."""
+    import torch
+
+    x = t[t0:t1, heads].contiguous()
+    if x.dtype == torch.bfloat16:
+        return synth.to_f64(x.view(torch.int16).cpu().numpy().view(np.uint16))
+    return x.cpu().numpy().astype(np.float64)
+
+
+def rel_err_device(got, ref, rows: int = 65536) -> float:
+    """max |got - ref| / RMS(ref) over whole device tensors, accumulated on
+    the device in row slices (no full-size temporaries or host copies)."""
+    mx, ss, n = 0.0, 0.0, 0
+    for r0 in range(0, ref.shape[0], rows):
+        g = got[r0:r0 + rows].double()
+        f = ref[r0:r0 + rows].double()
+        mx = max(mx, float((g - f).abs().max()))
+        ss += float((f * f).sum())
+        n += f.numel()
+    return mx / (ss / n) ** 0.5
