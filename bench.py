@@ -82,38 +82,167 @@ def decode_bytes_per_step(N: int, H: int, dk: int, dv: int, in_bytes: int = 2) -
     return N * H * (2 * 4 * dk * dv + in_bytes * (3 * dk + 2 * dv + 1) + 4 * dv)
 
 
-def cpu_baseline(T: int = 65536, slice_tokens: int = 8192) -> dict:
-    """The fp64 oracle timed on this host's cores over a bounded sample of the
-    forward workload: its first T tokens, all 96 heads, fed in slices of
-    ``slice_tokens`` with the state carried from slice to slice (the same
-    recurrence; bounded host memory).  Input generation is outside the timed
-    region."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_time(w, lens, heads, t_lim=None, nthreads=None, step=None):
+    """Oracle (fp64 token recurrence) time over the sequences `lens` of
+    workload w restricted to `heads` (first t_lim tokens of each sequence, in
+    8192-token slices with the state carried; decode: one step over every
+    sequence).  Input generation is outside the timed region.  Returns
+    (seconds, token-heads processed)."""
     import numpy as np
 
     import oracle
     import synth
 
-    w = synth.WORKLOADS[3]
-    H = w.heads
-    threads = oracle.threads()
-    state = None
-    dt = 0.0
-    for t0 in range(0, T, slice_tokens):
-        n = min(slice_tokens, T - t0)
-        x = {}
-        for name in synth.TOKEN_TENSORS:
+    nthreads = nthreads or oracle.threads()
+    cu = np.concatenate([[0], np.cumsum(w.seq_lens())]).astype(np.int64)
+    dt, done = 0.0, 0
+    every = list(heads) == list(range(w.heads))
+
+    def rows(name, t0, t1, st=0):
+        """tokens [t0, t1) of `heads` as fp64 [n, len(heads), L] (b: [n, len(heads)])"""
+        if every:  # contiguous rows: one generator call
             L = synth.token_row_len(w, name)
-            arr = synth.host_normal(synth.key(w.seed, name), n * H, L, dtype=w.dtype,
-                                    std=w.std_of(name), base=t0 * H * L)
-            x[name] = synth.to_f64(arr).reshape((n, H) if name == "b" else (n, H, L))
-        t_start = time.perf_counter()
-        _, state = oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"],
-                              np.array([0, n]), state, nthreads=threads)
-        dt += time.perf_counter() - t_start
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 token recurrence over tokens [0, {T}) of the 1x1048576-token "
-                      f"workload, all 96 heads (d=128), in {slice_tokens}-token slices with "
-                      f"the state carried, {threads} threads, {dt:.1f} s of oracle time"}
+            arr = synth.host_normal(synth.key(w.seed, name, st), (t1 - t0) * w.heads, L,
+                                    dtype=w.dtype, std=w.std_of(name), base=t0 * w.heads * L)
+            arr = synth.to_f64(arr)
+            return arr.reshape(t1 - t0, w.heads) if name == "b" else \
+                arr.reshape(t1 - t0, w.heads, L)
+        return np.stack([synth.to_f64(synth.host_head_slice(w, name, t0, t1, h, step=st))
+                         for h in heads], axis=1)
+
+    if step is not None:  # decode: one token per sequence per step, the state carried
+        N = w.num_seqs
+        if every:
+            st = synth.host_state(w, N).astype(np.float64)
+        else:
+            st = np.stack([np.stack([synth.host_state_item(w, n, h) for h in heads])
+                           for n in range(N)]).astype(np.float64)
+        for s_ in step:
+            x = {n: rows(n, 0, N, s_) for n in synth.TOKEN_TENSORS}
+            t0 = time.perf_counter()
+            oracle.decode_step(*(x[n] for n in synth.TOKEN_TENSORS), st, nthreads=nthreads)
+            dt += time.perf_counter() - t0
+            done += N * len(heads)
+        return dt, done
+    for n in lens:
+        L = int(cu[n + 1] - cu[n])
+        L = L if t_lim is None else min(L, t_lim)
+        state = None
+        if w.s0_std is not None:
+            state = np.stack([synth.host_state_item(w, n, h) for h in heads])[None].astype(
+                np.float64)
+        for s0 in range(0, L, 8192):
+            s1 = min(L, s0 + 8192)
+            x = {nm: rows(nm, int(cu[n]) + s0, int(cu[n]) + s1) for nm in synth.TOKEN_TENSORS}
+            t0 = time.perf_counter()
+            _, state = oracle.fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["gate"],
+                                  np.array([0, s1 - s0]), state, nthreads=nthreads)
+            dt += time.perf_counter() - t0
+            done += (s1 - s0) * len(heads)
+    return dt, done
+
+
+def cpu_baseline() -> dict:
+    """The fp64 oracle timed on this host's cores, per workload, on all cores
+    (<= 16 threads: the host share of one GPU) and on one core, each over a
+    bounded sample whose token-heads are stated; tokens/s counts positions
+    across all of a workload's heads (token-heads/s divided by H).  The
+    headline `value` is the long-context workload's all-core rate."""
+    import oracle
+    import synth
+
+    threads = oracle.threads()
+    W = synth.WORKLOADS
+    plan = {  # workload -> (sequences, heads, tokens per sequence or None, decode steps)
+        0: (list(range(W[0].num_seqs)), list(range(W[0].heads)), None, None),
+        1: (list(range(W[1].num_seqs)), list(range(W[1].heads)), None, None),
+        2: (list(range(W[2].num_seqs)), list(range(0, W[2].heads, 12)), None, None),
+        3: ([0], list(range(W[3].heads)), 32768, None),
+        4: (None, list(range(W[4].heads)), None, list(range(W[4].decode_steps))),
+    }
+    one_core = {0: ([0], [0], None, None), 1: ([0], [0], 4096, None), 2: ([0], [0], 8192, None),
+                3: ([0], [0], 16384, None), 4: (None, list(range(16)), None, [0])}
+    per = {}
+    for i, w in W.items():
+        row = {"workload": w.name}
+        for label, spec, nt in (("all_cores", plan[i], threads), ("one_core", one_core[i], 1)):
+            seqs, heads, t_lim, steps = spec
+            if steps is not None:
+                dt, done = _oracle_time(w, None, heads, nthreads=nt, step=steps)
+            else:
+                dt, done = _oracle_time(w, seqs, heads, t_lim, nthreads=nt)
+            row[label] = {"tokens_per_s": done / w.heads / dt, "token_heads": done,
+                          "seconds": dt, "threads": nt}
+        per[str(i)] = row
+    head = per["3"]["all_cores"]
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 token recurrence over tokens [0, 32768) of the 1x1048576-token "
+                      f"workload, all 96 heads (d=128), in 8192-token slices with the state "
+                      f"carried, {threads} threads, {head['seconds']:.1f} s of oracle time",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(), "per_config": per}
+
+
+def fwd_config_leg(i: int, stream, reps: int = 25, warmup: int = 3) -> dict:
+    """kda_fwd_chunked on workload i (device-generated inputs and initial
+    states, resident before timing): `warmup` untimed calls, then `reps`
+    calls each bracketed by HIP events on the launch stream; the median."""
+    import torch
+
+    import delta_rule_linear_kda_amd as kda
+    import synth
+
+    w = synth.WORKLOADS[i]
+    lens = w.seq_lens()
+    T, H = int(sum(lens)), w.heads
+    x = {n: synth.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    s0 = synth.device_state(w, w.num_seqs)
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32, device="cuda")
+    o = torch.empty((T, H, w.dv), dtype=torch.float32, device="cuda")
+    sf = torch.empty((w.num_seqs, H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws_bytes = kda.fwd_workspace_bytes(w.num_seqs, T, H, w.dk, w.dv)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    args = tuple(x[n] for n in ("q", "k", "v", "a", "b", "gate"))
+
+    def call():
+        kda.fwd_chunked(*args, cu, s0, out=o, final_state=sf, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    med = ms[len(ms) // 2]
+    th = T * H
+    nbytes = fwd_bytes_per_token_head(w.dk, w.dv) * th + 4 * w.num_seqs * H * w.dk * w.dv * (
+        2 if s0 is not None else 1)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    out = {"workload": w.name, "tokens": T, "heads": H, "reps": reps, "ms_median": med,
+           "ms_min": ms[0], "ms_max": ms[-1], "tokens_per_s": T / (med * 1e-3),
+           "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+           "frac_bf16_mfma_alg": falg_per_token_head(w.dk, w.dv) * th / (med * 1e-3) / 1e12
+           / BF16_PEAK_TFLOPS,
+           "frac_bf16_mfma_alg_c64": falg_per_token_head(w.dk, w.dv, 64) * th / (med * 1e-3)
+           / 1e12 / BF16_PEAK_TFLOPS,
+           "form": "two-pass" if ws_bytes > 0 else "fused", "workspace_bytes": ws_bytes}
+    del x, o, sf, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def kcp_share(T: int, stream, reps: int = 3) -> dict:
@@ -397,6 +526,11 @@ def main() -> int:
     ap.add_argument("--only-bwd", action="store_true", help="time only the backward")
     ap.add_argument("--only-kcp-share", action="store_true",
                     help="run only the 12-head direct vs segment-form comparison")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload forward legs (4 x 4096 x 32, varlen 16 x 96)")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="time only the per-workload forward legs")
+    ap.add_argument("--only-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--trace-spans", metavar="TRACE_CSV")
@@ -428,6 +562,13 @@ def main() -> int:
         return 0
     if args.only_bwd:
         print(json.dumps({"bwd": backward(stream)}), flush=True)
+        return 0
+    if args.only_configs:
+        print(json.dumps({"fwd_configs": {str(i): fwd_config_leg(i, stream) for i in (1, 2)}}),
+              flush=True)
+        return 0
+    if args.only_cpu_baseline:
+        print(json.dumps({"cpu_baseline": cpu_baseline()}), flush=True)
         return 0
     if args.only_layer:
         wl = synth.WORKLOADS[3]
@@ -488,10 +629,10 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    fwd_avg = fwd_ms[len(fwd_ms) // 2]  # medians over the timed steps
+    dec_avg = dec_ms[len(dec_ms) // 2]
     ms_step = wall * 1e3 / args.steps
 
     th = T * H
@@ -520,10 +661,13 @@ def main() -> int:
         "config": {"workload": f"kda_fwd_bf16_T{T}_H96_d128 + kda_decode_bf16_N256_H96_d128 "
                                f"x{D} steps", "fwd_tokens": T, "heads": H, "dk": dk, "dv": dv,
                    "chunk": CHUNK, "decode_seqs": N, "decode_steps": D},
-        "fwd": {"ms": fwd_avg, "tokens_per_s": fwd_tps, "GB_per_s": fwd_gbs,
+        "fwd": {"ms": fwd_avg, "ms_min": fwd_ms[0], "ms_max": fwd_ms[-1],
+                "tokens_per_s": fwd_tps, "GB_per_s": fwd_gbs,
                 "frac_hbm": fwd_gbs / HBM_PEAK_GBS,
                 "TFLOP_per_s_alg": flops / (fwd_avg * 1e-3) / 1e12,
                 "frac_bf16_mfma_alg": flops / (fwd_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                "frac_bf16_mfma_alg_c64": falg_per_token_head(dk, dv, 64) * th / (fwd_avg * 1e-3)
+                / 1e12 / BF16_PEAK_TFLOPS,
                 "falg_per_token_head": falg, "bytes_per_token_head": fwd_bytes_per_token_head(dk, dv)},
         "decode": {"ms_per_step": dec_step_ms, "GB_per_s": dec_gbs,
                    "frac_hbm": dec_gbs / HBM_PEAK_GBS,
@@ -540,9 +684,11 @@ def main() -> int:
         out["layer"] = layer_ops(xin["q"], xin["gate"], o, stream)
     if not args.no_kcp_share:
         out["cp_share"] = cp_share(xin, stream)
-    if not args.no_kcp_share or not args.no_bwd:
+    if not args.no_kcp_share or not args.no_bwd or not args.no_configs:
         del xin, o, dec_in
         torch.cuda.empty_cache()
+    if not args.no_configs:
+        out["fwd_configs"] = {str(i): fwd_config_leg(i, stream) for i in (1, 2)}
     if not args.no_bwd:
         out["bwd"] = backward(stream)
     if not args.no_kcp_share:

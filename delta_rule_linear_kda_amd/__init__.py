@@ -161,7 +161,7 @@ def ckpt_count(cu_seqlens_host, interval: int) -> int:
 def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
                 output_final_state: bool = True, out=None, final_state=None,
                 checkpoint_interval: Optional[int] = None, checkpoints=None,
-                stream=None):
+                workspace=None, stream=None):
     """Chunked KDA forward over packed sequences (C ABI ``kda_fwd_chunked``, or
     ``kda_fwd_chunked_ckpt`` when ``checkpoint_interval`` is given).
 
@@ -171,7 +171,9 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     final_state fp32 [N, H, dk, dv] or None), plus the recorded states fp32
     [n_ckpt, H, dk, dv] as a third element when ``checkpoint_interval`` is
     given (slot layout: see ``kda_fwd_chunked_ckpt``).  ``final_state`` may be
-    passed as the same tensor as ``initial_state`` for an in-place update."""
+    passed as the same tensor as ``initial_state`` for an in-place update.
+    ``workspace``: a uint8 device tensor of at least ``fwd_workspace_bytes``
+    bytes to use instead of a fresh one."""
     import torch
 
     T, H, dk = q.shape
@@ -185,7 +187,11 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     ws_bytes = fwd_workspace_bytes(N, T, H, dk, dv, dt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if workspace is not None and ws_bytes:
+        ws = workspace
+        ws_bytes = workspace.numel()
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
     if checkpoint_interval is None:
         rc = lib().kda_fwd_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a),

@@ -22,7 +22,8 @@
 //   S  <- diag(Gamma_end) S + Kend^T U
 // with Kt = kh*exp(b - p), Kh = kh*exp(p - b) (off-diagonal tiles rescaled by
 // exp(p_row_tile - p_col_tile) <= 1), Qt = qh*exp(b - p), Qbar = qh*exp(b),
-// Kbar = kh*exp(b), Kend = kh*exp(b_end - b), Gamma_end = exp(b_end).
+// Kbar = kh*exp(b), Kend = kh*exp(b_end - b), Gamma_end = exp(b_end); Kend's row
+// factor is taken in two steps, to the tile's end and from there to the chunk's.
 //
 // Work decomposition: one workgroup of 4 wavefronts per (sequence, head,
 // 64-column slice of d_v).  The fp32 state slice (dk x 64) stays in MFMA
@@ -103,11 +104,13 @@ struct Layout {
   static constexpr int oP = oA + kC * L64;       // P
   static constexpr int oV = oP + kC * L64;       // V slice
   static constexpr int oE = oV + kC * LDV;       // [4][DK] exp(p_tile)
-  static constexpr int oF = oE + 4 * DK;         // [4][DK] exp(b_end - p_tile)
+  static constexpr int oF = oE + 4 * DK;         // [4][DK] exp(e_tile - p_tile)
   static constexpr int oD = oF + 4 * DK;         // [6][DK] exp(p_t - p_u), u < t
   static constexpr int oGe = oD + 6 * DK;        // [DK]    exp(b_end)
   static constexpr int oBeta = oGe + DK;         // [64]    beta
-  static constexpr int total = oBeta + kC;       // floats
+  static constexpr int oF2 = oBeta + kC;         // [4][DK] exp(b_end - e_tile)
+  static constexpr int total = oF2 + 4 * DK;     // floats
+  static_assert(total * 4 <= 160 * 1024, "LDS budget");
   static_assert(kC * LDK <= 2 * kC * L64, "cumsum scratch must fit in the A and P tiles");
 };
 
@@ -138,6 +141,7 @@ __global__ void __launch_bounds__(kThreads)
   float* sV = smem + L::oV;
   float* sE = smem + L::oE;
   float* sF = smem + L::oF;
+  float* sF2 = smem + L::oF2;
   float* sD = smem + L::oD;
   float* sGe = smem + L::oGe;
   float* sBeta = smem + L::oBeta;
@@ -259,8 +263,15 @@ __global__ void __launch_bounds__(kThreads)
       const float be = sG[(kC - 1) * LDK + c];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
+        // Kend of a row of tile tt is kh exp(p - b) exp(e - p) exp(b_end - e)
+        // with e the cumulative decay at the tile's last row: both tile
+        // factors stay normal wherever the product is not negligible (a
+        // single exp(b_end - p) would fall below fp32's normal range while
+        // exp(p - b) reaches e^80)
+        const float e = tt < 3 ? p[tt + 1] : be;
         sE[tt * DK + c] = fast_exp(p[tt]);
-        sF[tt * DK + c] = fast_exp(be - p[tt]);
+        sF[tt * DK + c] = fast_exp(e - p[tt]);
+        sF2[tt * DK + c] = fast_exp(be - e);
 #pragma unroll
         for (int u = 0; u < tt; ++u) sD[pair_idx(tt, u) * DK + c] = fast_exp(p[tt] - p[u]);
       }
@@ -352,6 +363,12 @@ __global__ void __launch_bounds__(kThreads)
       for (int idx = t - 64; idx < 6 * 256; idx += kThreads - 64) {
         const int pr = idx / 256, e = idx % 256;
         sX[(16 * kUpperPairs[pr][0] + e / 16) * L64 + 16 * kUpperPairs[pr][1] + e % 16] = 0.f;
+      }
+      // Kh is not read again before the state update: turn it into Kend in
+      // place, (Kh exp(e - p)) exp(b_end - e) per row of tile tt
+      for (int idx = t - 64; idx < kC * DK; idx += kThreads - 64) {
+        const int row = idx / DK, c = idx % DK, tt = row / kTile;
+        sKh[row * LDK + c] = sKh[row * LDK + c] * sF[tt * DK + c] * sF2[tt * DK + c];
       }
     }
     lds_barrier();
@@ -470,7 +487,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 32 * kb + kperm(g, j);
-          av[j] = sKh[i * LDK + c] * sF[(i / kTile) * DK + c];
+          av[j] = sKh[i * LDK + c];  // Kend (formed in place in stage 5)
           bv[j] = U[2 * kb + (j >> 2)][j & 3];
         }
         Pol::mma(acc, av, bv);

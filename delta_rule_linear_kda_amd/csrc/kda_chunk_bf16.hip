@@ -273,7 +273,9 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
               qbf[j] = (_Float16)qbar;
             }
             const float kbar = tau ? kt * e0[j] : kt;
-            const float kend = kh * fend[tau][j];
+            // tile 0's rows: (kh exp(p_1)) exp(b_end - p_1), both factors
+            // normal wherever the product is not negligible
+            const float kend = tau ? kh * fend[1][j] : (kh * e0[j]) * fend[1][j];
             ktb[j] = (__bf16)kt;
             khh[j] = (__bf16)kh;
             khl[j] = (__bf16)(kh - (float)khh[j]);
@@ -503,12 +505,14 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
+    // this wave's state columns are held as S 2^(esc - 127) (fp16 range of the
+    // state-chain operands)
+    int esc = 127;
     typedef __attribute__((ext_vector_type(CPL / 2))) uint32_t uvec_t;
     constexpr int NPASS = RPW / 4;
     uvec_t nq_[NPASS], nk_[NPASS];  // q, k rows for the norms of the next chunk
     uint32_t rv[8];                 // v of the chunk the chain works on (word with the bf16)
     uint32_t rgr[8];                // gate of that chunk (word with the bf16)
-    float rg[8];                    // sigmoid(gate) of that chunk, for its output
     f32x4_t O[2], U[2];
     auto load_qk = [&](int64_t c0, int g, int li) {
       const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
@@ -565,8 +569,10 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float y = O[j >> 2][j & 3];
-        if (gate) y *= rg[j];  // sigmoid(gate), formed in E
+        float y = O[j >> 2][j & 3] * pow2f(254 - esc);
+        if (gate)  // sigmoid(gate) of the chunk, from its loaded words
+          y *= rcpf_fast(
+              1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> (16u * (jcol & 1))) << 16)));
         __builtin_amdgcn_raw_buffer_store_b32(
             __float_as_uint(y), rs, 4 * (vo_lane + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)),
             0, 0);
@@ -600,18 +606,13 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         return r;
       };
 
-      // ---- E: sigmoid(gate) of c; norms of chunk it; U0, U = U0 - W S, O = Qbar S
+      // ---- E: norms of chunk it; U0, U = U0 - W S, O = Qbar S
       // The consumers of the registers loaded in the previous W stage run on
       // every iteration (at it = 0 the gate words are unused, at it = nch the
       // norms of the clamped chunk go to the LDS buffer no one reads then), so
       // every path waits for those loads at the same place and no later
       // reuse of their registers needs a drain of the memory counter, which
       // would also wait for the output stores.
-      if (!TRANS) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          rg[j] = rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((rgr[j] >> hsh) << 16)));
-      }
       {
         float* nqo = bNQ(it & 1);
         float* nko = bNK(it & 1);
@@ -636,6 +637,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         }
       }
       if (act) {
+        // the state columns' range for this chunk's fp16 operands
+        rescale_state(S, esc, col_max4(abs_max(S)));
         const float* xb = bX(p);
         const float* be = bBeta(p);
         if (tslice) {  // no value rows: U0 = 0
@@ -656,6 +659,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             split_bf16x8(xx, xh, xl);
             U[rt] = mma_x3(xh, xl, rh, rl, f32x4_t{0.f, 0.f, 0.f, 0.f});
           }
+          const float sc = pow2f(esc);  // U0 on the state columns' scale
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) U[rt][jj] *= sc;
         }
         const uint16_t* wp = bW(p);
         const uint16_t* qbp = bQB(p);
@@ -686,37 +694,64 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       // ---- AP: O += P U; S <- diag(Gamma_end) S + Kend^T diag(nk) U -------------
       if (act) {
         const float* nk = bNK(p);
-        f16x8_t uf;
-        bf16x8_t uh, ul;
+        f16x8_t uf, ufl;  // diag(nk) U as fp16 hi + lo for Kend^T U
+        float uinv;
+        bool ubig;
         {
           float uu[8], us[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) uu[j] = U[j >> 2][j & 3];
+          if constexpr (!TRANS) {  // O += P U first (U as bf16 hi + lo)
+            bf16x8_t uh, ul;
+            split_bf16x8(uu, uh, ul);
+            const uint16_t* ph = bPH(p);
+            const uint16_t* pl = bPL(p);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              const int off = (16 * rt + li) * LT + 4 * g;
+              O[rt] = mma_x3(lds4x2<bf16x8_t>(ph + off), lds4x2<bf16x8_t>(pl + off), uh, ul, O[rt]);
+            }
+          }
           const float4 n0 = *reinterpret_cast<const float4*>(nk + 4 * g);
           const float4 n1 = *reinterpret_cast<const float4*>(nk + 16 + 4 * g);
           us[0] = uu[0] * n0.x; us[1] = uu[1] * n0.y; us[2] = uu[2] * n0.z; us[3] = uu[3] * n0.w;
           us[4] = uu[4] * n1.x; us[5] = uu[5] * n1.y; us[6] = uu[6] * n1.z; us[7] = uu[7] * n1.w;
-          uf = pack_f16x8(us);
-          if constexpr (!TRANS) split_bf16x8(uu, uh, ul);
-        }
-        if constexpr (!TRANS) {
-          const uint16_t* ph = bPH(p);
-          const uint16_t* pl = bPL(p);
+          // the fp16 copy of diag(nk) U: its column's range (rare: a factor f)
+          float m = 0.f;
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const int off = (16 * rt + li) * LT + 4 * g;
-            O[rt] = mma_x3(lds4x2<bf16x8_t>(ph + off), lds4x2<bf16x8_t>(pl + off), uh, ul, O[rt]);
-          }
+          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(us[j]));
+          float f;
+          ubig = u_range(col_max4(m), f, uinv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) us[j] *= f;
+          split_f16x8(us, uf, ufl);
         }
         const float* ge = bGE(p);
         const uint16_t* kep = bKE(p);
+        // S <- 1/f (f diag(Gamma_end) S + Kend^T (f diag(nk) U)); f = 1 but on
+        // the rare path
+        const bool ub = __any(ubig);
+        if (ub) {
+          const float f = pow2f(254 - bexp(uinv));
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[ct][jj] *= f;
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const float4 gv = *reinterpret_cast<const float4*>(ge + 16 * ct + 4 * g);
           f32x4_t acc;
           acc[0] = gv.x * S[ct][0]; acc[1] = gv.y * S[ct][1];
           acc[2] = gv.z * S[ct][2]; acc[3] = gv.w * S[ct][3];
-          S[ct] = mma_f16(lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g), uf, acc);
+          const f16x8_t ke = lds4x2<f16x8_t>(kep + (16 * ct + li) * LT + 4 * g);
+          S[ct] = mma_f16(ke, uf, mma_f16(ke, ufl, acc));
+        }
+        if (ub) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[ct][jj] *= uinv;
         }
         // Record the state after the first `done` tokens when that is a
         // multiple of the recording interval.
@@ -726,10 +761,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           if (slot < ckpt_cap) {
             const uint32_t st_lane = 4 * g * dvt + 16 * sw + li;
             const auto sp = sbase(ckpt + (slot * H + h) * DK * dvt + col0);
+            const float isc = pow2f(254 - esc);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj];
+              for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj] * isc;
           }
         }
       }
@@ -762,10 +798,11 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       const int lane = threadIdx.x % 64, g = lane / 16, li = lane % 16;
       const uint32_t st_lane = 4 * g * sdv + 16 * sw + li;
       const auto sp = sbase(s_final + st_off);
+      const float isc = pow2f(254 - esc);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * sdv] = S[ct][jj];
+        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * sdv] = S[ct][jj] * isc;
     }
   }
 }

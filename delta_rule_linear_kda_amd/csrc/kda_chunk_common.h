@@ -91,11 +91,84 @@ __device__ __forceinline__ float row_last16(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x01F0));
 }
 
+// ---- fp16 range of the state-chain operands ---------------------------------
+// The state S and the pseudo-values U enter the W S, Qbar S and Kend^T U
+// products as fp16, whose largest value is 65504, while the state itself is
+// fp32 and unbounded (a caller's initial state, large values).  Each state
+// column j is therefore carried as S_j 2^(esc_j - 127) with a per-column
+// power of two (exact): when the column's largest magnitude leaves
+// [2^2, 2^10) it is brought back to [2^6, 2^7), which keeps the fp16 copy of
+// S in range while its smaller entries keep fp16's relative precision.  U
+// (U0 and every product with U carry the same column scale) is checked where
+// its fp16 copy is formed: if a column of it would reach 2^15 it is scaled
+// down by another power of two f for the Kend^T U product, whose result is
+// scaled back by 1/f (a rare path).
+
+// 2^(e - 127) for a biased exponent e in [1, 254].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)e << 23); }
+// Biased exponent of |x| (0 for zero and subnormals, 255 for inf and NaN).
+__device__ __forceinline__ int bexp(float x) { return (int)((__float_as_uint(x) >> 23) & 0xffu); }
+// Largest value over the four lanes (li, li + 16, li + 32, li + 48) that
+// hold one column of a 16x16 accumulator tile.
+__device__ __forceinline__ float col_max4(float m) {
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  return fmaxf(m, __shfl_xor(m, 32, 64));
+}
+// Largest magnitude of this lane's part of a state column.
+template <int N>
+__device__ __forceinline__ float abs_max(const f32x4_t (&S)[N]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(S[i][j]));
+  return m;
+}
+// Rescales the lane's part of a state column (column max m, already taken
+// over the column's four lanes) when m leaves [2^2, 2^10); esc is the
+// column's biased scale exponent, kept in [4, 250].  Taken by the whole wave
+// or not at all (a wave-uniform branch), so it costs nothing in the common
+// case.
+template <int N>
+__device__ __forceinline__ void rescale_state(f32x4_t (&S)[N], int& esc, float m) {
+  const int E = bexp(m);
+  const bool need = E != 0 && E != 255 && (E < 127 + 2 || E >= 127 + 10);
+  if (__any(need)) {
+    const int en = need ? min(250, max(4, esc + (127 + 6) - E)) : esc;
+    const int d = en - esc;  // |d| <= 246: applied as two factors of at most 2^123
+    const float r1 = pow2f(127 + d / 2), r2 = pow2f(127 + d - d / 2);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = S[i][j] * r1 * r2;
+    esc = en;
+  }
+}
+// Factor f = 2^(141 - E) that brings a column of U whose fp16 copy would
+// reach 2^15 (biased exponent E of its max) into [2^14, 2^15), and 1/f; 1
+// and 1 otherwise.  Returns whether this lane's column needs it.
+__device__ __forceinline__ bool u_range(float mu, float& f, float& finv) {
+  const int E = bexp(mu);
+  const bool big = E >= 127 + 15 && E != 255;
+  f = big ? pow2f(268 - E) : 1.f;
+  finv = big ? pow2f(E - 14) : 1.f;
+  return big;
+}
+
 __device__ __forceinline__ f16x8_t pack_f16x8(const float (&x)[8]) {
   f16x8_t r;
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = (_Float16)x[j];
   return r;
+}
+// fp16 hi + lo parts of 8 values (hi = fp16(x), lo = fp16(x - hi)).
+__device__ __forceinline__ void split_f16x8(const float (&x)[8], f16x8_t& hi, f16x8_t& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const _Float16 hv = (_Float16)x[j];
+    hi[j] = hv;
+    lo[j] = (_Float16)(x[j] - (float)hv);
+  }
 }
 __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
 #pragma unroll

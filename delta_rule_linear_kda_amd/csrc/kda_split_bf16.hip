@@ -10,8 +10,9 @@
 //           chunk), independently: the decay-scaled operands, A, P, the
 //           inverse X = (I + A)^-1 and W, written as one "chunk record" with
 //           every row scale folded in: X diag(beta) (bf16 hi/lo), P (bf16
-//           hi/lo), Gamma_end, diag(nq) Qbar, -W and (Kend diag(nk))^T
-//           (fp16), 33,280 bytes at d_k = 128 (nq, nk: 1/|q|, 1/|k|);
+//           hi/lo, lower block-triangular parts only), Gamma_end, diag(nq)
+//           Qbar, -W and Kend diag(nk) (fp16), 30,208 bytes at d_k = 128
+//           (nq, nk: 1/|q|, 1/|k|);
 //   pass 2  chunk_state_bf16_kernel  per (sequence, head) -- or per
 //           (sequence, head, 64-column d_v slice) when there are few items --
 //           the sequential chain over the records: U0 = X diag(beta) V,
@@ -402,7 +403,9 @@ __global__ void __launch_bounds__(64 * (DK / 16))
           qlb[j] = (__bf16)(qt - (float)qhb[j]);
           qbr[tau][j] = tau ? qt * e0[j] : qt;
           const float kbar = tau ? kt * e0[j] : kt;
-          ker[tau][j] = kh * fend[tau][j];
+          // tile 0's rows: (kh exp(p_1)) exp(b_end - p_1), both factors
+          // normal wherever the product is not negligible
+          ker[tau][j] = tau ? kh * fend[1][j] : (kh * e0[j]) * fend[1][j];
           ktb[j] = (__bf16)kt;
           khh[j] = (__bf16)kh;
           khl[j] = (__bf16)(kh - (float)khh[j]);
@@ -839,6 +842,12 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       for (int ct = 0; ct < NCT; ++ct) S[t][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // column tile t of the state is held as S 2^(esc[t] - 127) (fp16 range of
+  // the state-chain operands)
+  int esc[CT];
+#pragma unroll
+  for (int t = 0; t < CT; ++t) esc[t] = 127;
+
   if (cnt > 0) {
     int64_t ck_off = 0;  // first recorded-state slot of this sequence
     if (CKPT)
@@ -892,6 +901,9 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       constexpr int B = decltype(Bc)::value;
       const int cc = c_begin + s;
       gate_fetch(s + 1, std::integral_constant<int, B ^ 1>());
+      // the state columns' range for this chunk's fp16 operands
+#pragma unroll
+      for (int t = 0; t < CT; ++t) rescale_state(S[t], esc[t], col_max4(abs_max(S[t])));
       const unsigned char* rb = smem + B * dBuf;
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(rb + R::dXH);
       const uint16_t* xl = reinterpret_cast<const uint16_t*>(rb + R::dXL);
@@ -945,6 +957,12 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
           U[t][rt] = mma_bf16(aXH[rt], vb, mma_bf16(aXL[rt], vb, f32x4_t{0.f, 0.f, 0.f, 0.f}));
         O[t][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         O[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // U0 on the state column's scale
+        const float sc = pow2f(esc[t]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) U[t][rt][jj] *= sc;
       }
       // U += (-W) S, O = Qbar' S
 #pragma unroll
@@ -960,18 +978,35 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             O[t][rt] = mma_f16(aQ[rt][kb], sbk, O[t][rt]);
           }
         }
-      // O += P U (U as bf16 hi + lo); Kend'^T U takes U in fp16
-      f16x8_t uf[CT];
+      // O += P U (U as bf16 hi + lo); Kend'^T U takes U as fp16 hi + lo (the
+      // state keeps the product to fp16's rounding of Kend' alone)
+      f16x8_t uf[CT], ufl[CT];
+      float uscale[CT], uinv[CT];
+      bool ubig = false;
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
         bf16x8_t uh, ul;
         float uu[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) uu[j] = U[t][j >> 2][j & 3];
-        uf[t] = pack_f16x8(uu);
         split_bf16x8(uu, uh, ul);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) O[t][rt] = mma_x3(aPH[rt], aPL[rt], uh, ul, O[t][rt]);
+        ubig |= u_range(col_max4(abs_max(U[t])), uscale[t], uinv[t]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uu[j] *= uscale[t];
+        split_f16x8(uu, uf[t], ufl[t]);
+      }
+      // a column of U beyond fp16's range (rare): S <- 1/f (f diag(Gamma_end) S
+      // + Kend'^T (f U)), the state pre- and post-scaled by powers of two
+      const bool ub = __any(ubig);
+      if (ub) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[t][ct][jj] *= uscale[t];
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -982,8 +1017,16 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
           f32x4_t acc;
           acc[0] = gv.x * S[t][ct][0]; acc[1] = gv.y * S[t][ct][1];
           acc[2] = gv.z * S[t][ct][2]; acc[3] = gv.w * S[t][ct][3];
-          S[t][ct] = mma_f16(ke, uf[t], acc);
+          S[t][ct] = mma_f16(ke, uf[t], mma_f16(ke, ufl[t], acc));
         }
+      }
+      if (ub) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) S[t][ct][jj] *= uinv[t];
       }
       if constexpr (CKPT) {
         // the state after the first `done` tokens, when that is a multiple of
@@ -997,11 +1040,14 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             __asm__ volatile("" : "+v"(ad));
             float* sp = reinterpret_cast<float*>(ad);
 #pragma unroll
-            for (int t = 0; t < CT; ++t)
+            for (int t = 0; t < CT; ++t) {
+              const float isc = pow2f(254 - esc[t]);
 #pragma unroll
               for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) sp[16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj];
+                for (int jj = 0; jj < 4; ++jj)
+                  sp[16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj] * isc;
+            }
           }
         }
       }
@@ -1017,7 +1063,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
         for (int t = 0; t < CT; ++t)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            float y = O[t][j >> 2][j & 3];
+            float y = O[t][j >> 2][j & 3] * pow2f(254 - esc[t]);
             if constexpr (GATE)
               y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][t][j] >> hsh) << 16)));
             __builtin_amdgcn_raw_buffer_store_b32(
@@ -1054,11 +1100,14 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
   if (s_dst) {
     const auto sp = sbase(s_dst + st_off);
 #pragma unroll
-    for (int t = 0; t < CT; ++t)
+    for (int t = 0; t < CT; ++t) {
+      const float isc = pow2f(254 - esc[t]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sp[st_lane + 16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj];
+        for (int jj = 0; jj < 4; ++jj)
+          sp[st_lane + 16 * t + (16 * ct + jj) * dvt] = S[t][ct][jj] * isc;
+    }
   }
 }
 

@@ -13,8 +13,15 @@ factors reach e^80):
            attention in closed form; pinned on the CPU)
   orth     orthonormal keys with beta = 1 (b = +inf) and g = 0 (a = -inf):
            causal linear attention (pinned on the CPU)
-  big_s0   initial states ~ N(0, 1e3^2) and N(0, 1e5^2), values x 1e3: the
-           fp32 state must not be limited by a 16-bit operand's range
+  big_s0   initial states ~ N(0, s^2) and values x s for s = 1e3, 1e5: the
+           fp32 state must not be limited by a 16-bit operand's range (65504)
+  mixed    initial states ~ N(0, 1e10) with values x 1e3 over 60,000 tokens:
+           the first outputs are ~1000 times the later ones; checked for
+           finite results, the final state, and the outputs after the first
+           5,920 tokens (the state-path products carry fp16's relative
+           precision of the state's current scale, so the transient's own
+           rounding is ~3e-4 of its scale, which the whole sequence's RMS
+           does not reflect)
 Paths: the fused kernel (enough (sequence, head) pairs to fill the device),
 the two-pass form with 64-column state slices (few pairs) and with
 whole-head state workgroups, the two-pass form over several blocks of chunks
@@ -65,7 +72,7 @@ def _round_to(arr_f32, like):
     return arr_f32.astype(np.float32)
 
 
-def apply_case(case, x, lens, dk, seed=5):
+def apply_case(case, x, lens, dk, seed=5, v_scale=1e3):
     """Modify host inputs x in place for `case` (sequence lengths `lens`)."""
     rng = np.random.default_rng(seed)
     H = x["q"].shape[1]
@@ -93,7 +100,7 @@ def apply_case(case, x, lens, dk, seed=5):
             x["b"] = _const(x["b"], np.inf)
             x["a"] = _const(x["a"], -np.inf)
     elif case == "big_v":
-        vf = synth.to_f64(x["v"]).astype(np.float32) * np.float32(1e3)
+        vf = synth.to_f64(x["v"]).astype(np.float32) * np.float32(v_scale)
         x["v"] = _round_to(vf, x["v"])
     else:
         raise ValueError(case)
@@ -118,7 +125,7 @@ def run_small(path, case, s0_std=None):
     T = sum(lens)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     x = kc.host_inputs(w, T)
-    apply_case(case if case != "big_s0" else "big_v", x, lens, dk)
+    apply_case(case if case != "big_s0" else "big_v", x, lens, dk, v_scale=s0_std or 1.0)
     s0 = kc.host_state(w, len(lens)) if s0_std else None
     dev = {n: kc.to_torch(x[n]) for n in x}
     o, sf = kda.fwd_chunked(*(dev[n] for n in NAMES),
@@ -132,6 +139,10 @@ def run_small(path, case, s0_std=None):
     eo, es = kc.rel_err(o, o_ref), kc.rel_err(sf, sf_ref)
     tol = kc.TOL_F32 if w.dtype == synth.F32 else kc.TOL_BF16
     print(f"    err o={eo:.3e} state={es:.3e} (tol {tol:.0e})", flush=True)
+    if es > tol / 4:  # where the state's worst element sits
+        i = np.unravel_index(np.argmax(np.abs(sf - sf_ref)), sf.shape)
+        print(f"    worst state element {i}: gpu {sf[i]:.6e} ref {sf_ref[i]:.6e} "
+              f"rms {np.sqrt(np.mean(sf_ref ** 2)):.3e}", flush=True)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(sf))
     assert eo <= tol and es <= tol
 
@@ -145,8 +156,8 @@ def test_edge_small(path, case):
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("s0_std", [1e3, 1e5])
 def test_large_state_and_values(path, s0_std):
-    """Initial states of std 1e3 / 1e5 and values x 1e3 (the state and U can
-    exceed 65504, the largest fp16 value)."""
+    """Initial states of std s and values x s for s = 1e3, 1e5 (the state
+    and U exceed 65504, the largest fp16 value)."""
     run_small(path, "big_s0", s0_std=s0_std)
 
 
@@ -154,14 +165,14 @@ MULTI_T = 60_000
 MULTI_HEADS = [0, 7, 19, 31, 40, 52, 63, 71, 80, 88, 94, 95]
 
 
-@pytest.mark.parametrize("case", ["a_pinf", "a_p8", "a_mix", "big_s0"])
+@pytest.mark.parametrize("case", ["a_pinf", "a_p8", "a_mix", "big_s0", "mixed"])
 def test_edge_multi_block(case):
     """The two-pass form over several blocks of chunks (1 x 60,000 tokens x
     96 heads: a quarter-size first block, then full blocks): every output
     row and the final state of 12 heads against the oracle over the whole
     sequence."""
     _require_gpu()
-    w = kc.custom_workload(W3, s0_std=1e5 if case == "big_s0" else None)
+    w = kc.custom_workload(W3, s0_std=1e5 if case in ("big_s0", "mixed") else None)
     T, H = MULTI_T, w.heads
     ws = kda.fwd_workspace_bytes(1, T, H, w.dk, w.dv)
     print(f"[case] edge multi-block {case} T={T} H={H} workspace={ws}", flush=True)
@@ -173,7 +184,7 @@ def test_edge_multi_block(case):
     elif case == "a_mix":
         dev["a"] = torch.where(dev["a"] < 0, float("-inf"), float("inf")).to(torch.bfloat16)
     else:
-        dev["v"] = (dev["v"].float() * 1e3).to(torch.bfloat16)
+        dev["v"] = (dev["v"].float() * (1e5 if case == "big_s0" else 1e3)).to(torch.bfloat16)
     s0 = kc.device_state(w, 1)
     cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
     o, sf = kda.fwd_chunked(*(dev[n] for n in NAMES), cu, s0)
@@ -184,13 +195,23 @@ def test_edge_multi_block(case):
     def fetch(t0, t1):
         return {nm: kc.device_rows_f64(dev[nm], t0, t1, MULTI_HEADS) for nm in NAMES}
 
+
+    per_slice = []
+    skip = 5920 if case == "mixed" else 0  # the mixed case's transient (see above)
+
     def on_slice(t0, t1, o_ref):
-        acc.add(o[t0:t1, MULTI_HEADS].cpu().numpy(), o_ref)
+        got = o[t0:t1, MULTI_HEADS].cpu().numpy()
+        if t0 >= skip:
+            acc.add(got, o_ref)
+        per_slice.append((t0, float(np.abs(got - o_ref).max()), float(np.sqrt(np.mean(o_ref ** 2)))))
 
     s0_h = None if s0 is None else s0[0, MULTI_HEADS].cpu().numpy()[None].astype(np.float64)
-    s_ref = kc.oracle_stream(fetch, T, s0_h, on_slice=on_slice)
+    s_ref = kc.oracle_stream(fetch, T, s0_h, slice_tokens=5920, on_slice=on_slice)
     es = kc.rel_err(sf[0, MULTI_HEADS].cpu().numpy(), s_ref[0])
     print(f"    err o={acc.err():.3e} state={es:.3e}", flush=True)
+    if acc.err() > kc.TOL_BF16 / 4:
+        for t0, mx, rms in per_slice:
+            print(f"      tokens from {t0}: max |diff| {mx:.3e}, slice rms {rms:.3e}", flush=True)
     assert acc.err() <= kc.TOL_BF16 and es <= kc.TOL_BF16
 
 
@@ -210,7 +231,7 @@ def test_edge_decode(dtype, case):
     worst = 0.0
     for s in range(3):
         x = {n: kc.host_tokens(w, n, N, step=s) for n in synth.TOKEN_TENSORS}
-        apply_case(case if case != "big_s0" else "big_v", x, [1] * N, w.dk, seed=s)
+        apply_case(case if case != "big_s0" else "big_v", x, [1] * N, w.dk, seed=s, v_scale=1e5)
         dev = {n: kc.to_torch(x[n]) for n in x}
         o = kda.decode_step(*(dev[n] for n in NAMES), state)
         o_ref = oracle.decode_step(*(kc.f64(x[n]) for n in NAMES), s_ref)
