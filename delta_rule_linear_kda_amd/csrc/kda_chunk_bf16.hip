@@ -638,7 +638,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       }
       if (act) {
         // the state columns' range for this chunk's fp16 operands
-        rescale_state(S, esc, col_max4(abs_max(S)));
+        rescale_state(S, esc);
         const float* xb = bX(p);
         const float* be = bBeta(p);
         if (tslice) {  // no value rows: U0 = 0
@@ -717,20 +717,14 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           us[0] = uu[0] * n0.x; us[1] = uu[1] * n0.y; us[2] = uu[2] * n0.z; us[3] = uu[3] * n0.w;
           us[4] = uu[4] * n1.x; us[5] = uu[5] * n1.y; us[6] = uu[6] * n1.z; us[7] = uu[7] * n1.w;
           // the fp16 copy of diag(nk) U: its column's range (rare: a factor f)
-          float m = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(us[j]));
-          float f;
-          ubig = u_range(col_max4(m), f, uinv);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) us[j] *= f;
+          uinv = u_range(us, ubig);
           split_f16x8(us, uf, ufl);
         }
         const float* ge = bGE(p);
         const uint16_t* kep = bKE(p);
         // S <- 1/f (f diag(Gamma_end) S + Kend^T (f diag(nk) U)); f = 1 but on
         // the rare path
-        const bool ub = __any(ubig);
+        const bool ub = ubig;
         if (ub) {
           const float f = pow2f(254 - bexp(uinv));
 #pragma unroll

@@ -97,12 +97,14 @@ __device__ __forceinline__ float row_last16(float x) {
 // fp32 and unbounded (a caller's initial state, large values).  Each state
 // column j is therefore carried as S_j 2^(esc_j - 127) with a per-column
 // power of two (exact): when the column's largest magnitude leaves
-// [2^2, 2^10) it is brought back to [2^6, 2^7), which keeps the fp16 copy of
-// S in range while its smaller entries keep fp16's relative precision.  U
-// (U0 and every product with U carry the same column scale) is checked where
-// its fp16 copy is formed: if a column of it would reach 2^15 it is scaled
-// down by another power of two f for the Kend^T U product, whose result is
-// scaled back by 1/f (a rare path).
+// [2^-8, 2^10) it is brought back to [2^6, 2^7), which keeps the fp16 copy of
+// S in range and its entries above fp16's subnormals.  U (U0 and every
+// product with U carry the same column scale) is checked where its fp16 copy
+// is formed: if a column of it would reach 2^15 it is scaled down by another
+// power of two f for the Kend^T U product, whose result is scaled back by
+// 1/f.  Both checks are lane-local in the common case (each lane tests its
+// own entries, then one wave vote); only when some lane is out of range does
+// the wave form the exact column maxima over the column's four lanes.
 
 // 2^(e - 127) for a biased exponent e in [1, 254].
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)e << 23); }
@@ -124,16 +126,14 @@ __device__ __forceinline__ float abs_max(const f32x4_t (&S)[N]) {
     for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(S[i][j]));
   return m;
 }
-// Rescales the lane's part of a state column (column max m, already taken
-// over the column's four lanes) when m leaves [2^2, 2^10); esc is the
-// column's biased scale exponent, kept in [4, 250].  Taken by the whole wave
-// or not at all (a wave-uniform branch), so it costs nothing in the common
-// case.
+// Keeps the lane's part of a state column in range (see above); esc is the
+// column's biased scale exponent, kept in [4, 250].
 template <int N>
-__device__ __forceinline__ void rescale_state(f32x4_t (&S)[N], int& esc, float m) {
-  const int E = bexp(m);
-  const bool need = E != 0 && E != 255 && (E < 127 + 2 || E >= 127 + 10);
-  if (__any(need)) {
+__device__ __forceinline__ void rescale_state(f32x4_t (&S)[N], int& esc) {
+  const float ml = abs_max(S);
+  if (__any(ml >= 1024.f || (ml < 0x1p-8f && ml > 0.f))) {  // wave-uniform, rare
+    const int E = bexp(col_max4(ml));
+    const bool need = E != 0 && E != 255 && (E < 127 - 8 || E >= 127 + 10);
     const int en = need ? min(250, max(4, esc + (127 + 6) - E)) : esc;
     const int d = en - esc;  // |d| <= 246: applied as two factors of at most 2^123
     const float r1 = pow2f(127 + d / 2), r2 = pow2f(127 + d - d / 2);
@@ -144,15 +144,26 @@ __device__ __forceinline__ void rescale_state(f32x4_t (&S)[N], int& esc, float m
     esc = en;
   }
 }
-// Factor f = 2^(141 - E) that brings a column of U whose fp16 copy would
-// reach 2^15 (biased exponent E of its max) into [2^14, 2^15), and 1/f; 1
-// and 1 otherwise.  Returns whether this lane's column needs it.
-__device__ __forceinline__ bool u_range(float mu, float& f, float& finv) {
-  const int E = bexp(mu);
-  const bool big = E >= 127 + 15 && E != 255;
-  f = big ? pow2f(268 - E) : 1.f;
-  finv = big ? pow2f(E - 14) : 1.f;
-  return big;
+// For 8 entries x of a column of U (in place): scales them by f = 2^(141 - E)
+// when the column's largest magnitude (biased exponent E) reaches 2^15, so
+// that the column lies in [2^14, 2^15), and returns 1/f (1 otherwise).  The
+// wave takes the exact column maxima only when some lane has an entry at or
+// above 2^15; *any_big tells whether it did.
+__device__ __forceinline__ float u_range(float (&x)[8], bool& any_big) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+  any_big = __any(m >= 32768.f);
+  float finv = 1.f;
+  if (any_big) {  // wave-uniform, rare
+    const int E = bexp(col_max4(m));
+    const bool big = E >= 127 + 15 && E != 255;
+    const float f = big ? pow2f(268 - E) : 1.f;
+    finv = big ? pow2f(E - 14) : 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] *= f;
+  }
+  return finv;
 }
 
 __device__ __forceinline__ f16x8_t pack_f16x8(const float (&x)[8]) {

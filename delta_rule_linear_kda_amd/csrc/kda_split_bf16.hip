@@ -903,7 +903,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       gate_fetch(s + 1, std::integral_constant<int, B ^ 1>());
       // the state columns' range for this chunk's fp16 operands
 #pragma unroll
-      for (int t = 0; t < CT; ++t) rescale_state(S[t], esc[t], col_max4(abs_max(S[t])));
+      for (int t = 0; t < CT; ++t) rescale_state(S[t], esc[t]);
       const unsigned char* rb = smem + B * dBuf;
       const uint16_t* xh = reinterpret_cast<const uint16_t*>(rb + R::dXH);
       const uint16_t* xl = reinterpret_cast<const uint16_t*>(rb + R::dXL);
@@ -981,8 +981,8 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       // O += P U (U as bf16 hi + lo); Kend'^T U takes U as fp16 hi + lo (the
       // state keeps the product to fp16's rounding of Kend' alone)
       f16x8_t uf[CT], ufl[CT];
-      float uscale[CT], uinv[CT];
-      bool ubig = false;
+      float uinv[CT];
+      bool ub = false;
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
         bf16x8_t uh, ul;
@@ -992,21 +992,20 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
         split_bf16x8(uu, uh, ul);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) O[t][rt] = mma_x3(aPH[rt], aPL[rt], uh, ul, O[t][rt]);
-        ubig |= u_range(col_max4(abs_max(U[t])), uscale[t], uinv[t]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) uu[j] *= uscale[t];
+        bool big;
+        uinv[t] = u_range(uu, big);
+        ub |= big;
         split_f16x8(uu, uf[t], ufl[t]);
       }
       // a column of U beyond fp16's range (rare): S <- 1/f (f diag(Gamma_end) S
       // + Kend'^T (f U)), the state pre- and post-scaled by powers of two
-      const bool ub = __any(ubig);
       if (ub) {
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) S[t][ct][jj] *= uscale[t];
+            for (int jj = 0; jj < 4; ++jj) S[t][ct][jj] *= pow2f(254 - bexp(uinv[t]));
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
