@@ -1160,8 +1160,10 @@ namespace {
 
 // Per device: a second stream (default priority) for the state pass, and
 // the events that order it against the chunk-record pass on the caller's
-// stream.  Created on first use and kept for the process; one mutex
-// serialises the enqueueing (not the GPU work) of concurrent calls.
+// stream.  Created on the first multi-block call on that device (on the
+// device of the caller's stream) and kept for the process; one mutex
+// serialises the enqueueing (not the GPU work) of concurrent calls, which on
+// one device share this stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t start = nullptr, built[2] = {nullptr, nullptr}, used[2] = {nullptr, nullptr};
@@ -1169,17 +1171,28 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[64];
 
-hipError_t side_stream(SideStream** out) {
+hipError_t side_stream(hipStream_t stream, SideStream** out) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = hipStreamGetDevice(stream, &dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   SideStream& ss = g_side[dev];
   if (!ss.s) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    hipEvent_t* evs[5] = {&ss.start, &ss.built[0], &ss.built[1], &ss.used[0], &ss.used[1]};
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    SideStream made;
+    e = hipStreamCreateWithFlags(&made.s, hipStreamNonBlocking);
+    hipEvent_t* evs[5] = {&made.start, &made.built[0], &made.built[1], &made.used[0],
+                          &made.used[1]};
     for (hipEvent_t* ev : evs)
-      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+      if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    ss = made;
   }
   *out = &ss;
   return hipSuccess;
@@ -1230,7 +1243,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (w.blocks > 1) {
-    if ((e = side_stream(&side)) != hipSuccess) return e;
+    if ((e = side_stream(stream, &side)) != hipSuccess) return e;
     s2 = side->s;
     if ((e = hipEventRecord(side->start, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, side->start, 0)) != hipSuccess) return e;

@@ -24,15 +24,25 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, row-major, owned by the
  *     caller, 16-byte aligned -- except b, which needs only the alignment of
- *     its element type, and cu_seqlens (4 bytes).  The library never allocates, frees, retains a
- *     pointer past the call, or synchronises; work is enqueued on `stream`
- *     (a hipStream_t; NULL = the default stream) and ordered by it.
+ *     its element type, and cu_seqlens (4 bytes).  The library never
+ *     allocates or frees device memory, retains a pointer past the call, or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and ordered by it.
+ *   - One exception to statelessness: when the two-pass bf16 forward needs
+ *     more than one block of chunk records (very long inputs, e.g. 1M tokens
+ *     x 96 heads), it runs each block's state pass on a second stream beside
+ *     the next block's record pass.  That stream and five events are created
+ *     per device, on the device of the caller's stream, at the first such
+ *     call and kept until the process ends; the enqueueing of such calls is
+ *     serialised by a mutex, and concurrent calls on one device share the
+ *     stream (their state passes run in call order).  The caller's stream
+ *     waits for all of it, so the call is still ordered by `stream` alone.
  *   - Host-checkable problems are reported by the return code BEFORE anything
  *     is enqueued.  Preconditions that live in device memory (cu_seqlens
  *     starting at 0, nondecreasing, ending at total_tokens) are the caller's
  *     responsibility; violating them is undefined behaviour.
  *   - A launch failure is reported as KDA_ERR_HIP.  No C++ exception crosses
- *     the ABI.  Functions are stateless and may be called from any thread.
+ *     the ABI.  Functions may be called from any thread.
  *   - Results are deterministic: repeated calls on the same inputs give
  *     bitwise-identical outputs (no atomics in any reduction).
  */
