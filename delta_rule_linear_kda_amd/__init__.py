@@ -6,7 +6,8 @@ supplies device memory and the current stream.  If the library is missing the
 import of any entry point raises -- there is no fallback path.
 
 Entry points (same names as the C ABI):
-  * ``fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, ...)``
+  * ``fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, ...)``,
+    ``fwd_chunked_noalloc(...)`` (same, without a workspace)
   * ``decode_step(q, k, v, a, b, gate, state, ...)``
   * ``segment_transition(k, v, a, b, cu_seqlens, ...)``,
     ``segment_compose(seg_offsets, trans, ...)``,
@@ -30,12 +31,13 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL_POINTER", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
     4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP",
+    8: "KDA_ERR_SCRATCH",
 }
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
            "kda_fwd_ckpt_count", "kda_segment_transition", "kda_segment_compose",
            "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_shortconv_swish_l2",
            "kda_rmsnorm_gate", "kda_bwd_workspace_bytes", "kda_bwd_chunked", "kda_decode_step",
-           "kda_status_str", "kda_abi_version")
+           "kda_status_str", "kda_abi_version", "kda_fwd_chunked_noalloc")
 
 
 class KdaError(RuntimeError):
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked.restype = ctypes.c_int
         L.kda_fwd_chunked.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+        L.kda_fwd_chunked_noalloc.restype = ctypes.c_int
+        L.kda_fwd_chunked_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_fwd_chunked_ckpt.restype = ctypes.c_int
         L.kda_fwd_chunked_ckpt.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_int32, vp, ctypes.c_int64, vp,
@@ -212,6 +216,35 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     if rc != 0:
         raise KdaError(rc, "kda_fwd_chunked_ckpt")
     return out, final_state, checkpoints
+
+
+def fwd_chunked_noalloc(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *, out=None,
+                        final_state=None, stream=None):
+    """``kda_fwd_chunked_noalloc``: the forward with its scratch in the
+    library's fixed device array (no workspace; raises KdaError with
+    KDA_ERR_SCRATCH when the shape needs more).  Arguments and results as
+    ``fwd_chunked`` (out and final_state are allocated here when not given;
+    pass them for a call that allocates nothing)."""
+    import torch
+
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.float32, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
+    rc = lib().kda_fwd_chunked_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(b), _ptr(gate), _ptr(cu_seqlens),
+                                       _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                       _stream(q.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_chunked_noalloc")
+    return out, final_state
 
 
 def segment_transition(k, v, a, b, cu_seqlens, *, out=None, stream=None):

@@ -80,6 +80,8 @@ const char* kda_status_str(kda_status st) {
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch";
+    case KDA_ERR_SCRATCH:
+      return "KDA_ERR_SCRATCH: the problem needs more scratch than the no-allocation forward holds";
   }
   return "unknown kda_status";
 }
@@ -249,6 +251,29 @@ kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, const voi
   if (!aligned16(ckpt_states)) return KDA_ERR_MISALIGNED;
   return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state,
                   ckpt_interval, ckpt_states, ckpt_capacity, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_chunked_noalloc(const kda_shape* shape, const void* q, const void* k,
+                                   const void* v, const void* a, const void* b, const void* gate,
+                                   const int32_t* cu_seqlens, const float* initial_state, void* o,
+                                   float* final_state, void* stream) {
+  kda_status st = check_shape(shape);
+  if (st != KDA_OK) return st;
+  const kda_shape& s = *shape;
+  bool empty = false;
+  st = check_fwd(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
+                 nullptr, 0, &empty);
+  if (st != KDA_OK || empty) return st;
+  kda::FwdArgs p = fwd_args(s, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!fwd_uses_split(s))  // the kernels of these shapes use no workspace
+    return kda::launch_fwd_chunked(p, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  kda::SplitLayout w;
+  if (!kda::noalloc_layout(s.num_seqs, s.total_tokens, s.num_heads, s.dk, s.dv, &w))
+    return KDA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (kda::noalloc_scratch(hs, &ws) != hipSuccess) return KDA_ERR_HIP;
+  return kda::launch_fwd_split_bf16(p, ws, hs, &w) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_fwd_ckpt_count(int32_t num_seqs, const int32_t* cu_seqlens_host,

@@ -46,9 +46,28 @@ struct SplitLayout {
   uint64_t rec[2], slot[2], carry, bt, total;  // bt: b transposed to [H, T] bf16
 };
 constexpr uint64_t kSplitRecordBudget = 4ull << 30;  // bytes of chunk records per block
+// Layout for a record budget of `record_budget` bytes over `buffers` (1 or 2)
+// record buffers.
 SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk,
-                         int dv);
-hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream);
+                         int dv, uint64_t record_budget = kSplitRecordBudget, int buffers = 2);
+// With `layout` given, the blocks run one after another on `stream` alone
+// (no second stream); otherwise the default layout and the overlapped
+// schedule.
+hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream,
+                                 const SplitLayout* layout = nullptr);
+
+// The forward entry point that allocates nothing (kda_fwd_chunked_noalloc)
+// takes its workspace from a fixed device array of this many bytes, one per
+// device, which the library holds until the process ends.
+constexpr uint64_t kNoAllocScratchBytes = 256ull << 20;
+// Layout of the two-pass form inside that array (one record buffer, blocks
+// sized to what is left after the fixed parts); false when the shape does
+// not fit.
+bool noalloc_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk, int dv,
+                    SplitLayout* out);
+// Device address of the array on the device of `stream` (resolved once per
+// device).
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 // Backward: sub-chunks per 64-token chunk whose start states each
 // wavefront keeps in global scratch (kda_bwd.hip).

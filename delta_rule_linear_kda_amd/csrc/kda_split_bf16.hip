@@ -1118,20 +1118,21 @@ constexpr uint64_t rec_bytes() {
 }  // namespace
 
 SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk,
-                         int dv) {
+                         int dv, uint64_t record_budget, int buffers) {
   SplitLayout w{};
   const uint64_t rb = dk == 128 ? rec_bytes<128>() : rec_bytes<64>();
   const uint64_t N = (uint64_t)num_seqs, H = (uint64_t)num_heads;
   const uint64_t nch_max = std::max<uint64_t>(1, ((uint64_t)total_tokens + kC - 1) / kC);
   const uint64_t all = H * (nch_max + N);  // records of every chunk (upper bound)
-  const uint64_t budget = kSplitRecordBudget / rb;
+  const uint64_t budget = record_budget / rb;
+  const uint64_t nb = buffers > 1 ? 2 : 1;
   uint64_t bc, recs;
   if (all <= budget) {  // one block
     bc = nch_max;
     recs = all;
-  } else {  // blocks in two record buffers, so that a block's records are
+  } else {  // blocks in (two) record buffers, so that a block's records are
             // built while the previous block's are consumed
-    bc = std::max<uint64_t>(8, budget / 2 / std::max<uint64_t>(1, H * N));
+    bc = std::max<uint64_t>(8, budget / nb / std::max<uint64_t>(1, H * N));
     recs = std::min(all, H * N * bc);
   }
   bc = std::min<uint64_t>(bc, 0x7fffffffull / rb);  // a sequence's block stays under 2 GiB
@@ -1140,7 +1141,7 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
   auto up = [](uint64_t x) { return (x + 255) / 256 * 256; };
   w.bc = (int)bc;
   w.blocks = (int)((nch_max + bc - 1) / bc);
-  w.nbuf = w.blocks > 1 ? 2 : 1;
+  w.nbuf = w.blocks > 1 ? (int)nb : 1;
   uint64_t off = 0;
   for (int i = 0; i < w.nbuf; ++i) {
     w.rec[i] = off;
@@ -1204,10 +1205,12 @@ hipError_t side_stream(hipStream_t stream, SideStream** out) {
 // b % 2; its state pass runs on the side stream once they are done, while
 // block b + 1's records are built.  Block b + 2 reuses buffer b % 2 after
 // block b's state pass; the caller's stream waits for the last state pass.
-hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream) {
+hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream,
+                                 const SplitLayout* layout) {
   const int64_t items = (int64_t)p.num_seqs * p.num_heads;
   if (items == 0) return hipSuccess;
-  const SplitLayout w = split_layout(p.num_seqs, p.total_tokens, p.num_heads, p.dk, p.dv);
+  const SplitLayout w =
+      layout ? *layout : split_layout(p.num_seqs, p.total_tokens, p.num_heads, p.dk, p.dv);
   unsigned char* base = static_cast<unsigned char*>(workspace);
   float* carry = w.blocks > 1 ? reinterpret_cast<float*>(base + w.carry) : nullptr;
   uint16_t* bt = reinterpret_cast<uint16_t*>(base + w.bt);
@@ -1231,7 +1234,8 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   // times over, at most 16 chunks each
   const int64_t want = 8LL * device_cus();
 
-  std::lock_guard<std::mutex> lock(g_side_mu);
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  if (!layout) lock.lock();  // the side stream is shared per device
   SideStream* side = nullptr;
   hipStream_t s2 = stream;  // one block: everything on the caller's stream
   hipError_t e;
@@ -1242,7 +1246,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
                        (long long)p.total_tokens, H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (w.blocks > 1) {
+  if (w.blocks > 1 && !layout) {
     if ((e = side_stream(stream, &side)) != hipSuccess) return e;
     s2 = side->s;
     if ((e = hipEventRecord(side->start, stream)) != hipSuccess) return e;
@@ -1307,6 +1311,56 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   if (side && (e = hipStreamWaitEvent(stream, side->used[(nblocks - 1) % w.nbuf], 0)) !=
                   hipSuccess)
     return e;
+  return hipSuccess;
+}
+
+// ---- workspace of the forward that allocates nothing -------------------------
+// A fixed device array, one per device the library runs on (each device's
+// code object holds its own copy, at its own address); host code never
+// passes the array's name to a kernel, only the address resolved below.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+bool noalloc_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_heads, int dk, int dv,
+                    SplitLayout* out) {
+  auto up = [](uint64_t x) { return (x + 255) / 256 * 256; };
+  const uint64_t N = (uint64_t)num_seqs, H = (uint64_t)num_heads;
+  // the parts whose size does not depend on the block length: record
+  // offsets, carried states, b transposed
+  const uint64_t fixed = up((N + 1) * 4) + up(N * H * (uint64_t)dk * (uint64_t)dv * 4) +
+                         up(H * (uint64_t)std::max<int64_t>(total_tokens, 0) * 2);
+  if (fixed + 256 >= kNoAllocScratchBytes) return false;
+  const SplitLayout w = split_layout(num_seqs, total_tokens, num_heads, dk, dv,
+                                     kNoAllocScratchBytes - fixed - 256, 1);
+  if (w.total > kNoAllocScratchBytes) return false;  // 8 chunks of every pair do not fit
+  *out = w;
+  return true;
+}
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {  // once per device, with that device current
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return hipSuccess;
 }
 

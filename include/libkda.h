@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5u
+#define KDA_ABI_VERSION 6u
 
 #if defined(__GNUC__)
 #define KDA_API __attribute__((visibility("default")))
@@ -77,7 +77,9 @@ typedef enum kda_status {
   KDA_ERR_MISALIGNED = 4,   /* a tensor pointer is not aligned as required   */
   KDA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required    */
   KDA_ERR_ALIAS = 6,        /* an output overlaps an input it must not       */
-  KDA_ERR_HIP = 7           /* the HIP runtime rejected a launch             */
+  KDA_ERR_HIP = 7,          /* the HIP runtime rejected a launch             */
+  KDA_ERR_SCRATCH = 8       /* kda_fwd_chunked_noalloc: the problem needs    */
+                            /* more than its fixed scratch                   */
 } kda_status;
 
 /* Problem description shared by both operations. */
@@ -161,6 +163,29 @@ KDA_API kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, c
                                 float* final_state, int32_t ckpt_interval, float* ckpt_states,
                                 int64_t ckpt_capacity, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* kda_fwd_chunked for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation and arguments without a workspace.  The scratch the
+ * two-pass bf16 form needs (chunk records, carried states, b transposed) is
+ * a fixed device array of 256 MiB held by the library on every device it
+ * runs on until the process ends; nothing is allocated or freed per call,
+ * and no second stream is used (all work on `stream`, blocks of chunks one
+ * after another, sized to fit the array).  Limit: 2 H T + 4 N H dk dv bytes
+ * (b transposed, carried states) plus 8 chunk records of every (sequence,
+ * head) pair (8 x 30,208 bytes at dk = 128) must fit in 256 MiB, else
+ * KDA_ERR_SCRATCH and nothing is enqueued -- e.g. 1 x 1,048,576 tokens x 96
+ * heads fits, 2 x 1,048,576 x 96 does not.  Shapes that take the fused
+ * kernel or fp32 inputs use no scratch at all.  Every call on a device
+ * shares that device's array: calls that overlap in time on one device
+ * (concurrent streams) race and give undefined results; calls ordered on
+ * one stream are safe (each rewrites what it reads).
+ * Errors: as kda_fwd_chunked (no WORKSPACE), plus SCRATCH. */
+KDA_API kda_status kda_fwd_chunked_noalloc(const kda_shape* shape, const void* q, const void* k,
+                                           const void* v, const void* a, const void* b,
+                                           const void* gate, const int32_t* cu_seqlens,
+                                           const float* initial_state, void* o,
+                                           float* final_state, void* stream);
 
 /* Number of state slots kda_fwd_chunked_ckpt fills for HOST-resident
  * cu_seqlens [num_seqs + 1] (same validity rules as the device array).

@@ -12,7 +12,7 @@ import delta_rule_linear_kda_amd as kda
 from delta_rule_linear_kda_amd import Shape
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULLP, SHAPE, DTYPE, MISAL, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+OK, NULLP, SHAPE, DTYPE, MISAL, WS, ALIAS, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 8
 
 
 def header_symbols():
@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert kda.abi_version() == 5
-    for code in range(8):
+    assert kda.abi_version() == 6
+    for code in range(9):
         assert kda.status_str(code).startswith(kda.STATUS[code])
     assert kda.status_str(99) == "unknown kda_status"
 
@@ -422,3 +422,39 @@ def test_bwd_rejects():
     assert bwd(s, dk=GP["dq"] + 64) == ALIAS          # two gradients overlap
     assert bwd(s, ws=GP["ds0"]) == ALIAS              # workspace over an output
     assert bwd(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+def fwd_noalloc(shape, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_fwd_chunked_noalloc(
+        ctypes.byref(shape) if shape is not None else None, args["q"], args["k"], args["v"],
+        args["a"], args["b"], args["gate"], args["cu"], args["s0"], args["o"], args["sf"], None)
+
+
+def test_noalloc_rejects_like_fwd():
+    """The forward without a workspace validates its arguments as
+    kda_fwd_chunked does, before anything is enqueued."""
+    assert fwd_noalloc(None) == NULLP
+    assert fwd_noalloc(good_shape(dk=96)) == SHAPE
+    assert fwd_noalloc(good_shape(in_dtype=7)) == DTYPE
+    for name in ["q", "k", "v", "a", "b", "o", "cu"]:
+        assert fwd_noalloc(good_shape(), **{name: None}) == NULLP, name
+    for name in ["q", "gate", "s0", "o", "sf"]:
+        assert fwd_noalloc(good_shape(), **{name: P[name] + 8}) == MISAL, name
+    assert fwd_noalloc(good_shape(), o=P["q"]) == ALIAS
+    assert fwd_noalloc(good_shape(), sf=P["s0"] + 16) == ALIAS
+    assert fwd_noalloc(good_shape(num_seqs=0, total_tokens=0)) == OK
+
+
+@pytest.mark.parametrize("N,T,H,dk", [(1, 2 << 20, 96, 128), (1, 1 << 20, 120, 128),
+                                      (3, 3_000_000, 40, 128)])
+def test_noalloc_rejects_beyond_its_scratch(N, T, H, dk):
+    """Two-pass shapes whose fixed parts (b transposed: 2 H T bytes; carried
+    states: 4 N H dk dv bytes) plus 8 chunk records per (sequence, head)
+    exceed the 256 MiB array: KDA_ERR_SCRATCH (no GPU touched)."""
+    s = good_shape(num_seqs=N, total_tokens=T, num_heads=H, dk=dk)
+    if not _uses_split(N, H, 128):
+        pytest.skip("fused-kernel shape: no scratch")
+    far = {name: BASE + i * (1 << 39) for i, name in enumerate(P) if name != "ws_bytes"}
+    assert fwd_noalloc(s, **far) == SCRATCH
