@@ -353,6 +353,38 @@ def layer_ops(q, gate, o, stream, reps: int = 5) -> dict:
                              "frac_hbm": bb / ms_b / 1e6 / HBM_PEAK_GBS}}
 
 
+def fused_norm_leg(xin: dict, cu, o, sf, fwd_ms: float, norm_ms: float, stream,
+                   reps: int = 3) -> dict:
+    """The forward with the head-wise RMSNorm -> sigmoid gate applied in its
+    output stage (kda_fwd_chunked_rmsnorm_gate) on the resident long-context
+    tensors, against the forward followed by the separate norm pass."""
+    import torch
+
+    import delta_rule_linear_kda_amd as kda
+
+    T, H, dk = xin["q"].shape
+    dv = xin["v"].shape[2]
+    nw = torch.ones(dv, dtype=torch.float32, device=o.device)
+    ws = torch.empty(max(kda.fwd_workspace_bytes(1, T, H, dk, dv), 1), dtype=torch.uint8,
+                     device=o.device)
+    args = tuple(xin[n] for n in ("q", "k", "v", "a", "b", "gate"))
+
+    def call():
+        kda.fwd_chunked_rmsnorm_gate(*args, cu, None, nw, 1e-6, out=o, final_state=sf,
+                                     workspace=ws, stream=stream)
+
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": ms, "forward_then_norm_pass_ms": fwd_ms + norm_ms,
+            "saved_ms": fwd_ms + norm_ms - ms}
+
+
 def backward(stream, reps: int = 3) -> dict:
     """kda_bwd_chunked on the training-shaped prefill workload (4 x 4096
     tokens, 32 heads, d = 128, bf16 inputs, zero initial state, fp32 dy):
@@ -682,6 +714,8 @@ def main() -> int:
         out["roofline"]["traffic_write"] = tr["write"]
     if not args.no_layer:
         out["layer"] = layer_ops(xin["q"], xin["gate"], o, stream)
+        out["layer"]["fwd_rmsnorm_gate"] = fused_norm_leg(
+            xin, cu, o, sf, fwd_avg, out["layer"]["rmsnorm_gate"]["ms"], stream)
     if not args.no_kcp_share:
         out["cp_share"] = cp_share(xin, stream)
     if not args.no_kcp_share or not args.no_bwd or not args.no_configs:

@@ -7,7 +7,8 @@ import of any entry point raises -- there is no fallback path.
 
 Entry points (same names as the C ABI):
   * ``fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, ...)``,
-    ``fwd_chunked_noalloc(...)`` (same, without a workspace)
+    ``fwd_chunked_noalloc(...)`` (same, without a workspace),
+    ``fwd_chunked_rmsnorm_gate(...)`` (with the head-wise RMSNorm before the gate)
   * ``decode_step(q, k, v, a, b, gate, state, ...)``
   * ``segment_transition(k, v, a, b, cu_seqlens, ...)``,
     ``segment_compose(seg_offsets, trans, ...)``,
@@ -37,7 +38,8 @@ EXPORTS = ("kda_fwd_workspace_bytes", "kda_fwd_chunked", "kda_fwd_chunked_ckpt",
            "kda_fwd_ckpt_count", "kda_segment_transition", "kda_segment_compose",
            "kda_fwd_kcp_workspace_bytes", "kda_fwd_chunked_kcp", "kda_shortconv_swish_l2",
            "kda_rmsnorm_gate", "kda_bwd_workspace_bytes", "kda_bwd_chunked", "kda_decode_step",
-           "kda_status_str", "kda_abi_version", "kda_fwd_chunked_noalloc")
+           "kda_status_str", "kda_abi_version", "kda_fwd_chunked_noalloc",
+           "kda_fwd_chunked_rmsnorm_gate")
 
 
 class KdaError(RuntimeError):
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked.restype = ctypes.c_int
         L.kda_fwd_chunked.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+        L.kda_fwd_chunked_rmsnorm_gate.restype = ctypes.c_int
+        L.kda_fwd_chunked_rmsnorm_gate.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.c_float, vp, vp, vp, ctypes.c_size_t,
+                                                   vp]
         L.kda_fwd_chunked_noalloc.restype = ctypes.c_int
         L.kda_fwd_chunked_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kda_fwd_chunked_ckpt.restype = ctypes.c_int
@@ -216,6 +222,40 @@ def fwd_chunked(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *,
     if rc != 0:
         raise KdaError(rc, "kda_fwd_chunked_ckpt")
     return out, final_state, checkpoints
+
+
+def fwd_chunked_rmsnorm_gate(q, k, v, a, b, gate, cu_seqlens, initial_state=None,
+                             norm_weight=None, norm_eps: float = 1e-6, *, out=None,
+                             final_state=None, workspace=None, stream=None):
+    """``kda_fwd_chunked_rmsnorm_gate``: y = sigmoid(gate) * norm_weight *
+    o / sqrt(mean(o^2) + norm_eps) per (token, head) row of the forward's
+    output o.  Returns (y fp32 [T, H, dv], final_state)."""
+    import torch
+
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.float32, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    ws_bytes = fwd_workspace_bytes(N, T, H, dk, dv, dt)
+    if workspace is not None and ws_bytes:
+        ws, ws_bytes = workspace, workspace.numel()
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    shape = Shape(N, T, H, dk, dv, dt, KDA_F32)
+    rc = lib().kda_fwd_chunked_rmsnorm_gate(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(a), _ptr(b), _ptr(gate), _ptr(cu_seqlens),
+                                            _ptr(initial_state), _ptr(norm_weight),
+                                            float(norm_eps), _ptr(out), _ptr(final_state),
+                                            _ptr(ws), ws_bytes, _stream(q.device, stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_chunked_rmsnorm_gate")
+    return out, final_state
 
 
 def fwd_chunked_noalloc(q, k, v, a, b, gate, cu_seqlens, initial_state=None, *, out=None,

@@ -187,7 +187,8 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
                     const void* a, const void* b, const void* gate, const int32_t* cu_seqlens,
                     const float* initial_state, void* o, float* final_state,
                     int32_t ckpt_interval, float* ckpt, int64_t ckpt_capacity, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool norm = false,
+                    const float* norm_weight = nullptr, float norm_eps = 0.f) {
   kda_status st = check_shape(shape);
   if (st != KDA_OK) return st;
   const kda_shape& s = *shape;
@@ -213,14 +214,49 @@ kda_status fwd_impl(const kda_shape* shape, const void* q, const void* k, const 
       return KDA_ERR_ALIAS;
   }
 
+  if (norm) {  // the norm's weight: read-only, disjoint from the output
+    if (!(norm_eps >= 0.f) || norm_eps > 1.f) return KDA_ERR_BAD_SHAPE;
+    if (!aligned16(norm_weight)) return KDA_ERR_MISALIGNED;
+    const Sizes z = byte_sizes(shape, s.total_tokens);
+    const Span sw(norm_weight, uint64_t(s.dv) * 4);
+    if (overlap(sw, Span(o, z.o)) || overlap(sw, Span(final_state, z.st)) ||
+        overlap(sw, Span(workspace, need)))
+      return KDA_ERR_ALIAS;
+  }
+
   kda::FwdArgs p = fwd_args(s, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state);
   p.ckpt_interval = ckpt_capacity > 0 ? ckpt_interval : 0;
   p.ckpt = ckpt;
   p.ckpt_capacity = ckpt_capacity;
-  const hipError_t e = fwd_uses_split(s)
-                           ? kda::launch_fwd_split_bf16(p, workspace, static_cast<hipStream_t>(stream))
-                           : kda::launch_fwd_chunked(p, static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool split = fwd_uses_split(s);
+  // The head-wise RMSNorm runs in the output stage of the two-pass form's
+  // whole-head state pass; elsewhere the forward writes the ungated output
+  // and one more pass applies norm and gate in place.
+  const bool norm_fused = norm && split && kda::split_whole_head(s.num_seqs, s.num_heads, s.dv);
+  if (norm_fused) {
+    p.norm = true;
+    p.norm_weight = norm_weight;
+    p.norm_eps = norm_eps;
+  } else if (norm) {
+    p.gate = nullptr;
+  }
+  hipError_t e = split ? kda::launch_fwd_split_bf16(p, workspace, hs)
+                       : kda::launch_fwd_chunked(p, hs);
   if (e != hipSuccess) return KDA_ERR_HIP;
+  if (norm && !norm_fused && s.total_tokens > 0) {
+    kda::RmsGateArgs r;
+    r.num_heads = s.num_heads;
+    r.dv = s.dv;
+    r.total_tokens = s.total_tokens;
+    r.in_bf16 = s.in_dtype == KDA_BF16;
+    r.o = static_cast<const float*>(o);
+    r.gate = gate;
+    r.weight = norm_weight;
+    r.eps = norm_eps;
+    r.y = static_cast<float*>(o);
+    if ((e = kda::launch_rmsnorm_gate(r, hs)) != hipSuccess) return KDA_ERR_HIP;
+  }
   return KDA_OK;
 }
 
@@ -251,6 +287,16 @@ kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, const voi
   if (!aligned16(ckpt_states)) return KDA_ERR_MISALIGNED;
   return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state,
                   ckpt_interval, ckpt_states, ckpt_capacity, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_chunked_rmsnorm_gate(const kda_shape* shape, const void* q, const void* k,
+                                        const void* v, const void* a, const void* b,
+                                        const void* gate, const int32_t* cu_seqlens,
+                                        const float* initial_state, const float* norm_weight,
+                                        float norm_eps, void* o, float* final_state,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(shape, q, k, v, a, b, gate, cu_seqlens, initial_state, o, final_state, 0,
+                  nullptr, 0, workspace, workspace_bytes, stream, true, norm_weight, norm_eps);
 }
 
 kda_status kda_fwd_chunked_noalloc(const kda_shape* shape, const void* q, const void* k,

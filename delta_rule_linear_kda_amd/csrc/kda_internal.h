@@ -34,6 +34,12 @@ struct FwdArgs {
   // [N, H, dk, dv + dk]; gate, initial_state, o, final_state and the
   // recorded states are not used.
   float* transition = nullptr;
+  // Head-wise RMSNorm before the gate (kda_fwd_chunked_rmsnorm_gate): only
+  // on the two-pass form's whole-head state pass (split_norm_fused says
+  // when); weight [dv] or null (ones).
+  bool norm = false;
+  const float* norm_weight = nullptr;
+  float norm_eps = 0.f;
 };
 
 // Two-pass bf16 forward (kda_split_bf16.hip): workspace layout.  Chunks are
@@ -55,6 +61,9 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
 // schedule.
 hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream,
                                  const SplitLayout* layout = nullptr);
+// Whether the two-pass form runs whole-head state workgroups for this shape
+// (then the head-wise RMSNorm can be applied in its output stage).
+bool split_whole_head(int64_t num_seqs, int64_t num_heads, int dv);
 
 // The forward entry point that allocates nothing (kda_fwd_chunked_noalloc)
 // takes its workspace from a fixed device array of this many bytes, one per

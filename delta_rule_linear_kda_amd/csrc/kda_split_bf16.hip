@@ -660,7 +660,13 @@ constexpr int kWideItems = 32;   // above this many items, one workgroup per ite
 constexpr int kAhead = 2;        // chunks requested ahead of the one written to LDS
 constexpr int kStepPeriod = 2;   // chunks per iteration of the stream waves' unrolled loop
 
-template <int DK, int SW, int CT, bool CKPT, bool GATE>
+// NORM (whole-head workgroups only): the output row of each (token, head)
+// passes a head-wise RMSNorm with weight norm_w [d_v] and norm_eps before the
+// gate (page "[Paper Review] Kimi K3...", section "Kimi Delta Attention
+// (KDA)", "Full-rank gate" paragraph); the row's sum of squares is reduced
+// over the lanes of each state wave, then over the state waves through LDS
+// across one more barrier per chunk.
+template <int DK, int SW, int CT, bool CKPT, bool GATE, bool NORM = false>
 __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
                             const int32_t* __restrict__ cu_seqlens,
@@ -669,7 +675,8 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
                             const float* __restrict__ s_init, float* __restrict__ carry,
                             float* __restrict__ s_final, float* __restrict__ o, int H,
                             int num_items, int dvt, int nsl, int c_begin, int bc, int ckpt_iv,
-                            float* __restrict__ ckpt, long long ckpt_cap) {
+                            float* __restrict__ ckpt, long long ckpt_cap,
+                            const float* __restrict__ norm_w, float norm_eps) {
   using R = Rec<DK>;
   constexpr int DV = 16 * CT * SW;
   constexpr int NCT = DK / 16, NKB = DK / 32;
@@ -683,8 +690,10 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
   constexpr int VPR = DV * 2 / 16;                  // 16-byte segments per tile row
   constexpr int VSEG = kC * VPR / NTS;              // tile segments per stream thread
   static_assert(dBuf % 16 == 0 && (kC * VPR) % NTS == 0 && VSEG >= 1, "layout");
-  static_assert(2 * dBuf <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf];
+  constexpr int kNormPart = NORM ? 32 * SW * 4 : 0;  // row sums [32 rows][SW]
+  static_assert(2 * dBuf + kNormPart <= 160 * 1024, "LDS budget");
+  static_assert(!NORM || !CKPT, "no recorded states with the norm");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf + kNormPart];
 
   // Block -> (item, slice): the nsl slices of an item sit 8 blocks apart, on
   // the same XCD, so the second slice's record reads hit that XCD's L2.
@@ -810,8 +819,12 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     // waves run the same number of barriers), so every request is issued on
     // every path and each wait covers exactly one set.
     for (int s0 = 0; s0 < cnt; s0 += kStepPeriod) {
-      put(1, I1()); fetch(s0 + 3, I1()); lds_barrier();
-      put(0, I0()); fetch(s0 + 4, I0()); lds_barrier();
+      put(1, I1()); fetch(s0 + 3, I1());
+      if constexpr (NORM) lds_barrier();  // the state waves' row sums
+      lds_barrier();
+      put(0, I0()); fetch(s0 + 4, I0());
+      if constexpr (NORM) lds_barrier();
+      lds_barrier();
     }
     return;
   }
@@ -896,6 +909,10 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       }
     };
     f32x4_t O[CT][2], U[CT][2];
+    static_assert(!NORM || SW == 4, "row sums read as one float4");
+    float nwt[CT];  // the norm's weight at the lane's columns
+#pragma unroll
+    for (int t = 0; t < CT; ++t) nwt[t] = NORM && norm_w ? norm_w[jcol + 16 * t] : 1.f;
     // Chunk c_begin + s from LDS buffer B (gate words in set B).
     auto chunk_step = [&](int s, auto Bc) __attribute__((always_inline)) {
       constexpr int B = decltype(Bc)::value;
@@ -1051,24 +1068,57 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
         }
       }
       // gated output through a buffer resource whose range ends after the
-      // chunk's last valid row
+      // chunk's last valid row; with the norm, every factor but the row's
+      // 1 / sqrt(mean(o^2) + eps) is applied before the workgroup meets to
+      // sum the rows' squares over the state waves
       {
         const int64_t c0 = tok_beg + (int64_t)kC * cc;
         const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
         const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
+        float yv[CT][8];
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float y = O[t][j >> 2][j & 3] * pow2f(254 - esc[t]);
+            O[t][j >> 2][j & 3] = y;  // the unscaled output, for the row sums
+            if constexpr (NORM) y *= nwt[t];
             if constexpr (GATE)
               y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][t][j] >> hsh) << 16)));
-            __builtin_amdgcn_raw_buffer_store_b32(
-                __float_as_uint(y), rs,
-                4 * (vo_lane + 16 * t + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
+            yv[t][j] = y;
           }
+        if constexpr (NORM) {  // the rows' sums of squares over the state waves
+          float* part = reinterpret_cast<float*>(smem + 2 * dBuf);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float ss = 0.f;
+#pragma unroll
+              for (int t = 0; t < CT; ++t) ss += O[t][rt][jj] * O[t][rt][jj];
+              ss = row_sum16(ss);  // over the wave's 16 columns of each tile
+              if (li == 0) part[(16 * rt + 4 * g + jj) * SW + sw] = ss;
+            }
+          lds_barrier();
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float4 pr = *reinterpret_cast<const float4*>(part + (16 * rt + 4 * g + jj) * SW);
+              const float rsq = rsqrtf((pr.x + pr.y + pr.z + pr.w) * (1.f / DV) + norm_eps);
+#pragma unroll
+              for (int t = 0; t < CT; ++t) yv[t][4 * rt + jj] *= rsq;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(yv[t][j]), rs,
+                4 * (vo_lane + 16 * t + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
       }
       lds_barrier();
     };
@@ -1084,6 +1134,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       } else {
         gate_fetch(s + 1, std::integral_constant<int, 1>());
         idle_stores();
+        if constexpr (NORM) lds_barrier();
         lds_barrier();
       }
       if (s + 1 < cnt) {
@@ -1091,6 +1142,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       } else {
         gate_fetch(s + 2, std::integral_constant<int, 0>());
         idle_stores();
+        if constexpr (NORM) lds_barrier();
         lds_barrier();
       }
     }
@@ -1201,6 +1253,10 @@ hipError_t side_stream(hipStream_t stream, SideStream** out) {
 
 }  // namespace
 
+bool split_whole_head(int64_t num_seqs, int64_t num_heads, int dv) {
+  return dv == 128 && num_seqs * num_heads > kWideItems;
+}
+
 // Block b's plan and record pass run on the caller's stream into buffer
 // b % 2; its state pass runs on the side stream once they are done, while
 // block b + 1's records are built.  Block b + 2 reuses buffer b % 2 after
@@ -1219,7 +1275,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   // (128 columns) when there are enough items to fill the GPU with both
   // passes; with few items the state chain is the whole cost, and 64-column
   // slices (one tile per state wave, two workgroups per item) shorten it.
-  const bool wide = p.dv == 128 && items > kWideItems;
+  const bool wide = split_whole_head(p.num_seqs, p.num_heads, p.dv);
   const int nsl = wide ? 1 : p.dv / 64;
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;
@@ -1285,11 +1341,18 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
                          s2, (const uint16_t*)p.v, (const uint16_t*)p.gate, p.cu_seqlens, slot,
                          (const unsigned char*)rec, p.initial_state, carry, p.final_state,
                          (float*)p.o, H, (int)items, p.dv, nsl, c_begin, nb, p.ckpt_interval,
-                         p.ckpt, (long long)p.ckpt_capacity);
+                         p.ckpt, (long long)p.ckpt_capacity, p.norm_weight, p.norm_eps);
     };
     const bool gt = p.gate != nullptr;
     auto pick = [&](auto dkc, auto ctc) {
       constexpr int K = decltype(dkc)::value, T = decltype(ctc)::value;
+      if constexpr (T == 2) {
+        if (p.norm) {  // whole-head workgroups only (the caller checks)
+          gt ? launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, false, true, true>)
+             : launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, false, false, true>);
+          return;
+        }
+      }
       if (ck)
         gt ? launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, true, true>)
            : launch_state(chunk_state_bf16_kernel<K, kStateWaves, T, true, false>);

@@ -164,6 +164,33 @@ KDA_API kda_status kda_fwd_chunked_ckpt(const kda_shape* shape, const void* q, c
                                 int64_t ckpt_capacity, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* kda_fwd_chunked with the head-wise RMSNorm before the output gate (page
+ * "[Paper Review] Kimi K3...", section "Kimi Delta Attention (KDA)",
+ * "Full-rank gate" paragraph; weight and epsilon are not printed there):
+ *     o_t  = S_t^T qh_t                      (the recurrence above)
+ *     y_t  = sigmoid(gate_t) * norm_weight * o_t / sqrt(mean_c(o_t^2) + norm_eps)
+ * the mean over the head's dv channels, for every (token, head) row.
+ *   norm_weight  [dv] fp32 shared by the heads, or NULL (ones); 16-byte
+ *                aligned; not overlapping o, final_state or the workspace
+ *   norm_eps     in [0, 1]
+ *   o            [T, H, dv] fp32 receives y
+ * Everything else (workspace included) as for kda_fwd_chunked.  With bf16
+ * inputs and enough (sequence, head) pairs for the two-pass form's
+ * whole-head state pass (more than 32 pairs at dv = 128 and fewer pairs
+ * than compute units, e.g. 1 x 1M tokens x 96 heads) the norm is applied in
+ * the forward's output stage (no extra pass over o); otherwise the forward
+ * writes the ungated output and one more pass applies norm and gate in
+ * place.  Same results either way up to rounding.
+ * Errors: as kda_fwd_chunked; BAD_SHAPE also for norm_eps outside [0, 1]. */
+KDA_API kda_status kda_fwd_chunked_rmsnorm_gate(const kda_shape* shape, const void* q,
+                                                const void* k, const void* v, const void* a,
+                                                const void* b, const void* gate,
+                                                const int32_t* cu_seqlens,
+                                                const float* initial_state,
+                                                const float* norm_weight, float norm_eps,
+                                                void* o, float* final_state, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
 /* kda_fwd_chunked for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same operation and arguments without a workspace.  The scratch the

@@ -458,3 +458,25 @@ def test_noalloc_rejects_beyond_its_scratch(N, T, H, dk):
         pytest.skip("fused-kernel shape: no scratch")
     far = {name: BASE + i * (1 << 39) for i, name in enumerate(P) if name != "ws_bytes"}
     assert fwd_noalloc(s, **far) == SCRATCH
+
+
+def fwd_norm(shape, weight=BASE + 12 * (1 << 36), eps=1e-5, **over):
+    args = dict(P)
+    args.update(over)
+    return kda.lib().kda_fwd_chunked_rmsnorm_gate(
+        ctypes.byref(shape) if shape is not None else None, args["q"], args["k"], args["v"],
+        args["a"], args["b"], args["gate"], args["cu"], args["s0"], weight, ctypes.c_float(eps),
+        args["o"], args["sf"], args["ws"], args["ws_bytes"], None)
+
+
+def test_fwd_rmsnorm_gate_rejects():
+    assert fwd_norm(None) == NULLP
+    assert fwd_norm(good_shape(dk=96)) == SHAPE
+    assert fwd_norm(good_shape(), eps=-1.0) == SHAPE
+    assert fwd_norm(good_shape(), eps=float("nan")) == SHAPE
+    assert fwd_norm(good_shape(), eps=2.0) == SHAPE
+    assert fwd_norm(good_shape(), weight=BASE + 12 * (1 << 36) + 4) == MISAL
+    assert fwd_norm(good_shape(), weight=P["o"]) == ALIAS          # weight inside the output
+    assert fwd_norm(good_shape(), o=P["q"]) == ALIAS
+    assert fwd_norm(good_shape(), ws=None) == WS
+    assert fwd_norm(good_shape(num_seqs=0, total_tokens=0)) == OK

@@ -194,3 +194,124 @@ def test_kda_layer_chain(base):
     tol = _tol(W0.dtype)
     print(f"    err o={eo:.3e} y={ey:.3e} state={es:.3e} (tol {tol:.0e})", flush=True)
     assert eo <= tol and es <= tol and ey <= tol
+
+
+# --- the forward with the head-wise RMSNorm before the gate ------------------
+# path -> (base workload, heads, lens): the two-pass form's whole-head state
+# pass applies the norm in its output stage (more than 32 pairs at dv = 128,
+# fewer than the compute units); the other shapes run the forward, then the
+# norm pass in place.
+NORM_PATHS = {
+    "fused_in_state_pass": (1, 40, [300, 17, 0, 129]),
+    "state_pass_no_gate": (1, 40, [300, 17, 0, 129]),
+    "fused_kernel": (1, 32, [256, 256, 130, 256]),
+    "sliced_state_pass": (1, 3, [300, 17, 0, 129]),
+    "fp32": (0, 2, [200, 0, 77]),
+}
+
+
+def norm_err(y, y_ref, o_ref):
+    """Error of a normed output against the oracle chain, per row scaled by
+    the row's conditioning: the norm divides each (token, head) row by its own
+    RMS, so the forward's rounding (bounded against RMS(o)) reaches a row of y
+    amplified by kappa = RMS(o) / rms(row).  Returns (max over elements of
+    |y - y_ref| / (RMS(y_ref) max(1, kappa_row)), plain max |y - y_ref| /
+    RMS(y_ref), fraction of rows with kappa > 4)."""
+    y = np.asarray(y, dtype=np.float64)
+    d = np.abs(y - y_ref)
+    rms_y = np.sqrt(np.mean(y_ref ** 2))
+    rms_o = np.sqrt(np.mean(o_ref ** 2))
+    row = np.sqrt(np.mean(o_ref ** 2, axis=-1, keepdims=True))
+    kappa = np.maximum(1.0, rms_o / np.maximum(row, 1e-300))
+    return (float(np.max(d / (rms_y * kappa))), float(np.max(d) / rms_y),
+            float(np.mean(kappa > 4.0)))
+
+
+@pytest.mark.parametrize("path", list(NORM_PATHS))
+@pytest.mark.parametrize("with_w", [True, False])
+def test_fwd_rmsnorm_gate(path, with_w):
+    """kda_fwd_chunked_rmsnorm_gate against the oracles chained: the forward
+    without gate, then RMSNorm (weight, eps) and the sigmoid gate."""
+    _require_gpu()
+    base, H, lens = NORM_PATHS[path]
+    W = synth.WORKLOADS[base]
+    w = kc.custom_workload(W, heads=H, s0_std=0.02,
+                           dk=128 if base else 64, dv=128 if base else 64)
+    gate = path != "state_pass_no_gate"
+    print(f"[case] fwd rmsnorm gate path={path} weight={with_w} H={H} lens={lens}", flush=True)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = kc.host_inputs(w, T)
+    s0 = kc.host_state(w, len(lens))
+    nw = (synth.host_normal(synth.key(0, "norm_w"), 1, w.dv, dtype=synth.F32, mean=1.0,
+                            std=0.3)[0] if with_w else None)
+    eps = 1e-5
+    dev = {n: kc.to_torch(x[n]) for n in x}
+    y, sf = kda.fwd_chunked_rmsnorm_gate(
+        *(dev[n] if (n != "gate" or gate) else None for n in ("q", "k", "v", "a", "b", "gate")),
+        torch.from_numpy(cu.astype(np.int32)).cuda(), torch.from_numpy(s0).cuda(),
+        torch.from_numpy(nw).cuda() if nw is not None else None, eps)
+    torch.cuda.synchronize()
+    xr = {n: kc.f64(x[n]) for n in x}
+    o_ref, sf_ref = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["a"], xr["b"], None, cu,
+                               s0.astype(np.float64))
+    y_ref = layer.rmsnorm_gate(o_ref, xr["gate"] if gate else None, nw, eps)
+    ey, plain, frac = norm_err(y.cpu().numpy(), y_ref, o_ref)
+    es = kc.rel_err(sf.cpu().numpy(), sf_ref)
+    tol = _tol(w.dtype)
+    print(f"    err y={ey:.3e} (unscaled {plain:.3e}, rows with kappa > 4: {frac:.2%}) "
+          f"state={es:.3e} (tol {tol:.0e})", flush=True)
+    assert np.all(np.isfinite(y.cpu().numpy()))
+    assert ey <= tol and es <= tol
+    # the norm in the forward's output stage equals the forward followed by
+    # the separate norm pass (the same fp32 o; only the order of the row sums
+    # differs)
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    o2, sf2 = kda.fwd_chunked(*(dev[n] for n in ("q", "k", "v", "a", "b")), None, cu_d,
+                              torch.from_numpy(s0).cuda())
+    y2 = kda.rmsnorm_gate(o2, dev["gate"] if gate else None,
+                          torch.from_numpy(nw).cuda() if nw is not None else None, eps)
+    torch.cuda.synchronize()
+    e2 = kc.rel_err(y.cpu().numpy(), y2.cpu().numpy())
+    print(f"    against the forward then the norm pass: {e2:.3e}", flush=True)
+    assert e2 <= 1e-5 and torch.equal(sf, sf2)
+
+
+def test_fwd_rmsnorm_gate_many_blocks():
+    """The norm in the output stage of the two-pass form over several blocks
+    (1 x 60,000 tokens x 96 heads): every row of 12 heads against the oracle
+    chain, the oracle streamed."""
+    _require_gpu()
+    w = kc.custom_workload(synth.WORKLOADS[3], s0_std=0.02)
+    T, H = 60_000, w.heads
+    heads = [0, 7, 19, 31, 40, 52, 63, 71, 80, 88, 94, 95]
+    print(f"[case] fwd rmsnorm gate many blocks T={T} H={H}", flush=True)
+    dev = {n: synth.device_tokens(w, n, T) for n in synth.TOKEN_TENSORS}
+    s0 = synth.device_state(w, 1)
+    nw = synth.host_normal(synth.key(0, "norm_w"), 1, w.dv, dtype=synth.F32, mean=1.0,
+                           std=0.3)[0]
+    eps = 1e-5
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    y, sf = kda.fwd_chunked_rmsnorm_gate(*(dev[n] for n in ("q", "k", "v", "a", "b", "gate")),
+                                         cu, s0, torch.from_numpy(nw).cuda(), eps)
+    torch.cuda.synchronize()
+    names = ("q", "k", "v", "a", "b", "gate")
+    got, refs, o_refs = [], [], []
+
+    def fetch(t0, t1):
+        return {nm: kc.device_rows_f64(dev[nm], t0, t1, heads) for nm in names}
+
+    def on_slice(t0, t1, o_ref):
+        g = kc.device_rows_f64(dev["gate"], t0, t1, heads)
+        got.append(y[t0:t1, heads].cpu().numpy())
+        refs.append(layer.rmsnorm_gate(o_ref, g, nw, eps))
+        o_refs.append(o_ref)
+
+    s_ref = kc.oracle_stream(fetch, T, s0[0, heads].cpu().numpy()[None].astype(np.float64),
+                             gate=False, on_slice=on_slice)
+    ey, plain, frac = norm_err(np.concatenate(got), np.concatenate(refs),
+                               np.concatenate(o_refs))
+    es = kc.rel_err(sf[0, heads].cpu().numpy(), s_ref[0])
+    print(f"    err y={ey:.3e} (unscaled {plain:.3e}, rows with kappa > 4: {frac:.2%}) "
+          f"state={es:.3e}", flush=True)
+    assert ey <= kc.TOL_BF16 and es <= kc.TOL_BF16
