@@ -663,9 +663,8 @@ constexpr int kStepPeriod = 2;   // chunks per iteration of the stream waves' un
 // NORM (whole-head workgroups only): the output row of each (token, head)
 // passes a head-wise RMSNorm with weight norm_w [d_v] and norm_eps before the
 // gate (page "[Paper Review] Kimi K3...", section "Kimi Delta Attention
-// (KDA)", "Full-rank gate" paragraph); the row's sum of squares is reduced
-// over the lanes of each state wave, then over the state waves through LDS
-// across one more barrier per chunk.
+// (KDA)", "Full-rank gate" paragraph), applied by the stream waves, which hold
+// whole rows in the output stage.
 template <int DK, int SW, int CT, bool CKPT, bool GATE, bool NORM = false>
 __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     chunk_state_bf16_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ gate,
@@ -690,10 +689,21 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
   constexpr int VPR = DV * 2 / 16;                  // 16-byte segments per tile row
   constexpr int VSEG = kC * VPR / NTS;              // tile segments per stream thread
   static_assert(dBuf % 16 == 0 && (kC * VPR) % NTS == 0 && VSEG >= 1, "layout");
-  constexpr int kNormPart = NORM ? 32 * SW * 4 : 0;  // row sums [32 rows][SW]
-  static_assert(2 * dBuf + kNormPart <= 160 * 1024, "LDS budget");
+  // With the norm (whole-head workgroups), the stream waves also run the
+  // output stage: the state waves leave each chunk's unscaled output rows in
+  // one half of an fp32 buffer [2][32][OP]; in the next step the stream
+  // waves, which hold whole rows there, apply the head-wise RMSNorm and
+  // sigmoid(gate) and store them with 16-byte accesses.  (Without the norm
+  // the state waves store their own outputs: handing that stage over as well
+  // measured 1.5 ms slower on the 1M-token forward.)
+  constexpr bool OS = CT == 2 && NORM;
+  static_assert(!NORM || OS, "the norm needs whole-head workgroups");
   static_assert(!NORM || !CKPT, "no recorded states with the norm");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf + kNormPart];
+  constexpr int OP = DV + 4;  // fp32 row pitch of the output buffer
+  constexpr int dO = 2 * dBuf;
+  constexpr int kOutBytes = OS ? 2 * kC * OP * 4 : 0;
+  static_assert(2 * dBuf + kOutBytes <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dBuf + kOutBytes];
 
   // Block -> (item, slice): the nsl slices of an item sit 8 blocks apart, on
   // the same XCD, so the second slice's record reads hit that XCD's L2.
@@ -810,22 +820,91 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
             u32x2_t{0u, 0u};
     }
     static_assert(NTS * 8 == 2 * 4 * 32 * 8, "8-byte zero pieces: eight per thread");
+    // Output stage (OS): thread st owns row ro, columns oc .. oc + 15 of a
+    // chunk's output; gate words of chunk j arrive one step ahead in set j & 1.
+    const int ro = st >> 3, oc = 16 * (st & 7);
+    u32x4_t Rg[2][2] = {};
+    float nwo[16];  // the norm's weight at those columns
+#pragma unroll
+    for (int i = 0; i < 16; ++i) nwo[i] = NORM && norm_w ? norm_w[oc + i] : 1.f;
+    auto gate_fetch_o = [&](int j, auto Kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(Kc)::value;
+      if constexpr (OS && GATE) {
+        const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + min(j, cnt - 1));
+        const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
+        const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(gate + (c0 * H + h) * dvt + col0), 0,
+            (uint32_t)nr * (uint32_t)(H * dvt) * 2u, kBufferRsrcFlags);
+        const uint32_t off = 2u * (uint32_t)(ro * H * dvt + oc);
+        Rg[K][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
+        Rg[K][1] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(gr, off + 16, 0, 0));
+      }
+    };
+    // Chunk c_begin + j's rows from output half j & 1 (every step issues the
+    // same stores; an empty range when there is no such chunk).
+    auto out_stage = [&](int j, auto Kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(Kc)::value;
+      if constexpr (OS) {
+        const bool live = j >= 0 && j < cnt;
+        const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + max(min(j, cnt - 1), 0));
+        const int nr = live ? (int)(tok_end - c0 < kC ? tok_end - c0 : kC) : 0;
+        const float* ob = reinterpret_cast<const float*>(smem + dO) + K * kC * OP + ro * OP + oc;
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 x = *reinterpret_cast<const float4*>(ob + 4 * i);
+          y[4 * i] = x.x; y[4 * i + 1] = x.y; y[4 * i + 2] = x.z; y[4 * i + 3] = x.w;
+        }
+        if constexpr (NORM) {  // the row's mean square over its 8 threads
+          float ss = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ss += y[i] * y[i];
+          ss += __shfl_xor(ss, 1, 64);
+          ss += __shfl_xor(ss, 2, 64);
+          ss += __shfl_xor(ss, 4, 64);
+          const float rsq = rsqrtf(ss * (1.f / DV) + norm_eps);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y[i] *= rsq * nwo[i];
+        }
+        if constexpr (GATE) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t w = Rg[K][i / 8][(i % 8) / 2];
+            const float gv = (i & 1) ? bf16hi(w) : bf16lo(w);
+            y[i] *= rcpf_fast(1.f + exp2f_fast(-kLog2e * gv));
+          }
+        }
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
+        const uint32_t off = 4u * (uint32_t)(ro * H * dvt + oc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, f32x4_t{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}),
+              rs, off + 16u * i, 0, 0);
+      }
+    };
     put(0, I0());
     fetch(2, I0());
+    gate_fetch_o(0, I0());
     lds_barrier();
     // Step s: chunk s + 1 (register set (s + 1) % 2) into buffer (s + 1) & 1,
-    // then chunk s + 3 requested into that set.  Two steps per iteration make
-    // both indices static; a step past the last chunk repeats it (the state
-    // waves run the same number of barriers), so every request is issued on
-    // every path and each wait covers exactly one set.
+    // then chunk s + 3 requested into that set; with the output stage, chunk
+    // s - 1's rows out and chunk s + 1's gate words requested.  Two steps per
+    // iteration make both indices static; a step past the last chunk repeats
+    // it (the state waves run the same number of barriers), so every request
+    // is issued on every path and each wait covers exactly one set.
     for (int s0 = 0; s0 < cnt; s0 += kStepPeriod) {
       put(1, I1()); fetch(s0 + 3, I1());
-      if constexpr (NORM) lds_barrier();  // the state waves' row sums
+      out_stage(s0 - 1, I1()); gate_fetch_o(s0 + 1, I1());
       lds_barrier();
       put(0, I0()); fetch(s0 + 4, I0());
-      if constexpr (NORM) lds_barrier();
+      out_stage(s0, I0()); gate_fetch_o(s0 + 2, I0());
       lds_barrier();
     }
+    // the last step's rows (an empty range when that step was idle)
+    out_stage(((cnt + kStepPeriod - 1) / kStepPeriod) * kStepPeriod - 1, I1());
     return;
   }
 
@@ -885,7 +964,7 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     // K; rows past the sequence's end read as zero (their range is empty).
     auto gate_fetch = [&](int s, auto Kc) __attribute__((always_inline)) {
       constexpr int K = decltype(Kc)::value;
-      if constexpr (GATE) {
+      if constexpr (GATE && !OS) {
         const int64_t c0 = tok_beg + (int64_t)kC * (c_begin + min(s, cnt - 1));
         const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
         const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
@@ -902,17 +981,13 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
     // nothing is written, but the count of memory operations per step stays
     // the same on every path.
     auto idle_stores = [&]() __attribute__((always_inline)) {
-      if constexpr (GATE) {
+      if constexpr (GATE && !OS) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, kBufferRsrcFlags);
 #pragma unroll
         for (int j = 0; j < 8 * CT; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, rs, 4 * j, 0, 0);
       }
     };
     f32x4_t O[CT][2], U[CT][2];
-    static_assert(!NORM || SW == 4, "row sums read as one float4");
-    float nwt[CT];  // the norm's weight at the lane's columns
-#pragma unroll
-    for (int t = 0; t < CT; ++t) nwt[t] = NORM && norm_w ? norm_w[jcol + 16 * t] : 1.f;
     // Chunk c_begin + s from LDS buffer B (gate words in set B).
     auto chunk_step = [&](int s, auto Bc) __attribute__((always_inline)) {
       constexpr int B = decltype(Bc)::value;
@@ -1067,58 +1142,37 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
           }
         }
       }
-      // gated output through a buffer resource whose range ends after the
-      // chunk's last valid row; with the norm, every factor but the row's
-      // 1 / sqrt(mean(o^2) + eps) is applied before the workgroup meets to
-      // sum the rows' squares over the state waves
-      {
+      if constexpr (OS) {
+        // the unscaled output rows into half s & 1 of the output buffer (the
+        // stream waves gate and store them in the next step)
+        float* ob = reinterpret_cast<float*>(smem + dO) + (s & 1) * kC * OP;
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          const float isc = pow2f(254 - esc[t]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            ob[(16 * (j >> 2) + 4 * g + (j & 3)) * OP + 16 * (CT * sw + t) + li] =
+                O[t][j >> 2][j & 3] * isc;
+        }
+      } else {
+        // gated output through a buffer resource whose range ends after the
+        // chunk's last valid row
         const int64_t c0 = tok_beg + (int64_t)kC * cc;
         const int nr = (int)(tok_end - c0 < kC ? tok_end - c0 : kC);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             o + (c0 * H + h) * dvt + col0, 0, nr * H * dvt * 4, kBufferRsrcFlags);
         const uint32_t vo_lane = (4 * g) * H * dvt + jcol;
-        float yv[CT][8];
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float y = O[t][j >> 2][j & 3] * pow2f(254 - esc[t]);
-            O[t][j >> 2][j & 3] = y;  // the unscaled output, for the row sums
-            if constexpr (NORM) y *= nwt[t];
             if constexpr (GATE)
               y *= rcpf_fast(1.f + exp2f_fast(-kLog2e * __uint_as_float((gw[B][t][j] >> hsh) << 16)));
-            yv[t][j] = y;
-          }
-        if constexpr (NORM) {  // the rows' sums of squares over the state waves
-          float* part = reinterpret_cast<float*>(smem + 2 * dBuf);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float ss = 0.f;
-#pragma unroll
-              for (int t = 0; t < CT; ++t) ss += O[t][rt][jj] * O[t][rt][jj];
-              ss = row_sum16(ss);  // over the wave's 16 columns of each tile
-              if (li == 0) part[(16 * rt + 4 * g + jj) * SW + sw] = ss;
-            }
-          lds_barrier();
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float4 pr = *reinterpret_cast<const float4*>(part + (16 * rt + 4 * g + jj) * SW);
-              const float rsq = rsqrtf((pr.x + pr.y + pr.z + pr.w) * (1.f / DV) + norm_eps);
-#pragma unroll
-              for (int t = 0; t < CT; ++t) yv[t][4 * rt + jj] *= rsq;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < CT; ++t)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
             __builtin_amdgcn_raw_buffer_store_b32(
-                __float_as_uint(yv[t][j]), rs,
+                __float_as_uint(y), rs,
                 4 * (vo_lane + 16 * t + (uint32_t)((16 * (j >> 2) + (j & 3)) * H * dvt)), 0, 0);
+          }
       }
       lds_barrier();
     };
@@ -1134,7 +1188,6 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       } else {
         gate_fetch(s + 1, std::integral_constant<int, 1>());
         idle_stores();
-        if constexpr (NORM) lds_barrier();
         lds_barrier();
       }
       if (s + 1 < cnt) {
@@ -1142,7 +1195,6 @@ __global__ void __launch_bounds__(64 * (SW + kStreamWaves))
       } else {
         gate_fetch(s + 2, std::integral_constant<int, 0>());
         idle_stores();
-        if constexpr (NORM) lds_barrier();
         lds_barrier();
       }
     }
