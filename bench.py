@@ -55,7 +55,7 @@ CHUNK = 32                   # chunk length of the bf16 forward kernels
 # The bf16 forward transposes b, then runs in blocks of chunks, each block a
 # plan kernel, the chunk-record pass and the state pass; the roofline is taken
 # over the whole forward call (every launch of these kernels).
-FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, 4, 2, false, true>",
+FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, 4, 2, false, true, false>",
                "split_plan_kernel", "b_transpose_kernel")
 FWD_KERNEL = "split forward: " + " + ".join(FWD_KERNELS[:2]) + " (per block of chunks)"
 FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_split_bf16.hip")
@@ -515,6 +515,62 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def util_summary(pmc_csv: str) -> str:
+    """Per-kernel utilization from one rocprofv3 --pmc run of GRBM_GUI_ACTIVE,
+    SQ_ACTIVE_INST_VALU, SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_LDS,
+    SQ_LDS_BANK_CONFLICT, SQ_INSTS_VALU, SQ_INSTS_MFMA (csv output), as
+    rocprofv3 defines the derived metrics, GRBM_GUI_ACTIVE taken per XCD (the
+    csv sums its 8 instances): VALUBusy = SQ_ACTIVE_INST_VALU / CUs /
+    GRBM_GUI_ACTIVE, MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
+    GRBM_GUI_ACTIVE), LDSinst and LDSconf likewise per CU."""
+    import collections
+    import csv
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(float)
+    seen = collections.defaultdict(set)
+    with open(pmc_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"].replace("void ", "").replace("kda::(anonymous namespace)::", "")
+            k = k.replace("(anonymous namespace)::", "").split("(")[0]
+            agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            if r["Dispatch_Id"] not in seen[k]:
+                seen[k].add(r["Dispatch_Id"])
+                dur[k] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    cu, simd = 256, 1024
+    lines = []
+    for k, c in agg.items():
+        g = c["GRBM_GUI_ACTIVE"] / 8
+        if g == 0:
+            continue
+        n = len(seen[k])
+        lines.append(
+            f"{k[:60]:<60} n={n:4d} dur={dur[k] * 1e3 / n:8.3f}ms "
+            f"clk={g / n / (dur[k] / n) / 1e9:5.2f}GHz "
+            f"VALUBusy={100 * c['SQ_ACTIVE_INST_VALU'] / cu / g:5.1f}% "
+            f"MfmaUtil={100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * simd):5.1f}% "
+            f"LDSinst={100 * c['SQ_ACTIVE_INST_LDS'] / cu / g:5.1f}% "
+            f"LDSconf={100 * c['SQ_LDS_BANK_CONFLICT'] / cu / g:5.1f}% "
+            f"VALUinsts/MFMA={c['SQ_INSTS_VALU'] / max(1, c['SQ_INSTS_MFMA']):7.1f}")
+    return "\n".join(lines) + "\n"
+
+
+def kernel_stats(stats_csv: str) -> str:
+    """The kernel table of a rocprofv3 --kernel-trace --stats csv: calls,
+    average / min / max duration (us), share of the total."""
+    import csv
+
+    lines = [f"{'kernel':<78} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    with open(stats_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            k = r["Name"].replace("void ", "").replace("kda::(anonymous namespace)::", "")
+            k = k.replace("(anonymous namespace)::", "").split("(")[0]
+            lines.append(f"{k[:78]:<78} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                         f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+                         f"{float(r['Percentage']):6.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def trace_spans(trace_csv: str) -> str:
     """Per forward call: first start to last end of its kernels' dispatches
     (calls are separated by the decode launches that follow each forward)."""
@@ -566,10 +622,18 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--trace-spans", metavar="TRACE_CSV")
+    ap.add_argument("--util-summary", metavar="PMC_CSV")
+    ap.add_argument("--kernel-stats", metavar="STATS_CSV")
     args = ap.parse_args()
 
     if args.trace_spans:
         sys.stdout.write(trace_spans(args.trace_spans))
+        return 0
+    if args.util_summary:
+        sys.stdout.write(util_summary(args.util_summary))
+        return 0
+    if args.kernel_stats:
+        sys.stdout.write(kernel_stats(args.kernel_stats))
         return 0
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(*args.pmc_summary))
