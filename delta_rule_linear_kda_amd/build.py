@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_chunk_bf16.hip",
-           "kda_split_bf16.hip", "kda_segments.hip", "kda_layer.hip", "kda_bwd.hip"]
+           "kda_split_bf16.hip", "kda_segments.hip", "kda_layer.hip", "kda_bwd.hip",
+           "kda_bwd_chunk.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 FLAGS = [

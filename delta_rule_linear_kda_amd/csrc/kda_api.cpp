@@ -668,21 +668,40 @@ kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, const void* 
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int32_t kBwdCkpt = 64;  // tokens between the forward states the backward restarts from
-constexpr int32_t kBwdSlice = 8;  // state columns per backward wavefront
+constexpr int32_t kBwdCkpt = 64;  // tokens between the forward states the token form restarts from
+constexpr int32_t kBwdSlice = 8;  // state columns per token-form wavefront
 
+// bf16 inputs run the chunked form (kda_bwd_chunk.hip): the forward's states
+// every kda::bwd_chunk_len() tokens, its ungated output, the adjoint state at
+// each chunk's end and the chunk offsets.  fp32 inputs run the token form
+// (kda_bwd.hip): states every 64 tokens, the ungated output, per-slice
+// partial sums and sub-chunk start states.
 struct BwdLayout {
-  uint64_t ckpt, o_raw, p_dqh, p_dkh, p_dal, p_dbeta, sub, total;
+  bool chunked;
+  uint64_t ckpt, o_raw, p_dqh, p_dkh, p_dal, p_dbeta, sub, dse, cbase, kbase, total;
   int64_t slots;
 };
 
 BwdLayout bwd_layout(const kda_shape& s) {
-  BwdLayout w;
+  BwdLayout w{};
   const uint64_t th = uint64_t(s.total_tokens) * uint64_t(s.num_heads);
+  const uint64_t st = uint64_t(s.num_heads) * s.dk * s.dv * 4;  // one state per head
+  w.chunked = s.in_dtype == KDA_BF16;
+  w.ckpt = 0;
+  if (w.chunked) {
+    const int64_t cl = kda::bwd_chunk_len();
+    w.slots = s.total_tokens / cl;  // >= sum over sequences of floor(L_n / cl)
+    w.o_raw = round_up(uint64_t(w.slots) * st, 256);
+    w.dse = w.o_raw + round_up(th * s.dv * 4, 256);
+    const uint64_t chunks = uint64_t(s.total_tokens / cl + s.num_seqs);  // >= sum of ceil(L_n / cl)
+    w.cbase = w.dse + round_up(chunks * st, 256);
+    w.kbase = w.cbase + round_up(uint64_t(s.num_seqs + 1) * 4, 256);
+    w.total = w.kbase + round_up(uint64_t(s.num_seqs + 1) * 4, 256);
+    return w;
+  }
   const uint64_t nsl = uint64_t(s.dv / kBwdSlice);
   w.slots = s.total_tokens / kBwdCkpt;  // >= sum over sequences of floor(L_n / 64)
-  w.ckpt = 0;
-  w.o_raw = round_up(uint64_t(w.slots) * uint64_t(s.num_heads) * s.dk * s.dv * 4, 256);
+  w.o_raw = round_up(uint64_t(w.slots) * st, 256);
   w.p_dqh = w.o_raw + round_up(th * s.dv * 4, 256);
   w.p_dkh = w.p_dqh + round_up(nsl * th * s.dk * 4, 256);
   w.p_dal = w.p_dkh + round_up(nsl * th * s.dk * 4, 256);
@@ -753,14 +772,40 @@ kda_status kda_bwd_chunked(const kda_shape* shape, const void* q, const void* k,
   }
   unsigned char* base = static_cast<unsigned char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // 1. the forward with states recorded every 64 tokens and the ungated output
+  // 1. the forward with its states recorded and the ungated output
   kda::FwdArgs f = fwd_args(s, q, k, v, a, b, nullptr, cu_seqlens, initial_state,
                             base + w.o_raw, nullptr);
-  f.ckpt_interval = kBwdCkpt;
+  f.ckpt_interval = w.chunked ? kda::bwd_chunk_len() : kBwdCkpt;
   f.ckpt = reinterpret_cast<float*>(base + w.ckpt);
   f.ckpt_capacity = w.slots;
+  if (w.chunked) {
+    // 2. the adjoint chain over chunks (beside the forward), then every
+    // chunk's gradients
+    kda::BwdChunkArgs c;
+    c.num_seqs = s.num_seqs;
+    c.num_heads = s.num_heads;
+    c.dk = s.dk;
+    c.dv = s.dv;
+    c.total_tokens = s.total_tokens;
+    c.in_bf16 = true;
+    c.q = q; c.k = k; c.v = v; c.a = a; c.b = b; c.gate = gate;
+    c.cu_seqlens = cu_seqlens;
+    c.initial_state = initial_state;
+    c.dy = dy;
+    c.d_final_state = d_final_state;
+    c.o_raw = reinterpret_cast<const float*>(base + w.o_raw);
+    c.ckpt = reinterpret_cast<const float*>(base + w.ckpt);
+    c.dse = reinterpret_cast<float*>(base + w.dse);
+    c.cbase = reinterpret_cast<int32_t*>(base + w.cbase);
+    c.kbase = reinterpret_cast<int32_t*>(base + w.kbase);
+    c.dq_out = dq; c.dk_out = dk; c.dv_out = dv; c.da_out = da; c.db_out = db;
+    c.dgate_out = gate ? dgate : nullptr;
+    c.d_s0 = d_initial_state;
+    if (kda::launch_bwd_chunked(c, f, hs) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+  }
   if (kda::launch_fwd_chunked(f, hs) != hipSuccess) return KDA_ERR_HIP;
-  // 2. the adjoint recurrence and the reduction over column slices
+  // 2. the adjoint recurrence token by token and the reduction over column slices
   kda::BwdArgs p;
   p.num_seqs = s.num_seqs;
   p.num_heads = s.num_heads;

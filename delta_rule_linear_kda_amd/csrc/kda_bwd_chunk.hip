@@ -1,0 +1,1183 @@
+// kda_bwd_chunk.hip - chunked backward of the KDA recurrence on gfx950:
+// gradients of L = sum_t <dy_t, y_t> + <dS_final, S_final> with respect to q,
+// k, v, a, b, gate and the initial state, on bf16x3 matrix-core products
+// (fp32 accuracy to about 2^-16 per product).
+//
+// The recurrence is the one of page "[Paper Review] Kimi K3...", section
+// "Kimi Delta Attention (KDA)", in its chunkwise form (same section: the
+// recurrence is parallelisable per chunk).  The pages give no backward; it is
+// reverse mode through the chunk form.  Per chunk of n <= 32 tokens with
+// start state S (b = chunk-local cumulative log-decay, Gamma = exp(b),
+// Qbar = qh Gamma, Kbar = kh Gamma, Kend = kh exp(b_end - b),
+// Mkk = strict_lower(kh exp(b) (kh exp(-b))^T), P = lower(qh exp(b) (kh exp(-b))^T),
+// X = (I + diag(beta) Mkk)^-1):
+//   Vt = V - Kbar S,  U = X diag(beta) Vt,  O = Qbar S + P U,
+//   S_end = diag(Gamma_end) S + Kend^T U.
+// With dO = dy sigmoid(gate) and dS_end the adjoint of S_end:
+//   dU = P^T dO + Kend dS_end,   Z = X^T dU,   dV = diag(beta) Z
+//   dS = diag(Gamma_end) dS_end + Qbar^T dO - Kbar^T diag(beta) Z   (chunk start)
+//   dbeta_r = sum_j Z_rj Vt_rj - sum_i (Z U^T)_ri Mkk_ri
+//   dMkk = -diag(beta) (Z U^T) (strict lower),  dP = dO U^T (lower)
+//   dQbar = dO S^T,  dKbar = -diag(beta) Z S^T,  dKend = U dS_end^T,
+//   dGamma_end = rowsum(dS_end * S)
+// then through the pairwise decays of Mkk and P (left factor exp(b_r), right
+// exp(-b_i), each taken against the 16-token tile references as in the
+// forward, so that every factor stays finite: the lower bound g_min = -5 of
+// the "Lower-bounded decay" paragraph keeps a tile's cumulative decay in
+// [-80, 0]) to dqh, dkh and the gradient of b, whose suffix sums over the
+// chunk give the gradient of g = -5 sigmoid(a); last the input maps (L2 norm,
+// sigmoid).
+//
+// Kernels (after the forward has recorded the state every 32 tokens and the
+// ungated output):
+//   bwd_plan_kernel      per-sequence chunk and recorded-state offsets
+//   bwd_dstate_kernel    the adjoint chain: one workgroup per (sequence,
+//                        head, 64 state columns) walks the chunks last to
+//                        first and stores dS_end of every chunk
+//   bwd_chunk_kernel     one workgroup per (chunk, head), all chunks in
+//                        parallel: every gradient of the chunk's tokens from
+//                        its start state and dS_end
+#include <mutex>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kCB = 32;      // chunk length (tokens)
+constexpr int kTl = 16;      // tile length (tokens)
+constexpr int kL32 = kCB + 4;  // padded row stride of [32][32] tiles
+constexpr int kPlanThr = 256;
+
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+// Matrix-core products over one 32-wide block of the contraction index: lane
+// l supplies 8 values of row m = l % 16 of A and 8 of column n = l % 16 of B;
+// slot j of lane group g = l / 16 stands for one contraction index (any
+// bijection onto the block, the same for A and B).  The 16x16 fp32 result
+// tile: lane l holds rows 4 (l / 16) + 0..3 of column l % 16.
+//
+// Each fp32 operand is split into bf16 hi + lo (hi = x truncated to bf16,
+// lo = x - hi rounded to bf16) and the block is three bf16 MFMAs
+// (v_mfma_f32_16x16x32_bf16), hi*hi + hi*lo + lo*hi with fp32 accumulation:
+// the "bf16x3" method (Henry, Tang & Heinecke, 2019), about 2^-16 relative
+// error per product, with fp32's exponent range (the tile factors reach e^80).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+struct F8 {
+  bf16x8_t h, l;
+};
+__device__ __forceinline__ F8 split8(const float (&x)[8]) {
+  uint32_t u[8], w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u[j] = __float_as_uint(x[j]);
+    w[j] = __float_as_uint(x[j] - __uint_as_float(u[j] & 0xFFFF0000u));
+  }
+  u32x4_t hv, lv;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    hv[p] = __builtin_amdgcn_perm(u[2 * p + 1], u[2 * p], 0x07060302u);  // upper halves
+    const uint32_t l0 = w[2 * p] + 0x7FFFu + ((w[2 * p] >> 16) & 1u);    // round to nearest even
+    const uint32_t l1 = w[2 * p + 1] + 0x7FFFu + ((w[2 * p + 1] >> 16) & 1u);
+    lv[p] = __builtin_amdgcn_perm(l1, l0, 0x07060302u);
+  }
+  return {__builtin_bit_cast(bf16x8_t, hv), __builtin_bit_cast(bf16x8_t, lv)};
+}
+__device__ __forceinline__ void mma3(f32x4_t& acc, const F8& a, const F8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.l, b.h, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.l, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma3(f32x4_t& acc, const float (&a)[8], const F8& b) {
+  mma3(acc, split8(a), b);
+}
+__device__ __forceinline__ void mma3(f32x4_t& acc, const float (&a)[8], const float (&b)[8]) {
+  mma3(acc, split8(a), split8(b));
+}
+
+// Contraction index of slot j for lane group g when the B operand is formed
+// from two stacked 16-row result tiles held in registers (rows 0-15 then 16-31).
+__device__ __forceinline__ int kperm(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+// Sum over the 16 lanes of each row of 16 (lanes 16 q .. 16 q + 15), in every
+// lane of the row: rotations within the row by 8, 4, 2 and 1 lanes (DPP).
+template <int CTRL>
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_ror<0x128>(x);  // row_ror:8
+  x += dpp_ror<0x124>(x);  // row_ror:4
+  x += dpp_ror<0x122>(x);  // row_ror:2
+  return x + dpp_ror<0x121>(x);  // row_ror:1
+}
+
+// 8 consecutive floats from LDS (16-byte aligned), and 4 + 4 floats at p and
+// p + 16 (the contraction order of a B operand formed from two stacked result
+// tiles: slot j < 4 is index 4 g + j, slot j >= 4 is index 16 + 4 g + j - 4).
+__device__ __forceinline__ void lds8f(const float* p, float (&x)[8]) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  const float4 w = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+__device__ __forceinline__ void st8f(float* p, const float (&x)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void lds44f(const float* p, float (&x)[8]) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  const float4 w = *reinterpret_cast<const float4*>(p + 16);
+  x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+
+// Chunk offsets per sequence: cbase[n] = sum over m < n of ceil(L_m / 32)
+// (the chunks), kbase[n] = sum of floor(L_m / 32) (the forward's states
+// recorded every 32 tokens); cbase[N], kbase[N] are the totals.
+__global__ void __launch_bounds__(kPlanThr)
+    bwd_plan_kernel(const int32_t* __restrict__ cu_seqlens, int N, int32_t* __restrict__ cbase,
+                    int32_t* __restrict__ kbase) {
+  __shared__ int sc[kPlanThr], sk[kPlanThr];
+  const int t = threadIdx.x;
+  const int per = (N + kPlanThr - 1) / kPlanThr;
+  const int n0 = min(N, t * per), n1 = min(N, n0 + per);
+  int mc = 0, mk = 0;
+  for (int n = n0; n < n1; ++n) {
+    const int L = cu_seqlens[n + 1] - cu_seqlens[n];
+    mc += (L + kCB - 1) / kCB;
+    mk += L / kCB;
+  }
+  sc[t] = mc;
+  sk[t] = mk;
+  __syncthreads();
+  for (int d = 1; d < kPlanThr; d <<= 1) {  // inclusive scans
+    const int xc = t >= d ? sc[t - d] : 0, xk = t >= d ? sk[t - d] : 0;
+    __syncthreads();
+    sc[t] += xc;
+    sk[t] += xk;
+    __syncthreads();
+  }
+  int oc = sc[t] - mc, ok = sk[t] - mk;
+  for (int n = n0; n < n1; ++n) {
+    const int L = cu_seqlens[n + 1] - cu_seqlens[n];
+    cbase[n] = oc;
+    kbase[n] = ok;
+    oc += (L + kCB - 1) / kCB;
+    ok += L / kCB;
+  }
+  if (t == kPlanThr - 1) {
+    cbase[N] = sc[t];
+    kbase[N] = sk[t];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-local preparation shared by both kernels: the rows of the chunk's q,
+// k, a (rows past the end are zero, so they add nothing and keep b flat),
+// their L2 norms, g = -5 sigmoid(a) and its chunk-local inclusive cumsum b
+// (into sB), the per-tile factors, and the scaled operands
+//   Qt = qh exp(b - p), Kt = kh exp(b - p), Kh = kh exp(p - b)
+// with p the cumulative decay before the row's 16-token tile (0 or b_15).
+// Factor tables (DK each): sE[tt] = exp(p_tt), sF[tt] = exp(e_tt - p_tt)
+// (e_tt = b at the tile's last row), sF2[tt] = exp(b_end - e_tt),
+// sD = exp(p_1 - p_0), sGe = exp(b_end).
+// ---------------------------------------------------------------------------
+template <typename TI, int DK, int NTHR>
+__device__ __forceinline__ void chunk_prep(const TI* __restrict__ q, const TI* __restrict__ k,
+                                           const TI* __restrict__ a, int64_t c0, int nrows, int H,
+                                           int h, float* sB, float* sQt, float* sKt, float* sKh,
+                                           float* sE, float* sF, float* sF2, float* sD,
+                                           float* sGe) {
+  constexpr int LDK = DK + 4;
+  constexpr int NSEG = DK / 8;
+  constexpr int NIT = (kCB * NSEG + NTHR - 1) / NTHR;
+  const int t = threadIdx.x;
+  float qh[NIT][8], kh[NIT][8];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int idx = t + NTHR * it, row = idx / NSEG, seg = idx % NSEG;
+    if (idx < kCB * NSEG) {  // uniform per wave: kCB * NSEG is a multiple of 64
+      float qx[8], kx[8], ax[8];
+      const bool valid = row < nrows;
+      if (valid) {
+        const int64_t off = ((c0 + row) * H + h) * (int64_t)DK + seg * 8;
+        ld8(q + off, qx);
+        ld8(k + off, kx);
+        ld8(a + off, ax);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qx[j] = kx[j] = ax[j] = 0.f;
+      }
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sq += qx[j] * qx[j];
+        sk += kx[j] * kx[j];
+      }
+      sq = group_sum<NSEG>(sq);
+      sk = group_sum<NSEG>(sk);
+      const float rq = rsqrtf(sq + kNormEps), rk = rsqrtf(sk + kNormEps);
+      float g8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qh[it][j] = qx[j] * rq;
+        kh[it][j] = kx[j] * rk;
+        g8[j] = valid ? kGMin * sigm(ax[j]) : 0.f;
+      }
+      st8f(sB + row * LDK + seg * 8, g8);
+    }
+  }
+  lds_barrier();
+  if (t < DK) {  // cumsum along the chunk, then the factors of channel t
+    const int c = t;
+    float run = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < kCB; ++r) {
+      run += sB[r * LDK + c];
+      sB[r * LDK + c] = run;
+    }
+    const float p1 = sB[(kTl - 1) * LDK + c], be = run;
+    sE[c] = 1.f;
+    sE[DK + c] = __expf(p1);
+    sF[c] = __expf(p1);            // e_0 = p_1, p_0 = 0
+    sF[DK + c] = __expf(be - p1);  // e_1 = b_end
+    sF2[c] = __expf(be - p1);
+    sF2[DK + c] = 1.f;
+    sD[c] = __expf(p1);
+    sGe[c] = __expf(be);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int idx = t + NTHR * it, row = idx / NSEG, seg = idx % NSEG;
+    if (idx < kCB * NSEG) {
+      float b8[8], p8[8], q8[8], k8[8], h8[8];
+      lds8f(sB + row * LDK + seg * 8, b8);
+      if (row < kTl) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p8[j] = 0.f;
+      } else {
+        lds8f(sB + (kTl - 1) * LDK + seg * 8, p8);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = b8[j] - p8[j];  // in [-80, 0]
+        const float er = __expf(x);
+        q8[j] = qh[it][j] * er;
+        k8[j] = kh[it][j] * er;
+        h8[j] = kh[it][j] * __expf(-x);
+      }
+      st8f(sQt + row * LDK + seg * 8, q8);
+      st8f(sKt + row * LDK + seg * 8, k8);
+      st8f(sKh + row * LDK + seg * 8, h8);
+    }
+  }
+  lds_barrier();
+}
+
+// Mkk and P tiles of the chunk (six 16x16 jobs: Mkk (0,0), (1,0), (1,1) and P
+// the same, contraction over the DK channels), job j on wave j % nwaves:
+// Mkk_ri = sum_c Kt_rc Kh_ic [exp(p_1 - p_0) when i is in tile 0 and r in
+// tile 1], strictly lower; P likewise from Qt, lower with the diagonal.  Mkk
+// goes to sM (scaled by beta_r when `scale_beta`: the A = diag(beta) Mkk of
+// X), P to sP and its transpose to sPT.  The upper tiles are the caller's.
+template <int DK>
+__device__ __forceinline__ void key_products(int wave, int nwaves, int g, int li,
+                                             const float* sQt, const float* sKt,
+                                             const float* sKh, const float* sD,
+                                             const float* sBeta, bool scale_beta, float* sM,
+                                             float* sP, float* sPT) {
+  constexpr int LDK = DK + 4;
+  for (int job = wave; job < 6; job += nwaves) {
+    const bool isP = job >= 3;
+    const int jb = job % 3;
+    const int tr = jb == 0 ? 0 : 1, ti = jb == 2 ? 1 : 0;
+    const float* rows = isP ? sQt : sKt;
+    const bool dsc = ti < tr;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      float av[8], bv[8];
+      const int cb = 32 * kb + 8 * g;
+      lds8f(rows + (16 * tr + li) * LDK + cb, av);
+      lds8f(sKh + (16 * ti + li) * LDK + cb, bv);
+      if (dsc) {
+        float dv8[8];
+        lds8f(sD + cb, dv8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] *= dv8[j];
+      }
+      mma3(acc, av, bv);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
+      if (isP) {
+        const float pv = i <= r ? acc[jj] : 0.f;
+        sP[r * kL32 + i] = pv;
+        sPT[i * kL32 + r] = pv;
+      } else {
+        sM[r * kL32 + i] = i < r ? (scale_beta ? acc[jj] * sBeta[r] : acc[jj]) : 0.f;
+      }
+    }
+  }
+}
+
+// Zero of the upper 16x16 tile (rows 0-15, columns 16-31) of a [32][32] tile
+// set, and of the lower-left tile of its transpose, by one wave.
+__device__ __forceinline__ void zero_upper(int lane, float* M, float* MT) {
+#pragma unroll
+  for (int e = lane; e < 256; e += 64) {
+    M[(e / 16) * kL32 + 16 + e % 16] = 0.f;
+    if (MT) MT[(16 + e / 16) * kL32 + e % 16] = 0.f;
+  }
+}
+
+// X = (I + diag(beta) Mkk)^-1 (unit lower triangular, 32 x 32) by wave 0,
+// into sX and its transpose sXT: the two diagonal 16x16 blocks by forward
+// substitution (one lane per block column), then X_10 = -X_11 A_10 X_00
+// through the scratch tile sT.  `betaM` says whether sM already holds
+// diag(beta) Mkk.
+__device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const float* sM,
+                                        const float* sBeta, bool betaM, float* sX, float* sXT,
+                                        float* sT) {
+  if (wave != 0) return;
+  if (lane < 32) {
+    const int tb = lane / 16, jc = lane % 16;
+    const float* blk = sM + (16 * tb) * kL32 + 16 * tb;
+    float x[16];
+    // row r of the block is read (4 x 16 bytes) while row r - 1 is solved
+    float4 cur[4], nxt[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = *reinterpret_cast<const float4*>(blk + 4 * q4);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r < 15) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          nxt[q4] = *reinterpret_cast<const float4*>(blk + (r + 1) * kL32 + 4 * q4);
+      }
+      const float arow[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
+                              cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                              cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+      const float br = betaM ? 1.f : sBeta[16 * tb + r];
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc += arow[i] * x[i];
+      x[r] = (r == jc ? 1.f : 0.f) - br * acc;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sX[(16 * tb + r) * kL32 + 16 * tb + jc] = x[r];
+      sXT[(16 * tb + jc) * kL32 + 16 * tb + r] = x[r];
+    }
+  }
+  zero_upper(lane, sX, sXT);
+  lds_wave_fence();
+  // sT = A_10 X_00, rows 4g + jj, column li
+  float y[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int r = 4 * g + jj;
+    const float br = betaM ? 1.f : sBeta[16 + r];
+    float s = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) s += sM[(16 + r) * kL32 + kk] * sX[kk * kL32 + li];
+    y[jj] = br * s;
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) sT[(4 * g + jj) * 16 + li] = y[jj];
+  lds_wave_fence();
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int r = 4 * g + jj;
+    float s = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) s += sX[(16 + r) * kL32 + 16 + kk] * sT[kk * 16 + li];
+    sX[(16 + r) * kL32 + li] = -s;
+    sXT[li * kL32 + 16 + r] = -s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The adjoint chain.  Workgroup (sequence, head, 64 columns of d_v), 4 waves;
+// wave w owns columns 16 w .. 16 w + 15 of the slice and holds those columns
+// of dS (d_k rows) in matrix-core result tiles: dS[ct] = rows 16 ct + 4 g +
+// 0..3, column 16 w + li.  Per chunk, last first: store dS (= dS_end of the
+// chunk), then
+//   Y = P^T dO + Kend dS,  Z = X^T Y,  dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z.
+// The operands read along the chunk's rows are kept transposed (P^T, X^T,
+// Qbar^T, (beta Kbar)^T, dO^T), so that every matrix-core operand is a
+// contiguous LDS read.
+// ---------------------------------------------------------------------------
+constexpr int kDsThr = 256;
+constexpr int kDsCols = 64;
+
+template <int DK>
+struct DsLayout {
+  static constexpr int LDK = DK + 4;
+  static constexpr int oB = 0;
+  static constexpr int oQt = oB + kCB * LDK;
+  static constexpr int oKt = oQt + kCB * LDK;
+  static constexpr int oKh = oKt + kCB * LDK;    // Kh, then Kend
+  static constexpr int oQbT = oKh + kCB * LDK;   // Qbar^T [DK][32]
+  static constexpr int oKbT = oQbT + DK * kL32;  // (beta Kbar)^T [DK][32]
+  static constexpr int oM = oKbT + DK * kL32;    // diag(beta) Mkk
+  static constexpr int oP = oM + kCB * kL32;
+  static constexpr int oPT = oP + kCB * kL32;
+  static constexpr int oX = oPT + kCB * kL32;
+  static constexpr int oXT = oX + kCB * kL32;
+  static constexpr int oT = oXT + kCB * kL32;    // 16 x 16 scratch
+  static constexpr int oDOT = oT + 256;          // dO^T slice [64][32]
+  static constexpr int oE = oDOT + kDsCols * kL32;
+  static constexpr int oF = oE + 2 * DK;
+  static constexpr int oF2 = oF + 2 * DK;
+  static constexpr int oD = oF2 + 2 * DK;
+  static constexpr int oGe = oD + DK;
+  static constexpr int oBeta = oGe + DK;
+  static constexpr int total = oBeta + kCB;
+  static_assert(total * 4 <= 160 * 1024, "LDS budget");
+};
+
+template <typename TI, int DK>
+__global__ void __launch_bounds__(kDsThr)
+    bwd_dstate_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                      const TI* __restrict__ a, const TI* __restrict__ bl,
+                      const TI* __restrict__ gate, const float* __restrict__ dy,
+                      const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
+                      const float* __restrict__ d_sfinal, float* __restrict__ dse,
+                      float* __restrict__ d_s0, int H, int DV) {
+  using Ly = DsLayout<DK>;
+  constexpr int LDK = Ly::LDK;
+  constexpr int NCT = DK / 16, NKB = DK / 32;
+  extern __shared__ float smem[];
+  float* sB = smem + Ly::oB;
+  float* sQt = smem + Ly::oQt;
+  float* sKt = smem + Ly::oKt;
+  float* sKh = smem + Ly::oKh;
+  float* sQbT = smem + Ly::oQbT;
+  float* sKbT = smem + Ly::oKbT;
+  float* sM = smem + Ly::oM;
+  float* sP = smem + Ly::oP;
+  float* sPT = smem + Ly::oPT;
+  float* sX = smem + Ly::oX;
+  float* sXT = smem + Ly::oXT;
+  float* sT = smem + Ly::oT;
+  float* sDOT = smem + Ly::oDOT;
+  float* sE = smem + Ly::oE;
+  float* sF = smem + Ly::oF;
+  float* sF2 = smem + Ly::oF2;
+  float* sD = smem + Ly::oD;
+  float* sGe = smem + Ly::oGe;
+  float* sBeta = smem + Ly::oBeta;
+
+  const int nsl = DV / kDsCols;
+  const int slice = blockIdx.x % nsl;
+  const int item = blockIdx.x / nsl;
+  const int n = item / H, h = item % H;
+  const int j0 = slice * kDsCols;
+  const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
+  const int jl = 16 * wave + li;  // column within the slice
+  const int jcol = j0 + jl;
+  const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
+  const int64_t st_off = (int64_t)item * DK * DV;
+  const int nch = (int)((tok_end - tok_beg + kCB - 1) / kCB);
+  const int64_t cb0 = cbase[n];
+
+  f32x4_t dS[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      dS[ct][jj] = d_sfinal ? d_sfinal[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] : 0.f;
+
+  for (int m = nch - 1; m >= 0; --m) {
+    const int64_t c0 = tok_beg + (int64_t)kCB * m;
+    const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+    // dS_end of this chunk
+    {
+      float* dst = dse + ((cb0 + m) * H + h) * (int64_t)DK * DV;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = dS[ct][jj];
+    }
+    // dO^T slice (thread: row t % 32, 8 columns) and beta
+    {
+      const int row = t % kCB, seg = t / kCB;  // kCB * 8 segments = 256 threads
+      float d8[8];
+      if (row < nrows) {
+        const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + j0 + seg * 8;
+        ld8(dy + off, d8);
+        if (gate) {
+          float g8[8];
+          ld8(gate + off, g8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) d8[j] *= sigm(g8[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d8[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sDOT[(seg * 8 + j) * kL32 + row] = d8[j];
+    }
+    if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
+    chunk_prep<TI, DK, kDsThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+    key_products<DK>(wave, kDsThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
+    if (wave == 3) zero_upper(lane, sP, sPT);
+    lds_barrier();
+    solve_x(wave, lane, g, li, sM, sBeta, true, sX, sXT, sT);
+    // The operands of the chain: Qbar^T, (beta Kbar)^T, Kend in place.
+    // (thread: row idx % 32, channels 4 (idx / 32) + 0..3: row reads and
+    // transposed writes both spread over the LDS banks)
+    for (int idx = t; idx < kCB * DK / 4; idx += kDsThr) {
+      const int row = idx % kCB, c = 4 * (idx / kCB), tt = row / kTl;
+      const float br = sBeta[row];
+      const float4 e = *reinterpret_cast<const float4*>(sE + tt * DK + c);
+      const float4 f = *reinterpret_cast<const float4*>(sF + tt * DK + c);
+      const float4 f2 = *reinterpret_cast<const float4*>(sF2 + tt * DK + c);
+      const float4 qv = *reinterpret_cast<const float4*>(sQt + row * LDK + c);
+      const float4 kv = *reinterpret_cast<const float4*>(sKt + row * LDK + c);
+      float4* kh = reinterpret_cast<float4*>(sKh + row * LDK + c);
+      const float4 hv = *kh;
+      sQbT[(c + 0) * kL32 + row] = qv.x * e.x;
+      sQbT[(c + 1) * kL32 + row] = qv.y * e.y;
+      sQbT[(c + 2) * kL32 + row] = qv.z * e.z;
+      sQbT[(c + 3) * kL32 + row] = qv.w * e.w;
+      sKbT[(c + 0) * kL32 + row] = kv.x * e.x * br;
+      sKbT[(c + 1) * kL32 + row] = kv.y * e.y * br;
+      sKbT[(c + 2) * kL32 + row] = kv.z * e.z * br;
+      sKbT[(c + 3) * kL32 + row] = kv.w * e.w * br;
+      *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
+    }
+    lds_barrier();
+
+    F8 dOf;  // column jl of dO, rows 8 g + 0..7
+    {
+      float dOv[8];
+      lds8f(sDOT + jl * kL32 + 8 * g, dOv);
+      dOf = split8(dOv);
+    }
+    F8 dSf[NKB];  // dS as B operand (rows 32 kb + kperm(g, j))
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float bv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = dS[2 * kb + (j >> 2)][j & 3];
+      dSf[kb] = split8(bv);
+    }
+    // Y = P^T dO + Kend dS (rows 16 tt + 4 g + jj, column jl)
+    f32x4_t Y[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      Y[tt] = {0.f, 0.f, 0.f, 0.f};
+      float av[8];
+      lds8f(sPT + (16 * tt + li) * kL32 + 8 * g, av);
+      mma3(Y[tt], av, dOf);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        lds44f(sKh + (16 * tt + li) * LDK + 32 * kb + 4 * g, av);
+        mma3(Y[tt], av, dSf[kb]);
+      }
+    }
+    // Z = X^T Y
+    f32x4_t Z[2];
+    {
+      float bv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = Y[j >> 2][j & 3];
+      const F8 yf = split8(bv);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        Z[tt] = {0.f, 0.f, 0.f, 0.f};
+        float av[8];
+        lds44f(sXT + (16 * tt + li) * kL32 + 4 * g, av);
+        mma3(Z[tt], av, yf);
+      }
+    }
+    // dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z
+    F8 zf;
+    {
+      float zv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zv[j] = Z[j >> 2][j & 3];
+      zf = split8(zv);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t acc;
+      const float4 ge = *reinterpret_cast<const float4*>(sGe + 16 * ct + 4 * g);
+      acc[0] = ge.x * dS[ct][0]; acc[1] = ge.y * dS[ct][1];
+      acc[2] = ge.z * dS[ct][2]; acc[3] = ge.w * dS[ct][3];
+      const int c = 16 * ct + li;
+      float av[8];
+      lds8f(sQbT + c * kL32 + 8 * g, av);
+      mma3(acc, av, dOf);
+      lds44f(sKbT + c * kL32 + 4 * g, av);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) av[j] = -av[j];
+      mma3(acc, av, zf);
+      dS[ct] = acc;
+    }
+    lds_barrier();  // LDS is rewritten by the next chunk
+  }
+  if (d_s0) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        d_s0[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = dS[ct][jj];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gradients of one chunk.  Workgroup (chunk, head), 8 waves.  In the
+// column-owning stages wave w owns column tile w (16 columns of d_v, later 16
+// channels of d_k) over both 16-row tiles of the chunk.
+// ---------------------------------------------------------------------------
+constexpr int kGrThr = 512;
+
+template <int DK, int DV>
+struct GrLayout {
+  static constexpr int LDK = DK + 4, LDV = DV + 4;
+  static constexpr int oB = 0;                 // cumsum b
+  static constexpr int oQt = oB + kCB * LDK;   // Qt, later dqh
+  static constexpr int oKt = oQt + kCB * LDK;  // Kt, later dkh
+  static constexpr int oKh = oKt + kCB * LDK;  // Kh, later the gradient of b
+  static constexpr int oM = oKh + kCB * LDK;   // Mkk (without beta)
+  static constexpr int oP = oM + kCB * kL32;   // P, later dP
+  static constexpr int oPT = oP + kCB * kL32;  // P^T, later dP^T
+  static constexpr int oX = oPT + kCB * kL32;  // X, later dMkk
+  static constexpr int oXT = oX + kCB * kL32;  // X^T, later dMkk^T
+  static constexpr int oT = oXT + kCB * kL32;  // 16 x 16 scratch
+  static constexpr int oDO = oT + 256;         // dO [32][DV]
+  static constexpr int oU = oDO + kCB * LDV;   // U
+  static constexpr int oZ = oU + kCB * LDV;    // Z
+  static constexpr int oE = oZ + kCB * LDV;
+  static constexpr int oF = oE + 2 * DK;
+  static constexpr int oF2 = oF + 2 * DK;
+  static constexpr int oD = oF2 + 2 * DK;
+  static constexpr int oGe = oD + DK;
+  static constexpr int oBeta = oGe + DK;
+  static constexpr int oRed = oBeta + kCB;     // [16][32] partial row sums of dbeta
+  static constexpr int total = oRed + 16 * kCB;
+  static_assert(total * 4 <= 160 * 1024, "LDS budget");
+};
+
+template <typename TI, int DK, int DV>
+__global__ void __launch_bounds__(kGrThr)
+    bwd_chunk_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                     const TI* __restrict__ v, const TI* __restrict__ a,
+                     const TI* __restrict__ bl, const TI* __restrict__ gate,
+                     const float* __restrict__ dy, const float* __restrict__ o_raw,
+                     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
+                     const int32_t* __restrict__ kbase, const float* __restrict__ s_init,
+                     const float* __restrict__ ckpt, const float* __restrict__ dse,
+                     float* __restrict__ dq_out, float* __restrict__ dk_out,
+                     float* __restrict__ dv_out, float* __restrict__ da_out,
+                     float* __restrict__ db_out, float* __restrict__ dgate_out, int N, int H) {
+  using Ly = GrLayout<DK, DV>;
+  constexpr int LDK = Ly::LDK, LDV = Ly::LDV;
+  constexpr int NKB = DK / 32, NVB = DV / 32;
+  extern __shared__ float smem[];
+  float* sB = smem + Ly::oB;
+  float* sQt = smem + Ly::oQt;
+  float* sKt = smem + Ly::oKt;
+  float* sKh = smem + Ly::oKh;
+  float* sM = smem + Ly::oM;
+  float* sP = smem + Ly::oP;
+  float* sPT = smem + Ly::oPT;
+  float* sX = smem + Ly::oX;
+  float* sXT = smem + Ly::oXT;
+  float* sT = smem + Ly::oT;
+  float* sDO = smem + Ly::oDO;
+  float* sU = smem + Ly::oU;
+  float* sZ = smem + Ly::oZ;
+  float* sE = smem + Ly::oE;
+  float* sF = smem + Ly::oF;
+  float* sF2 = smem + Ly::oF2;
+  float* sD = smem + Ly::oD;
+  float* sGe = smem + Ly::oGe;
+  float* sBeta = smem + Ly::oBeta;
+  float* sRed = smem + Ly::oRed;
+
+  const int ci = blockIdx.x / H, h = blockIdx.x % H;
+  if (ci >= cbase[N]) return;  // the grid covers an upper bound of the chunk count
+  int lo = 0, hi = N;          // the sequence n with cbase[n] <= ci < cbase[n + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cbase[mid] <= ci) lo = mid; else hi = mid;
+  }
+  const int n = lo;
+  const int m = ci - cbase[n];
+  const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
+  const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
+  const int64_t c0 = tok_beg + (int64_t)kCB * m;
+  const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+  const int64_t item = (int64_t)n * H + h;
+  // start state (null: zero) and dS_end of the chunk, [DK][DV] each
+  const float* S = m == 0 ? (s_init ? s_init + item * DK * DV : nullptr)
+                          : ckpt + (((int64_t)kbase[n] + m - 1) * H + h) * DK * DV;
+  const float* dSe = dse + (((int64_t)cbase[n] + m) * H + h) * DK * DV;
+  const bool vwave = wave < DV / 16;  // owns a column tile of d_v
+  const bool kwave = wave < DK / 16;  // owns a column tile of d_k
+  const int jc = 16 * wave + li;      // this lane's column (d_v or d_k)
+
+  // ---- loads: dO, dgate, beta; the chunk preparation ---------------------
+  for (int idx = t; idx < kCB * (DV / 8); idx += kGrThr) {
+    const int row = idx / (DV / 8), seg = idx % (DV / 8);
+    float d8[8];
+    if (row < nrows) {
+      const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + seg * 8;
+      ld8(dy + off, d8);
+      if (gate) {
+        float g8[8], o8[8];
+        ld8(gate + off, g8);
+        ld8(o_raw + off, o8);
+        float dg8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float sg = sigm(g8[j]);
+          dg8[j] = d8[j] * o8[j] * sg * (1.f - sg);
+          d8[j] *= sg;
+        }
+        *reinterpret_cast<float4*>(dgate_out + off) = make_float4(dg8[0], dg8[1], dg8[2], dg8[3]);
+        *reinterpret_cast<float4*>(dgate_out + off + 4) = make_float4(dg8[4], dg8[5], dg8[6], dg8[7]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d8[j] = 0.f;
+    }
+    *reinterpret_cast<float4*>(sDO + row * LDV + seg * 8) = make_float4(d8[0], d8[1], d8[2], d8[3]);
+    *reinterpret_cast<float4*>(sDO + row * LDV + seg * 8 + 4) = make_float4(d8[4], d8[5], d8[6], d8[7]);
+  }
+  if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
+  chunk_prep<TI, DK, kGrThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  // The value-side B operands, requested before the key products and the
+  // solve for X: column jc of S and of dS_end, rows 32 kb + 8 g + 0..7.
+  float Sv[NKB][8], Ev[NKB][8];
+  if (vwave) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = (int64_t)(32 * kb + 8 * g + j) * DV + jc;
+        Sv[kb][j] = S ? S[e] : 0.f;
+        Ev[kb][j] = dSe[e];
+      }
+  }
+  key_products<DK>(wave, kGrThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, false, sM, sP, sPT);
+  if (wave == 6) zero_upper(lane, sP, sPT);
+  if (wave == 7) zero_upper(lane, sM, nullptr);
+  lds_barrier();
+
+  // ---- value side, columns of wave w: Vt = V - Kbar S, dU = P^T dO + Kend
+  // dS_end (no X needed: beside wave 0's solve for X), then U = X diag(beta)
+  // Vt, Z = X^T dU, dV = diag(beta) Z, dbeta partial sum_j Z Vt.
+  solve_x(wave, lane, g, li, sM, sBeta, false, sX, sXT, sT);
+  f32x4_t Vt[2], dU[2];
+  if (vwave) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        Vt[tt][jj] = r < nrows ? ld_elem(v, ((c0 + r) * H + h) * (int64_t)DV + jc) : 0.f;
+        dU[tt][jj] = 0.f;
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int cb = 32 * kb + 8 * g;
+      float kf[8], f2[8];
+      const F8 sf = split8(Sv[kb]), ef = split8(Ev[kb]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float ek[8], av[8];
+        lds8f(sE + tt * DK + cb, ek);
+        lds8f(sKt + (16 * tt + li) * LDK + cb, av);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] = -av[j] * ek[j];
+        if (S) mma3(Vt[tt], av, sf);
+        lds8f(sF + tt * DK + cb, kf);
+        lds8f(sF2 + tt * DK + cb, f2);
+        lds8f(sKh + (16 * tt + li) * LDK + cb, av);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] *= kf[j] * f2[j];
+        mma3(dU[tt], av, ef);
+      }
+    }
+    float dov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dov[j] = sDO[(8 * g + j) * LDV + jc];
+    const F8 dof = split8(dov);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float av[8];
+      lds8f(sPT + (16 * tt + li) * kL32 + 8 * g, av);
+      mma3(dU[tt], av, dof);
+    }
+  }
+  lds_barrier();  // X
+  // The d_k-side B operands of the next stage, requested now: row jc of S and
+  // of dS_end, columns 32 kb + 8 g + 0..7.
+  float Sr[NVB][8], Er[NVB][8];
+  if (kwave) {
+#pragma unroll
+    for (int kb = 0; kb < NVB; ++kb) {
+      const int64_t e = (int64_t)jc * DV + 32 * kb + 8 * g;
+      if (S) {
+        ld8(S + e, Sr[kb]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Sr[kb][j] = 0.f;
+      }
+      ld8(dSe + e, Er[kb]);
+    }
+  }
+  if (vwave) {
+    f32x4_t U[2], Z[2];
+    float bu[8], bz[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bu[j] = sBeta[kperm(g, j)] * Vt[j >> 2][j & 3];
+      bz[j] = dU[j >> 2][j & 3];
+    }
+    const F8 buf = split8(bu), bzf = split8(bz);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      U[tt] = Z[tt] = {0.f, 0.f, 0.f, 0.f};
+      float av[8];
+      lds44f(sX + (16 * tt + li) * kL32 + 4 * g, av);
+      mma3(U[tt], av, buf);
+      lds44f(sXT + (16 * tt + li) * kL32 + 4 * g, av);
+      mma3(Z[tt], av, bzf);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        sU[r * LDV + jc] = U[tt][jj];
+        sZ[r * LDV + jc] = Z[tt][jj];
+        if (r < nrows) dv_out[((c0 + r) * H + h) * (int64_t)DV + jc] = sBeta[r] * Z[tt][jj];
+        const float part = row16_sum(Z[tt][jj] * Vt[tt][jj]);
+        if (li == 0) sRed[wave * kCB + r] = part;
+      }
+  }
+  lds_barrier();
+
+  // ---- dP = dO U^T, Z U^T (waves 0-5); dQbar, dKbar, dKend (d_k waves) ----
+  if (wave < 6) {
+    const bool isZ = wave >= 3;
+    const int jb = wave % 3;
+    const int tr = jb == 0 ? 0 : 1, ti = jb == 2 ? 1 : 0;
+    const float* rows = isZ ? sZ : sDO;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NVB; ++kb) {
+      float av[8], bv[8];
+      const int cb = 32 * kb + 8 * g;
+      lds8f(rows + (16 * tr + li) * LDV + cb, av);
+      lds8f(sU + (16 * ti + li) * LDV + cb, bv);
+      mma3(acc, av, bv);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
+      if (!isZ) {
+        const float dp = i <= r ? acc[jj] : 0.f;
+        sP[r * kL32 + i] = dp;
+        sPT[i * kL32 + r] = dp;
+      } else {
+        const float zu = i < r ? acc[jj] : 0.f;
+        // dbeta_r -= sum_i (Z U^T)_ri Mkk_ri;  dMkk = -beta_r (Z U^T)
+        const float part = row16_sum(zu * sM[r * kL32 + i]);
+        if (li == 0) sRed[(8 + jb) * kCB + r] = -part;
+        const float dm = -sBeta[r] * zu;
+        sX[r * kL32 + i] = dm;
+        sXT[i * kL32 + r] = dm;
+      }
+    }
+  } else if (wave == 6) {
+    zero_upper(lane, sP, sPT);
+  } else {
+    zero_upper(lane, sX, sXT);
+  }
+  f32x4_t dQb[2], dKb[2], dKe[2];
+  float dge = 0.f;  // dGamma_end of channel jc (partial over this lane group's columns)
+  if (kwave) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) dQb[tt] = dKb[tt] = dKe[tt] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NVB; ++kb) {
+      const int jb0 = 32 * kb + 8 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dge += Sr[kb][j] * Er[kb][j];
+      const F8 srf = split8(Sr[kb]), erf = split8(Er[kb]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int r = 16 * tt + li;
+        float ao[8], az[8], au[8];
+        const float br = -sBeta[r];
+        lds8f(sDO + r * LDV + jb0, ao);
+        lds8f(sZ + r * LDV + jb0, az);
+        lds8f(sU + r * LDV + jb0, au);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) az[j] *= br;
+        mma3(dQb[tt], ao, srf);
+        mma3(dKb[tt], az, srf);
+        mma3(dKe[tt], au, erf);
+      }
+    }
+    dge += __shfl_xor(dge, 16, 64);
+    dge += __shfl_xor(dge, 32, 64);
+  }
+  lds_barrier();
+
+  // ---- through the pairwise decays, then per element ----------------------
+  // accLk = dMkk (Kh D), accLq = dP (Kh D) (rows r), accR = dMkk^T (Kt D) +
+  // dP^T (Qt D) (rows i); D = exp(p_1 - p_0) between a row in tile 1 and a
+  // column in tile 0.
+  if (kwave) {
+    const int c = jc;
+    const float dc = sD[c];
+    f32x4_t accLk[2], accLq[2], accR[2];
+    float bk[8], bkd[8], bkt[8], bqt[8], bktd[8], bqtd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = 8 * g + j;
+      bk[j] = sKh[i * LDK + c];
+      bkd[j] = i < kTl ? bk[j] * dc : bk[j];
+      bkt[j] = sKt[i * LDK + c];
+      bqt[j] = sQt[i * LDK + c];
+      bktd[j] = i >= kTl ? bkt[j] * dc : bkt[j];
+      bqtd[j] = i >= kTl ? bqt[j] * dc : bqt[j];
+    }
+    const F8 fbk = split8(bk), fbkd = split8(bkd), fbkt = split8(bkt), fbqt = split8(bqt),
+             fbktd = split8(bktd), fbqtd = split8(bqtd);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      accLk[tt] = accLq[tt] = accR[tt] = {0.f, 0.f, 0.f, 0.f};
+      float am[8], ap[8];
+      lds8f(sX + (16 * tt + li) * kL32 + 8 * g, am);
+      lds8f(sP + (16 * tt + li) * kL32 + 8 * g, ap);
+      const F8 fam = split8(am), fap = split8(ap);
+      mma3(accLk[tt], fam, tt == 1 ? fbkd : fbk);
+      mma3(accLq[tt], fap, tt == 1 ? fbkd : fbk);
+      lds8f(sXT + (16 * tt + li) * kL32 + 8 * g, am);
+      lds8f(sPT + (16 * tt + li) * kL32 + 8 * g, ap);
+      mma3(accR[tt], am, tt == 0 ? fbktd : fbkt);
+      mma3(accR[tt], ap, tt == 0 ? fbqtd : fbqt);
+    }
+    // per element (r = 16 tt + 4 g + jj, channel c)
+    float dbv[2][4], dqv[2][4], dkv[2][4];
+    float colsum = 0.f;  // sum over rows of dKend Kend
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float et = sE[tt * DK + c];
+      const float kf = sF[tt * DK + c] * sF2[tt * DK + c];
+      const float p = tt == 0 ? 0.f : sB[(kTl - 1) * LDK + c];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        const float x = sB[r * LDK + c] - p;
+        const float fr = __expf(x), gr = __expf(-x);
+        const float qt = sQt[r * LDK + c], kt = sKt[r * LDK + c], khv = sKh[r * LDK + c];
+        const float ke = dKe[tt][jj] * khv * kf;
+        colsum += ke;
+        dqv[tt][jj] = dQb[tt][jj] * fr * et + fr * accLq[tt][jj];
+        dkv[tt][jj] = dKb[tt][jj] * fr * et + dKe[tt][jj] * gr * kf + fr * accLk[tt][jj] +
+                      gr * accR[tt][jj];
+        dbv[tt][jj] = dQb[tt][jj] * qt * et + dKb[tt][jj] * kt * et - ke + qt * accLq[tt][jj] +
+                      kt * accLk[tt][jj] - khv * accR[tt][jj];
+      }
+    }
+    colsum += __shfl_xor(colsum, 16, 64);
+    colsum += __shfl_xor(colsum, 32, 64);
+    // b_end = b at row 31 (rows past the end keep b flat): its gradient goes to row 31
+    if (g == 3) dbv[1][3] += colsum + dge * sGe[c];
+    // Only this wave reads or writes channel c of these rows in this stage.
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        sQt[r * LDK + c] = dqv[tt][jj];
+        sKt[r * LDK + c] = dkv[tt][jj];
+        sKh[r * LDK + c] = dbv[tt][jj];
+      }
+  }
+  lds_barrier();
+
+  // ---- outputs ------------------------------------------------------------
+  // da: suffix sums of the b-gradient along the chunk times dg/da =
+  // -5 sigmoid(a) (1 - sigmoid(a)) = g (1 + g / 5), g = b_r - b_{r-1}.
+  if (t < DK) {
+    const int c = t;
+    float run = 0.f;
+    for (int r = kCB - 1; r >= 0; --r) {
+      run += sKh[r * LDK + c];
+      if (r < nrows) {
+        const float gv = sB[r * LDK + c] - (r > 0 ? sB[(r - 1) * LDK + c] : 0.f);
+        da_out[((c0 + r) * H + h) * (int64_t)DK + c] = run * gv * (1.f + gv * (1.f / 5.f));
+      }
+    }
+  }
+  // dq, dk through the L2 norms: 16 lanes per row.
+  {
+    constexpr int CPL = DK / 16;
+    const int r = t / 16, l16 = t % 16;
+    if (r < nrows) {
+      const int64_t off = ((c0 + r) * H + h) * (int64_t)DK + CPL * l16;
+      float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        qv[cc] = ld_elem(q, off + cc);
+        kv[cc] = ld_elem(k, off + cc);
+        sq += qv[cc] * qv[cc];
+        sk += kv[cc] * kv[cc];
+        qd += qv[cc] * sQt[r * LDK + CPL * l16 + cc];
+        kd += kv[cc] * sKt[r * LDK + CPL * l16 + cc];
+      }
+      sq = group_sum<16>(sq);
+      sk = group_sum<16>(sk);
+      qd = group_sum<16>(qd);
+      kd = group_sum<16>(kd);
+      const float rq = rsqrtf(sq + kNormEps), rk = rsqrtf(sk + kNormEps);
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        dq_out[off + cc] = rq * sQt[r * LDK + CPL * l16 + cc] - rq * rq * rq * qd * qv[cc];
+        dk_out[off + cc] = rk * sKt[r * LDK + CPL * l16 + cc] - rk * rk * rk * kd * kv[cc];
+      }
+      if (l16 == 0) {
+        float dbeta = 0.f;
+        for (int w = 0; w < DV / 16; ++w) dbeta += sRed[w * kCB + r];
+        if (r >= kTl) {
+          dbeta += sRed[(8 + 1) * kCB + r] + sRed[(8 + 2) * kCB + r];
+        } else {
+          dbeta += sRed[8 * kCB + r];
+        }
+        const float beta = sBeta[r];
+        db_out[(c0 + r) * H + h] = dbeta * beta * (1.f - beta);
+      }
+    }
+  }
+}
+
+template <typename TI, int DK, int DV>
+hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) {
+  const size_t lds = sizeof(float) * GrLayout<DK, DV>::total;
+  auto kern = bwd_chunk_kernel<TI, DK, DV>;
+  static bool configured = false;  // raising the dynamic LDS limit is idempotent
+  if (!configured) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGrThr), lds, stream, (const TI*)p.q,
+                     (const TI*)p.k, (const TI*)p.v, (const TI*)p.a, (const TI*)p.b,
+                     (const TI*)p.gate, p.dy, p.o_raw, p.cu_seqlens, p.cbase, p.kbase,
+                     p.initial_state, p.ckpt, p.dse, p.dq_out, p.dk_out, p.dv_out, p.da_out,
+                     p.db_out, p.dgate_out, p.num_seqs, p.num_heads);
+  return hipGetLastError();
+}
+
+template <typename TI, int DK>
+hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
+  const size_t lds = sizeof(float) * DsLayout<DK>::total;
+  auto kern = bwd_dstate_kernel<TI, DK>;
+  static bool configured = false;
+  if (!configured) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int64_t grid = (int64_t)p.num_seqs * p.num_heads * (p.dv / kDsCols);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDsThr), lds, stream, (const TI*)p.q,
+                     (const TI*)p.k, (const TI*)p.a, (const TI*)p.b, (const TI*)p.gate, p.dy,
+                     p.cu_seqlens, p.cbase, p.d_final_state, p.dse, p.d_s0, p.num_heads, p.dv);
+  return hipGetLastError();
+}
+
+// Per device: the events that fork the adjoint chain onto the second stream
+// and join it back, created on first use (on the device of the caller's
+// stream) and kept for the process; one mutex serialises the enqueueing.
+struct BwdEvents {
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_bwd_mu;
+BwdEvents g_bwd_ev[64];
+
+hipError_t bwd_events(hipStream_t stream, BwdEvents** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  BwdEvents& be = g_bwd_ev[dev];
+  if (!be.fork) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    BwdEvents made;
+    e = hipEventCreateWithFlags(&made.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&made.join, hipEventDisableTiming);
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    be = made;
+  }
+  *out = &be;
+  return hipSuccess;
+}
+
+template <typename TI>
+hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(kPlanThr), 0, stream, p.cu_seqlens,
+                     p.num_seqs, p.cbase, p.kbase);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    // the adjoint chain needs the plan only: it runs on the second stream
+    // while the forward records the states on the caller's stream
+    std::lock_guard<std::mutex> lock(g_bwd_mu);
+    BwdEvents* ev = nullptr;
+    hipStream_t s2 = nullptr;
+    if ((e = bwd_events(stream, &ev)) != hipSuccess) return e;
+    if ((e = device_side_stream(stream, &s2)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s2, ev->fork, 0)) != hipSuccess) return e;
+    e = p.dk == 128 ? launch_dstate<TI, 128>(p, s2) : launch_dstate<TI, 64>(p, s2);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(ev->join, s2)) != hipSuccess) return e;
+    if ((e = launch_fwd_chunked(f, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, ev->join, 0)) != hipSuccess) return e;
+  }
+  const int64_t grid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
+  if (grid == 0) return hipSuccess;
+  if (p.dk == 128)
+    return p.dv == 128 ? launch_grad<TI, 128, 128>(p, grid, stream)
+                       : launch_grad<TI, 128, 64>(p, grid, stream);
+  return p.dv == 128 ? launch_grad<TI, 64, 128>(p, grid, stream)
+                     : launch_grad<TI, 64, 64>(p, grid, stream);
+}
+
+}  // namespace
+
+int bwd_chunk_len() { return kCB; }
+
+hipError_t launch_bwd_chunked(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream) {
+  if ((int64_t)p.num_seqs * p.num_heads == 0) return launch_fwd_chunked(f, stream);
+  return p.in_bf16 ? launch_t<uint16_t>(p, f, stream) : launch_t<float>(p, f, stream);
+}
+
+}  // namespace kda

@@ -135,6 +135,36 @@ struct BwdArgs {
 };
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
 
+// Chunked backward (kda_bwd_chunk.hip): the forward's states recorded every
+// bwd_chunk_len() tokens (slot layout of kda_fwd_chunked_ckpt) and its
+// ungated output are computed by the caller into the workspace first.
+struct BwdChunkArgs {
+  int32_t num_seqs, num_heads, dk, dv;
+  int64_t total_tokens;
+  bool in_bf16;
+  const void *q, *k, *v, *a, *b, *gate;  // gate may be null
+  const int32_t* cu_seqlens;
+  const float* initial_state;   // may be null
+  const float* dy;              // [T, H, dv]
+  const float* d_final_state;   // may be null
+  const float* o_raw;           // [T, H, dv] ungated forward output
+  const float* ckpt;            // states after every bwd_chunk_len() tokens of each sequence
+  float* dse;                   // [T / len + N, H, dk, dv]: adjoint state at each chunk's end
+  int32_t *cbase, *kbase;       // [N + 1] each: chunk and recorded-state offsets
+  float *dq_out, *dk_out, *dv_out, *da_out, *db_out, *dgate_out, *d_s0;  // dgate, d_s0 may be null
+};
+int bwd_chunk_len();
+// Enqueues the whole chunked backward on `stream`: the chunk plan, the
+// adjoint chain on the device's second stream beside the forward `f` (which
+// records the states and the ungated output the gradients read), then the
+// per-chunk gradients once both are done.
+hipError_t launch_bwd_chunked(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream);
+
+// The per-device second stream (default priority, created on first use on the
+// device of `stream` and kept for the process) that the forward's state
+// passes and the backward's adjoint chain run on beside the caller's stream.
+hipError_t device_side_stream(hipStream_t stream, hipStream_t* out);
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

@@ -1305,6 +1305,14 @@ hipError_t side_stream(hipStream_t stream, SideStream** out) {
 
 }  // namespace
 
+hipError_t device_side_stream(hipStream_t stream, hipStream_t* out) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  const hipError_t e = side_stream(stream, &side);
+  if (e == hipSuccess) *out = side->s;
+  return e;
+}
+
 bool split_whole_head(int64_t num_seqs, int64_t num_heads, int dv) {
   return dv == 128 && num_seqs * num_heads > kWideItems;
 }

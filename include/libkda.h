@@ -37,6 +37,9 @@
  *     serialised by a mutex, and concurrent calls on one device share the
  *     stream (their state passes run in call order).  The caller's stream
  *     waits for all of it, so the call is still ordered by `stream` alone.
+ *     The bf16 backward (kda_bwd_chunked) uses the same per-device stream
+ *     for its adjoint chain beside its forward recomputation, with two more
+ *     events per device and a mutex of its own, under the same rules.
  *   - Host-checkable problems are reported by the return code BEFORE anything
  *     is enqueued.  Preconditions that live in device memory (cu_seqlens
  *     starting at 0, nondecreasing, ending at total_tokens) are the caller's
@@ -352,7 +355,12 @@ KDA_API kda_status kda_rmsnorm_gate(const kda_shape* shape, const float* o, cons
  *   d_initial_state [N, H, dk, dv] fp32 out, or NULL
  *   workspace      kda_bwd_workspace_bytes(shape) bytes, 16-byte aligned
  * Outputs and workspace must not overlap any input or each other.  The
- * forward is recomputed inside (states recorded every 64 tokens); results are
+ * forward is recomputed inside.  bf16 inputs run the chunked form: the states
+ * recorded every 32 tokens, the adjoint state carried back across 32-token
+ * chunks on the device's second stream (beside the recomputation), then every
+ * chunk's gradients in parallel on matrix-core products (bf16 hi + lo
+ * operands, fp32 accumulation).  fp32 inputs run the token form in fp32
+ * (states every 64 tokens, the adjoint carried token by token).  Results are
  * deterministic (no atomics).
  * Errors: NULL_POINTER, BAD_SHAPE, BAD_DTYPE, MISALIGNED, WORKSPACE, ALIAS, HIP. */
 KDA_API kda_status kda_bwd_workspace_bytes(const kda_shape* shape, size_t* bytes);

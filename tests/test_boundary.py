@@ -399,9 +399,17 @@ def test_bwd_workspace_query():
     up = lambda x: (x + 255) // 256 * 256
     N, T, H, dk, dv = 2, 300, 4, 128, 128
     th, nsl = T * H, dv // 8
-    exp = (up((T // 64) * H * dk * dv * 4) + up(th * dv * 4) + 3 * up(nsl * th * dk * 4)
-           + up(nsl * th * 4) + up(N * H * nsl * 16 * dk * 8 * 4))
+    st = H * dk * dv * 4
+    # bf16 inputs (chunked form, 32-token chunks): states every 32 tokens, the
+    # ungated output, the adjoint state at each chunk's end, two offset tables
+    exp = (up((T // 32) * st) + up(th * dv * 4) + up((T // 32 + N) * st)
+           + 2 * up((N + 1) * 4))
     assert kda.bwd_workspace_bytes(N, T, H, dk, dv) == exp
+    # fp32 inputs (token form): states every 64 tokens, the ungated output,
+    # per-slice partial sums and sub-chunk start states
+    exp = (up((T // 64) * st) + up(th * dv * 4) + 3 * up(nsl * th * dk * 4)
+           + up(nsl * th * 4) + up(N * H * nsl * 16 * dk * 8 * 4))
+    assert kda.bwd_workspace_bytes(N, T, H, dk, dv, kda.KDA_F32) == exp
     out = ctypes.c_size_t(0)
     assert kda.lib().kda_bwd_workspace_bytes(None, ctypes.byref(out)) == NULLP
 
