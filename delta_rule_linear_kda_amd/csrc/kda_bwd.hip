@@ -431,9 +431,11 @@ __global__ void __launch_bounds__(256)
   for (int c = 0; c < CPL; ++c) {
     dq[row * DK + c0 + c] = rq * dqh[c] - rq * rq * rq * qd * qv[c];
     dk[row * DK + c0 + c] = rk * dkh[c] - rk * rk * rk * kd * kv[c];
-    const float sa = sigm(ld_elem(a, row * DK + c0 + c));
+    const float av = ld_elem(a, row * DK + c0 + c);
+    const float sa = sigm(av);
     const float al = __expf(kGMin * sa);
-    da[row * DK + c0 + c] = dal[c] * al * kGMin * sa * (1.f - sa);
+    // sigmoid'(a) = sigmoid(a) sigmoid(-a): no cancellation as sigmoid(a) -> 1
+    da[row * DK + c0 + c] = dal[c] * al * kGMin * sa * sigm(-av);
   }
   if (li == 0) {
     const float beta = sigm(ld_elem(bl, row));

@@ -947,6 +947,15 @@ __global__ void __launch_bounds__(kGrThr)
   if (kwave) {
     const int c = jc;
     const float dc = sD[c];
+    // decay logits of this lane's elements, for dg/da
+    float av_[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        av_[tt][jj] = r < nrows ? ld_elem(a, ((c0 + r) * H + h) * (int64_t)DK + c) : 0.f;
+      }
     f32x4_t accLk[2], accLq[2], accR[2];
     float bk[8], bkd[8], bkt[8], bqt[8], bktd[8], bqtd[8];
 #pragma unroll
@@ -1002,7 +1011,8 @@ __global__ void __launch_bounds__(kGrThr)
     colsum += __shfl_xor(colsum, 32, 64);
     // b_end = b at row 31 (rows past the end keep b flat): its gradient goes to row 31
     if (g == 3) dbv[1][3] += colsum + dge * sGe[c];
-    // Only this wave reads or writes channel c of these rows in this stage.
+    // Only this wave reads or writes channel c of these rows in this stage
+    // (sB's reads above are issued before its writes below).
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -1011,22 +1021,20 @@ __global__ void __launch_bounds__(kGrThr)
         sQt[r * LDK + c] = dqv[tt][jj];
         sKt[r * LDK + c] = dkv[tt][jj];
         sKh[r * LDK + c] = dbv[tt][jj];
+        // dg/da = -5 sigmoid(a) sigmoid(-a) (no cancellation as sigmoid(a) -> 1)
+        sB[r * LDK + c] = kGMin * sigm(av_[tt][jj]) * sigm(-av_[tt][jj]);
       }
   }
   lds_barrier();
 
   // ---- outputs ------------------------------------------------------------
-  // da: suffix sums of the b-gradient along the chunk times dg/da =
-  // -5 sigmoid(a) (1 - sigmoid(a)) = g (1 + g / 5), g = b_r - b_{r-1}.
+  // da: suffix sums of the b-gradient along the chunk times dg/da (in sB).
   if (t < DK) {
     const int c = t;
     float run = 0.f;
     for (int r = kCB - 1; r >= 0; --r) {
       run += sKh[r * LDK + c];
-      if (r < nrows) {
-        const float gv = sB[r * LDK + c] - (r > 0 ? sB[(r - 1) * LDK + c] : 0.f);
-        da_out[((c0 + r) * H + h) * (int64_t)DK + c] = run * gv * (1.f + gv * (1.f / 5.f));
-      }
+      if (r < nrows) da_out[((c0 + r) * H + h) * (int64_t)DK + c] = run * sB[r * LDK + c];
     }
   }
   // dq, dk through the L2 norms: 16 lanes per row.

@@ -8,6 +8,7 @@ import pytest
 import oracle
 import synth
 from tests import kda_cases as kc
+from tests.test_gpu_edge import apply_case
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +29,16 @@ def _cotangents(w, T, N, seed):
     return dy, dsf
 
 
-def run_bwd(w, lens, gate=True, with_s0=True, with_dsf=True, label=""):
+def run_bwd(w, lens, gate=True, with_s0=True, with_dsf=True, label="", case=None, v_scale=1.0,
+            tol_over=None):
     _require_gpu()
     print(f"[case] bwd {label} {w.name} H={w.heads} dk={w.dk} dv={w.dv} lens={lens} "
-          f"gate={gate} s0={with_s0} dsf={with_dsf}", flush=True)
+          f"gate={gate} s0={with_s0} dsf={with_dsf} case={case}", flush=True)
     T, N = sum(lens), len(lens)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     x = kc.host_inputs(w, T)
+    if case is not None:
+        apply_case(case, x, lens, w.dk, v_scale=v_scale)
     s0 = kc.host_state(w, N) if with_s0 else None
     dy, dsf = _cotangents(w, T, N, seed=3)
     dev = {n: kc.to_torch(x[n]) for n in x}
@@ -60,7 +64,7 @@ def run_bwd(w, lens, gate=True, with_s0=True, with_dsf=True, label=""):
     print("    err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {tol:.0e})",
           flush=True)
     for key, e in errs.items():
-        assert e <= tol, (key, e)
+        assert e <= (tol_over or {}).get(key, tol), (key, e)
     return g
 
 
@@ -127,3 +131,37 @@ def test_bwd_full_workload_sampled():
               flush=True)
         for key, e in errs.items():
             assert e <= kc.TOL_BF16, (n, h, key, e)
+
+
+# The decay edge cases of the "Lower-bounded decay" paragraph (tile sums at
+# -80, factors e^80), one-hot and orthonormal keys, and large values over
+# large initial states, through both backward forms.
+EDGE_LENS = [128, 57, 0, 100]
+
+
+# With every decay logit at +8 (alpha = 6.7e-3 per token) the gradient of the
+# decay logits is a sum of read-out and erase terms of the chunk-start states
+# that cancel to about 1/15 of their size, so da carries the recomputed
+# states' error amplified about 15x: the bf16 forward's states are within
+# about 3e-3 (fp16 operands on the state path), and an fp64 model of the
+# chunked backward with 3e-3 relative noise on those states gives 4.6e-2.
+# da is held to 1e-1 there; every other gradient to 2e-2.
+DA_SATURATED_BF16 = 1e-1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", ["a_pinf", "a_p8", "a_mix", "onehot", "orth"])
+def test_bwd_edge_cases(dtype, case):
+    base = synth.WORKLOADS[1] if dtype == "bf16" else synth.WORKLOADS[0]
+    w = kc.custom_workload(base, heads=2, dk=128, dv=128, s0_std=0.02)
+    over = {"da": DA_SATURATED_BF16} if (dtype, case) == ("bf16", "a_p8") else None
+    run_bwd(w, EDGE_LENS, label=f"edge {dtype}", case=case, tol_over=over)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_large_state_and_values(dtype):
+    """Initial states of std 1e3 and values x 1e3: the gradients' products
+    keep fp32's exponent range."""
+    base = synth.WORKLOADS[1] if dtype == "bf16" else synth.WORKLOADS[0]
+    w = kc.custom_workload(base, heads=2, dk=128, dv=128, s0_std=1e3)
+    run_bwd(w, EDGE_LENS, label=f"large {dtype}", case="big_v", v_scale=1e3)
