@@ -405,8 +405,10 @@ __device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const
 }
 
 // ---------------------------------------------------------------------------
-// The adjoint chain.  Workgroup (sequence, head, 64 columns of d_v), 4 waves;
-// wave w owns columns 16 w .. 16 w + 15 of the slice and holds those columns
+// The adjoint chain.  Workgroup (sequence, head): one wave per 16 columns of
+// d_v (8 at d_v = 128), so the chunk's preparation is done once per head and
+// two waves share each SIMD; wave w owns columns 16 w .. 16 w + 15 and holds
+// those columns
 // of dS (d_k rows) in matrix-core result tiles: dS[ct] = rows 16 ct + 4 g +
 // 0..3, column 16 w + li.  Per chunk, last first: store dS (= dS_end of the
 // chunk), then
@@ -415,10 +417,7 @@ __device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const
 // Qbar^T, (beta Kbar)^T, dO^T), so that every matrix-core operand is a
 // contiguous LDS read.
 // ---------------------------------------------------------------------------
-constexpr int kDsThr = 256;
-constexpr int kDsCols = 64;
-
-template <int DK>
+template <int DK, int DV>
 struct DsLayout {
   static constexpr int LDK = DK + 4;
   static constexpr int oB = 0;
@@ -433,8 +432,8 @@ struct DsLayout {
   static constexpr int oX = oPT + kCB * kL32;
   static constexpr int oXT = oX + kCB * kL32;
   static constexpr int oT = oXT + kCB * kL32;    // 16 x 16 scratch
-  static constexpr int oDOT = oT + 256;          // dO^T slice [64][32]
-  static constexpr int oE = oDOT + kDsCols * kL32;
+  static constexpr int oDOT = oT + 256;          // dO^T [DV][32]
+  static constexpr int oE = oDOT + DV * kL32;
   static constexpr int oF = oE + 2 * DK;
   static constexpr int oF2 = oF + 2 * DK;
   static constexpr int oD = oF2 + 2 * DK;
@@ -444,15 +443,16 @@ struct DsLayout {
   static_assert(total * 4 <= 160 * 1024, "LDS budget");
 };
 
-template <typename TI, int DK>
-__global__ void __launch_bounds__(kDsThr)
+template <typename TI, int DK, int DV>
+__global__ void __launch_bounds__(4 * DV)
     bwd_dstate_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                       const TI* __restrict__ a, const TI* __restrict__ bl,
                       const TI* __restrict__ gate, const float* __restrict__ dy,
                       const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
                       const float* __restrict__ d_sfinal, float* __restrict__ dse,
-                      float* __restrict__ d_s0, int H, int DV) {
-  using Ly = DsLayout<DK>;
+                      float* __restrict__ d_s0, int H) {
+  using Ly = DsLayout<DK, DV>;
+  constexpr int kDsThr = 4 * DV;  // 64 lanes per 16 columns
   constexpr int LDK = Ly::LDK;
   constexpr int NCT = DK / 16, NKB = DK / 32;
   extern __shared__ float smem[];
@@ -476,13 +476,11 @@ __global__ void __launch_bounds__(kDsThr)
   float* sGe = smem + Ly::oGe;
   float* sBeta = smem + Ly::oBeta;
 
-  const int nsl = DV / kDsCols;
-  const int slice = blockIdx.x % nsl;
-  const int item = blockIdx.x / nsl;
+  const int item = blockIdx.x;
   const int n = item / H, h = item % H;
-  const int j0 = slice * kDsCols;
+  constexpr int j0 = 0;
   const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
-  const int jl = 16 * wave + li;  // column within the slice
+  const int jl = 16 * wave + li;  // this lane's column
   const int jcol = j0 + jl;
   const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
   const int64_t st_off = (int64_t)item * DK * DV;
@@ -507,9 +505,9 @@ __global__ void __launch_bounds__(kDsThr)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = dS[ct][jj];
     }
-    // dO^T slice (thread: row t % 32, 8 columns) and beta
+    // dO^T (thread: row t % 32, 8 columns) and beta
     {
-      const int row = t % kCB, seg = t / kCB;  // kCB * 8 segments = 256 threads
+      const int row = t % kCB, seg = t / kCB;  // kCB rows x DV / 8 segments = every thread
       float d8[8];
       if (row < nrows) {
         const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + j0 + seg * 8;
@@ -1097,10 +1095,10 @@ hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <typename TI, int DK>
+template <typename TI, int DK, int DV>
 hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
-  const size_t lds = sizeof(float) * DsLayout<DK>::total;
-  auto kern = bwd_dstate_kernel<TI, DK>;
+  const size_t lds = sizeof(float) * DsLayout<DK, DV>::total;
+  auto kern = bwd_dstate_kernel<TI, DK, DV>;
   static bool configured = false;
   if (!configured) {
     const hipError_t e =
@@ -1108,10 +1106,10 @@ hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int64_t grid = (int64_t)p.num_seqs * p.num_heads * (p.dv / kDsCols);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDsThr), lds, stream, (const TI*)p.q,
+  const int64_t grid = (int64_t)p.num_seqs * p.num_heads;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(4 * DV), lds, stream, (const TI*)p.q,
                      (const TI*)p.k, (const TI*)p.a, (const TI*)p.b, (const TI*)p.gate, p.dy,
-                     p.cu_seqlens, p.cbase, p.d_final_state, p.dse, p.d_s0, p.num_heads, p.dv);
+                     p.cu_seqlens, p.cbase, p.d_final_state, p.dse, p.d_s0, p.num_heads);
   return hipGetLastError();
 }
 
@@ -1164,7 +1162,10 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
     if ((e = device_side_stream(stream, &s2)) != hipSuccess) return e;
     if ((e = hipEventRecord(ev->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, ev->fork, 0)) != hipSuccess) return e;
-    e = p.dk == 128 ? launch_dstate<TI, 128>(p, s2) : launch_dstate<TI, 64>(p, s2);
+    if (p.dk == 128)
+      e = p.dv == 128 ? launch_dstate<TI, 128, 128>(p, s2) : launch_dstate<TI, 128, 64>(p, s2);
+    else
+      e = p.dv == 128 ? launch_dstate<TI, 64, 128>(p, s2) : launch_dstate<TI, 64, 64>(p, s2);
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ev->join, s2)) != hipSuccess) return e;
     if ((e = launch_fwd_chunked(f, stream)) != hipSuccess) return e;
