@@ -741,6 +741,10 @@ kda_status kda_bwd_chunked(const kda_shape* shape, const void* q, const void* k,
   if (s.num_seqs == 0) return s.total_tokens == 0 ? KDA_OK : KDA_ERR_BAD_SHAPE;
   const BwdLayout w = bwd_layout(s);
   if (w.total > uint64_t(kMaxElems)) return KDA_ERR_BAD_SHAPE;
+  // the chunked form launches one workgroup per (chunk, head)
+  if (w.chunked && (s.total_tokens / kda::bwd_chunk_len() + s.num_seqs) * int64_t(s.num_heads) >
+                       int64_t(0x7fffffff))
+    return KDA_ERR_BAD_SHAPE;
   if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
   if (s.total_tokens > 0 &&
       (!q || !k || !v || !a || !b || !dy || !dq || !dk || !dv || !da || !db))

@@ -1080,12 +1080,12 @@ template <typename TI, int DK, int DV>
 hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) {
   const size_t lds = sizeof(float) * GrLayout<DK, DV>::total;
   auto kern = bwd_chunk_kernel<TI, DK, DV>;
-  static bool configured = false;  // raising the dynamic LDS limit is idempotent
-  if (!configured) {
+  // Dynamic LDS above the default limit: set on every call (the attribute is
+  // the device's, and a process may drive several devices or threads).
+  {
     const hipError_t e =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGrThr), lds, stream, (const TI*)p.q,
                      (const TI*)p.k, (const TI*)p.v, (const TI*)p.a, (const TI*)p.b,
@@ -1099,12 +1099,12 @@ template <typename TI, int DK, int DV>
 hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
   const size_t lds = sizeof(float) * DsLayout<DK, DV>::total;
   auto kern = bwd_dstate_kernel<TI, DK, DV>;
-  static bool configured = false;
-  if (!configured) {
+  // Dynamic LDS above the default limit: set on every call (the attribute is
+  // the device's, and a process may drive several devices or threads).
+  {
     const hipError_t e =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   const int64_t grid = (int64_t)p.num_seqs * p.num_heads;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(4 * DV), lds, stream, (const TI*)p.q,

@@ -538,12 +538,12 @@ template <typename TI, int DK, class Pol>
 hipError_t launch_t(const FwdArgs& p, hipStream_t stream) {
   const size_t lds = sizeof(float) * Layout<DK>::total;
   auto kern = chunk_fwd_kernel<TI, DK, Pol>;
-  static bool configured = false;  // raising the dynamic LDS limit is idempotent
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // Dynamic LDS above the default limit: set on every call (the attribute is
+  // the device's, and a process may drive several devices or threads).
+  {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   const bool tr = p.transition != nullptr;
   const int sdv = tr ? p.dv + p.dk : p.dv;
