@@ -678,7 +678,7 @@ constexpr int32_t kBwdSlice = 8;  // state columns per token-form wavefront
 // partial sums and sub-chunk start states.
 struct BwdLayout {
   bool chunked;
-  uint64_t ckpt, o_raw, p_dqh, p_dkh, p_dal, p_dbeta, sub, dse, cbase, kbase, total;
+  uint64_t ckpt, o_raw, p_dqh, p_dkh, p_dal, p_dbeta, sub, dse, crec, cbase, kbase, total;
   int64_t slots;
 };
 
@@ -694,7 +694,10 @@ BwdLayout bwd_layout(const kda_shape& s) {
     w.o_raw = round_up(uint64_t(w.slots) * st, 256);
     w.dse = w.o_raw + round_up(th * s.dv * 4, 256);
     const uint64_t chunks = uint64_t(s.total_tokens / cl + s.num_seqs);  // >= sum of ceil(L_n / cl)
-    w.cbase = w.dse + round_up(chunks * st, 256);
+    w.crec = w.dse + round_up(chunks * st, 256);
+    w.cbase = w.crec + round_up(chunks * uint64_t(s.num_heads) *
+                                    uint64_t(kda::bwd_chain_record_floats(s.dk)) * 4,
+                                256);
     w.kbase = w.cbase + round_up(uint64_t(s.num_seqs + 1) * 4, 256);
     w.total = w.kbase + round_up(uint64_t(s.num_seqs + 1) * 4, 256);
     return w;
@@ -800,6 +803,7 @@ kda_status kda_bwd_chunked(const kda_shape* shape, const void* q, const void* k,
     c.o_raw = reinterpret_cast<const float*>(base + w.o_raw);
     c.ckpt = reinterpret_cast<const float*>(base + w.ckpt);
     c.dse = reinterpret_cast<float*>(base + w.dse);
+    c.crec = reinterpret_cast<float*>(base + w.crec);
     c.cbase = reinterpret_cast<int32_t*>(base + w.cbase);
     c.kbase = reinterpret_cast<int32_t*>(base + w.kbase);
     c.dq_out = dq; c.dk_out = dk; c.dv_out = dv; c.da_out = da; c.db_out = db;

@@ -28,15 +28,20 @@
 // chunk give the gradient of g = -5 sigmoid(a); last the input maps (L2 norm,
 // sigmoid).
 //
-// Kernels (after the forward has recorded the state every 32 tokens and the
-// ungated output):
-//   bwd_plan_kernel      per-sequence chunk and recorded-state offsets
-//   bwd_dstate_kernel    the adjoint chain: one workgroup per (sequence,
-//                        head, 64 state columns) walks the chunks last to
-//                        first and stores dS_end of every chunk
-//   bwd_chunk_kernel     one workgroup per (chunk, head), all chunks in
-//                        parallel: every gradient of the chunk's tokens from
-//                        its start state and dS_end
+// Kernels:
+//   bwd_plan_kernel       per-sequence chunk and recorded-state offsets
+//   bwd_chainprep_kernel  one workgroup per (chunk, head), all in parallel:
+//                         the adjoint chain's chunk-local operands (Qbar^T,
+//                         (beta Kbar)^T, Kend, P^T, X^T, Gamma_end) as a record
+//   bwd_chain_kernel      the adjoint chain: one workgroup per (sequence,
+//                         head) walks the chunks last to first over the
+//                         records and stores dS_end of every chunk
+//   bwd_chunk_kernel      one workgroup per (chunk, head), all in parallel:
+//                         every gradient of the chunk's tokens from its start
+//                         state (recorded by the forward every 32 tokens) and
+//                         dS_end
+// The first three need no forward state: they run on the device's second
+// stream beside the forward recomputation.
 #include <mutex>
 
 #include "kda_device.h"
@@ -405,20 +410,27 @@ __device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const
 }
 
 // ---------------------------------------------------------------------------
-// The adjoint chain.  Workgroup (sequence, head): one wave per 16 columns of
-// d_v (8 at d_v = 128), so the chunk's preparation is done once per head and
-// two waves share each SIMD; wave w owns columns 16 w .. 16 w + 15 and holds
-// those columns
-// of dS (d_k rows) in matrix-core result tiles: dS[ct] = rows 16 ct + 4 g +
-// 0..3, column 16 w + li.  Per chunk, last first: store dS (= dS_end of the
-// chunk), then
-//   Y = P^T dO + Kend dS,  Z = X^T Y,  dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z.
-// The operands read along the chunk's rows are kept transposed (P^T, X^T,
-// Qbar^T, (beta Kbar)^T, dO^T), so that every matrix-core operand is a
-// contiguous LDS read.
+// The adjoint chain, in two kernels.  Per chunk it needs only chunk-local
+// operands besides dS:
+//   Y = P^T dO + Kend dS,  Z = X^T Y,  dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z,
+// so bwd_chainprep_kernel forms them for every (chunk, head) in parallel and
+// stores them as a chain record, and bwd_chain_kernel walks each head's
+// chunks last to first reading the records (the next chunk's record and dO
+// are fetched while the current chunk is processed).
+// Record, fp32 (the operands read along the chunk's rows transposed, so that
+// every matrix-core operand is a contiguous read):
+//   Qbar^T [DK][32] | (beta Kbar)^T [DK][32] | Kend [32][DK] | P^T [32][32] |
+//   X^T [32][32] | Gamma_end [DK]
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
-struct DsLayout {
+template <int DK>
+struct ChainRec {
+  static constexpr int oQbT = 0, oKbT = DK * kCB, oKe = 2 * DK * kCB, oPT = 3 * DK * kCB,
+                       oXT = oPT + kCB * kCB, oGe = oXT + kCB * kCB, floats = oGe + DK;
+  static_assert(floats % 4 == 0, "float4 copies");
+};
+
+template <int DK>
+struct PrepLayout {
   static constexpr int LDK = DK + 4;
   static constexpr int oB = 0;
   static constexpr int oQt = oB + kCB * LDK;
@@ -432,8 +444,7 @@ struct DsLayout {
   static constexpr int oX = oPT + kCB * kL32;
   static constexpr int oXT = oX + kCB * kL32;
   static constexpr int oT = oXT + kCB * kL32;    // 16 x 16 scratch
-  static constexpr int oDOT = oT + 256;          // dO^T [DV][32]
-  static constexpr int oE = oDOT + DV * kL32;
+  static constexpr int oE = oT + 256;
   static constexpr int oF = oE + 2 * DK;
   static constexpr int oF2 = oF + 2 * DK;
   static constexpr int oD = oF2 + 2 * DK;
@@ -443,18 +454,19 @@ struct DsLayout {
   static_assert(total * 4 <= 160 * 1024, "LDS budget");
 };
 
-template <typename TI, int DK, int DV>
-__global__ void __launch_bounds__(4 * DV)
-    bwd_dstate_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
-                      const TI* __restrict__ a, const TI* __restrict__ bl,
-                      const TI* __restrict__ gate, const float* __restrict__ dy,
-                      const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
-                      const float* __restrict__ d_sfinal, float* __restrict__ dse,
-                      float* __restrict__ d_s0, int H) {
-  using Ly = DsLayout<DK, DV>;
-  constexpr int kDsThr = 4 * DV;  // 64 lanes per 16 columns
+constexpr int kPrepThr = 512;
+
+// Chain records of every (chunk, head): workgroup (chunk, head), 8 waves.
+template <typename TI, int DK>
+__global__ void __launch_bounds__(kPrepThr)
+    bwd_chainprep_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+                         const TI* __restrict__ a, const TI* __restrict__ bl,
+                         const int32_t* __restrict__ cu_seqlens,
+                         const int32_t* __restrict__ cbase, float* __restrict__ crec, int N,
+                         int H) {
+  using Ly = PrepLayout<DK>;
+  using R = ChainRec<DK>;
   constexpr int LDK = Ly::LDK;
-  constexpr int NCT = DK / 16, NKB = DK / 32;
   extern __shared__ float smem[];
   float* sB = smem + Ly::oB;
   float* sQt = smem + Ly::oQt;
@@ -468,7 +480,6 @@ __global__ void __launch_bounds__(4 * DV)
   float* sX = smem + Ly::oX;
   float* sXT = smem + Ly::oXT;
   float* sT = smem + Ly::oT;
-  float* sDOT = smem + Ly::oDOT;
   float* sE = smem + Ly::oE;
   float* sF = smem + Ly::oF;
   float* sF2 = smem + Ly::oF2;
@@ -476,85 +487,221 @@ __global__ void __launch_bounds__(4 * DV)
   float* sGe = smem + Ly::oGe;
   float* sBeta = smem + Ly::oBeta;
 
+  const int ci = blockIdx.x / H, h = blockIdx.x % H;
+  if (ci >= cbase[N]) return;  // the grid covers an upper bound of the chunk count
+  int lo = 0, hi = N;          // the sequence n with cbase[n] <= ci < cbase[n + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cbase[mid] <= ci) lo = mid; else hi = mid;
+  }
+  const int n = lo;
+  const int m = ci - cbase[n];
+  const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
+  const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
+  const int64_t c0 = tok_beg + (int64_t)kCB * m;
+  const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+
+  if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
+  chunk_prep<TI, DK, kPrepThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
+  if (wave == 6) zero_upper(lane, sP, sPT);
+  lds_barrier();
+  solve_x(wave, lane, g, li, sM, sBeta, true, sX, sXT, sT);
+  // Qbar^T, (beta Kbar)^T, Kend in place (thread: row idx % 32, channels
+  // 4 (idx / 32) + 0..3: row reads and transposed writes both spread over the
+  // LDS banks)
+  for (int idx = t; idx < kCB * DK / 4; idx += kPrepThr) {
+    const int row = idx % kCB, c = 4 * (idx / kCB), tt = row / kTl;
+    const float br = sBeta[row];
+    const float4 e = *reinterpret_cast<const float4*>(sE + tt * DK + c);
+    const float4 f = *reinterpret_cast<const float4*>(sF + tt * DK + c);
+    const float4 f2 = *reinterpret_cast<const float4*>(sF2 + tt * DK + c);
+    const float4 qv = *reinterpret_cast<const float4*>(sQt + row * LDK + c);
+    const float4 kv = *reinterpret_cast<const float4*>(sKt + row * LDK + c);
+    float4* kh = reinterpret_cast<float4*>(sKh + row * LDK + c);
+    const float4 hv = *kh;
+    sQbT[(c + 0) * kL32 + row] = qv.x * e.x;
+    sQbT[(c + 1) * kL32 + row] = qv.y * e.y;
+    sQbT[(c + 2) * kL32 + row] = qv.z * e.z;
+    sQbT[(c + 3) * kL32 + row] = qv.w * e.w;
+    sKbT[(c + 0) * kL32 + row] = kv.x * e.x * br;
+    sKbT[(c + 1) * kL32 + row] = kv.y * e.y * br;
+    sKbT[(c + 2) * kL32 + row] = kv.z * e.z * br;
+    sKbT[(c + 3) * kL32 + row] = kv.w * e.w * br;
+    *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
+  }
+  lds_barrier();
+  float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
+  for (int i4 = t; i4 < R::floats / 4; i4 += kPrepThr) {
+    const int e = 4 * i4;
+    const float* src;
+    if (e < R::oKbT) {
+      src = sQbT + (e / kCB) * kL32 + e % kCB;
+    } else if (e < R::oKe) {
+      src = sKbT + ((e - R::oKbT) / kCB) * kL32 + (e - R::oKbT) % kCB;
+    } else if (e < R::oPT) {
+      src = sKh + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
+    } else if (e < R::oXT) {
+      src = sPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
+    } else if (e < R::oGe) {
+      src = sXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
+    } else {
+      src = sGe + (e - R::oGe);
+    }
+    *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src);
+  }
+}
+
+// The chain: workgroup (sequence, head), one wave per 16 columns of d_v; wave
+// w holds columns 16 w .. 16 w + 15 of dS (d_k rows) in matrix-core result
+// tiles: dS[ct] = rows 16 ct + 4 g + 0..3, column 16 w + li.  Two LDS buffers
+// of [record | dO^T]; per chunk, last first: store dS (= dS_end of the
+// chunk), request the next chunk's record and dO, run the chain on this
+// chunk's buffer, then write the requested data to the other buffer.
+template <int DK, int DV>
+struct ChainLayout {
+  static constexpr int LDK = DK + 4;
+  static constexpr int oQbT = 0;                 // [DK][36]
+  static constexpr int oKbT = oQbT + DK * kL32;  // [DK][36]
+  static constexpr int oKe = oKbT + DK * kL32;   // [32][LDK]
+  static constexpr int oPT = oKe + kCB * LDK;    // [32][36]
+  static constexpr int oXT = oPT + kCB * kL32;   // [32][36]
+  static constexpr int oGe = oXT + kCB * kL32;   // [DK]
+  static constexpr int oDOT = oGe + DK;          // dO^T [DV][36]
+  static constexpr int buf = oDOT + DV * kL32;   // floats per buffer
+  static constexpr int total = 2 * buf;
+  static_assert(total * 4 <= 160 * 1024, "LDS budget");
+};
+
+template <typename TI, int DK, int DV>
+__device__ __forceinline__ void chain_fetch(const float* __restrict__ src,
+                                            const TI* __restrict__ gate,
+                                            const float* __restrict__ dy, int64_t tok_beg,
+                                            int64_t tok_end, int m, int H, int h, int t,
+                                            f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
+                                            float (&d8)[8], float (&g8)[8], bool& have_row) {
+  using R = ChainRec<DK>;
+  constexpr int NTHR = 4 * DV;
+  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;
+#pragma unroll
+  for (int i = 0; i < NR4; ++i) {
+    const int i4 = t + NTHR * i;
+    if (NTHR * (i + 1) <= R::floats / 4 || i4 < R::floats / 4)
+      rv[i] = *reinterpret_cast<const f32x4_t*>(src + 4 * i4);
+  }
+  const int64_t c0 = tok_beg + (int64_t)kCB * m;
+  const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+  const int row = t % kCB, seg = t / kCB;
+  have_row = row < nrows;
+  if (have_row) {
+    const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + seg * 8;
+    ld8(dy + off, d8);
+    if (gate) ld8(gate + off, g8);
+  }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void chain_stash(float* b, int t, bool gated,
+                                            const f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
+                                            const float (&d8)[8], const float (&g8)[8],
+                                            bool have_row) {
+  using R = ChainRec<DK>;
+  using Ly = ChainLayout<DK, DV>;
+  constexpr int NTHR = 4 * DV;
+  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;
+  constexpr int LDK = Ly::LDK;
+#pragma unroll
+  for (int i = 0; i < NR4; ++i) {
+    const int i4 = t + NTHR * i;
+    if (NTHR * (i + 1) <= R::floats / 4 || i4 < R::floats / 4) {
+      const int e = 4 * i4;
+      float* d;
+      if (e < R::oKbT) {
+        d = b + Ly::oQbT + (e / kCB) * kL32 + e % kCB;
+      } else if (e < R::oKe) {
+        d = b + Ly::oKbT + ((e - R::oKbT) / kCB) * kL32 + (e - R::oKbT) % kCB;
+      } else if (e < R::oPT) {
+        d = b + Ly::oKe + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
+      } else if (e < R::oXT) {
+        d = b + Ly::oPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
+      } else if (e < R::oGe) {
+        d = b + Ly::oXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
+      } else {
+        d = b + Ly::oGe + (e - R::oGe);
+      }
+      *reinterpret_cast<f32x4_t*>(d) = rv[i];
+    }
+  }
+  const int row = t % kCB, seg = t / kCB;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    b[Ly::oDOT + (seg * 8 + j) * kL32 + row] =
+        have_row ? (gated ? d8[j] * sigm(g8[j]) : d8[j]) : 0.f;
+}
+
+template <typename TI, int DK, int DV>
+__global__ void __launch_bounds__(4 * DV)
+    bwd_chain_kernel(const TI* __restrict__ gate, const float* __restrict__ dy,
+                     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
+                     const float* __restrict__ crec, const float* __restrict__ d_sfinal,
+                     float* __restrict__ dse, float* __restrict__ d_s0, int H) {
+  using Ly = ChainLayout<DK, DV>;
+  using R = ChainRec<DK>;
+  constexpr int NTHR = 4 * DV;  // 64 lanes per 16 columns
+  constexpr int LDK = Ly::LDK;
+  constexpr int NCT = DK / 16, NKB = DK / 32;
+  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;  // record float4 per thread
+  extern __shared__ float smem[];
+
   const int item = blockIdx.x;
   const int n = item / H, h = item % H;
-  constexpr int j0 = 0;
   const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
   const int jl = 16 * wave + li;  // this lane's column
-  const int jcol = j0 + jl;
   const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
   const int64_t st_off = (int64_t)item * DK * DV;
   const int nch = (int)((tok_end - tok_beg + kCB - 1) / kCB);
   const int64_t cb0 = cbase[n];
 
+  // The data of chunk m in registers: its record and this thread's 8 values
+  // of dy and gate (row t % 32, columns 8 (t / 32) + 0..7), requested by
+  // chain_fetch() and used only in chain_stash() (dO = dy sigmoid(gate) formed
+  // there), so the loads stay in flight during the chain.
+  f32x4_t rv[NR4];  // (native vectors: an array of HIP's float4 class stays in scratch)
+  float d8[8], g8[8];
+  bool have_row = false;
   f32x4_t dS[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-      dS[ct][jj] = d_sfinal ? d_sfinal[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] : 0.f;
+      dS[ct][jj] = d_sfinal ? d_sfinal[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jl] : 0.f;
 
+  if (nch > 0) {
+    chain_fetch<TI, DK, DV>(crec + ((cb0 + nch - 1) * H + h) * (int64_t)R::floats, gate, dy,
+                            tok_beg, tok_end, nch - 1, H, h, t, rv, d8, g8, have_row);
+    chain_stash<DK, DV>(smem + ((nch - 1) & 1) * Ly::buf, t, gate != nullptr, rv, d8, g8, have_row);
+    lds_barrier();
+  }
   for (int m = nch - 1; m >= 0; --m) {
-    const int64_t c0 = tok_beg + (int64_t)kCB * m;
-    const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+    const float* b = smem + (m & 1) * Ly::buf;
+    const float* sQbT = b + Ly::oQbT;
+    const float* sKbT = b + Ly::oKbT;
+    const float* sKe = b + Ly::oKe;
+    const float* sPT = b + Ly::oPT;
+    const float* sXT = b + Ly::oXT;
+    const float* sGe = b + Ly::oGe;
+    const float* sDOT = b + Ly::oDOT;
     // dS_end of this chunk
     {
       float* dst = dse + ((cb0 + m) * H + h) * (int64_t)DK * DV;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = dS[ct][jj];
+        for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * ct + 4 * g + jj) * DV + jl] = dS[ct][jj];
     }
-    // dO^T (thread: row t % 32, 8 columns) and beta
-    {
-      const int row = t % kCB, seg = t / kCB;  // kCB rows x DV / 8 segments = every thread
-      float d8[8];
-      if (row < nrows) {
-        const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + j0 + seg * 8;
-        ld8(dy + off, d8);
-        if (gate) {
-          float g8[8];
-          ld8(gate + off, g8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) d8[j] *= sigm(g8[j]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d8[j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sDOT[(seg * 8 + j) * kL32 + row] = d8[j];
-    }
-    if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
-    chunk_prep<TI, DK, kDsThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
-    key_products<DK>(wave, kDsThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
-    if (wave == 3) zero_upper(lane, sP, sPT);
-    lds_barrier();
-    solve_x(wave, lane, g, li, sM, sBeta, true, sX, sXT, sT);
-    // The operands of the chain: Qbar^T, (beta Kbar)^T, Kend in place.
-    // (thread: row idx % 32, channels 4 (idx / 32) + 0..3: row reads and
-    // transposed writes both spread over the LDS banks)
-    for (int idx = t; idx < kCB * DK / 4; idx += kDsThr) {
-      const int row = idx % kCB, c = 4 * (idx / kCB), tt = row / kTl;
-      const float br = sBeta[row];
-      const float4 e = *reinterpret_cast<const float4*>(sE + tt * DK + c);
-      const float4 f = *reinterpret_cast<const float4*>(sF + tt * DK + c);
-      const float4 f2 = *reinterpret_cast<const float4*>(sF2 + tt * DK + c);
-      const float4 qv = *reinterpret_cast<const float4*>(sQt + row * LDK + c);
-      const float4 kv = *reinterpret_cast<const float4*>(sKt + row * LDK + c);
-      float4* kh = reinterpret_cast<float4*>(sKh + row * LDK + c);
-      const float4 hv = *kh;
-      sQbT[(c + 0) * kL32 + row] = qv.x * e.x;
-      sQbT[(c + 1) * kL32 + row] = qv.y * e.y;
-      sQbT[(c + 2) * kL32 + row] = qv.z * e.z;
-      sQbT[(c + 3) * kL32 + row] = qv.w * e.w;
-      sKbT[(c + 0) * kL32 + row] = kv.x * e.x * br;
-      sKbT[(c + 1) * kL32 + row] = kv.y * e.y * br;
-      sKbT[(c + 2) * kL32 + row] = kv.z * e.z * br;
-      sKbT[(c + 3) * kL32 + row] = kv.w * e.w * br;
-      *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
-    }
-    lds_barrier();
+    if (m > 0)
+      chain_fetch<TI, DK, DV>(crec + ((cb0 + m - 1) * H + h) * (int64_t)R::floats, gate, dy,
+                              tok_beg, tok_end, m - 1, H, h, t, rv, d8, g8, have_row);
 
     F8 dOf;  // column jl of dO, rows 8 g + 0..7
     {
@@ -580,7 +727,7 @@ __global__ void __launch_bounds__(4 * DV)
       mma3(Y[tt], av, dOf);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        lds44f(sKh + (16 * tt + li) * LDK + 32 * kb + 4 * g, av);
+        lds44f(sKe + (16 * tt + li) * LDK + 32 * kb + 4 * g, av);
         mma3(Y[tt], av, dSf[kb]);
       }
     }
@@ -623,14 +770,17 @@ __global__ void __launch_bounds__(4 * DV)
       mma3(acc, av, zf);
       dS[ct] = acc;
     }
-    lds_barrier();  // LDS is rewritten by the next chunk
+    if (m > 0)
+      chain_stash<DK, DV>(smem + ((m - 1) & 1) * Ly::buf, t, gate != nullptr, rv, d8, g8,
+                          have_row);
+    lds_barrier();  // the next chunk's buffer is complete; this one is free
   }
   if (d_s0) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        d_s0[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jcol] = dS[ct][jj];
+        d_s0[st_off + (int64_t)(16 * ct + 4 * g + jj) * DV + jl] = dS[ct][jj];
   }
 }
 
@@ -1095,10 +1245,10 @@ hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <typename TI, int DK, int DV>
-hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
-  const size_t lds = sizeof(float) * DsLayout<DK, DV>::total;
-  auto kern = bwd_dstate_kernel<TI, DK, DV>;
+template <typename TI, int DK>
+hipError_t launch_chainprep(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) {
+  const size_t lds = sizeof(float) * PrepLayout<DK>::total;
+  auto kern = bwd_chainprep_kernel<TI, DK>;
   // Dynamic LDS above the default limit: set on every call (the attribute is
   // the device's, and a process may drive several devices or threads).
   {
@@ -1106,10 +1256,25 @@ hipError_t launch_dstate(const BwdChunkArgs& p, hipStream_t stream) {
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThr), lds, stream, (const TI*)p.q,
+                     (const TI*)p.k, (const TI*)p.a, (const TI*)p.b, p.cu_seqlens, p.cbase,
+                     p.crec, p.num_seqs, p.num_heads);
+  return hipGetLastError();
+}
+
+template <typename TI, int DK, int DV>
+hipError_t launch_chain(const BwdChunkArgs& p, hipStream_t stream) {
+  const size_t lds = sizeof(float) * ChainLayout<DK, DV>::total;
+  auto kern = bwd_chain_kernel<TI, DK, DV>;
+  {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int64_t grid = (int64_t)p.num_seqs * p.num_heads;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(4 * DV), lds, stream, (const TI*)p.q,
-                     (const TI*)p.k, (const TI*)p.a, (const TI*)p.b, (const TI*)p.gate, p.dy,
-                     p.cu_seqlens, p.cbase, p.d_final_state, p.dse, p.d_s0, p.num_heads);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(4 * DV), lds, stream, (const TI*)p.gate,
+                     p.dy, p.cu_seqlens, p.cbase, p.crec, p.d_final_state, p.dse, p.d_s0,
+                     p.num_heads);
   return hipGetLastError();
 }
 
@@ -1162,10 +1327,16 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
     if ((e = device_side_stream(stream, &s2)) != hipSuccess) return e;
     if ((e = hipEventRecord(ev->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, ev->fork, 0)) != hipSuccess) return e;
+    const int64_t cgrid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
+    if (cgrid > 0) {
+      e = p.dk == 128 ? launch_chainprep<TI, 128>(p, cgrid, s2)
+                      : launch_chainprep<TI, 64>(p, cgrid, s2);
+      if (e != hipSuccess) return e;
+    }
     if (p.dk == 128)
-      e = p.dv == 128 ? launch_dstate<TI, 128, 128>(p, s2) : launch_dstate<TI, 128, 64>(p, s2);
+      e = p.dv == 128 ? launch_chain<TI, 128, 128>(p, s2) : launch_chain<TI, 128, 64>(p, s2);
     else
-      e = p.dv == 128 ? launch_dstate<TI, 64, 128>(p, s2) : launch_dstate<TI, 64, 64>(p, s2);
+      e = p.dv == 128 ? launch_chain<TI, 64, 128>(p, s2) : launch_chain<TI, 64, 64>(p, s2);
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ev->join, s2)) != hipSuccess) return e;
     if ((e = launch_fwd_chunked(f, stream)) != hipSuccess) return e;
@@ -1183,6 +1354,9 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
 }  // namespace
 
 int bwd_chunk_len() { return kCB; }
+int bwd_chain_record_floats(int dk) {
+  return dk == 128 ? ChainRec<128>::floats : ChainRec<64>::floats;
+}
 
 hipError_t launch_bwd_chunked(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream) {
   if ((int64_t)p.num_seqs * p.num_heads == 0) return launch_fwd_chunked(f, stream);

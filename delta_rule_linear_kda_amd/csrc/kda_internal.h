@@ -150,10 +150,13 @@ struct BwdChunkArgs {
   const float* o_raw;           // [T, H, dv] ungated forward output
   const float* ckpt;            // states after every bwd_chunk_len() tokens of each sequence
   float* dse;                   // [T / len + N, H, dk, dv]: adjoint state at each chunk's end
+  float* crec;                  // [T / len + N, H, bwd_chain_record_floats(dk)]: chain operands
   int32_t *cbase, *kbase;       // [N + 1] each: chunk and recorded-state offsets
   float *dq_out, *dk_out, *dv_out, *da_out, *db_out, *dgate_out, *d_s0;  // dgate, d_s0 may be null
 };
 int bwd_chunk_len();
+// fp32 values per (chunk, head) of the adjoint chain's operand record.
+int bwd_chain_record_floats(int dk);
 // Enqueues the whole chunked backward on `stream`: the chunk plan, the
 // adjoint chain on the device's second stream beside the forward `f` (which
 // records the states and the ungated output the gradients read), then the
