@@ -40,8 +40,8 @@
 //                         every gradient of the chunk's tokens from its start
 //                         state (recorded by the forward every 32 tokens) and
 //                         dS_end
-// The first three need no forward state: they run on the device's second
-// stream beside the forward recomputation.
+// The first three need no forward state: the chain runs on the device's
+// second stream beside the forward recomputation.
 #include <mutex>
 
 #include "kda_device.h"
@@ -137,6 +137,14 @@ __device__ __forceinline__ void lds44f(const float* p, float (&x)[8]) {
   const float4 w = *reinterpret_cast<const float4*>(p + 16);
   x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
   x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+
+// Element offset of the 4-row run (rows 16 ct + 4 (l / 16) + 0..3, column
+// 16 w + l % 16) in the tile layout of a [DK][DV] adjoint state: runs ordered
+// by row tile ct, then column tile w, then lane l, so that a wave storing its
+// result tiles writes 1 KB contiguous per tile.
+__device__ __forceinline__ int64_t dse_tile(int ct, int w, int l, int DV) {
+  return ((int64_t)(ct * (DV / 16) + w) * 64 + l) * 4;
 }
 
 // Chunk offsets per sequence: cbase[n] = sum over m < n of ceil(L_m / 32)
@@ -432,33 +440,33 @@ struct ChainRec {
 template <int DK>
 struct PrepLayout {
   static constexpr int LDK = DK + 4;
+  // The chunk-local cumsum b during the preparation; once the scaled operands
+  // are formed, Mkk, P, P^T and the solve's 16 x 16 scratch in its place.
   static constexpr int oB = 0;
-  static constexpr int oQt = oB + kCB * LDK;
+  static constexpr int oM = 0, oP = oM + kCB * kL32, oPT = oP + kCB * kL32, oT = oPT + kCB * kL32;
+  static constexpr int r0 = kCB * LDK > oT + 256 ? kCB * LDK : oT + 256;
+  static constexpr int oQt = oB + r0;
   static constexpr int oKt = oQt + kCB * LDK;
   static constexpr int oKh = oKt + kCB * LDK;    // Kh, then Kend
-  static constexpr int oQbT = oKh + kCB * LDK;   // Qbar^T [DK][32]
-  static constexpr int oKbT = oQbT + DK * kL32;  // (beta Kbar)^T [DK][32]
-  static constexpr int oM = oKbT + DK * kL32;    // diag(beta) Mkk
-  static constexpr int oP = oM + kCB * kL32;
-  static constexpr int oPT = oP + kCB * kL32;
-  static constexpr int oX = oPT + kCB * kL32;
+  static constexpr int oX = oKh + kCB * LDK;
   static constexpr int oXT = oX + kCB * kL32;
-  static constexpr int oT = oXT + kCB * kL32;    // 16 x 16 scratch
-  static constexpr int oE = oT + 256;
+  // Factor tables: exp(p_0) (tile 0 of E) and exp(b_end - e_1) (tile 1 of
+  // F2) are both all ones and share storage: [F2 tile 0 | ones | E tile 1].
+  static constexpr int oF2 = oXT + kCB * kL32;
+  static constexpr int oE = oF2 + DK;
   static constexpr int oF = oE + 2 * DK;
-  static constexpr int oF2 = oF + 2 * DK;
-  static constexpr int oD = oF2 + 2 * DK;
+  static constexpr int oD = oF + 2 * DK;
   static constexpr int oGe = oD + DK;
   static constexpr int oBeta = oGe + DK;
   static constexpr int total = oBeta + kCB;
-  static_assert(total * 4 <= 160 * 1024, "LDS budget");
+  static_assert(total * 4 <= 80 * 1024, "LDS budget: two workgroups per CU");
 };
 
 constexpr int kPrepThr = 512;
 
 // Chain records of every (chunk, head): workgroup (chunk, head), 8 waves.
 template <typename TI, int DK>
-__global__ void __launch_bounds__(kPrepThr)
+__global__ void __launch_bounds__(kPrepThr, 2)
     bwd_chainprep_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                          const TI* __restrict__ a, const TI* __restrict__ bl,
                          const int32_t* __restrict__ cu_seqlens,
@@ -472,8 +480,6 @@ __global__ void __launch_bounds__(kPrepThr)
   float* sQt = smem + Ly::oQt;
   float* sKt = smem + Ly::oKt;
   float* sKh = smem + Ly::oKh;
-  float* sQbT = smem + Ly::oQbT;
-  float* sKbT = smem + Ly::oKbT;
   float* sM = smem + Ly::oM;
   float* sP = smem + Ly::oP;
   float* sPT = smem + Ly::oPT;
@@ -507,9 +513,10 @@ __global__ void __launch_bounds__(kPrepThr)
   if (wave == 6) zero_upper(lane, sP, sPT);
   lds_barrier();
   solve_x(wave, lane, g, li, sM, sBeta, true, sX, sXT, sT);
-  // Qbar^T, (beta Kbar)^T, Kend in place (thread: row idx % 32, channels
-  // 4 (idx / 32) + 0..3: row reads and transposed writes both spread over the
-  // LDS banks)
+  // Qbar^T and (beta Kbar)^T straight into the record, Kend in place
+  // (thread: row idx % 32, channels 4 (idx / 32) + 0..3: row reads spread
+  // over the LDS banks, record writes coalesced along the rows)
+  float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
   for (int idx = t; idx < kCB * DK / 4; idx += kPrepThr) {
     const int row = idx % kCB, c = 4 * (idx / kCB), tt = row / kTl;
     const float br = sBeta[row];
@@ -520,26 +527,22 @@ __global__ void __launch_bounds__(kPrepThr)
     const float4 kv = *reinterpret_cast<const float4*>(sKt + row * LDK + c);
     float4* kh = reinterpret_cast<float4*>(sKh + row * LDK + c);
     const float4 hv = *kh;
-    sQbT[(c + 0) * kL32 + row] = qv.x * e.x;
-    sQbT[(c + 1) * kL32 + row] = qv.y * e.y;
-    sQbT[(c + 2) * kL32 + row] = qv.z * e.z;
-    sQbT[(c + 3) * kL32 + row] = qv.w * e.w;
-    sKbT[(c + 0) * kL32 + row] = kv.x * e.x * br;
-    sKbT[(c + 1) * kL32 + row] = kv.y * e.y * br;
-    sKbT[(c + 2) * kL32 + row] = kv.z * e.z * br;
-    sKbT[(c + 3) * kL32 + row] = kv.w * e.w * br;
+    dst[R::oQbT + (c + 0) * kCB + row] = qv.x * e.x;
+    dst[R::oQbT + (c + 1) * kCB + row] = qv.y * e.y;
+    dst[R::oQbT + (c + 2) * kCB + row] = qv.z * e.z;
+    dst[R::oQbT + (c + 3) * kCB + row] = qv.w * e.w;
+    dst[R::oKbT + (c + 0) * kCB + row] = kv.x * e.x * br;
+    dst[R::oKbT + (c + 1) * kCB + row] = kv.y * e.y * br;
+    dst[R::oKbT + (c + 2) * kCB + row] = kv.z * e.z * br;
+    dst[R::oKbT + (c + 3) * kCB + row] = kv.w * e.w * br;
     *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
   }
   lds_barrier();
-  float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
-  for (int i4 = t; i4 < R::floats / 4; i4 += kPrepThr) {
+  // Kend, P^T, X^T, Gamma_end
+  for (int i4 = t + R::oKe / 4; i4 < R::floats / 4; i4 += kPrepThr) {
     const int e = 4 * i4;
     const float* src;
-    if (e < R::oKbT) {
-      src = sQbT + (e / kCB) * kL32 + e % kCB;
-    } else if (e < R::oKe) {
-      src = sKbT + ((e - R::oKbT) / kCB) * kL32 + (e - R::oKbT) % kCB;
-    } else if (e < R::oPT) {
+    if (e < R::oPT) {
       src = sKh + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
     } else if (e < R::oXT) {
       src = sPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
@@ -579,8 +582,9 @@ __device__ __forceinline__ void chain_fetch(const float* __restrict__ src,
                                             const float* __restrict__ dy, int64_t tok_beg,
                                             int64_t tok_end, int m, int H, int h, int t,
                                             f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
-                                            float (&d8)[8], float (&g8)[8], bool& have_row) {
+                                            float (&d8)[8], u32x4_t& g8, bool& have_row) {
   using R = ChainRec<DK>;
+  static_assert(sizeof(TI) == 2, "bf16 gate: 8 values in 16 bytes");
   constexpr int NTHR = 4 * DV;
   constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;
 #pragma unroll
@@ -596,14 +600,16 @@ __device__ __forceinline__ void chain_fetch(const float* __restrict__ src,
   if (have_row) {
     const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + seg * 8;
     ld8(dy + off, d8);
-    if (gate) ld8(gate + off, g8);
+    // the gate's raw 16-byte row piece: unpacked in chain_stash, so that no
+    // wait for the loads (and the stores before them) lands here
+    if (gate) g8 = *reinterpret_cast<const u32x4_t*>(gate + off);
   }
 }
 
 template <int DK, int DV>
 __device__ __forceinline__ void chain_stash(float* b, int t, bool gated,
                                             const f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
-                                            const float (&d8)[8], const float (&g8)[8],
+                                            const float (&d8)[8], const u32x4_t& g8,
                                             bool have_row) {
   using R = ChainRec<DK>;
   using Ly = ChainLayout<DK, DV>;
@@ -634,9 +640,10 @@ __device__ __forceinline__ void chain_stash(float* b, int t, bool gated,
   }
   const int row = t % kCB, seg = t / kCB;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    b[Ly::oDOT + (seg * 8 + j) * kL32 + row] =
-        have_row ? (gated ? d8[j] * sigm(g8[j]) : d8[j]) : 0.f;
+  for (int j = 0; j < 8; ++j) {
+    const float gv = __uint_as_float(j % 2 ? (g8[j / 2] & 0xFFFF0000u) : (g8[j / 2] << 16));
+    b[Ly::oDOT + (seg * 8 + j) * kL32 + row] = have_row ? (gated ? d8[j] * sigm(gv) : d8[j]) : 0.f;
+  }
 }
 
 template <typename TI, int DK, int DV>
@@ -667,7 +674,8 @@ __global__ void __launch_bounds__(4 * DV)
   // chain_fetch() and used only in chain_stash() (dO = dy sigmoid(gate) formed
   // there), so the loads stay in flight during the chain.
   f32x4_t rv[NR4];  // (native vectors: an array of HIP's float4 class stays in scratch)
-  float d8[8], g8[8];
+  float d8[8];
+  u32x4_t g8 = {0u, 0u, 0u, 0u};
   bool have_row = false;
   f32x4_t dS[NCT];
 #pragma unroll
@@ -691,13 +699,12 @@ __global__ void __launch_bounds__(4 * DV)
     const float* sXT = b + Ly::oXT;
     const float* sGe = b + Ly::oGe;
     const float* sDOT = b + Ly::oDOT;
-    // dS_end of this chunk
+    // dS_end of this chunk, in the tile layout (each wave writes 1 KB runs)
     {
       float* dst = dse + ((cb0 + m) * H + h) * (int64_t)DK * DV;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * ct + 4 * g + jj) * DV + jl] = dS[ct][jj];
+        *reinterpret_cast<f32x4_t*>(dst + dse_tile(ct, wave, lane, DV)) = dS[ct];
     }
     if (m > 0)
       chain_fetch<TI, DK, DV>(crec + ((cb0 + m - 1) * H + h) * (int64_t)R::floats, gate, dy,
@@ -912,13 +919,18 @@ __global__ void __launch_bounds__(kGrThr)
   float Sv[NKB][8], Ev[NKB][8];
   if (vwave) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t e = (int64_t)(32 * kb + 8 * g + j) * DV + jc;
-        Sv[kb][j] = S ? S[e] : 0.f;
-        Ev[kb][j] = dSe[e];
+      for (int j = 0; j < 8; ++j) Sv[kb][j] = S ? S[(int64_t)(32 * kb + 8 * g + j) * DV + jc] : 0.f;
+      // rows 32 kb + 8 g + 0..7 of column jc: two runs of 4 in the tile layout
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(
+            dSe + dse_tile(2 * kb + g / 2, wave, 16 * (2 * (g % 2) + hf) + li, DV));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Ev[kb][4 * hf + jj] = v4[jj];
       }
+    }
   }
   key_products<DK>(wave, kGrThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, false, sM, sP, sPT);
   if (wave == 6) zero_upper(lane, sP, sPT);
@@ -985,7 +997,11 @@ __global__ void __launch_bounds__(kGrThr)
 #pragma unroll
         for (int j = 0; j < 8; ++j) Sr[kb][j] = 0.f;
       }
-      ld8(dSe + e, Er[kb]);
+      // row jc, columns 32 kb + 8 g + 0..7 (tile layout: one element per run)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        Er[kb][j] = dSe[dse_tile(wave, 2 * kb + g / 2, 16 * (li / 4) + 8 * (g % 2) + j, DV) +
+                        li % 4];
     }
   }
   if (vwave) {
@@ -1317,9 +1333,17 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
                      p.num_seqs, p.cbase, p.kbase);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // The chain's operand records first, alone on the caller's stream (a
+  // parallel pass over every chunk); then the serial chain (one workgroup per
+  // head) on the second stream while the forward records the states on the
+  // caller's stream and fills the CUs the chain leaves idle.
+  const int64_t cgrid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
+  if (cgrid > 0) {
+    e = p.dk == 128 ? launch_chainprep<TI, 128>(p, cgrid, stream)
+                    : launch_chainprep<TI, 64>(p, cgrid, stream);
+    if (e != hipSuccess) return e;
+  }
   {
-    // the adjoint chain needs the plan only: it runs on the second stream
-    // while the forward records the states on the caller's stream
     std::lock_guard<std::mutex> lock(g_bwd_mu);
     BwdEvents* ev = nullptr;
     hipStream_t s2 = nullptr;
@@ -1327,12 +1351,6 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
     if ((e = device_side_stream(stream, &s2)) != hipSuccess) return e;
     if ((e = hipEventRecord(ev->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, ev->fork, 0)) != hipSuccess) return e;
-    const int64_t cgrid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
-    if (cgrid > 0) {
-      e = p.dk == 128 ? launch_chainprep<TI, 128>(p, cgrid, s2)
-                      : launch_chainprep<TI, 64>(p, cgrid, s2);
-      if (e != hipSuccess) return e;
-    }
     if (p.dk == 128)
       e = p.dv == 128 ? launch_chain<TI, 128, 128>(p, s2) : launch_chain<TI, 128, 64>(p, s2);
     else
@@ -1342,8 +1360,8 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
     if ((e = launch_fwd_chunked(f, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, ev->join, 0)) != hipSuccess) return e;
   }
-  const int64_t grid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
-  if (grid == 0) return hipSuccess;
+  if (cgrid == 0) return hipSuccess;
+  const int64_t grid = cgrid;
   if (p.dk == 128)
     return p.dv == 128 ? launch_grad<TI, 128, 128>(p, grid, stream)
                        : launch_grad<TI, 128, 64>(p, grid, stream);
@@ -1360,7 +1378,9 @@ int bwd_chain_record_floats(int dk) {
 
 hipError_t launch_bwd_chunked(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream) {
   if ((int64_t)p.num_seqs * p.num_heads == 0) return launch_fwd_chunked(f, stream);
-  return p.in_bf16 ? launch_t<uint16_t>(p, f, stream) : launch_t<float>(p, f, stream);
+  // bf16 inputs only (fp32 inputs run the token form, kda_bwd.hip)
+  if (!p.in_bf16) return hipErrorInvalidValue;
+  return launch_t<uint16_t>(p, f, stream);
 }
 
 }  // namespace kda

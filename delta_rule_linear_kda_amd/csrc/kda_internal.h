@@ -149,7 +149,7 @@ struct BwdChunkArgs {
   const float* d_final_state;   // may be null
   const float* o_raw;           // [T, H, dv] ungated forward output
   const float* ckpt;            // states after every bwd_chunk_len() tokens of each sequence
-  float* dse;                   // [T / len + N, H, dk, dv]: adjoint state at each chunk's end
+  float* dse;                   // [T / len + N, H, dk x dv]: adjoint state at each chunk's end (tile layout, kda_bwd_chunk.hip)
   float* crec;                  // [T / len + N, H, bwd_chain_record_floats(dk)]: chain operands
   int32_t *cbase, *kbase;       // [N + 1] each: chunk and recorded-state offsets
   float *dq_out, *dk_out, *dv_out, *da_out, *db_out, *dgate_out, *d_s0;  // dgate, d_s0 may be null
