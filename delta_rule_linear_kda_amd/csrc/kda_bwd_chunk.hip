@@ -56,6 +56,18 @@ constexpr int kL32 = kCB + 4;  // padded row stride of [32][32] tiles
 constexpr int kPlanThr = 256;
 
 __device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+// A bf16 input element loaded ahead of its use as the aligned 32-bit word that
+// holds it (element i of a row-major tensor with even rows), converted where
+// it is used: the empty asm keeps the compiler from moving the conversion (and
+// with it the wait for the load, which also covers every earlier request) up
+// to the load.
+__device__ __forceinline__ uint32_t word_of(const uint16_t* p, int64_t i) {
+  return *reinterpret_cast<const uint32_t*>(p + (i & ~(int64_t)1));
+}
+__device__ __forceinline__ float late_f32(uint32_t u, bool high) {
+  asm volatile("" : "+v"(u));
+  return __uint_as_float(high ? (u & 0xFFFF0000u) : (u << 16));
+}
 
 // Matrix-core products over one 32-wide block of the contraction index: lane
 // l supplies 8 values of row m = l % 16 of A and 8 of column n = l % 16 of B;
@@ -198,15 +210,50 @@ __global__ void __launch_bounds__(kPlanThr)
 // (e_tt = b at the tile's last row), sF2[tt] = exp(b_end - e_tt),
 // sD = exp(p_1 - p_0), sGe = exp(b_end).
 // ---------------------------------------------------------------------------
-template <typename TI, int DK, int NTHR>
-__device__ __forceinline__ void chunk_prep(const TI* __restrict__ q, const TI* __restrict__ k,
-                                           const TI* __restrict__ a, int64_t c0, int nrows, int H,
-                                           int h, float* sB, float* sQt, float* sKt, float* sKh,
-                                           float* sE, float* sF, float* sF2, float* sD,
-                                           float* sGe) {
+// The chunk's q, k, a rows as bf16 words (8 channels per thread and round),
+// requested ahead of the rest of the preparation so that their wait can be
+// shared with other requests; rows past the sequence's end read its last row
+// and are masked in chunk_prep.
+template <int DK, int NTHR>
+struct PrepRows {
+  static constexpr int NSEG = DK / 8;
+  static constexpr int NIT = (kCB * NSEG + NTHR - 1) / NTHR;
+  u32x4_t q[NIT], k[NIT], a[NIT];
+};
+template <int DK, int NTHR>
+__device__ __forceinline__ void prep_rows(const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ a, int64_t c0, int nrows,
+                                          int H, int h, PrepRows<DK, NTHR>& in) {
+  using PR = PrepRows<DK, NTHR>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < PR::NIT; ++it) {
+    const int idx = t + NTHR * it, row = idx / PR::NSEG, seg = idx % PR::NSEG;
+    if (idx < kCB * PR::NSEG) {  // uniform per wave: kCB * NSEG is a multiple of 64
+      const int rr = row < nrows ? row : nrows - 1;
+      const int64_t off = ((c0 + rr) * H + h) * (int64_t)DK + seg * 8;
+      in.q[it] = *reinterpret_cast<const u32x4_t*>(q + off);
+      in.k[it] = *reinterpret_cast<const u32x4_t*>(k + off);
+      in.a[it] = *reinterpret_cast<const u32x4_t*>(a + off);
+    }
+  }
+}
+__device__ __forceinline__ void unpack8(const u32x4_t& w, bool valid, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = valid ? __uint_as_float(w[i] << 16) : 0.f;
+    x[2 * i + 1] = valid ? __uint_as_float(w[i] & 0xFFFF0000u) : 0.f;
+  }
+}
+
+template <int DK, int NTHR>
+__device__ __forceinline__ void chunk_prep(const PrepRows<DK, NTHR>& in, int nrows, float* sB,
+                                           float* sQt, float* sKt, float* sKh, float* sE,
+                                           float* sF, float* sF2, float* sD, float* sGe) {
   constexpr int LDK = DK + 4;
   constexpr int NSEG = DK / 8;
-  constexpr int NIT = (kCB * NSEG + NTHR - 1) / NTHR;
+  constexpr int NIT = PrepRows<DK, NTHR>::NIT;
   const int t = threadIdx.x;
   float qh[NIT][8], kh[NIT][8];
 #pragma unroll
@@ -215,15 +262,9 @@ __device__ __forceinline__ void chunk_prep(const TI* __restrict__ q, const TI* _
     if (idx < kCB * NSEG) {  // uniform per wave: kCB * NSEG is a multiple of 64
       float qx[8], kx[8], ax[8];
       const bool valid = row < nrows;
-      if (valid) {
-        const int64_t off = ((c0 + row) * H + h) * (int64_t)DK + seg * 8;
-        ld8(q + off, qx);
-        ld8(k + off, kx);
-        ld8(a + off, ax);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qx[j] = kx[j] = ax[j] = 0.f;
-      }
+      unpack8(in.q[it], valid, qx);
+      unpack8(in.k[it], valid, kx);
+      unpack8(in.a[it], valid, ax);
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -507,8 +548,12 @@ __global__ void __launch_bounds__(kPrepThr, 2)
   const int64_t c0 = tok_beg + (int64_t)kCB * m;
   const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
 
-  if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
-  chunk_prep<TI, DK, kPrepThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  PrepRows<DK, kPrepThr> rows;
+  prep_rows<DK, kPrepThr>(q, k, a, c0, nrows, H, h, rows);
+  const int64_t eb = (c0 + (t < nrows ? t : nrows - 1)) * H + h;  // b of row t
+  const uint32_t bw = word_of(bl, eb);  // every thread: a valid row
+  if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
+  chunk_prep<DK, kPrepThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
   if (wave == 6) zero_upper(lane, sP, sPT);
   lds_barrier();
@@ -884,40 +929,66 @@ __global__ void __launch_bounds__(kGrThr)
   const bool kwave = wave < DK / 16;  // owns a column tile of d_k
   const int jc = 16 * wave + li;      // this lane's column (d_v or d_k)
 
-  // ---- loads: dO, dgate, beta; the chunk preparation ---------------------
-  for (int idx = t; idx < kCB * (DV / 8); idx += kGrThr) {
-    const int row = idx / (DV / 8), seg = idx % (DV / 8);
-    float d8[8];
-    if (row < nrows) {
-      const int64_t off = ((c0 + row) * H + h) * (int64_t)DV + seg * 8;
-      ld8(dy + off, d8);
-      if (gate) {
-        float g8[8], o8[8];
-        ld8(gate + off, g8);
-        ld8(o_raw + off, o8);
-        float dg8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float sg = sigm(g8[j]);
-          dg8[j] = d8[j] * o8[j] * sg * (1.f - sg);
-          d8[j] *= sg;
-        }
-        *reinterpret_cast<float4*>(dgate_out + off) = make_float4(dg8[0], dg8[1], dg8[2], dg8[3]);
-        *reinterpret_cast<float4*>(dgate_out + off + 4) = make_float4(dg8[4], dg8[5], dg8[6], dg8[7]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) d8[j] = 0.f;
+  // ---- loads: q, k, a, b, dO, dgate; the chunk preparation ---------------
+  // (requested together: one wait for all of them)
+  PrepRows<DK, kGrThr> rows;
+  prep_rows<DK, kGrThr>(q, k, a, c0, nrows, H, h, rows);
+  const int64_t eb = (c0 + (t < nrows ? t : nrows - 1)) * H + h;  // b of row t
+  const uint32_t bw = word_of(bl, eb);  // every thread: a valid row
+  // dO (with sigma(gate) applied) into LDS and dgate out: one 8-column
+  // segment per thread; rows past the end read the last row and are zeroed.
+  // Every LDS write comes before the dgate stores, so no later wait for a
+  // load of this prologue also waits for those stores.
+  constexpr int NDO = kCB * (DV / 8);
+  static_assert(NDO <= kGrThr, "one dO segment per thread");
+  const int drow = t / (DV / 8), dseg = t % (DV / 8);
+  const bool dthr = NDO == kGrThr || t < NDO;  // (a branch only when d_v < 128)
+  const bool dvalid = dthr && drow < nrows;
+  const int64_t doff =
+      ((c0 + (drow < nrows ? drow : nrows - 1)) * H + h) * (int64_t)DV + dseg * 8;
+  float d8[8], g8[8], o8[8];
+  if (dthr) {
+    ld8(dy + doff, d8);
+    if (gate) {
+      ld8(gate + doff, g8);
+      ld8(o_raw + doff, o8);
     }
-    *reinterpret_cast<float4*>(sDO + row * LDV + seg * 8) = make_float4(d8[0], d8[1], d8[2], d8[3]);
-    *reinterpret_cast<float4*>(sDO + row * LDV + seg * 8 + 4) = make_float4(d8[4], d8[5], d8[6], d8[7]);
   }
-  if (t < kCB) sBeta[t] = t < nrows ? sigm(ld_elem(bl, (c0 + t) * H + h)) : 0.f;
-  chunk_prep<TI, DK, kGrThr>(q, k, a, c0, nrows, H, h, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
+  float dg8[8];
+  if (dthr) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (gate) {
+        const float sg = sigm(g8[j]);
+        dg8[j] = d8[j] * o8[j] * sg * (1.f - sg);
+        d8[j] *= sg;
+      }
+      if (!dvalid) d8[j] = 0.f;
+    }
+    st8f(sDO + drow * LDV + dseg * 8, d8);
+  }
+  if (gate && dvalid) {
+    *reinterpret_cast<float4*>(dgate_out + doff) = make_float4(dg8[0], dg8[1], dg8[2], dg8[3]);
+    *reinterpret_cast<float4*>(dgate_out + doff + 4) = make_float4(dg8[4], dg8[5], dg8[6], dg8[7]);
+  }
+  chunk_prep<DK, kGrThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   // The value-side B operands, requested before the key products and the
   // solve for X: column jc of S and of dS_end, rows 32 kb + 8 g + 0..7.
   float Sv[NKB][8], Ev[NKB][8];
+  // v of this lane's rows r = 16 tt + 4 g + jj (clamped to the last row of the
+  // chunk, masked where used): unconditional, so the eight requests share one
+  // wait instead of one each.
+  static_assert(sizeof(TI) == 2, "bf16 inputs");
+  uint32_t vraw[2][4];  // bf16 bits
   if (vwave) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj, rr = r < nrows ? r : nrows - 1;
+        vraw[tt][jj] = word_of(v, ((c0 + rr) * H + h) * (int64_t)DV + jc);
+      }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -948,7 +1019,7 @@ __global__ void __launch_bounds__(kGrThr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj;
-        Vt[tt][jj] = r < nrows ? ld_elem(v, ((c0 + r) * H + h) * (int64_t)DV + jc) : 0.f;
+        Vt[tt][jj] = r < nrows ? late_f32(vraw[tt][jj], jc & 1) : 0.f;
         dU[tt][jj] = 0.f;
       }
 #pragma unroll
@@ -987,7 +1058,15 @@ __global__ void __launch_bounds__(kGrThr)
   // The d_k-side B operands of the next stage, requested now: row jc of S and
   // of dS_end, columns 32 kb + 8 g + 0..7.
   float Sr[NVB][8], Er[NVB][8];
+  uint32_t araw[2][4];  // bf16 bits of the decay logits of this lane's elements (rows as vraw, channel jc)
   if (kwave) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj, rr = r < nrows ? r : nrows - 1;
+        araw[tt][jj] = word_of(a, ((c0 + rr) * H + h) * (int64_t)DK + jc);
+      }
 #pragma unroll
     for (int kb = 0; kb < NVB; ++kb) {
       const int64_t e = (int64_t)jc * DV + 32 * kb + 8 * g;
@@ -1118,7 +1197,7 @@ __global__ void __launch_bounds__(kGrThr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj;
-        av_[tt][jj] = r < nrows ? ld_elem(a, ((c0 + r) * H + h) * (int64_t)DK + c) : 0.f;
+        av_[tt][jj] = r < nrows ? late_f32(araw[tt][jj], c & 1) : 0.f;
       }
     f32x4_t accLk[2], accLq[2], accR[2];
     float bk[8], bkd[8], bkt[8], bqt[8], bktd[8], bqtd[8];
