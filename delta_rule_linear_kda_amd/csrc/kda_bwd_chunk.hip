@@ -75,8 +75,9 @@ __device__ __forceinline__ float late_f32(uint32_t u, bool high) {
 // bijection onto the block, the same for A and B).  The 16x16 fp32 result
 // tile: lane l holds rows 4 (l / 16) + 0..3 of column l % 16.
 //
-// Each fp32 operand is split into bf16 hi + lo (hi = x truncated to bf16,
-// lo = x - hi rounded to bf16) and the block is three bf16 MFMAs
+// Each fp32 operand is split into bf16 hi + lo (hi = x rounded to bf16, lo =
+// x - hi, exact in fp32, rounded to bf16; gfx950's packed fp32 -> bf16
+// conversion does both roundings) and the block is three bf16 MFMAs
 // (v_mfma_f32_16x16x32_bf16), hi*hi + hi*lo + lo*hi with fp32 accumulation:
 // the "bf16x3" method (Henry, Tang & Heinecke, 2019), about 2^-16 relative
 // error per product, with fp32's exponent range (the tile factors reach e^80).
@@ -84,20 +85,20 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 struct F8 {
   bf16x8_t h, l;
 };
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+// Two fp32 values rounded to nearest-even bf16, packed (a in the low half).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 __device__ __forceinline__ F8 split8(const float (&x)[8]) {
-  uint32_t u[8], w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u[j] = __float_as_uint(x[j]);
-    w[j] = __float_as_uint(x[j] - __uint_as_float(u[j] & 0xFFFF0000u));
-  }
   u32x4_t hv, lv;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    hv[p] = __builtin_amdgcn_perm(u[2 * p + 1], u[2 * p], 0x07060302u);  // upper halves
-    const uint32_t l0 = w[2 * p] + 0x7FFFu + ((w[2 * p] >> 16) & 1u);    // round to nearest even
-    const uint32_t l1 = w[2 * p + 1] + 0x7FFFu + ((w[2 * p + 1] >> 16) & 1u);
-    lv[p] = __builtin_amdgcn_perm(l1, l0, 0x07060302u);
+    const uint32_t hw = pk_bf16(x[2 * p], x[2 * p + 1]);
+    hv[p] = hw;
+    lv[p] = pk_bf16(x[2 * p] - __uint_as_float(hw << 16),
+                    x[2 * p + 1] - __uint_as_float(hw & 0xFFFF0000u));
   }
   return {__builtin_bit_cast(bf16x8_t, hv), __builtin_bit_cast(bf16x8_t, lv)};
 }
