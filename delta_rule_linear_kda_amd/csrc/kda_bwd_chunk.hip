@@ -152,6 +152,35 @@ __device__ __forceinline__ void lds44f(const float* p, float (&x)[8]) {
   x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
 }
 
+// Operands kept in LDS already split: a bf16 hi plane and a lo plane of the
+// same shape (u16 elements, row stride ld).  8 consecutive elements of a row
+// as the F8 of a matrix-core operand (16-byte aligned), a split row segment
+// written, and one element written.
+__device__ __forceinline__ F8 ld8h(const uint16_t* hp, const uint16_t* lp, int off) {
+  return {__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(hp + off)),
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lp + off))};
+}
+__device__ __forceinline__ void st8h(uint16_t* hp, uint16_t* lp, int off, const float (&x)[8]) {
+  const F8 f = split8(x);
+  *reinterpret_cast<u32x4_t*>(hp + off) = __builtin_bit_cast(u32x4_t, f.h);
+  *reinterpret_cast<u32x4_t*>(lp + off) = __builtin_bit_cast(u32x4_t, f.l);
+}
+__device__ __forceinline__ void st1h(uint16_t* hp, uint16_t* lp, int off, float x) {
+  const __bf16 h = (__bf16)x;
+  hp[off] = __builtin_bit_cast(uint16_t, h);
+  lp[off] = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
+}
+// 8 elements of a column (rows r0 + 0..7, row stride ld) as an F8.
+__device__ __forceinline__ F8 col8h(const uint16_t* hp, const uint16_t* lp, int off, int ld) {
+  u32x4_t hv, lv;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hv[q] = (uint32_t)hp[off + 2 * q * ld] | ((uint32_t)hp[off + (2 * q + 1) * ld] << 16);
+    lv[q] = (uint32_t)lp[off + 2 * q * ld] | ((uint32_t)lp[off + (2 * q + 1) * ld] << 16);
+  }
+  return {__builtin_bit_cast(bf16x8_t, hv), __builtin_bit_cast(bf16x8_t, lv)};
+}
+
 // Element offset of the 4-row run (rows 16 ct + 4 (l / 16) + 0..3, column
 // 16 w + l % 16) in the tile layout of a [DK][DV] adjoint state: runs ordered
 // by row tile ct, then column tile w, then lane l, so that a wave storing its
@@ -388,6 +417,25 @@ __device__ __forceinline__ void zero_upper(int lane, float* M, float* MT) {
   for (int e = lane; e < 256; e += 64) {
     M[(e / 16) * kL32 + 16 + e % 16] = 0.f;
     if (MT) MT[(16 + e / 16) * kL32 + e % 16] = 0.f;
+  }
+}
+// Element (r, i) of a split [32][32] plane: rows of 32 u16 (64 bytes) whose
+// 16-byte groups are permuted by row (group i / 8 stored at (i / 8) xor
+// ((r / 2) % 4)), so that sixteen rows' reads of one group hit the banks as a
+// padded layout would, in 2 KB per plane.
+__device__ __forceinline__ int sw32(int r, int i) {
+  return r * 32 + ((((i >> 3) ^ (r >> 1)) & 3) << 3) + (i & 7);
+}
+// The upper tile of split [32][32] planes (hi and lo of M and of M^T) zeroed.
+__device__ __forceinline__ void zero_upper_h(int lane, uint16_t* Mh, uint16_t* Ml, uint16_t* MTh,
+                                             uint16_t* MTl) {
+#pragma unroll
+  for (int e = lane; e < 256; e += 64) {
+    const int o = sw32(e / 16, 16 + e % 16), oT = sw32(16 + e / 16, e % 16);
+    Mh[o] = 0;
+    Ml[o] = 0;
+    MTh[oT] = 0;
+    MTl[oT] = 0;
   }
 }
 
@@ -846,21 +894,25 @@ constexpr int kGrThr = 512;
 
 template <int DK, int DV>
 struct GrLayout {
-  static constexpr int LDK = DK + 4, LDV = DV + 4;
+  static constexpr int LDK = DK + 4;
+  static constexpr int LDH = DV + 8;           // row stride of the split [32][DV] planes (u16)
   static constexpr int oB = 0;                 // cumsum b
   static constexpr int oQt = oB + kCB * LDK;   // Qt, later dqh
   static constexpr int oKt = oQt + kCB * LDK;  // Kt, later dkh
   static constexpr int oKh = oKt + kCB * LDK;  // Kh, later the gradient of b
   static constexpr int oM = oKh + kCB * LDK;   // Mkk (without beta)
-  static constexpr int oP = oM + kCB * kL32;   // P, later dP
-  static constexpr int oPT = oP + kCB * kL32;  // P^T, later dP^T
-  static constexpr int oX = oPT + kCB * kL32;  // X, later dMkk
-  static constexpr int oXT = oX + kCB * kL32;  // X^T, later dMkk^T
+  // P, P^T, X, X^T (fp32), later dP, dP^T, dMkk, dMkk^T (split: a hi and a lo
+  // [32][32] u16 plane each, in the same space)
+  static constexpr int oP = oM + kCB * kL32;
+  static constexpr int oPT = oP + kCB * kL32;
+  static constexpr int oX = oPT + kCB * kL32;
+  static constexpr int oXT = oX + kCB * kL32;
   static constexpr int oT = oXT + kCB * kL32;  // 16 x 16 scratch
-  static constexpr int oDO = oT + 256;         // dO [32][DV]
-  static constexpr int oU = oDO + kCB * LDV;   // U
-  static constexpr int oZ = oU + kCB * LDV;    // Z
-  static constexpr int oE = oZ + kCB * LDV;
+  // dO, U, Z [32][DV], split: hi plane then lo plane (kCB * LDH u16 each)
+  static constexpr int oDO = oT + 256;
+  static constexpr int oU = oDO + kCB * LDH;
+  static constexpr int oZ = oU + kCB * LDH;
+  static constexpr int oE = oZ + kCB * LDH;
   static constexpr int oF = oE + 2 * DK;
   static constexpr int oF2 = oF + 2 * DK;
   static constexpr int oD = oF2 + 2 * DK;
@@ -884,7 +936,7 @@ __global__ void __launch_bounds__(kGrThr)
                      float* __restrict__ dv_out, float* __restrict__ da_out,
                      float* __restrict__ db_out, float* __restrict__ dgate_out, int N, int H) {
   using Ly = GrLayout<DK, DV>;
-  constexpr int LDK = Ly::LDK, LDV = Ly::LDV;
+  constexpr int LDK = Ly::LDK, LDH = Ly::LDH;
   constexpr int NKB = DK / 32, NVB = DV / 32;
   extern __shared__ float smem[];
   float* sB = smem + Ly::oB;
@@ -897,9 +949,21 @@ __global__ void __launch_bounds__(kGrThr)
   float* sX = smem + Ly::oX;
   float* sXT = smem + Ly::oXT;
   float* sT = smem + Ly::oT;
-  float* sDO = smem + Ly::oDO;
-  float* sU = smem + Ly::oU;
-  float* sZ = smem + Ly::oZ;
+  uint16_t* sDOh = reinterpret_cast<uint16_t*>(smem + Ly::oDO);
+  uint16_t* sDOl = sDOh + kCB * LDH;
+  uint16_t* sUh = reinterpret_cast<uint16_t*>(smem + Ly::oU);
+  uint16_t* sUl = sUh + kCB * LDH;
+  uint16_t* sZh = reinterpret_cast<uint16_t*>(smem + Ly::oZ);
+  uint16_t* sZl = sZh + kCB * LDH;
+  // the split dP, dP^T, dMkk, dMkk^T of stage E (over P, P^T, X, X^T)
+  uint16_t* sdPh = reinterpret_cast<uint16_t*>(smem + Ly::oP);
+  uint16_t* sdPl = sdPh + kCB * kCB;
+  uint16_t* sdPTh = reinterpret_cast<uint16_t*>(smem + Ly::oPT);
+  uint16_t* sdPTl = sdPTh + kCB * kCB;
+  uint16_t* sdMh = reinterpret_cast<uint16_t*>(smem + Ly::oX);
+  uint16_t* sdMl = sdMh + kCB * kCB;
+  uint16_t* sdMTh = reinterpret_cast<uint16_t*>(smem + Ly::oXT);
+  uint16_t* sdMTl = sdMTh + kCB * kCB;
   float* sE = smem + Ly::oE;
   float* sF = smem + Ly::oF;
   float* sF2 = smem + Ly::oF2;
@@ -967,7 +1031,7 @@ __global__ void __launch_bounds__(kGrThr)
       }
       if (!dvalid) d8[j] = 0.f;
     }
-    st8f(sDO + drow * LDV + dseg * 8, d8);
+    st8h(sDOh, sDOl, drow * LDH + dseg * 8, d8);
   }
   if (gate && dvalid) {
     *reinterpret_cast<float4*>(dgate_out + doff) = make_float4(dg8[0], dg8[1], dg8[2], dg8[3]);
@@ -1044,10 +1108,7 @@ __global__ void __launch_bounds__(kGrThr)
         mma3(dU[tt], av, ef);
       }
     }
-    float dov[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dov[j] = sDO[(8 * g + j) * LDV + jc];
-    const F8 dof = split8(dov);
+    const F8 dof = col8h(sDOh, sDOl, 8 * g * LDH + jc, LDH);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float av[8];
@@ -1107,8 +1168,8 @@ __global__ void __launch_bounds__(kGrThr)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj;
-        sU[r * LDV + jc] = U[tt][jj];
-        sZ[r * LDV + jc] = Z[tt][jj];
+        st1h(sUh, sUl, r * LDH + jc, U[tt][jj]);
+        st1h(sZh, sZl, r * LDH + jc, Z[tt][jj]);
         if (r < nrows) dv_out[((c0 + r) * H + h) * (int64_t)DV + jc] = sBeta[r] * Z[tt][jj];
         const float part = row16_sum(Z[tt][jj] * Vt[tt][jj]);
         if (li == 0) sRed[wave * kCB + r] = part;
@@ -1121,37 +1182,35 @@ __global__ void __launch_bounds__(kGrThr)
     const bool isZ = wave >= 3;
     const int jb = wave % 3;
     const int tr = jb == 0 ? 0 : 1, ti = jb == 2 ? 1 : 0;
-    const float* rows = isZ ? sZ : sDO;
+    const uint16_t* rh = isZ ? sZh : sDOh;
+    const uint16_t* rl = isZ ? sZl : sDOl;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NVB; ++kb) {
-      float av[8], bv[8];
       const int cb = 32 * kb + 8 * g;
-      lds8f(rows + (16 * tr + li) * LDV + cb, av);
-      lds8f(sU + (16 * ti + li) * LDV + cb, bv);
-      mma3(acc, av, bv);
+      mma3(acc, ld8h(rh, rl, (16 * tr + li) * LDH + cb), ld8h(sUh, sUl, (16 * ti + li) * LDH + cb));
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
       if (!isZ) {
         const float dp = i <= r ? acc[jj] : 0.f;
-        sP[r * kL32 + i] = dp;
-        sPT[i * kL32 + r] = dp;
+        st1h(sdPh, sdPl, sw32(r, i), dp);
+        st1h(sdPTh, sdPTl, sw32(i, r), dp);
       } else {
         const float zu = i < r ? acc[jj] : 0.f;
         // dbeta_r -= sum_i (Z U^T)_ri Mkk_ri;  dMkk = -beta_r (Z U^T)
         const float part = row16_sum(zu * sM[r * kL32 + i]);
         if (li == 0) sRed[(8 + jb) * kCB + r] = -part;
         const float dm = -sBeta[r] * zu;
-        sX[r * kL32 + i] = dm;
-        sXT[i * kL32 + r] = dm;
+        st1h(sdMh, sdMl, sw32(r, i), dm);
+        st1h(sdMTh, sdMTl, sw32(i, r), dm);
       }
     }
   } else if (wave == 6) {
-    zero_upper(lane, sP, sPT);
+    zero_upper_h(lane, sdPh, sdPl, sdPTh, sdPTl);
   } else {
-    zero_upper(lane, sX, sXT);
+    zero_upper_h(lane, sdMh, sdMl, sdMTh, sdMTl);
   }
   f32x4_t dQb[2], dKb[2], dKe[2];
   float dge = 0.f;  // dGamma_end of channel jc (partial over this lane group's columns)
@@ -1166,19 +1225,17 @@ __global__ void __launch_bounds__(kGrThr)
       const F8 srf = split8(Sr[kb]), erf = split8(Er[kb]);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int r = 16 * tt + li;
-        float ao[8], az[8], au[8];
-        const float br = -sBeta[r];
-        lds8f(sDO + r * LDV + jb0, ao);
-        lds8f(sZ + r * LDV + jb0, az);
-        lds8f(sU + r * LDV + jb0, au);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) az[j] *= br;
-        mma3(dQb[tt], ao, srf);
-        mma3(dKb[tt], az, srf);
-        mma3(dKe[tt], au, erf);
+        const int o = (16 * tt + li) * LDH + jb0;
+        mma3(dQb[tt], ld8h(sDOh, sDOl, o), srf);
+        mma3(dKb[tt], ld8h(sZh, sZl, o), srf);
+        mma3(dKe[tt], ld8h(sUh, sUl, o), erf);
       }
     }
+    // dKbar = -diag(beta) Z S^T: the row scale after the product
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dKb[tt][jj] *= -sBeta[16 * tt + 4 * g + jj];
     dge += __shfl_xor(dge, 16, 64);
     dge += __shfl_xor(dge, 32, 64);
   }
@@ -1217,16 +1274,11 @@ __global__ void __launch_bounds__(kGrThr)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       accLk[tt] = accLq[tt] = accR[tt] = {0.f, 0.f, 0.f, 0.f};
-      float am[8], ap[8];
-      lds8f(sX + (16 * tt + li) * kL32 + 8 * g, am);
-      lds8f(sP + (16 * tt + li) * kL32 + 8 * g, ap);
-      const F8 fam = split8(am), fap = split8(ap);
-      mma3(accLk[tt], fam, tt == 1 ? fbkd : fbk);
-      mma3(accLq[tt], fap, tt == 1 ? fbkd : fbk);
-      lds8f(sXT + (16 * tt + li) * kL32 + 8 * g, am);
-      lds8f(sPT + (16 * tt + li) * kL32 + 8 * g, ap);
-      mma3(accR[tt], am, tt == 0 ? fbktd : fbkt);
-      mma3(accR[tt], ap, tt == 0 ? fbqtd : fbqt);
+      const int o = sw32(16 * tt + li, 8 * g);
+      mma3(accLk[tt], ld8h(sdMh, sdMl, o), tt == 1 ? fbkd : fbk);
+      mma3(accLq[tt], ld8h(sdPh, sdPl, o), tt == 1 ? fbkd : fbk);
+      mma3(accR[tt], ld8h(sdMTh, sdMTl, o), tt == 0 ? fbktd : fbkt);
+      mma3(accR[tt], ld8h(sdPTh, sdPTl, o), tt == 0 ? fbqtd : fbqt);
     }
     // per element (r = 16 tt + 4 g + jj, channel c)
     float dbv[2][4], dqv[2][4], dkv[2][4];
@@ -1416,7 +1468,9 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
   // The chain's operand records first, alone on the caller's stream (a
   // parallel pass over every chunk); then the serial chain (one workgroup per
   // head) on the second stream while the forward records the states on the
-  // caller's stream and fills the CUs the chain leaves idle.
+  // caller's stream with one workgroup per head as well: split into d_v
+  // slices it would take every compute unit for its whole run (a workgroup
+  // per unit) and hold most of the chain's workgroups back until it ends.
   const int64_t cgrid = (p.total_tokens / kCB + p.num_seqs) * p.num_heads;
   if (cgrid > 0) {
     e = p.dk == 128 ? launch_chainprep<TI, 128>(p, cgrid, stream)
@@ -1437,7 +1491,9 @@ hipError_t launch_t(const BwdChunkArgs& p, const FwdArgs& f, hipStream_t stream)
       e = p.dv == 128 ? launch_chain<TI, 64, 128>(p, s2) : launch_chain<TI, 64, 64>(p, s2);
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ev->join, s2)) != hipSuccess) return e;
-    if ((e = launch_fwd_chunked(f, stream)) != hipSuccess) return e;
+    FwdArgs fw = f;
+    fw.whole_items = true;
+    if ((e = launch_fwd_chunked(fw, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, ev->join, 0)) != hipSuccess) return e;
   }
   if (cgrid == 0) return hipSuccess;

@@ -820,7 +820,8 @@ hipError_t launch_cfg(const FwdArgs& p, int nsl, hipStream_t stream) {
 
 // One workgroup per (sequence, head) when that fills the GPU; with fewer
 // items than half the compute units, d_v = 128 is split into two 64-column
-// slices per item (the key-side work is repeated, the state work halves).
+// slices per item (the key-side work is repeated, the state work halves),
+// unless the caller asks for whole items.
 //
 // The transition form has state rows of d_v + d_k columns: 64-column slices
 // while they fit the GPU in one round, otherwise (d_k = d_v = 128) two
@@ -836,7 +837,7 @@ hipError_t launch_fwd_chunked_bf16(const FwdArgs& p, hipStream_t stream) {
     }
     return launch_cfg<64, 64, true>(p, nsl64, stream);
   }
-  const bool split = p.dv == 128 && 2 * items <= device_cus();
+  const bool split = !p.whole_items && p.dv == 128 && 2 * items <= device_cus();
   if (p.dk == 128) {
     if (p.dv == 128 && !split) return launch_cfg<128, 128, false>(p, 1, stream);
     return launch_cfg<128, 64, false>(p, p.dv / 64, stream);

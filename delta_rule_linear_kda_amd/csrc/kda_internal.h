@@ -40,6 +40,10 @@ struct FwdArgs {
   bool norm = false;
   const float* norm_weight = nullptr;
   float norm_eps = 0.f;
+  // Fused bf16 form: one workgroup per (sequence, head) even when d_v slices
+  // would fill more compute units (the backward's recomputation, which then
+  // leaves the other half of the units to its adjoint chain).
+  bool whole_items = false;
 };
 
 // Two-pass bf16 forward (kda_split_bf16.hip): workspace layout.  Chunks are
