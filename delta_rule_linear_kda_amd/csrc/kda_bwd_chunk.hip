@@ -56,13 +56,30 @@ constexpr int kL32 = kCB + 4;  // padded row stride of [32][32] tiles
 constexpr int kPlanThr = 256;
 
 __device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+// A wave-uniform pointer pinned in scalar registers (and hidden from the
+// optimiser), so that p[lane_offset] with a 32-bit offset is addressed as
+// scalar base + 32-bit vector offset instead of 64-bit vector arithmetic.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> sbase(T* p) {
+  gptr<T> gp = (gptr<T>)p;
+  __asm__ volatile("" : "+s"(gp));
+  return gp;
+}
+// Element i of a scalar-based array, as a T pointer whose byte offset is
+// formed in 32 bits (the access's 32-bit vector offset).
+template <typename T, typename B>
+__device__ __forceinline__ gptr<T> gat(gptr<B> base, uint32_t i) {
+  return (gptr<T>)((__attribute__((address_space(1))) const char*)base + i * (uint32_t)sizeof(B));
+}
 // A bf16 input element loaded ahead of its use as the aligned 32-bit word that
 // holds it (element i of a row-major tensor with even rows), converted where
 // it is used: the empty asm keeps the compiler from moving the conversion (and
 // with it the wait for the load, which also covers every earlier request) up
 // to the load.
-__device__ __forceinline__ uint32_t word_of(const uint16_t* p, int64_t i) {
-  return *reinterpret_cast<const uint32_t*>(p + (i & ~(int64_t)1));
+__device__ __forceinline__ uint32_t word_of(gptr<const uint16_t> p, uint32_t i) {
+  return *gat<const uint32_t>(p, i & ~1u);
 }
 __device__ __forceinline__ float late_f32(uint32_t u, bool high) {
   asm volatile("" : "+v"(u));
@@ -82,6 +99,7 @@ __device__ __forceinline__ float late_f32(uint32_t u, bool high) {
 // the "bf16x3" method (Henry, Tang & Heinecke, 2019), about 2^-16 relative
 // error per product, with fp32's exponent range (the tile factors reach e^80).
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 struct F8 {
   bf16x8_t h, l;
 };
@@ -257,15 +275,17 @@ __device__ __forceinline__ void prep_rows(const uint16_t* __restrict__ q,
                                           int H, int h, PrepRows<DK, NTHR>& in) {
   using PR = PrepRows<DK, NTHR>;
   const int t = threadIdx.x;
+  const int64_t rb = (c0 * H + h) * (int64_t)DK;  // row 0 of the chunk, head h
+  const gptr<const uint16_t> qb = sbase(q + rb), kb = sbase(k + rb), ab = sbase(a + rb);
 #pragma unroll
   for (int it = 0; it < PR::NIT; ++it) {
     const int idx = t + NTHR * it, row = idx / PR::NSEG, seg = idx % PR::NSEG;
     if (idx < kCB * PR::NSEG) {  // uniform per wave: kCB * NSEG is a multiple of 64
       const int rr = row < nrows ? row : nrows - 1;
-      const int64_t off = ((c0 + rr) * H + h) * (int64_t)DK + seg * 8;
-      in.q[it] = *reinterpret_cast<const u32x4_t*>(q + off);
-      in.k[it] = *reinterpret_cast<const u32x4_t*>(k + off);
-      in.a[it] = *reinterpret_cast<const u32x4_t*>(a + off);
+      const uint32_t off = (uint32_t)(rr * H * DK + seg * 8);
+      in.q[it] = *gat<const u32x4_t>(qb, off);
+      in.k[it] = *gat<const u32x4_t>(kb, off);
+      in.a[it] = *gat<const u32x4_t>(ab, off);
     }
   }
 }
@@ -315,23 +335,38 @@ __device__ __forceinline__ void chunk_prep(const PrepRows<DK, NTHR>& in, int nro
     }
   }
   lds_barrier();
-  if (t < DK) {  // cumsum along the chunk, then the factors of channel t
-    const int c = t;
-    float run = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < kCB; ++r) {
-      run += sB[r * LDK + c];
-      sB[r * LDK + c] = run;
+  {  // cumsum along the chunk, then the factors of each channel
+    // TPC neighbouring lanes share a channel, each with RPT consecutive rows:
+    // a prefix over its rows, then over the lanes before it (shuffles).
+    constexpr int TPC = NTHR / DK, RPT = kCB / TPC;
+    static_assert(TPC * DK == NTHR && RPT * TPC == kCB && (TPC & (TPC - 1)) == 0, "scan split");
+    const int c = t / TPC, qq = t % TPC;
+    float x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = sB[(qq * RPT + i) * LDK + c];
+#pragma unroll
+    for (int i = 1; i < RPT; ++i) x[i] += x[i - 1];
+    float incl = x[RPT - 1];  // inclusive over the lanes qq' <= qq
+#pragma unroll
+    for (int d = 1; d < TPC; d <<= 1) {
+      const float y = __shfl_up(incl, d, TPC);
+      if (qq >= d) incl += y;
     }
-    const float p1 = sB[(kTl - 1) * LDK + c], be = run;
-    sE[c] = 1.f;
-    sE[DK + c] = __expf(p1);
-    sF[c] = __expf(p1);            // e_0 = p_1, p_0 = 0
-    sF[DK + c] = __expf(be - p1);  // e_1 = b_end
-    sF2[c] = __expf(be - p1);
-    sF2[DK + c] = 1.f;
-    sD[c] = __expf(p1);
-    sGe[c] = __expf(be);
+    const float before = incl - x[RPT - 1];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) sB[(qq * RPT + i) * LDK + c] = x[i] + before;
+    const float p1 = __shfl(incl, (threadIdx.x & 63 & ~(TPC - 1)) + (kTl / RPT - 1), 64);
+    const float be = __shfl(incl, (threadIdx.x & 63) | (TPC - 1), 64);
+    if (qq == 0) {
+      sE[c] = 1.f;
+      sE[DK + c] = __expf(p1);
+      sF[c] = __expf(p1);            // e_0 = p_1, p_0 = 0
+      sF[DK + c] = __expf(be - p1);  // e_1 = b_end
+      sF2[c] = __expf(be - p1);
+      sF2[DK + c] = 1.f;
+      sD[c] = __expf(p1);
+      sGe[c] = __expf(be);
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -599,8 +634,10 @@ __global__ void __launch_bounds__(kPrepThr, 2)
 
   PrepRows<DK, kPrepThr> rows;
   prep_rows<DK, kPrepThr>(q, k, a, c0, nrows, H, h, rows);
-  const int64_t eb = (c0 + (t < nrows ? t : nrows - 1)) * H + h;  // b of row t
-  const uint32_t bw = word_of(bl, eb);  // every thread: a valid row
+  // b of row t (a valid row), from an even base so that words stay aligned
+  const int64_t b0 = c0 * H + h;
+  const uint32_t eb = (uint32_t)((b0 & 1) + (t < nrows ? t : nrows - 1) * H);
+  const uint32_t bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
   if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
   chunk_prep<DK, kPrepThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
@@ -998,8 +1035,10 @@ __global__ void __launch_bounds__(kGrThr)
   // (requested together: one wait for all of them)
   PrepRows<DK, kGrThr> rows;
   prep_rows<DK, kGrThr>(q, k, a, c0, nrows, H, h, rows);
-  const int64_t eb = (c0 + (t < nrows ? t : nrows - 1)) * H + h;  // b of row t
-  const uint32_t bw = word_of(bl, eb);  // every thread: a valid row
+  // b of row t (a valid row), from an even base so that words stay aligned
+  const int64_t b0 = c0 * H + h;
+  const uint32_t eb = (uint32_t)((b0 & 1) + (t < nrows ? t : nrows - 1) * H);
+  const uint32_t bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
   // dO (with sigma(gate) applied) into LDS and dgate out: one 8-column
   // segment per thread; rows past the end read the last row and are zeroed.
   // Every LDS write comes before the dgate stores, so no later wait for a
@@ -1009,14 +1048,25 @@ __global__ void __launch_bounds__(kGrThr)
   const int drow = t / (DV / 8), dseg = t % (DV / 8);
   const bool dthr = NDO == kGrThr || t < NDO;  // (a branch only when d_v < 128)
   const bool dvalid = dthr && drow < nrows;
-  const int64_t doff =
-      ((c0 + (drow < nrows ? drow : nrows - 1)) * H + h) * (int64_t)DV + dseg * 8;
+  const int64_t rbv = (c0 * H + h) * (int64_t)DV;  // row 0 of the chunk, head h
+  const uint32_t doff = (uint32_t)((drow < nrows ? drow : nrows - 1) * H * DV + dseg * 8);
   float d8[8], g8[8], o8[8];
   if (dthr) {
-    ld8(dy + doff, d8);
+    const gptr<const f32x4_t> dp = gat<const f32x4_t>(sbase(dy + rbv), doff);
+    const f32x4_t d0 = dp[0], d1 = dp[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d8[j] = d0[j], d8[4 + j] = d1[j];
     if (gate) {
-      ld8(gate + doff, g8);
-      ld8(o_raw + doff, o8);
+      const u32x4_t gw = *gat<const u32x4_t>(sbase(gate + rbv), doff);
+      const gptr<const f32x4_t> op = gat<const f32x4_t>(sbase(o_raw + rbv), doff);
+      const f32x4_t o0 = op[0], o1 = op[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g8[2 * j] = __uint_as_float(gw[j] << 16);
+        g8[2 * j + 1] = __uint_as_float(gw[j] & 0xFFFF0000u);
+        o8[j] = o0[j];
+        o8[4 + j] = o1[j];
+      }
     }
   }
   if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
@@ -1034,8 +1084,9 @@ __global__ void __launch_bounds__(kGrThr)
     st8h(sDOh, sDOl, drow * LDH + dseg * 8, d8);
   }
   if (gate && dvalid) {
-    *reinterpret_cast<float4*>(dgate_out + doff) = make_float4(dg8[0], dg8[1], dg8[2], dg8[3]);
-    *reinterpret_cast<float4*>(dgate_out + doff + 4) = make_float4(dg8[4], dg8[5], dg8[6], dg8[7]);
+    const gptr<f32x4_t> gp = gat<f32x4_t>(sbase(dgate_out + rbv), doff);
+    gp[0] = f32x4_t{dg8[0], dg8[1], dg8[2], dg8[3]};
+    gp[1] = f32x4_t{dg8[4], dg8[5], dg8[6], dg8[7]};
   }
   chunk_prep<DK, kGrThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   // The value-side B operands, requested before the key products and the
@@ -1046,23 +1097,34 @@ __global__ void __launch_bounds__(kGrThr)
   // wait instead of one each.
   static_assert(sizeof(TI) == 2, "bf16 inputs");
   uint32_t vraw[2][4];  // bf16 bits
+  const gptr<const float> Sb = sbase(S), Eb = sbase(dSe);
   if (vwave) {
+    const gptr<const uint16_t> vb = sbase(v + rbv);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj, rr = r < nrows ? r : nrows - 1;
-        vraw[tt][jj] = word_of(v, ((c0 + rr) * H + h) * (int64_t)DV + jc);
+        vraw[tt][jj] = word_of(vb, (uint32_t)(rr * H * DV + jc));
       }
+    if (S) {  // (uniform)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Sv[kb][j] = *gat<const float>(Sb, (32 * kb + 8 * g + j) * DV + jc);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Sv[kb][j] = 0.f;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Sv[kb][j] = S ? S[(int64_t)(32 * kb + 8 * g + j) * DV + jc] : 0.f;
       // rows 32 kb + 8 g + 0..7 of column jc: two runs of 4 in the tile layout
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(
-            dSe + dse_tile(2 * kb + g / 2, wave, 16 * (2 * (g % 2) + hf) + li, DV));
+        const f32x4_t v4 = *gat<const f32x4_t>(
+            Eb, (uint32_t)dse_tile(2 * kb + g / 2, wave, 16 * (2 * (g % 2) + hf) + li, DV));
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) Ev[kb][4 * hf + jj] = v4[jj];
       }
@@ -1122,31 +1184,40 @@ __global__ void __launch_bounds__(kGrThr)
   float Sr[NVB][8], Er[NVB][8];
   uint32_t araw[2][4];  // bf16 bits of the decay logits of this lane's elements (rows as vraw, channel jc)
   if (kwave) {
+    const gptr<const uint16_t> ab = sbase(a + (c0 * H + h) * (int64_t)DK);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * tt + 4 * g + jj, rr = r < nrows ? r : nrows - 1;
-        araw[tt][jj] = word_of(a, ((c0 + rr) * H + h) * (int64_t)DK + jc);
+        araw[tt][jj] = word_of(ab, (uint32_t)(rr * H * DK + jc));
       }
+    if (S) {  // (uniform)
 #pragma unroll
-    for (int kb = 0; kb < NVB; ++kb) {
-      const int64_t e = (int64_t)jc * DV + 32 * kb + 8 * g;
-      if (S) {
-        ld8(S + e, Sr[kb]);
-      } else {
+      for (int kb = 0; kb < NVB; ++kb) {
+        const gptr<const f32x4_t> sp = gat<const f32x4_t>(Sb, jc * DV + 32 * kb + 8 * g);
+        const f32x4_t s0 = sp[0], s1 = sp[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Sr[kb][j] = s0[j], Sr[kb][4 + j] = s1[j];
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NVB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) Sr[kb][j] = 0.f;
-      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NVB; ++kb)
       // row jc, columns 32 kb + 8 g + 0..7 (tile layout: one element per run)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        Er[kb][j] = dSe[dse_tile(wave, 2 * kb + g / 2, 16 * (li / 4) + 8 * (g % 2) + j, DV) +
-                        li % 4];
-    }
+        Er[kb][j] = *gat<const float>(
+            Eb, (uint32_t)(dse_tile(wave, 2 * kb + g / 2, 16 * (li / 4) + 8 * (g % 2) + j, DV) +
+                           li % 4));
   }
   if (vwave) {
     f32x4_t U[2], Z[2];
+    const gptr<float> dvp = sbase(dv_out + rbv);
     float bu[8], bz[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1170,7 +1241,7 @@ __global__ void __launch_bounds__(kGrThr)
         const int r = 16 * tt + 4 * g + jj;
         st1h(sUh, sUl, r * LDH + jc, U[tt][jj]);
         st1h(sZh, sZl, r * LDH + jc, Z[tt][jj]);
-        if (r < nrows) dv_out[((c0 + r) * H + h) * (int64_t)DV + jc] = sBeta[r] * Z[tt][jj];
+        if (r < nrows) *gat<float>(dvp, r * H * DV + jc) = sBeta[r] * Z[tt][jj];
         const float part = row16_sum(Z[tt][jj] * Vt[tt][jj]);
         if (li == 0) sRed[wave * kCB + r] = part;
       }
@@ -1307,8 +1378,7 @@ __global__ void __launch_bounds__(kGrThr)
     colsum += __shfl_xor(colsum, 32, 64);
     // b_end = b at row 31 (rows past the end keep b flat): its gradient goes to row 31
     if (g == 3) dbv[1][3] += colsum + dge * sGe[c];
-    // Only this wave reads or writes channel c of these rows in this stage
-    // (sB's reads above are issued before its writes below).
+    // Only this wave reads or writes channel c of these rows in this stage.
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -1316,48 +1386,87 @@ __global__ void __launch_bounds__(kGrThr)
         const int r = 16 * tt + 4 * g + jj;
         sQt[r * LDK + c] = dqv[tt][jj];
         sKt[r * LDK + c] = dkv[tt][jj];
-        sKh[r * LDK + c] = dbv[tt][jj];
-        // dg/da = -5 sigmoid(a) sigmoid(-a) (no cancellation as sigmoid(a) -> 1)
-        sB[r * LDK + c] = kGMin * sigm(av_[tt][jj]) * sigm(-av_[tt][jj]);
+      }
+    // da: the suffix sums of the b-gradient over the chunk (row r: rows >= r)
+    // times dg/da = -5 sigmoid(a) sigmoid(-a) (no cancellation as
+    // sigmoid(a) -> 1).  This lane holds rows 4 g + 0..3 of each tile; the
+    // later rows of its tile are in lane groups g + 1..3.
+    float suf[2][4], later[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      suf[tt][3] = dbv[tt][3];
+#pragma unroll
+      for (int jj = 2; jj >= 0; --jj) suf[tt][jj] = dbv[tt][jj] + suf[tt][jj + 1];
+      const float t1 = __shfl_down(suf[tt][0], 16, 64), t2 = __shfl_down(suf[tt][0], 32, 64),
+                  t3 = __shfl_down(suf[tt][0], 48, 64);
+      later[tt] = (g < 3 ? t1 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t3 : 0.f);
+    }
+    float tile1 = suf[1][0] + __shfl_xor(suf[1][0], 16, 64);  // all of tile 1
+    tile1 += __shfl_xor(tile1, 32, 64);
+    later[0] += tile1;
+    const gptr<float> dap = sbase(da_out + (c0 * H + h) * (int64_t)DK);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * tt + 4 * g + jj;
+        const float dgda = kGMin * sigm(av_[tt][jj]) * sigm(-av_[tt][jj]);
+        if (r < nrows) *gat<float>(dap, r * H * DK + c) = (suf[tt][jj] + later[tt]) * dgda;
       }
   }
   lds_barrier();
 
   // ---- outputs ------------------------------------------------------------
-  // da: suffix sums of the b-gradient along the chunk times dg/da (in sB).
-  if (t < DK) {
-    const int c = t;
-    float run = 0.f;
-    for (int r = kCB - 1; r >= 0; --r) {
-      run += sKh[r * LDK + c];
-      if (r < nrows) da_out[((c0 + r) * H + h) * (int64_t)DK + c] = run * sB[r * LDK + c];
-    }
-  }
   // dq, dk through the L2 norms: 16 lanes per row.
   {
     constexpr int CPL = DK / 16;
     const int r = t / 16, l16 = t % 16;
+    static_assert(CPL == 8 || CPL == 4, "d_k of 128 or 64");
     if (r < nrows) {
-      const int64_t off = ((c0 + r) * H + h) * (int64_t)DK + CPL * l16;
-      float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+      const int64_t rb = (c0 * H + h) * (int64_t)DK;  // row 0 of the chunk, head h
+      const uint32_t off = (uint32_t)(r * H * DK + CPL * l16);
+      float qv[CPL], kv[CPL], dqh[CPL], dkh[CPL], sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+      uint32_t qw[CPL / 2], kw[CPL / 2];
+      if constexpr (CPL == 8) {
+        const u32x4_t a4 = *gat<const u32x4_t>(sbase(q + rb), off);
+        const u32x4_t b4 = *gat<const u32x4_t>(sbase(k + rb), off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qw[i] = a4[i], kw[i] = b4[i];
+      } else {
+        const u32x2_t a2 = *gat<const u32x2_t>(sbase(q + rb), off);
+        const u32x2_t b2 = *gat<const u32x2_t>(sbase(k + rb), off);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) qw[i] = a2[i], kw[i] = b2[i];
+      }
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
-        qv[cc] = ld_elem(q, off + cc);
-        kv[cc] = ld_elem(k, off + cc);
+        qv[cc] = __uint_as_float(cc % 2 ? (qw[cc / 2] & 0xFFFF0000u) : (qw[cc / 2] << 16));
+        kv[cc] = __uint_as_float(cc % 2 ? (kw[cc / 2] & 0xFFFF0000u) : (kw[cc / 2] << 16));
+        dqh[cc] = sQt[r * LDK + CPL * l16 + cc];
+        dkh[cc] = sKt[r * LDK + CPL * l16 + cc];
         sq += qv[cc] * qv[cc];
         sk += kv[cc] * kv[cc];
-        qd += qv[cc] * sQt[r * LDK + CPL * l16 + cc];
-        kd += kv[cc] * sKt[r * LDK + CPL * l16 + cc];
+        qd += qv[cc] * dqh[cc];
+        kd += kv[cc] * dkh[cc];
       }
       sq = group_sum<16>(sq);
       sk = group_sum<16>(sk);
       qd = group_sum<16>(qd);
       kd = group_sum<16>(kd);
       const float rq = rsqrtf(sq + kNormEps), rk = rsqrtf(sk + kNormEps);
+      const gptr<f32x4_t> dqp = gat<f32x4_t>(sbase(dq_out + rb), off);
+      const gptr<f32x4_t> dkp = gat<f32x4_t>(sbase(dk_out + rb), off);
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        dq_out[off + cc] = rq * sQt[r * LDK + CPL * l16 + cc] - rq * rq * rq * qd * qv[cc];
-        dk_out[off + cc] = rk * sKt[r * LDK + CPL * l16 + cc] - rk * rk * rk * kd * kv[cc];
+      for (int c4 = 0; c4 < CPL / 4; ++c4) {
+        f32x4_t oq, ok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 4 * c4 + i;
+          oq[i] = rq * dqh[cc] - rq * rq * rq * qd * qv[cc];
+          ok[i] = rk * dkh[cc] - rk * rk * rk * kd * kv[cc];
+        }
+        dqp[c4] = oq;
+        dkp[c4] = ok;
       }
       if (l16 == 0) {
         float dbeta = 0.f;
@@ -1368,7 +1477,7 @@ __global__ void __launch_bounds__(kGrThr)
           dbeta += sRed[8 * kCB + r];
         }
         const float beta = sBeta[r];
-        db_out[(c0 + r) * H + h] = dbeta * beta * (1.f - beta);
+        *gat<float>(sbase(db_out + (c0 * H + h)), r * H) = dbeta * beta * (1.f - beta);
       }
     }
   }
