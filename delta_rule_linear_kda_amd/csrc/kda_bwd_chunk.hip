@@ -557,9 +557,12 @@ __device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const
 // ---------------------------------------------------------------------------
 template <int DK>
 struct ChainRec {
+  // the chain's operands (it reads the first `chain` floats), then Mkk for the
+  // chunk kernel; `floats` is the record's stride
   static constexpr int oQbT = 0, oKbT = DK * kCB, oKe = 2 * DK * kCB, oPT = 3 * DK * kCB,
-                       oXT = oPT + kCB * kCB, oGe = oXT + kCB * kCB, floats = oGe + DK;
-  static_assert(floats % 4 == 0, "float4 copies");
+                       oXT = oPT + kCB * kCB, oGe = oXT + kCB * kCB, chain = oGe + DK,
+                       oM = chain, floats = oM + kCB * kCB;
+  static_assert(chain % 4 == 0 && floats % 4 == 0, "float4 copies");
 };
 
 template <int DK>
@@ -640,10 +643,11 @@ __global__ void __launch_bounds__(kPrepThr, 2)
   const uint32_t bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
   if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
   chunk_prep<DK, kPrepThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
-  key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, true, sM, sP, sPT);
+  key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, false, sM, sP, sPT);
   if (wave == 6) zero_upper(lane, sP, sPT);
+  if (wave == 7) zero_upper(lane, sM, nullptr);
   lds_barrier();
-  solve_x(wave, lane, g, li, sM, sBeta, true, sX, sXT, sT);
+  solve_x(wave, lane, g, li, sM, sBeta, false, sX, sXT, sT);
   // Qbar^T and (beta Kbar)^T straight into the record, Kend in place
   // (thread: row idx % 32, channels 4 (idx / 32) + 0..3: row reads spread
   // over the LDS banks, record writes coalesced along the rows)
@@ -669,7 +673,7 @@ __global__ void __launch_bounds__(kPrepThr, 2)
     *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
   }
   lds_barrier();
-  // Kend, P^T, X^T, Gamma_end
+  // Kend, P^T, X^T, Gamma_end, Mkk
   for (int i4 = t + R::oKe / 4; i4 < R::floats / 4; i4 += kPrepThr) {
     const int e = 4 * i4;
     const float* src;
@@ -679,8 +683,10 @@ __global__ void __launch_bounds__(kPrepThr, 2)
       src = sPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
     } else if (e < R::oGe) {
       src = sXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
-    } else {
+    } else if (e < R::oM) {
       src = sGe + (e - R::oGe);
+    } else {
+      src = sM + ((e - R::oM) / kCB) * kL32 + (e - R::oM) % kCB;
     }
     *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(src);
   }
@@ -712,16 +718,16 @@ __device__ __forceinline__ void chain_fetch(const float* __restrict__ src,
                                             const TI* __restrict__ gate,
                                             const float* __restrict__ dy, int64_t tok_beg,
                                             int64_t tok_end, int m, int H, int h, int t,
-                                            f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
+                                            f32x4_t (&rv)[(ChainRec<DK>::chain / 4 + 4 * DV - 1) / (4 * DV)],
                                             float (&d8)[8], u32x4_t& g8, bool& have_row) {
   using R = ChainRec<DK>;
   static_assert(sizeof(TI) == 2, "bf16 gate: 8 values in 16 bytes");
   constexpr int NTHR = 4 * DV;
-  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;
+  constexpr int NR4 = (R::chain / 4 + NTHR - 1) / NTHR;
 #pragma unroll
   for (int i = 0; i < NR4; ++i) {
     const int i4 = t + NTHR * i;
-    if (NTHR * (i + 1) <= R::floats / 4 || i4 < R::floats / 4)
+    if (NTHR * (i + 1) <= R::chain / 4 || i4 < R::chain / 4)
       rv[i] = *reinterpret_cast<const f32x4_t*>(src + 4 * i4);
   }
   const int64_t c0 = tok_beg + (int64_t)kCB * m;
@@ -739,18 +745,18 @@ __device__ __forceinline__ void chain_fetch(const float* __restrict__ src,
 
 template <int DK, int DV>
 __device__ __forceinline__ void chain_stash(float* b, int t, bool gated,
-                                            const f32x4_t (&rv)[(ChainRec<DK>::floats / 4 + 4 * DV - 1) / (4 * DV)],
+                                            const f32x4_t (&rv)[(ChainRec<DK>::chain / 4 + 4 * DV - 1) / (4 * DV)],
                                             const float (&d8)[8], const u32x4_t& g8,
                                             bool have_row) {
   using R = ChainRec<DK>;
   using Ly = ChainLayout<DK, DV>;
   constexpr int NTHR = 4 * DV;
-  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;
+  constexpr int NR4 = (R::chain / 4 + NTHR - 1) / NTHR;
   constexpr int LDK = Ly::LDK;
 #pragma unroll
   for (int i = 0; i < NR4; ++i) {
     const int i4 = t + NTHR * i;
-    if (NTHR * (i + 1) <= R::floats / 4 || i4 < R::floats / 4) {
+    if (NTHR * (i + 1) <= R::chain / 4 || i4 < R::chain / 4) {
       const int e = 4 * i4;
       float* d;
       if (e < R::oKbT) {
@@ -788,7 +794,7 @@ __global__ void __launch_bounds__(4 * DV)
   constexpr int NTHR = 4 * DV;  // 64 lanes per 16 columns
   constexpr int LDK = Ly::LDK;
   constexpr int NCT = DK / 16, NKB = DK / 32;
-  constexpr int NR4 = (R::floats / 4 + NTHR - 1) / NTHR;  // record float4 per thread
+  constexpr int NR4 = (R::chain / 4 + NTHR - 1) / NTHR;  // record float4 per thread
   extern __shared__ float smem[];
 
   const int item = blockIdx.x;
@@ -944,9 +950,8 @@ struct GrLayout {
   static constexpr int oPT = oP + kCB * kL32;
   static constexpr int oX = oPT + kCB * kL32;
   static constexpr int oXT = oX + kCB * kL32;
-  static constexpr int oT = oXT + kCB * kL32;  // 16 x 16 scratch
   // dO, U, Z [32][DV], split: hi plane then lo plane (kCB * LDH u16 each)
-  static constexpr int oDO = oT + 256;
+  static constexpr int oDO = oXT + kCB * kL32;
   static constexpr int oU = oDO + kCB * LDH;
   static constexpr int oZ = oU + kCB * LDH;
   static constexpr int oE = oZ + kCB * LDH;
@@ -969,10 +974,12 @@ __global__ void __launch_bounds__(kGrThr)
                      const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cbase,
                      const int32_t* __restrict__ kbase, const float* __restrict__ s_init,
                      const float* __restrict__ ckpt, const float* __restrict__ dse,
-                     float* __restrict__ dq_out, float* __restrict__ dk_out,
-                     float* __restrict__ dv_out, float* __restrict__ da_out,
-                     float* __restrict__ db_out, float* __restrict__ dgate_out, int N, int H) {
+                     const float* __restrict__ crec, float* __restrict__ dq_out,
+                     float* __restrict__ dk_out, float* __restrict__ dv_out,
+                     float* __restrict__ da_out, float* __restrict__ db_out,
+                     float* __restrict__ dgate_out, int N, int H) {
   using Ly = GrLayout<DK, DV>;
+  using R = ChainRec<DK>;
   constexpr int LDK = Ly::LDK, LDH = Ly::LDH;
   constexpr int NKB = DK / 32, NVB = DV / 32;
   extern __shared__ float smem[];
@@ -981,11 +988,9 @@ __global__ void __launch_bounds__(kGrThr)
   float* sKt = smem + Ly::oKt;
   float* sKh = smem + Ly::oKh;
   float* sM = smem + Ly::oM;
-  float* sP = smem + Ly::oP;
   float* sPT = smem + Ly::oPT;
   float* sX = smem + Ly::oX;
   float* sXT = smem + Ly::oXT;
-  float* sT = smem + Ly::oT;
   uint16_t* sDOh = reinterpret_cast<uint16_t*>(smem + Ly::oDO);
   uint16_t* sDOl = sDOh + kCB * LDH;
   uint16_t* sUh = reinterpret_cast<uint16_t*>(smem + Ly::oU);
@@ -1048,6 +1053,12 @@ __global__ void __launch_bounds__(kGrThr)
   const int drow = t / (DV / 8), dseg = t % (DV / 8);
   const bool dthr = NDO == kGrThr || t < NDO;  // (a branch only when d_v < 128)
   const bool dvalid = dthr && drow < nrows;
+  // P^T, X^T and Mkk of the chunk from its record (the preparation kernel's)
+  const gptr<const f32x4_t> rec =
+      (gptr<const f32x4_t>)sbase(crec + ((int64_t)ci * H + h) * (int64_t)R::floats);
+  static_assert(R::oXT == R::oPT + kCB * kCB && 2 * kCB * kCB == 4 * kGrThr, "record split");
+  const f32x4_t rpx = rec[R::oPT / 4 + t];                       // P^T, then X^T
+  const f32x4_t rmk = rec[R::oM / 4 + (t < kCB * kCB / 4 ? t : 0)];  // Mkk
   const int64_t rbv = (c0 * H + h) * (int64_t)DV;  // row 0 of the chunk, head h
   const uint32_t doff = (uint32_t)((drow < nrows ? drow : nrows - 1) * H * DV + dseg * 8);
   float d8[8], g8[8], o8[8];
@@ -1082,6 +1093,17 @@ __global__ void __launch_bounds__(kGrThr)
       if (!dvalid) d8[j] = 0.f;
     }
     st8h(sDOh, sDOl, drow * LDH + dseg * 8, d8);
+  }
+  {  // the record's tiles into LDS: P^T, X^T and X (transposed), Mkk
+    const int e = 4 * t, row = (e % (kCB * kCB)) / kCB, col = e % kCB;
+    if (e < kCB * kCB) {
+      *reinterpret_cast<f32x4_t*>(sPT + row * kL32 + col) = rpx;
+    } else {
+      *reinterpret_cast<f32x4_t*>(sXT + row * kL32 + col) = rpx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sX[(col + j) * kL32 + row] = rpx[j];
+    }
+    if (e < kCB * kCB) *reinterpret_cast<f32x4_t*>(sM + row * kL32 + col) = rmk;
   }
   if (gate && dvalid) {
     const gptr<f32x4_t> gp = gat<f32x4_t>(sbase(dgate_out + rbv), doff);
@@ -1130,15 +1152,10 @@ __global__ void __launch_bounds__(kGrThr)
       }
     }
   }
-  key_products<DK>(wave, kGrThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, false, sM, sP, sPT);
-  if (wave == 6) zero_upper(lane, sP, sPT);
-  if (wave == 7) zero_upper(lane, sM, nullptr);
-  lds_barrier();
 
   // ---- value side, columns of wave w: Vt = V - Kbar S, dU = P^T dO + Kend
-  // dS_end (no X needed: beside wave 0's solve for X), then U = X diag(beta)
-  // Vt, Z = X^T dU, dV = diag(beta) Z, dbeta partial sum_j Z Vt.
-  solve_x(wave, lane, g, li, sM, sBeta, false, sX, sXT, sT);
+  // dS_end, then U = X diag(beta) Vt, Z = X^T dU, dV = diag(beta) Z, dbeta
+  // partial sum_j Z Vt.
   f32x4_t Vt[2], dU[2];
   if (vwave) {
 #pragma unroll
@@ -1178,7 +1195,6 @@ __global__ void __launch_bounds__(kGrThr)
       mma3(dU[tt], av, dof);
     }
   }
-  lds_barrier();  // X
   // The d_k-side B operands of the next stage, requested now: row jc of S and
   // of dS_end, columns 32 kb + 8 g + 0..7.
   float Sr[NVB][8], Er[NVB][8];
@@ -1497,8 +1513,8 @@ hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) 
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGrThr), lds, stream, (const TI*)p.q,
                      (const TI*)p.k, (const TI*)p.v, (const TI*)p.a, (const TI*)p.b,
                      (const TI*)p.gate, p.dy, p.o_raw, p.cu_seqlens, p.cbase, p.kbase,
-                     p.initial_state, p.ckpt, p.dse, p.dq_out, p.dk_out, p.dv_out, p.da_out,
-                     p.db_out, p.dgate_out, p.num_seqs, p.num_heads);
+                     p.initial_state, p.ckpt, p.dse, p.crec, p.dq_out, p.dk_out, p.dv_out,
+                     p.da_out, p.db_out, p.dgate_out, p.num_seqs, p.num_heads);
   return hipGetLastError();
 }
 

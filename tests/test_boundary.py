@@ -403,9 +403,10 @@ def test_bwd_workspace_query():
     # bf16 inputs (chunked form, 32-token chunks): states every 32 tokens, the
     # ungated output, the adjoint state at each chunk's end, the adjoint
     # chain's operand record per (chunk, head) (Qbar^T, (beta Kbar)^T, Kend:
-    # 32 x dk each; P^T, X^T: 32 x 32; Gamma_end: dk), two offset tables
+    # 32 x dk each; P^T, X^T: 32 x 32; Gamma_end: dk; then Mkk: 32 x 32), two
+    # offset tables
     chunks = T // 32 + N
-    rec = 3 * 32 * dk + 2 * 32 * 32 + dk
+    rec = 3 * 32 * dk + 3 * 32 * 32 + dk
     exp = (up((T // 32) * st) + up(th * dv * 4) + up(chunks * st) + up(chunks * H * rec * 4)
            + 2 * up((N + 1) * 4))
     assert kda.bwd_workspace_bytes(N, T, H, dk, dv) == exp
