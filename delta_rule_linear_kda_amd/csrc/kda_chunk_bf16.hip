@@ -175,11 +175,10 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         const int r = 16 * tau + li;
         const int rr = r < nr ? r : nr - 1;
         const uint32_t off = (uint32_t)(rr * H * DK) + 16 * wave + 4 * g;
-        if constexpr (!TRANS)
-          rq[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(qb_ + off);
-        rk[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(kb_ + off);
-        ra[tau] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(ab_ + off);
-        rb[tau] = bb_[(uint32_t)(rr * H)];
+        if constexpr (!TRANS) rq[tau] = *gat<const u32x2_t>(qb_, off);
+        rk[tau] = *gat<const u32x2_t>(kb_, off);
+        ra[tau] = *gat<const u32x2_t>(ab_, off);
+        rb[tau] = *gat<const uint16_t>(bb_, (uint32_t)(rr * H));
       }
     };
     if (nch > 0) {
@@ -499,7 +498,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) S[ct][jj] = sp[st_lane + (16 * ct + jj) * dvt];
+          for (int jj = 0; jj < 4; ++jj) S[ct][jj] = *gat<const float>(sp, st_lane + (16 * ct + jj) * dvt);
       } else {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -524,9 +523,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
         const int r = RPW * sw + 4 * ps + g;
         const int rr = r < nr ? r : nr - 1;
         const uint32_t off = (uint32_t)(rr * H * DK) + CPL * li;
-        if constexpr (!TRANS)
-          nq_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(qb_ + off);
-        nk_[ps] = *reinterpret_cast<const __attribute__((address_space(1))) uvec_t*>(kb_ + off);
+        if constexpr (!TRANS) nq_[ps] = *gat<const uvec_t>(qb_, off);
+        nk_[ps] = *gat<const uvec_t>(kb_, off);
       }
     };
     // v and gate arrive as the aligned 32-bit word holding the lane's bf16
@@ -540,7 +538,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       for (int i = 0; i < 8; ++i) {
         const int r = 16 * (i / 4) + 4 * g + (i % 4);
         const int rr = r < nr ? r : nr - 1;
-        rv[i] = vb_[(uint32_t)(rr * H * dvt + (jcol & ~1)) / 2];
+        rv[i] = *gat<const uint32_t>(vb_, (uint32_t)(rr * H * dvt + (jcol & ~1)) / 2);
       }
     };
     auto load_g = [&](int64_t c0, int g, int jcol) {
@@ -553,7 +551,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
       for (int i = 0; i < 8; ++i) {
         const int r = 16 * (i / 4) + 4 * g + (i % 4);
         const int rr = r < nr ? r : nr - 1;
-        rgr[i] = gb_[(uint32_t)(rr * H * dvt + (jcol & ~1)) / 2];
+        rgr[i] = *gat<const uint32_t>(gb_, (uint32_t)(rr * H * dvt + (jcol & ~1)) / 2);
       }
     };
     // Gated output of chunk c (its O accumulators), stored fp32 through a
@@ -759,7 +757,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * dvt] = S[ct][jj] * isc;
+              for (int jj = 0; jj < 4; ++jj) *gat<float>(sp, st_lane + (16 * ct + jj) * dvt) = S[ct][jj] * isc;
           }
         }
       }
@@ -796,7 +794,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sp[st_lane + (16 * ct + jj) * sdv] = S[ct][jj] * isc;
+        for (int jj = 0; jj < 4; ++jj) *gat<float>(sp, st_lane + (16 * ct + jj) * sdv) = S[ct][jj] * isc;
     }
   }
 }

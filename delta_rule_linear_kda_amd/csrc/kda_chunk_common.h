@@ -181,13 +181,23 @@ __device__ __forceinline__ void split_f16x8(const float (&x)[8], f16x8_t& hi, f1
     lo[j] = (_Float16)(x[j] - (float)hv);
   }
 }
+// bf16 hi + lo parts of 8 values, two at a time through the packed
+// conversion; hi is read back from its packed bits.
 __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  u32x4_t hv, lv;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 hv = (__bf16)x[j];
-    hi[j] = hv;
-    lo[j] = (__bf16)(x[j] - (float)hv);
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t hw = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2_t){x[2 * p], x[2 * p + 1]}, bf16x2_t));
+    hv[p] = hw;
+    const f32x2_t r = {x[2 * p] - __uint_as_float(hw << 16),
+                       x[2 * p + 1] - __uint_as_float(hw & 0xFFFF0000u)};
+    lv[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
   }
+  hi = __builtin_bit_cast(bf16x8_t, hv);
+  lo = __builtin_bit_cast(bf16x8_t, lv);
 }
 
 // 8 consecutive 16-bit values from LDS (16-byte aligned).
@@ -227,6 +237,13 @@ __device__ __forceinline__ gptr<T> sbase(T* p) {
   gptr<T> gp = (gptr<T>)p;
   __asm__ volatile("" : "+s"(gp));
   return gp;
+}
+// Element i of a scalar-based array as a T pointer, the byte offset formed in
+// 32 bits: `base[i]` would scale the zero-extended index in 64-bit vector
+// arithmetic, this is the access's 32-bit vector offset.
+template <typename T, typename B>
+__device__ __forceinline__ gptr<T> gat(gptr<B> base, uint32_t i) {
+  return (gptr<T>)((__attribute__((address_space(1))) const char*)base + i * (uint32_t)sizeof(B));
 }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
