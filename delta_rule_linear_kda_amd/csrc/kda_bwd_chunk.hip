@@ -272,9 +272,8 @@ template <int DK, int NTHR>
 __device__ __forceinline__ void prep_rows(const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k,
                                           const uint16_t* __restrict__ a, int64_t c0, int nrows,
-                                          int H, int h, PrepRows<DK, NTHR>& in) {
+                                          int H, int h, int t, PrepRows<DK, NTHR>& in) {
   using PR = PrepRows<DK, NTHR>;
-  const int t = threadIdx.x;
   const int64_t rb = (c0 * H + h) * (int64_t)DK;  // row 0 of the chunk, head h
   const gptr<const uint16_t> qb = sbase(q + rb), kb = sbase(k + rb), ab = sbase(a + rb);
 #pragma unroll
@@ -298,13 +297,13 @@ __device__ __forceinline__ void unpack8(const u32x4_t& w, bool valid, float (&x)
 }
 
 template <int DK, int NTHR>
-__device__ __forceinline__ void chunk_prep(const PrepRows<DK, NTHR>& in, int nrows, float* sB,
-                                           float* sQt, float* sKt, float* sKh, float* sE,
-                                           float* sF, float* sF2, float* sD, float* sGe) {
+__device__ __forceinline__ void chunk_prep(const PrepRows<DK, NTHR>& in, int nrows, int t,
+                                           float* sB, float* sQt, float* sKt, float* sKh,
+                                           float* sE, float* sF, float* sF2, float* sD,
+                                           float* sGe) {
   constexpr int LDK = DK + 4;
   constexpr int NSEG = DK / 8;
   constexpr int NIT = PrepRows<DK, NTHR>::NIT;
-  const int t = threadIdx.x;
   float qh[NIT][8], kh[NIT][8];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -355,8 +354,8 @@ __device__ __forceinline__ void chunk_prep(const PrepRows<DK, NTHR>& in, int nro
     const float before = incl - x[RPT - 1];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) sB[(qq * RPT + i) * LDK + c] = x[i] + before;
-    const float p1 = __shfl(incl, (threadIdx.x & 63 & ~(TPC - 1)) + (kTl / RPT - 1), 64);
-    const float be = __shfl(incl, (threadIdx.x & 63) | (TPC - 1), 64);
+    const float p1 = __shfl(incl, (t & 63 & ~(TPC - 1)) + (kTl / RPT - 1), 64);
+    const float be = __shfl(incl, (t & 63) | (TPC - 1), 64);
     if (qq == 0) {
       sE[c] = 1.f;
       sE[DK + c] = __expf(p1);
@@ -636,13 +635,13 @@ __global__ void __launch_bounds__(kPrepThr, 2)
   const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
 
   PrepRows<DK, kPrepThr> rows;
-  prep_rows<DK, kPrepThr>(q, k, a, c0, nrows, H, h, rows);
+  prep_rows<DK, kPrepThr>(q, k, a, c0, nrows, H, h, t, rows);
   // b of row t (a valid row), from an even base so that words stay aligned
   const int64_t b0 = c0 * H + h;
   const uint32_t eb = (uint32_t)((b0 & 1) + (t < nrows ? t : nrows - 1) * H);
   const uint32_t bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
   if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
-  chunk_prep<DK, kPrepThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  chunk_prep<DK, kPrepThr>(rows, nrows, t, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   key_products<DK>(wave, kPrepThr / 64, g, li, sQt, sKt, sKh, sD, sBeta, false, sM, sP, sPT);
   if (wave == 6) zero_upper(lane, sP, sPT);
   if (wave == 7) zero_upper(lane, sM, nullptr);
@@ -965,7 +964,77 @@ struct GrLayout {
   static_assert(total * 4 <= 160 * 1024, "LDS budget");
 };
 
-template <typename TI, int DK, int DV>
+// A (chunk, head) item of the chunk kernel: ci = chunk over all sequences,
+// n = its sequence, m = its index there, c0 = its first token, nrows = its
+// tokens (1..32).
+struct BwdItem {
+  int ci, h, n, m, nrows;
+  int64_t c0;
+};
+__device__ __forceinline__ BwdItem bwd_item(int w, int H, int N, const int32_t* cbase,
+                                            const int32_t* cu_seqlens) {
+  BwdItem it;
+  it.ci = w / H;
+  it.h = w % H;
+  int lo = 0, hi = N;  // the sequence n with cbase[n] <= ci < cbase[n + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cbase[mid] <= it.ci) lo = mid; else hi = mid;
+  }
+  it.n = lo;
+  it.m = it.ci - cbase[lo];
+  const int64_t te = cu_seqlens[lo + 1];
+  it.c0 = cu_seqlens[lo] + (int64_t)kCB * it.m;
+  it.nrows = (int)(te - it.c0 < kCB ? te - it.c0 : kCB);
+  return it;
+}
+// An item's prologue inputs, in registers: its q, k, a rows, the b word of
+// row t, dO, gate and o of one 8-column segment, and the record's P^T, X^T
+// (rpx) and Mkk (rmk) pieces.
+template <int DK>
+struct BwdPro {
+  PrepRows<DK, kGrThr> rows;
+  uint32_t bw;
+  f32x4_t d0, d1, o0, o1, rpx, rmk;
+  u32x4_t gw;
+};
+template <int DK, int DV, bool GATED>
+__device__ __forceinline__ void bwd_request(const BwdItem& it, const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ a,
+                                            const uint16_t* __restrict__ bl,
+                                            const float* __restrict__ dy,
+                                            const uint16_t* __restrict__ gate,
+                                            const float* __restrict__ o_raw,
+                                            const float* __restrict__ crec, int H, int t,
+                                            BwdPro<DK>& p) {
+  using R = ChainRec<DK>;
+  prep_rows<DK, kGrThr>(q, k, a, it.c0, it.nrows, H, it.h, t, p.rows);
+  // b of row t (a valid row), from an even base so that words stay aligned
+  const int64_t b0 = it.c0 * H + it.h;
+  const uint32_t eb = (uint32_t)((b0 & 1) + (t < it.nrows ? t : it.nrows - 1) * H);
+  p.bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
+  constexpr int NDO = kCB * (DV / 8);
+  const int drow = t / (DV / 8), dseg = t % (DV / 8);
+  const int64_t rbv = (it.c0 * H + it.h) * (int64_t)DV;
+  const uint32_t doff = (uint32_t)((drow < it.nrows ? drow : it.nrows - 1) * H * DV + dseg * 8);
+  if (NDO == kGrThr || t < NDO) {
+    const gptr<const f32x4_t> dp = gat<const f32x4_t>(sbase(dy + rbv), doff);
+    p.d0 = dp[0];
+    p.d1 = dp[1];
+    if constexpr (GATED) {
+      p.gw = *gat<const u32x4_t>(sbase(gate + rbv), doff);
+      const gptr<const f32x4_t> op = gat<const f32x4_t>(sbase(o_raw + rbv), doff);
+      p.o0 = op[0];
+      p.o1 = op[1];
+    }
+  }
+  const gptr<const float> rec = sbase(crec + ((int64_t)it.ci * H + it.h) * (int64_t)R::floats);
+  p.rpx = *gat<const f32x4_t>(rec, R::oPT + 4 * t);
+  p.rmk = *gat<const f32x4_t>(rec, R::oM + 4 * (t < kCB * kCB / 4 ? t : 0));
+}
+
+template <typename TI, int DK, int DV, bool GATED>
 __global__ void __launch_bounds__(kGrThr)
     bwd_chunk_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                      const TI* __restrict__ v, const TI* __restrict__ a,
@@ -1014,78 +1083,68 @@ __global__ void __launch_bounds__(kGrThr)
   float* sBeta = smem + Ly::oBeta;
   float* sRed = smem + Ly::oRed;
 
-  const int ci = blockIdx.x / H, h = blockIdx.x % H;
-  if (ci >= cbase[N]) return;  // the grid covers an upper bound of the chunk count
-  int lo = 0, hi = N;          // the sequence n with cbase[n] <= ci < cbase[n + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) / 2;
-    if (cbase[mid] <= ci) lo = mid; else hi = mid;
-  }
-  const int n = lo;
-  const int m = ci - cbase[n];
-  const int t = threadIdx.x, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
-  const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
-  const int64_t c0 = tok_beg + (int64_t)kCB * m;
-  const int nrows = (int)(tok_end - c0 < kCB ? tok_end - c0 : kCB);
+  // One workgroup per CU walks the (chunk, head) items w = blockIdx.x +
+  // k gridDim.x.  An item's prologue inputs (its q, k, a, b rows, dO, gate,
+  // o and record tiles, about 77 KB) are requested during the previous item,
+  // after that item's last loads: requested at the start of each item, as
+  // every CU did at once, they made a burst that kept HBM busy while the
+  // compute units waited (about 9K cycles per item).
+  constexpr int NDO = kCB * (DV / 8);
+  static_assert(NDO <= kGrThr, "one dO segment per thread");
+  static_assert(R::oXT == R::oPT + kCB * kCB && 2 * kCB * kCB == 4 * kGrThr, "record split");
+  const int total = cbase[N] * H;
+  int w = blockIdx.x;
+  if (w >= total) return;
+  BwdItem it = bwd_item(w, H, N, cbase, cu_seqlens);
+  BwdPro<DK> pro;
+  bwd_request<DK, DV, GATED>(it, q, k, a, bl, dy, gate, o_raw, crec, H, (int)threadIdx.x, pro);
+  for (;;) {
+  // Lane indices re-derived from an opaque copy each item (keeps the
+  // optimiser from hoisting every lane-dependent address out of the loop and
+  // holding them all in registers).
+  int t_ = threadIdx.x;
+  __asm__ volatile("" : "+v"(t_));
+  const int t = t_, wave = t / 64, lane = t % 64, g = lane / 16, li = lane % 16;
+  // owns a column tile of d_v (of d_k): every wave when there are as many tiles
+  const bool vwave = DV / 16 >= kGrThr / 64 || wave < DV / 16;
+  const bool kwave = DK / 16 >= kGrThr / 64 || wave < DK / 16;
+  const int jc = 16 * wave + li;      // this lane's column (d_v or d_k)
+  const int drow = t / (DV / 8), dseg = t % (DV / 8);
+  const bool dthr = NDO == kGrThr || t < NDO;  // (a branch only when d_v < 128)
+  const int ci = it.ci, h = it.h, n = it.n, m = it.m, nrows = it.nrows;
+  const int64_t c0 = it.c0;
   const int64_t item = (int64_t)n * H + h;
   // start state (null: zero) and dS_end of the chunk, [DK][DV] each
   const float* S = m == 0 ? (s_init ? s_init + item * DK * DV : nullptr)
                           : ckpt + (((int64_t)kbase[n] + m - 1) * H + h) * DK * DV;
   const float* dSe = dse + (((int64_t)cbase[n] + m) * H + h) * DK * DV;
-  const bool vwave = wave < DV / 16;  // owns a column tile of d_v
-  const bool kwave = wave < DK / 16;  // owns a column tile of d_k
-  const int jc = 16 * wave + li;      // this lane's column (d_v or d_k)
-
-  // ---- loads: q, k, a, b, dO, dgate; the chunk preparation ---------------
-  // (requested together: one wait for all of them)
-  PrepRows<DK, kGrThr> rows;
-  prep_rows<DK, kGrThr>(q, k, a, c0, nrows, H, h, rows);
-  // b of row t (a valid row), from an even base so that words stay aligned
   const int64_t b0 = c0 * H + h;
   const uint32_t eb = (uint32_t)((b0 & 1) + (t < nrows ? t : nrows - 1) * H);
-  const uint32_t bw = word_of(sbase(bl + (b0 & ~(int64_t)1)), eb);
-  // dO (with sigma(gate) applied) into LDS and dgate out: one 8-column
-  // segment per thread; rows past the end read the last row and are zeroed.
-  // Every LDS write comes before the dgate stores, so no later wait for a
-  // load of this prologue also waits for those stores.
-  constexpr int NDO = kCB * (DV / 8);
-  static_assert(NDO <= kGrThr, "one dO segment per thread");
-  const int drow = t / (DV / 8), dseg = t % (DV / 8);
-  const bool dthr = NDO == kGrThr || t < NDO;  // (a branch only when d_v < 128)
+  const uint32_t bw = pro.bw;
   const bool dvalid = dthr && drow < nrows;
-  // P^T, X^T and Mkk of the chunk from its record (the preparation kernel's)
-  const gptr<const f32x4_t> rec =
-      (gptr<const f32x4_t>)sbase(crec + ((int64_t)ci * H + h) * (int64_t)R::floats);
-  static_assert(R::oXT == R::oPT + kCB * kCB && 2 * kCB * kCB == 4 * kGrThr, "record split");
-  const f32x4_t rpx = rec[R::oPT / 4 + t];                       // P^T, then X^T
-  const f32x4_t rmk = rec[R::oM / 4 + (t < kCB * kCB / 4 ? t : 0)];  // Mkk
   const int64_t rbv = (c0 * H + h) * (int64_t)DV;  // row 0 of the chunk, head h
   const uint32_t doff = (uint32_t)((drow < nrows ? drow : nrows - 1) * H * DV + dseg * 8);
-  float d8[8], g8[8], o8[8];
+  const f32x4_t rpx = pro.rpx, rmk = pro.rmk;
+  float d8[8] = {}, g8[8] = {}, o8[8] = {};
   if (dthr) {
-    const gptr<const f32x4_t> dp = gat<const f32x4_t>(sbase(dy + rbv), doff);
-    const f32x4_t d0 = dp[0], d1 = dp[1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d8[j] = d0[j], d8[4 + j] = d1[j];
-    if (gate) {
-      const u32x4_t gw = *gat<const u32x4_t>(sbase(gate + rbv), doff);
-      const gptr<const f32x4_t> op = gat<const f32x4_t>(sbase(o_raw + rbv), doff);
-      const f32x4_t o0 = op[0], o1 = op[1];
+    for (int j = 0; j < 4; ++j) d8[j] = pro.d0[j], d8[4 + j] = pro.d1[j];
+    if constexpr (GATED) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        g8[2 * j] = __uint_as_float(gw[j] << 16);
-        g8[2 * j + 1] = __uint_as_float(gw[j] & 0xFFFF0000u);
-        o8[j] = o0[j];
-        o8[4 + j] = o1[j];
+        g8[2 * j] = __uint_as_float(pro.gw[j] << 16);
+        g8[2 * j + 1] = __uint_as_float(pro.gw[j] & 0xFFFF0000u);
+        o8[j] = pro.o0[j];
+        o8[4 + j] = pro.o1[j];
       }
     }
   }
   if (t < kCB) sBeta[t] = t < nrows ? sigm(late_f32(bw, eb & 1)) : 0.f;
-  float dg8[8];
+  float dg8[8] = {};
   if (dthr) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (gate) {
+      if constexpr (GATED) {
         const float sg = sigm(g8[j]);
         dg8[j] = d8[j] * o8[j] * sg * (1.f - sg);
         d8[j] *= sg;
@@ -1105,20 +1164,31 @@ __global__ void __launch_bounds__(kGrThr)
     }
     if (e < kCB * kCB) *reinterpret_cast<f32x4_t*>(sM + row * kL32 + col) = rmk;
   }
-  if (gate && dvalid) {
+  if (GATED && dvalid) {
     const gptr<f32x4_t> gp = gat<f32x4_t>(sbase(dgate_out + rbv), doff);
     gp[0] = f32x4_t{dg8[0], dg8[1], dg8[2], dg8[3]};
     gp[1] = f32x4_t{dg8[4], dg8[5], dg8[6], dg8[7]};
   }
-  chunk_prep<DK, kGrThr>(rows, nrows, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
+  // q, k words of this thread's output row (row t / 16, channels CPL (t % 16)
+  // + 0..CPL-1 with CPL = d_k / 16): kept from the prologue, whose layout is
+  // the same at d_k = 128, else requested before the next item's inputs
+  constexpr int CPL = DK / 16;
+  static_assert(CPL == 8 || CPL == 4, "d_k of 128 or 64");
+  u32x4_t oq4 = {}, ok4 = {};
+  if constexpr (DK == 128) {
+    static_assert(PrepRows<DK, kGrThr>::NIT == 1 && PrepRows<DK, kGrThr>::NSEG == 16, "layout");
+    oq4 = pro.rows.q[0];
+    ok4 = pro.rows.k[0];
+  }
+  chunk_prep<DK, kGrThr>(pro.rows, nrows, t, sB, sQt, sKt, sKh, sE, sF, sF2, sD, sGe);
   // The value-side B operands, requested before the key products and the
   // solve for X: column jc of S and of dS_end, rows 32 kb + 8 g + 0..7.
-  float Sv[NKB][8], Ev[NKB][8];
+  float Sv[NKB][8] = {}, Ev[NKB][8] = {};
   // v of this lane's rows r = 16 tt + 4 g + jj (clamped to the last row of the
   // chunk, masked where used): unconditional, so the eight requests share one
   // wait instead of one each.
   static_assert(sizeof(TI) == 2, "bf16 inputs");
-  uint32_t vraw[2][4];  // bf16 bits
+  uint32_t vraw[2][4] = {};  // bf16 bits
   const gptr<const float> Sb = sbase(S), Eb = sbase(dSe);
   if (vwave) {
     const gptr<const uint16_t> vb = sbase(v + rbv);
@@ -1156,7 +1226,7 @@ __global__ void __launch_bounds__(kGrThr)
   // ---- value side, columns of wave w: Vt = V - Kbar S, dU = P^T dO + Kend
   // dS_end, then U = X diag(beta) Vt, Z = X^T dU, dV = diag(beta) Z, dbeta
   // partial sum_j Z Vt.
-  f32x4_t Vt[2], dU[2];
+  f32x4_t Vt[2] = {}, dU[2] = {};
   if (vwave) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -1197,8 +1267,8 @@ __global__ void __launch_bounds__(kGrThr)
   }
   // The d_k-side B operands of the next stage, requested now: row jc of S and
   // of dS_end, columns 32 kb + 8 g + 0..7.
-  float Sr[NVB][8], Er[NVB][8];
-  uint32_t araw[2][4];  // bf16 bits of the decay logits of this lane's elements (rows as vraw, channel jc)
+  float Sr[NVB][8] = {}, Er[NVB][8] = {};
+  uint32_t araw[2][4] = {};  // bf16 bits of the decay logits of this lane's elements (rows as vraw, channel jc)
   if (kwave) {
     const gptr<const uint16_t> ab = sbase(a + (c0 * H + h) * (int64_t)DK);
 #pragma unroll
@@ -1299,7 +1369,7 @@ __global__ void __launch_bounds__(kGrThr)
   } else {
     zero_upper_h(lane, sdMh, sdMl, sdMTh, sdMTl);
   }
-  f32x4_t dQb[2], dKb[2], dKe[2];
+  f32x4_t dQb[2] = {}, dKb[2] = {}, dKe[2] = {};
   float dge = 0.f;  // dGamma_end of channel jc (partial over this lane group's columns)
   if (kwave) {
 #pragma unroll
@@ -1332,18 +1402,35 @@ __global__ void __launch_bounds__(kGrThr)
   // accLk = dMkk (Kh D), accLq = dP (Kh D) (rows r), accR = dMkk^T (Kt D) +
   // dP^T (Qt D) (rows i); D = exp(p_1 - p_0) between a row in tile 1 and a
   // column in tile 0.
+  // decay logits of this lane's elements, for dg/da (this item's last loads)
+  float av_[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * tt + 4 * g + jj;
+      av_[tt][jj] = kwave && r < nrows ? late_f32(araw[tt][jj], jc & 1) : 0.f;
+    }
+  if constexpr (DK != 128) {
+    const int r = t / 16, rr = r < nrows ? r : nrows - 1;
+    const int64_t rb = (c0 * H + h) * (int64_t)DK;
+    const uint32_t off = (uint32_t)(rr * H * DK + CPL * (t % 16));
+    const u32x2_t a2 = *gat<const u32x2_t>(sbase(q + rb), off);
+    const u32x2_t b2 = *gat<const u32x2_t>(sbase(k + rb), off);
+    oq4 = u32x4_t{a2[0], a2[1], 0u, 0u};
+    ok4 = u32x4_t{b2[0], b2[1], 0u, 0u};
+  }
+  // The next item's prologue inputs, requested after this item's last loads
+  // (the memory counter completes in order); after the last item the same
+  // requests are made for it again, so that every iteration issues the same
+  // memory operations and the compiler's wait counts hold on every path.
+  const int wn = w + gridDim.x;
+  const bool more = wn < total;  // (uniform)
+  const BwdItem nx = more ? bwd_item(wn, H, N, cbase, cu_seqlens) : it;
+  bwd_request<DK, DV, GATED>(nx, q, k, a, bl, dy, gate, o_raw, crec, H, t, pro);
   if (kwave) {
     const int c = jc;
     const float dc = sD[c];
-    // decay logits of this lane's elements, for dg/da
-    float av_[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * tt + 4 * g + jj;
-        av_[tt][jj] = r < nrows ? late_f32(araw[tt][jj], c & 1) : 0.f;
-      }
     f32x4_t accLk[2], accLq[2], accR[2];
     float bk[8], bkd[8], bkt[8], bqt[8], bktd[8], bqtd[8];
 #pragma unroll
@@ -1435,25 +1522,14 @@ __global__ void __launch_bounds__(kGrThr)
   // ---- outputs ------------------------------------------------------------
   // dq, dk through the L2 norms: 16 lanes per row.
   {
-    constexpr int CPL = DK / 16;
     const int r = t / 16, l16 = t % 16;
-    static_assert(CPL == 8 || CPL == 4, "d_k of 128 or 64");
     if (r < nrows) {
       const int64_t rb = (c0 * H + h) * (int64_t)DK;  // row 0 of the chunk, head h
       const uint32_t off = (uint32_t)(r * H * DK + CPL * l16);
       float qv[CPL], kv[CPL], dqh[CPL], dkh[CPL], sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
       uint32_t qw[CPL / 2], kw[CPL / 2];
-      if constexpr (CPL == 8) {
-        const u32x4_t a4 = *gat<const u32x4_t>(sbase(q + rb), off);
-        const u32x4_t b4 = *gat<const u32x4_t>(sbase(k + rb), off);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qw[i] = a4[i], kw[i] = b4[i];
-      } else {
-        const u32x2_t a2 = *gat<const u32x2_t>(sbase(q + rb), off);
-        const u32x2_t b2 = *gat<const u32x2_t>(sbase(k + rb), off);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) qw[i] = a2[i], kw[i] = b2[i];
-      }
+      for (int i = 0; i < CPL / 2; ++i) qw[i] = oq4[i], kw[i] = ok4[i];
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
         qv[cc] = __uint_as_float(cc % 2 ? (qw[cc / 2] & 0xFFFF0000u) : (qw[cc / 2] << 16));
@@ -1497,12 +1573,21 @@ __global__ void __launch_bounds__(kGrThr)
       }
     }
   }
+  if (!more) break;
+  w = wn;
+  it = nx;
+  lds_barrier();  // this item's outputs stage is done with LDS
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the last item's repeated requests
 }
 
 template <typename TI, int DK, int DV>
-hipError_t launch_grad(const BwdChunkArgs& p, int64_t grid, hipStream_t stream) {
+hipError_t launch_grad(const BwdChunkArgs& p, int64_t items, hipStream_t stream) {
   const size_t lds = sizeof(float) * GrLayout<DK, DV>::total;
-  auto kern = bwd_chunk_kernel<TI, DK, DV>;
+  auto kern = p.gate ? bwd_chunk_kernel<TI, DK, DV, true> : bwd_chunk_kernel<TI, DK, DV, false>;
+  // one workgroup per compute unit (139+ KB of LDS each), looping over items
+  const int64_t cus = device_cus();
+  const int64_t grid = items < cus ? items : cus;
   // Dynamic LDS above the default limit: set on every call (the attribute is
   // the device's, and a process may drive several devices or threads).
   {
