@@ -259,6 +259,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           const int r = 16 * tau + li;
           bf16x4_t ktb, qhb, qlb, khh, khl, k1h, k1l;
           f16x4_t qbf;
+          float qt4[4], kt4[4], kh4[4], y4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float x = cum[tau][j];  // log2(e) (b - p) <= 0
@@ -267,25 +268,24 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
             if constexpr (!TRANS) {
               const float qt = qf[tau][j] * er;
               const float qbar = tau ? qt * e0[j] : qt;
-              qhb[j] = (__bf16)qt;
-              qlb[j] = (__bf16)(qt - (float)qhb[j]);
+              qt4[j] = qt;
               qbf[j] = (_Float16)qbar;
             }
             const float kbar = tau ? kt * e0[j] : kt;
             // tile 0's rows: (kh exp(p_1)) exp(b_end - p_1), both factors
             // normal wherever the product is not negligible
             const float kend = tau ? kh * fend[1][j] : (kh * e0[j]) * fend[1][j];
-            ktb[j] = (__bf16)kt;
-            khh[j] = (__bf16)kh;
-            khl[j] = (__bf16)(kh - (float)khh[j]);
+            kt4[j] = kt;
+            kh4[j] = kh;
             kbt[j * LT + 16 * tau] = f16_bits(kbar);
             ket[j * LT + 16 * tau] = f16_bits(kend);
-            if (tau == 0) {  // column operand of the off-diagonal tile: Kh exp(p_1) <= 1
-              const float y = kh * e0[j];
-              k1h[j] = (__bf16)y;
-              k1l[j] = (__bf16)(y - (float)k1h[j]);
-            }
+            // column operand of the off-diagonal tile (tile 0): Kh exp(p_1) <= 1
+            y4[j] = kh * e0[j];
           }
+          if constexpr (!TRANS) split_bf16x4(qt4, qhb, qlb);
+          ktb = pack_bf16x4(kt4);
+          split_bf16x4(kh4, khh, khl);
+          if (tau == 0) split_bf16x4(y4, k1h, k1l);
           *reinterpret_cast<bf16x4_t*>(sKT + r * LB + cb) = ktb;
           *reinterpret_cast<bf16x4_t*>(sKHH + r * LB + cb) = khh;
           *reinterpret_cast<bf16x4_t*>(sKHL + r * LB + cb) = khl;
@@ -345,13 +345,20 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           const float nki = nk[16 * ti + li];
           const float4 nqr = *reinterpret_cast<const float4*>(nq + 16 * tr + 4 * g);
           const float nqv[4] = {nqr.x, nqr.y, nqr.z, nqr.w};
+          float pv[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
-            const float pv = i <= r ? acc[jj] * nqv[jj] * nki : 0.f;
-            const __bf16 hv = (__bf16)pv;
-            ph[r * LT + i] = __builtin_bit_cast(uint16_t, hv);
-            pl[r * LT + i] = bf16_bits(pv - (float)hv);
+            pv[jj] = i <= r ? acc[jj] * nqv[jj] * nki : 0.f;
+          }
+          uint32_t hw[2], lw[2];
+          split_pk_bf16(pv[0], pv[1], hw[0], lw[0]);
+          split_pk_bf16(pv[2], pv[3], hw[1], lw[1]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * tr + 4 * g + jj, i = 16 * ti + li;
+            ph[r * LT + i] = (uint16_t)(hw[jj / 2] >> (16 * (jj % 2)));
+            pl[r * LT + i] = (uint16_t)(lw[jj / 2] >> (16 * (jj % 2)));
           }
           if (job == 0) {  // the upper tile (0, 1) of P is zero
 #pragma unroll

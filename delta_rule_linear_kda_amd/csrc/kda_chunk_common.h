@@ -181,6 +181,29 @@ __device__ __forceinline__ void split_f16x8(const float (&x)[8], f16x8_t& hi, f1
     lo[j] = (_Float16)(x[j] - (float)hv);
   }
 }
+// Two values rounded to nearest-even bf16 in one packed conversion (a in the
+// low half), and the bf16 hi + lo parts of two values from it.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+__device__ __forceinline__ void split_pk_bf16(float a, float b, uint32_t& h, uint32_t& l) {
+  h = pk_bf16(a, b);
+  l = pk_bf16(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xFFFF0000u));
+}
+// 4 values as bf16 (and as bf16 hi + lo), two per packed conversion.
+__device__ __forceinline__ bf16x4_t pack_bf16x4(const float (&x)[4]) {
+  const u32x2_t w = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
+  return __builtin_bit_cast(bf16x4_t, w);
+}
+__device__ __forceinline__ void split_bf16x4(const float (&x)[4], bf16x4_t& hi, bf16x4_t& lo) {
+  uint32_t h0, l0, h1, l1;
+  split_pk_bf16(x[0], x[1], h0, l0);
+  split_pk_bf16(x[2], x[3], h1, l1);
+  hi = __builtin_bit_cast(bf16x4_t, u32x2_t{h0, h1});
+  lo = __builtin_bit_cast(bf16x4_t, u32x2_t{l0, l1});
+}
 // bf16 hi + lo parts of 8 values, two at a time through the packed
 // conversion; hi is read back from its packed bits.
 __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {

@@ -393,29 +393,29 @@ __global__ void __launch_bounds__(64 * (DK / 16))
       for (int tau = 0; tau < 2; ++tau) {
         const int r = 16 * tau + li;
         bf16x4_t ktb, qhb, qlb, khh, khl, k1h, k1l;
+        float qt4[4], kt4[4], kh4[4], y4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float x = cum[tau][j];  // log2(e) (b - p) <= 0
           const float er = exp2f_fast(x), ir = exp2f_fast(-x);
           const float kt = kf[tau][j] * er, kh = kf[tau][j] * ir;
           const float qt = qf[tau][j] * er;
-          qhb[j] = (__bf16)qt;
-          qlb[j] = (__bf16)(qt - (float)qhb[j]);
+          qt4[j] = qt;
           qbr[tau][j] = tau ? qt * e0[j] : qt;
           const float kbar = tau ? kt * e0[j] : kt;
           // tile 0's rows: (kh exp(p_1)) exp(b_end - p_1), both factors
           // normal wherever the product is not negligible
           ker[tau][j] = tau ? kh * fend[1][j] : (kh * e0[j]) * fend[1][j];
-          ktb[j] = (__bf16)kt;
-          khh[j] = (__bf16)kh;
-          khl[j] = (__bf16)(kh - (float)khh[j]);
+          kt4[j] = kt;
+          kh4[j] = kh;
           kbt[j * LT + 16 * tau] = f16_bits(kbar);
-          if (tau == 0) {  // column operand of the off-diagonal tile: Kh exp(p_1) <= 1
-            const float y = kh * e0[j];
-            k1h[j] = (__bf16)y;
-            k1l[j] = (__bf16)(y - (float)k1h[j]);
-          }
+          // column operand of the off-diagonal tile (tile 0): Kh exp(p_1) <= 1
+          y4[j] = kh * e0[j];
         }
+        split_bf16x4(qt4, qhb, qlb);
+        ktb = pack_bf16x4(kt4);
+        split_bf16x4(kh4, khh, khl);
+        if (tau == 0) split_bf16x4(y4, k1h, k1l);
         *reinterpret_cast<bf16x4_t*>(sKT + r * LB + cb) = ktb;
         *reinterpret_cast<bf16x4_t*>(sKHH + r * LB + cb) = khh;
         *reinterpret_cast<bf16x4_t*>(sKHL + r * LB + cb) = khl;
@@ -495,13 +495,13 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         const float4 nki = *reinterpret_cast<const float4*>(rNK + 16 * ti + 4 * g);
         const float nkv[4] = {nki.x, nki.y, nki.z, nki.w};
         bf16x4_t hv, lv;
+        float pv4[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int i = 16 * ti + 4 * g + jj;
-          const float pv = i <= r ? acc[jj] * nqr * nkv[jj] : 0.f;
-          hv[jj] = (__bf16)pv;
-          lv[jj] = (__bf16)(pv - (float)hv[jj]);
+          pv4[jj] = i <= r ? acc[jj] * nqr * nkv[jj] : 0.f;
         }
+        split_bf16x4(pv4, hv, lv);
         // (the upper tile (0, 1) of P and the upper parts of the diagonal
         // tiles beyond the kept columns are zero and not stored)
         if (tri_kept(r, 16 * ti + 4 * g)) {
@@ -601,12 +601,10 @@ __global__ void __launch_bounds__(64 * (DK / 16))
 #pragma unroll
           for (int half = 0; half <= rt; ++half) {  // block X01 is zero and not stored
             bf16x4_t hv, lv;
+            float xv4[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float xv = xx[rt][4 * half + j] * bt[4 * half + j];
-              hv[j] = (__bf16)xv;
-              lv[j] = (__bf16)(xv - (float)hv[j]);
-            }
+            for (int j = 0; j < 4; ++j) xv4[j] = xx[rt][4 * half + j] * bt[4 * half + j];
+            split_bf16x4(xv4, hv, lv);
             if (tri_kept(16 * rt + li, 16 * half + 4 * g)) {
               const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
               st64(R::cXH + off, hv);
