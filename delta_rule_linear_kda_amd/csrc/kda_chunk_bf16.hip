@@ -69,8 +69,12 @@ struct Cfg {
   static constexpr int RPW = kC / NS;        // norm rows per state wave
   static_assert(RPW % 4 == 0, "norm rows");
   // LDS strides (elements)
-  static constexpr int LB = DK + 8;          // 16-bit [32][DK]
-  static constexpr int LT = kC + 8;          // 16-bit [DK][32] and [32][32]
+  // Row strides: 16-byte operand reads from 16 rows (the prep waves' [32][DK]
+  // arrays) hit distinct banks with a stride of 4 (mod 32) dwords, 8-byte
+  // reads (the hand-over arrays and Kbar^T) with 2 (mod 32) dwords.
+  static constexpr int LB = DK + 8;          // 16-bit [32][DK], 16-byte reads
+  static constexpr int RB = DK + 4;          // 16-bit [32][DK], 8-byte reads
+  static constexpr int LT = kC + 4;          // 16-bit [DK][32] and [32][32], 8-byte reads
   static constexpr int LX = kC + 4;          // fp32 [32][32]
   static constexpr int LA = 20;              // fp32 [16][16] scratch
   // byte offsets.  Wave 0's scratch for the inverse first (many accesses).
@@ -84,9 +88,9 @@ struct Cfg {
   static constexpr int dBeta = dGE + DK * 4;                // beta fp32 [32]
   static constexpr int dNQ = dBeta + kC * 4;                // 1/|q| fp32 [32]
   static constexpr int dNK = dNQ + kC * 4;                  // 1/|k| fp32 [32]
-  static constexpr int dQB = dNK + kC * 4;                  // Qbar fp16 [32][LB]
-  static constexpr int dW = dQB + kC * LB * 2;              // -W fp16 [32][LB]
-  static constexpr int dKE = dW + kC * LB * 2;              // Kend^T fp16 [DK][LT]
+  static constexpr int dQB = dNK + kC * 4;                  // Qbar fp16 [32][RB]
+  static constexpr int dW = dQB + kC * RB * 2;              // -W fp16 [32][RB]
+  static constexpr int dKE = dW + kC * RB * 2;              // Kend^T fp16 [DK][LT]
   static constexpr int dSize = dKE + DK * LT * 2;
   static constexpr int oBuf = oA10 + 16 * LA * 4;           // two copies
   // prep-only scratch (written and read within one chunk)
@@ -114,7 +118,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
                           long long ckpt_cap) {
   using L = Cfg<DK, DV>;
   constexpr int NP = L::NP, CPL = L::CPL, RPW = L::RPW;
-  constexpr int LB = L::LB, LT = L::LT, LX = L::LX, LA = L::LA;
+  constexpr int LB = L::LB, RB = L::RB, LT = L::LT, LX = L::LX, LA = L::LA;
   constexpr int NCT = DK / 16, NKB = DK / 32;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
@@ -292,7 +296,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           if constexpr (!TRANS) {
             *reinterpret_cast<bf16x4_t*>(sQH + r * LB + cb) = qhb;
             *reinterpret_cast<bf16x4_t*>(sQL + r * LB + cb) = qlb;
-            *reinterpret_cast<f16x4_t*>(qbp + r * LB + cb) = qbf;
+            *reinterpret_cast<f16x4_t*>(qbp + r * RB + cb) = qbf;
           }
           if (tau == 0) {
             *reinterpret_cast<bf16x4_t*>(sK1H + li * LB + cb) = k1h;
@@ -472,7 +476,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           // acc[jj] = W[16 rt + li][16 wave + 4 g + jj]
           const f16x4_t wv = {(_Float16)(-acc[0]), (_Float16)(-acc[1]), (_Float16)(-acc[2]),
                               (_Float16)(-acc[3])};
-          *reinterpret_cast<f16x4_t*>(wp + (16 * rt + li) * LB + 16 * wave + 4 * g) = wv;
+          *reinterpret_cast<f16x4_t*>(wp + (16 * rt + li) * RB + 16 * wave + 4 * g) = wv;
         }
       }
       lds_barrier();  // B3: W in LDS; scratch free for the next chunk
@@ -679,9 +683,9 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           const f16x8_t sbk = s_f16(kb);
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
-            U[rt] = mma_f16(lds4x2<f16x8_t>(wp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk, U[rt]);
+            U[rt] = mma_f16(lds4x2<f16x8_t>(wp + (16 * rt + li) * RB + 32 * kb + 4 * g), sbk, U[rt]);
             if constexpr (!TRANS)
-              O[rt] = mma_f16(lds4x2<f16x8_t>(qbp + (16 * rt + li) * LB + 32 * kb + 4 * g), sbk,
+              O[rt] = mma_f16(lds4x2<f16x8_t>(qbp + (16 * rt + li) * RB + 32 * kb + 4 * g), sbk,
                               O[rt]);
           }
         }
