@@ -1393,8 +1393,7 @@ __global__ void __launch_bounds__(kGrThr)
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) dKb[tt][jj] *= -sBeta[16 * tt + 4 * g + jj];
-    dge += __shfl_xor(dge, 16, 64);
-    dge += __shfl_xor(dge, 32, 64);
+    dge = rows4_sum(dge);
   }
   lds_barrier();
 
@@ -1477,8 +1476,7 @@ __global__ void __launch_bounds__(kGrThr)
                       kt * accLk[tt][jj] - khv * accR[tt][jj];
       }
     }
-    colsum += __shfl_xor(colsum, 16, 64);
-    colsum += __shfl_xor(colsum, 32, 64);
+    colsum = rows4_sum(colsum);
     // b_end = b at row 31 (rows past the end keep b flat): its gradient goes to row 31
     if (g == 3) dbv[1][3] += colsum + dge * sGe[c];
     // Only this wave reads or writes channel c of these rows in this stage.
@@ -1500,12 +1498,15 @@ __global__ void __launch_bounds__(kGrThr)
       suf[tt][3] = dbv[tt][3];
 #pragma unroll
       for (int jj = 2; jj >= 0; --jj) suf[tt][jj] = dbv[tt][jj] + suf[tt][jj + 1];
-      const float t1 = __shfl_down(suf[tt][0], 16, 64), t2 = __shfl_down(suf[tt][0], 32, 64),
-                  t3 = __shfl_down(suf[tt][0], 48, 64);
-      later[tt] = (g < 3 ? t1 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t3 : 0.f);
+      // the sums of the lane groups after g: the next group's (g even) plus
+      // the upper pair's (g < 2), from the cross-row swaps (rows of 16 lanes)
+      const float x = suf[tt][0];
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      const float pair = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+      later[tt] = (g % 2 == 0 ? __uint_as_float(a[1]) : 0.f) + (g < 2 ? __uint_as_float(b[1]) : 0.f);
     }
-    float tile1 = suf[1][0] + __shfl_xor(suf[1][0], 16, 64);  // all of tile 1
-    tile1 += __shfl_xor(tile1, 32, 64);
+    const float tile1 = rows4_sum(suf[1][0]);  // all of tile 1
     later[0] += tile1;
     const gptr<float> dap = sbase(da_out + (c0 * H + h) * (int64_t)DK);
 #pragma unroll

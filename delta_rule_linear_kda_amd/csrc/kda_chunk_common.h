@@ -112,10 +112,7 @@ __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t
 __device__ __forceinline__ int bexp(float x) { return (int)((__float_as_uint(x) >> 23) & 0xffu); }
 // Largest value over the four lanes (li, li + 16, li + 32, li + 48) that
 // hold one column of a 16x16 accumulator tile.
-__device__ __forceinline__ float col_max4(float m) {
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  return fmaxf(m, __shfl_xor(m, 32, 64));
-}
+__device__ __forceinline__ float col_max4(float m) { return rows4_max(m); }
 // Largest magnitude of this lane's part of a state column.
 template <int N>
 __device__ __forceinline__ float abs_max(const f32x4_t (&S)[N]) {

@@ -105,4 +105,23 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Sum and maximum over the four 16-lane rows of a wave, lane position by lane
+// position (the lanes l, l ^ 16, l ^ 32, l ^ 48), through gfx950's cross-row
+// swaps: v_permlane16_swap(x, x) returns rows (0, 0, 2, 2) and (1, 1, 3, 3),
+// v_permlane32_swap(x, x) the lower and the upper half twice.  Vector ALU
+// only, no LDS traffic; the additions are those of an xor butterfly over
+// 16 and 32, so every lane gets the same bits.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 }  // namespace kda

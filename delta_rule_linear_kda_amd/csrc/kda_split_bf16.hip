@@ -344,10 +344,8 @@ __global__ void __launch_bounds__(64 * (DK / 16))
                   qf[tau][2] * qf[tau][2] + qf[tau][3] * qf[tau][3];
         pk[tau] = kf[tau][0] * kf[tau][0] + kf[tau][1] * kf[tau][1] +
                   kf[tau][2] * kf[tau][2] + kf[tau][3] * kf[tau][3];
-        pq[tau] += __shfl_xor(pq[tau], 16, 64);
-        pk[tau] += __shfl_xor(pk[tau], 16, 64);
-        pq[tau] += __shfl_xor(pq[tau], 32, 64);
-        pk[tau] += __shfl_xor(pk[tau], 32, 64);
+        pq[tau] = rows4_sum(pq[tau]);
+        pk[tau] = rows4_sum(pk[tau]);
       }
       if (g == 0) {
 #pragma unroll
