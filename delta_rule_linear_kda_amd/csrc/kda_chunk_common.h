@@ -85,10 +85,12 @@ __device__ __forceinline__ float quad_bcast(float x, int s) {  // s: compile-tim
   return s == 0 ? quad_bcast_t<0>(x) : s == 1 ? quad_bcast_t<1>(x) : s == 2 ? quad_bcast_t<2>(x)
                                                                             : quad_bcast_t<3>(x);
 }
-// Value of lane 15 of each row of 16 lanes, in every lane of the row.
+// Value of lane 15 of each row of 16 lanes, in every lane of the row: DPP
+// row_newbcast:15 (a vector ALU move; the same lanes as the ds_swizzle
+// broadcast it replaces, without the LDS crossbar).
 __device__ __forceinline__ float row_last16(float x) {
-  // ds_swizzle bit-mask mode: lane = (lane & 0x10) | 0x0f within 32 lanes.
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x01F0));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x15F, 0xf, 0xf, false));
 }
 
 // ---- fp16 range of the state-chain operands ---------------------------------
