@@ -58,7 +58,9 @@ CHUNK = 32                   # chunk length of the bf16 forward kernels
 FWD_KERNELS = ("chunk_prep_bf16_kernel<128>", "chunk_state_bf16_kernel<128, 4, 2, false, true, false>",
                "split_plan_kernel", "b_transpose_kernel")
 FWD_KERNEL = "split forward: " + " + ".join(FWD_KERNELS[:2]) + " (per block of chunks)"
-FWD_SOURCE = os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", "kda_split_bf16.hip")
+# the two-pass forward's kernel source and the headers its kernels include
+FWD_SOURCES = [os.path.join(ROOT, "delta_rule_linear_kda_amd", "csrc", f)
+               for f in ("kda_split_bf16.hip", "kda_chunk_common.h", "kda_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_fwd_bf16_T1048576_H96_d128.traffic.txt")
 COPY_PROBE_BYTES = 2 << 30
 
@@ -423,15 +425,17 @@ def backward(stream, reps: int = 3) -> dict:
             "bwd_over_fwd": bwd_ms / fwd_ms, "workspace_bytes": ws.numel()}
 
 
-def _sha256(path: str) -> str:
-    """sha256 of a C/HIP source's code: comments removed and whitespace
+def _sha256(paths: list) -> str:
+    """sha256 of C/HIP sources' code: comments removed and whitespace
     collapsed, so that editing a comment does not invalidate counters taken
     on unchanged code."""
     import hashlib
     import re
 
-    with open(path) as f:
-        text = f.read()
+    text = ""
+    for path in paths:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
@@ -448,7 +452,7 @@ def read_traffic() -> dict | None:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("kernel_code_sha256") != _sha256(FWD_SOURCE):
+        if kv.get("kernel_code_sha256") != _sha256(FWD_SOURCES):
             return None
         return {"fetch": float(kv["fetch_bytes_per_launch"]),
                 "write": float(kv["write_bytes_per_launch"])}
@@ -510,7 +514,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> str:
     lines += [
         f"fetch_bytes_per_launch: {fb:.0f}",
         f"write_bytes_per_launch: {wb:.0f}",
-        f"kernel_code_sha256: {_sha256(FWD_SOURCE)}",
+        f"kernel_code_sha256: {_sha256(FWD_SOURCES)}",
     ]
     return "\n".join(lines) + "\n"
 
