@@ -152,7 +152,33 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
   const int item = (blk / (8 * nsl)) * 8 + blk % 8;
   const int col0 = ((blk / 8) % nsl) * DV;  // first state / v column of this slice
   if (item >= num_items) return;            // whole workgroup; before any barrier
-  const int n = item / H, h = item % H;
+  const int h = item % H;
+  // Sequences longest first: workgroups start in block order, so the item
+  // ranks go to the sequences in decreasing length (ties by index), which
+  // shortens the tail of a batch of unequal lengths (longest-processing-time
+  // list scheduling).  With more sequences than threads, in index order.
+  int n = item / H;
+  {
+    const int N = num_items / H;
+    if (N > 1 && N <= L::NT) {  // uniform over the workgroup
+      int* sl = reinterpret_cast<int*>(smem);  // lengths [N], then the answer
+      const int t = threadIdx.x;
+      if (t < N) sl[t] = cu_seqlens[t + 1] - cu_seqlens[t];
+      __syncthreads();
+      if (t < N) {
+        const int lt = sl[t];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+          const int lm = sl[m];
+          rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
+        }
+        if (rank == n) sl[L::NT] = t;
+      }
+      __syncthreads();
+      n = sl[L::NT];
+      __syncthreads();  // the LDS is the kernel's own from here on
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
   const int64_t tok_beg = cu_seqlens[n], tok_end = cu_seqlens[n + 1];
   const int nch = (int)((tok_end - tok_beg + kC - 1) / kC);
@@ -488,7 +514,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
     // columns [d_v, d_v + d_k) carry the transition matrix (value rows zero).
     const int sdv = TRANS ? dvt + DK : dvt;
     const bool tslice = TRANS && col0 >= dvt;  // a slice of transition columns
-    const int64_t st_off = (int64_t)item * DK * sdv + col0;
+    const int64_t st_off = ((int64_t)n * H + h) * DK * sdv + col0;
     // First recorded-state slot of this sequence: the slots of the sequences
     // before it come first.
     int64_t ck_off = 0;
