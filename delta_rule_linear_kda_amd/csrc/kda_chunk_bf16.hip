@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
                                bf16hi(ra[tau][1])};
 #pragma unroll
           for (int j = 0; j < 4; ++j)  // g in log2 units: -5 log2(e) sigmoid(a)
-            cum[tau][j] = (kGMin * kLog2e) * rcpf_fast(1.f + exp2f_fast(-kLog2e * av[j]));
+            cum[tau][j] = log2_decay(av[j]);
         }
         float beta[2];
 #pragma unroll
@@ -656,11 +656,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
           float sq = 0.f, sk = 0.f;
 #pragma unroll
           for (int e = 0; e < CPL / 2; ++e) {
-            const float q0 = TRANS ? 0.f : bf16lo(nq_[ps][e]);
-            const float q1 = TRANS ? 0.f : bf16hi(nq_[ps][e]);
-            const float k0 = bf16lo(nk_[ps][e]), k1 = bf16hi(nk_[ps][e]);
-            if constexpr (!TRANS) sq += q0 * q0 + q1 * q1;
-            sk += k0 * k0 + k1 * k1;
+            if constexpr (!TRANS) sq = sq2_bf16(nq_[ps][e], sq);
+            sk = sq2_bf16(nk_[ps][e], sk);
           }
           if constexpr (!TRANS) sq = row_sum16(sq);
           sk = row_sum16(sk);

@@ -38,6 +38,20 @@ __device__ __forceinline__ f32x4_t mma_x3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh,
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcpf_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+// Log-decay in log2 units from the decay logit: g log2(e) = -5 log2(e)
+// sigmoid(a) = 1 / ((1 + e^-a) / (-5 log2(e))), the scale folded into one fma
+// before the reciprocal.
+__device__ __forceinline__ float log2_decay(float a) {
+  constexpr float kInv = 1.f / (kGMin * kLog2e);
+  return rcpf_fast(__builtin_fmaf(exp2f_fast(-kLog2e * a), kInv, kInv));
+}
+// acc + the squares of the two bf16 halves of w (one dot-product instruction;
+// the bf16 products are exact in fp32).
+__device__ __forceinline__ float sq2_bf16(uint32_t w, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2_t;
+  const b2_t x = __builtin_bit_cast(b2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
 
 // Data-parallel primitives within a row of 16 lanes.
 template <int CTRL>

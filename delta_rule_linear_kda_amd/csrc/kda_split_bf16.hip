@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(64 * (DK / 16))
                              bf16hi(ra[tau][1])};
 #pragma unroll
         for (int j = 0; j < 4; ++j)  // g in log2 units: -5 log2(e) sigmoid(a)
-          cum[tau][j] = (kGMin * kLog2e) * rcpf_fast(1.f + exp2f_fast(-kLog2e * av[j]));
+          cum[tau][j] = log2_decay(av[j]);
       }
       float beta[2] = {0.f, 0.f};  // only wave 0 publishes them
       if (wave == 0) {
@@ -340,10 +340,8 @@ __global__ void __launch_bounds__(64 * (DK / 16))
       float pq[2], pk[2];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        pq[tau] = qf[tau][0] * qf[tau][0] + qf[tau][1] * qf[tau][1] +
-                  qf[tau][2] * qf[tau][2] + qf[tau][3] * qf[tau][3];
-        pk[tau] = kf[tau][0] * kf[tau][0] + kf[tau][1] * kf[tau][1] +
-                  kf[tau][2] * kf[tau][2] + kf[tau][3] * kf[tau][3];
+        pq[tau] = sq2_bf16(rq[tau][1], sq2_bf16(rq[tau][0], 0.f));
+        pk[tau] = sq2_bf16(rk[tau][1], sq2_bf16(rk[tau][0], 0.f));
         pq[tau] = rows4_sum(pq[tau]);
         pk[tau] = rows4_sum(pk[tau]);
       }
