@@ -65,8 +65,10 @@ SplitLayout split_layout(int64_t num_seqs, int64_t total_tokens, int64_t num_hea
 // schedule.
 hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t stream,
                                  const SplitLayout* layout = nullptr);
-// Whether the two-pass form runs whole-head state workgroups for this shape
-// (then the head-wise RMSNorm can be applied in its output stage).
+// Whether the two-pass form can run whole-head state workgroups for this
+// shape: with the head-wise RMSNorm (applied in their output stage), and
+// without it where a block's state pass runs beside the next block's record
+// pass.
 bool split_whole_head(int64_t num_seqs, int64_t num_heads, int dv);
 
 // The forward entry point that allocates nothing (kda_fwd_chunked_noalloc)

@@ -39,7 +39,7 @@ def test_version_and_status_strings():
     assert kda.status_str(99) == "unknown kda_status"
 
 
-def _split_bytes(N, T, H, dk, dv):
+def _split_layout(N, T, H, dk, dv):
     """Host mirror of the two-pass forward's workspace: one block of chunk
     records (per 32-token chunk: X diag(beta) and P as bf16 hi/lo, each 32 x
     32 lower block-triangular with lower triangular diagonal blocks, stored
@@ -64,27 +64,41 @@ def _split_bytes(N, T, H, dk, dv):
     blocks = -(-nch_max // bc)
     nbuf = 2 if blocks > 1 else 1
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    return (nbuf * (up(recs * rb) + up((N + 1) * 4)) +
-            (up(N * H * dk * dv * 4) if blocks > 1 else 0) + up(H * T * 2))
+    total = (nbuf * (up(recs * rb) + up((N + 1) * 4)) +
+             (up(N * H * dk * dv * 4) if blocks > 1 else 0) + up(H * T * 2))
+    return total, blocks
 
 
-def _uses_split(N, H, dv, cus=256):
+def _split_bytes(*args):
+    return _split_layout(*args)[0]
+
+
+def _uses_split(N, T, H, dk, dv, cus=256):
     """The two-pass form runs when the fused kernel's workgroups ((sequence,
     head) pairs, two d_v slices each when that fits one round) would leave
-    compute units idle (no GPU here: the library assumes 256)."""
+    compute units idle, and with up to one pair per compute unit at
+    d_k = d_v = 128 when all records fit one block and sequences average at
+    least 1024 tokens (no GPU here: the library assumes 256 units)."""
     items = N * H
     fused = 2 * items if dv == 128 and 2 * items <= cus else items
-    return fused < cus
+    if fused < cus:
+        return True
+    return (dk == 128 and dv == 128 and items <= cus and T >= 1024 * N and
+            _split_layout(N, T, H, dk, dv)[1] == 1)
 
 
 def test_workspace_query():
     for args in [(4, 16384, 32, 128, 128), (1, 1 << 20, 96, 128, 128), (16, 131072, 96, 128, 128),
                  (3, 1000, 2, 64, 128), (1, 0, 4, 128, 64), (5000, 5000, 8, 128, 128),
-                 (2, 4096, 12, 64, 64), (1, 1 << 20, 12, 128, 128)]:
+                 (2, 4096, 12, 64, 64), (1, 1 << 20, 12, 128, 128), (4, 2048, 32, 128, 128),
+                 (4, 16384, 32, 64, 128), (2, 1 << 20, 64, 128, 128)]:
         N, T, H, dk, dv = args
-        exp = _split_bytes(*args) if _uses_split(N, H, dv) else 0
+        exp = _split_bytes(*args) if _uses_split(*args) else 0
         assert kda.fwd_workspace_bytes(*args) == exp, args
-    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == 0        # 256 workgroups: fused
+    # 4 x 4096 tokens x 32 heads: one block of records, then the chain alone
+    assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == _split_bytes(4, 16384, 32, 128, 128)
+    assert kda.fwd_workspace_bytes(4, 2048, 32, 128, 128) == 0      # short sequences: fused
+    assert kda.fwd_workspace_bytes(16, 131072, 96, 128, 128) == 0   # 1536 pairs: fused
     # the 1M-token, 96-head workload runs in blocks of records within about
     # 4 GiB, plus b transposed (2 H T bytes: 192 MiB)
     assert kda.fwd_workspace_bytes(1, 1 << 20, 96, 128, 128) < (4 << 30) + (256 << 20)
@@ -467,7 +481,7 @@ def test_noalloc_rejects_beyond_its_scratch(N, T, H, dk):
     states: 4 N H dk dv bytes) plus 8 chunk records per (sequence, head)
     exceed the 256 MiB array: KDA_ERR_SCRATCH (no GPU touched)."""
     s = good_shape(num_seqs=N, total_tokens=T, num_heads=H, dk=dk)
-    if not _uses_split(N, H, 128):
+    if not _uses_split(N, T, H, dk, 128):
         pytest.skip("fused-kernel shape: no scratch")
     far = {name: BASE + i * (1 << 39) for i, name in enumerate(P) if name != "ws_bytes"}
     assert fwd_noalloc(s, **far) == SCRATCH

@@ -23,9 +23,10 @@ factors reach e^80):
            rounding is ~3e-4 of its scale, which the whole sequence's RMS
            does not reflect)
 Paths: the fused kernel (enough (sequence, head) pairs to fill the device),
-the two-pass form with 64-column state slices (few pairs) and with
-whole-head state workgroups, the two-pass form over several blocks of chunks
-(1 x 60,000 tokens x 96 heads), the fp32 kernel, and decode.
+the two-pass form in one block of records (64-column state slices; few and
+many pairs), the two-pass form over several blocks of chunks with whole-head
+state workgroups (1 x 60,000 tokens x 96 heads), the fp32 kernel, and
+decode.
 """
 import numpy as np
 import pytest
@@ -110,7 +111,7 @@ def apply_case(case, x, lens, dk, seed=5, v_scale=1e3):
 PATHS = {
     "fused": (W1, 32, [128, 100, 77, 128], 128, 128),   # 128 pairs: two slices each fill 256 CUs
     "ct1": (W1, 3, [128, 57, 0, 100], 128, 128),       # 12 pairs: 64-column state slices
-    "ct2": (W1, 12, [128, 100, 77, 128], 128, 128),    # 48 pairs: whole-head state workgroups
+    "many": (W1, 12, [128, 100, 77, 128], 128, 128),   # 48 pairs, one block: 64-column slices
     "fp32": (W0, 2, [64, 50, 0, 64], 64, 64),
     "fp32_d128": (W0, 2, [128, 30], 128, 128),
 }
