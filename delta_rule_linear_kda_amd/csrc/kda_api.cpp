@@ -93,18 +93,20 @@ namespace {
 // bf16 inputs take the two-pass form when the fused kernel's workgroups
 // ((sequence, head) pairs, times two d_v slices when that still fits in one
 // round) would leave compute units of the current device idle.  With up to
-// one pair per compute unit at d_k = d_v = 128 they also take it when every
-// chunk record fits one block and sequences average at least 1024 tokens:
-// the record pass then runs on the whole GPU and the state chain alone in
-// 64-column slices, at about a quarter of the fused kernel's time per chunk
-// (4 x 4096 tokens x 32 heads: 0.53 against 0.62 ms).  Otherwise the fused
-// kernel, which has no record round trip.
+// three pairs per four compute units at d_k = d_v = 128 they also take it
+// when every chunk record fits one block and sequences average at least 1024
+// tokens: the record pass then runs on the whole GPU and the state chain
+// alone, at a quarter (64-column slices) to under half (whole heads) of the
+// fused kernel's time per chunk (4 x 4096 tokens x 32 heads: 0.53-0.56
+// against 0.66 ms; 6 x 4096 x 32: 0.75 against 0.83 ms; at 8 x 4096 x 32
+// the record pass's share tips it: 0.95 against 0.74 ms).  Otherwise the
+// fused kernel, which has no record round trip.
 bool fwd_uses_split(const kda_shape& s) {
   if (s.in_dtype != KDA_BF16 || s.num_seqs <= 0) return false;
   const int64_t items = int64_t(s.num_seqs) * s.num_heads, cus = kda::device_cus();
   const int64_t fused_wgs = s.dv == 128 && 2 * items <= cus ? 2 * items : items;
   if (fused_wgs < cus) return true;
-  return s.dk == 128 && s.dv == 128 && items <= cus &&
+  return s.dk == 128 && s.dv == 128 && 4 * items <= 3 * cus &&
          s.total_tokens >= 1024 * int64_t(s.num_seqs) &&
          kda::split_layout(s.num_seqs, s.total_tokens, s.num_heads, s.dk, s.dv).blocks == 1;
 }

@@ -156,11 +156,12 @@ __global__ void __launch_bounds__(64 * (DK / 16 + DV / 16))
   // Sequences longest first: workgroups start in block order, so the item
   // ranks go to the sequences in decreasing length (ties by index), which
   // shortens the tail of a batch of unequal lengths (longest-processing-time
-  // list scheduling).  With more sequences than threads, in index order.
+  // list scheduling).  With more than 256 sequences (a ranking loop of that
+  // length per workgroup, and tails short against the batch), in index order.
   int n = item / H;
   {
     const int N = num_items / H;
-    if (N > 1 && N <= L::NT) {  // uniform over the workgroup
+    if (N > 1 && N <= 256) {  // uniform over the workgroup
       int* sl = reinterpret_cast<int*>(smem);  // lengths [N], then the answer
       const int t = threadIdx.x;
       if (t < N) sl[t] = cu_seqlens[t + 1] - cu_seqlens[t];

@@ -1335,12 +1335,15 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
   const int H = p.num_heads, N = p.num_seqs;
   // Pass-2 workgroups: one per item with two 16-column tiles per state wave
   // (128 columns) when there are enough items to fill the GPU with both
-  // passes running side by side (blocks overlapped on two streams), or when
-  // the norm is applied in the output stage; otherwise 64-column slices (one
-  // tile per state wave, two workgroups per item), which shorten the chain
-  // where it runs alone (one block, or blocks in sequence).
+  // passes running side by side (blocks overlapped on two streams), when the
+  // norm is applied in the output stage, or when the slices would not fit
+  // one round (a slice workgroup, VGPR-bound, has its CU to itself);
+  // otherwise 64-column slices (one tile per state wave, two workgroups per
+  // item), which shorten the chain where it runs alone (one block, or blocks
+  // in sequence).
   const bool wide =
-      p.norm || (!layout && w.blocks > 1 && split_whole_head(p.num_seqs, p.num_heads, p.dv));
+      p.norm || (split_whole_head(p.num_seqs, p.num_heads, p.dv) &&
+                 ((!layout && w.blocks > 1) || 2 * items > device_cus()));
   const int nsl = wide ? 1 : p.dv / 64;
   const int64_t sgrid = (items + 7) / 8 * 8 * nsl;
   const bool ck = p.ckpt_interval > 0;

@@ -76,14 +76,14 @@ def _split_bytes(*args):
 def _uses_split(N, T, H, dk, dv, cus=256):
     """The two-pass form runs when the fused kernel's workgroups ((sequence,
     head) pairs, two d_v slices each when that fits one round) would leave
-    compute units idle, and with up to one pair per compute unit at
-    d_k = d_v = 128 when all records fit one block and sequences average at
-    least 1024 tokens (no GPU here: the library assumes 256 units)."""
+    compute units idle, and with up to three pairs per four compute units
+    at d_k = d_v = 128 when all records fit one block and sequences average
+    at least 1024 tokens (no GPU here: the library assumes 256 units)."""
     items = N * H
     fused = 2 * items if dv == 128 and 2 * items <= cus else items
     if fused < cus:
         return True
-    return (dk == 128 and dv == 128 and items <= cus and T >= 1024 * N and
+    return (dk == 128 and dv == 128 and 4 * items <= 3 * cus and T >= 1024 * N and
             _split_layout(N, T, H, dk, dv)[1] == 1)
 
 
@@ -91,13 +91,15 @@ def test_workspace_query():
     for args in [(4, 16384, 32, 128, 128), (1, 1 << 20, 96, 128, 128), (16, 131072, 96, 128, 128),
                  (3, 1000, 2, 64, 128), (1, 0, 4, 128, 64), (5000, 5000, 8, 128, 128),
                  (2, 4096, 12, 64, 64), (1, 1 << 20, 12, 128, 128), (4, 2048, 32, 128, 128),
-                 (4, 16384, 32, 64, 128), (2, 1 << 20, 64, 128, 128)]:
+                 (4, 16384, 32, 64, 128), (2, 1 << 20, 64, 128, 128), (6, 24576, 32, 128, 128),
+                 (8, 32768, 32, 128, 128)]:
         N, T, H, dk, dv = args
         exp = _split_bytes(*args) if _uses_split(*args) else 0
         assert kda.fwd_workspace_bytes(*args) == exp, args
     # 4 x 4096 tokens x 32 heads: one block of records, then the chain alone
     assert kda.fwd_workspace_bytes(4, 16384, 32, 128, 128) == _split_bytes(4, 16384, 32, 128, 128)
     assert kda.fwd_workspace_bytes(4, 2048, 32, 128, 128) == 0      # short sequences: fused
+    assert kda.fwd_workspace_bytes(8, 32768, 32, 128, 128) == 0     # 256 pairs: fused
     assert kda.fwd_workspace_bytes(16, 131072, 96, 128, 128) == 0   # 1536 pairs: fused
     # the 1M-token, 96-head workload runs in blocks of records within about
     # 4 GiB, plus b transposed (2 H T bytes: 192 MiB)

@@ -87,16 +87,16 @@ def test_fwd_bf16_dv_slicing(heads):
 @pytest.mark.parametrize("dk", [64, 128])
 def test_fwd_bf16_whole_head_state_pass(dk):
     """Many (sequence, head) items (160) in the two-pass form with one block
-    of records: the state pass runs alone, in 64-column slices (whole-head
-    state workgroups run where blocks overlap: the multi-block and
-    1M-token tests); ragged lengths and an empty sequence, against the
-    oracle."""
+    of records: 320 64-column slices would take two rounds, so each item
+    gets one whole-head state-pass workgroup (two 16-column tiles per state
+    wave); ragged lengths and an empty sequence, against the oracle."""
     w = kc.custom_workload(W1, dk=dk, dv=128, heads=40, s0_std=0.02)
     run_case(w, [300, 17, 0, 129], label=f"bf16 {dk}x128 H=40")
 
 
 def test_fwd_bf16_whole_head_state_pass_no_gate():
-    """Many items in one block without an output gate."""
+    """The whole-head state pass (160 items, one block) without an output
+    gate."""
     w = kc.custom_workload(W1, heads=40, s0_std=0.02)
     run_case(w, [190, 64], gate=False, label="no gate H=40")
 
