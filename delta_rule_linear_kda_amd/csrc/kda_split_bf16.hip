@@ -1387,6 +1387,13 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& p, void* workspace, hipStream_t 
     int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot[bi]);
     if (side && blk >= 2 && (e = hipStreamWaitEvent(stream, side->used[bi], 0)) != hipSuccess)
       return e;
+    // The plan also orders the two passes on the GPU: block b's state pass
+    // and block b + 1's record pass become ready together (both wait for
+    // block b's record pass), and this plan puts a few microseconds between
+    // them, so the state pass's 96 workgroups take their CUs first.  Planned
+    // ahead for every block instead, the record pass won that race, filled
+    // every CU, and each state pass took 3 ms instead of 1.75 (133 against
+    // 80 ms per forward).
     hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_seqlens,
                        N, c_begin, nb, slot);
     if (p.dk == 128)
