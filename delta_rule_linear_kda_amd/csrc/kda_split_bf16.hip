@@ -210,7 +210,6 @@ __global__ void __launch_bounds__(64 * (DK / 16))
                            int c_begin, int bc, int cpw, unsigned char* __restrict__ rec) {
   using R = Rec<DK>;
   constexpr int NP = R::NP, NT = 64 * NP;
-  constexpr int kXbWave = NP >= 8 ? 6 : 0;
   constexpr int LB = R::LB, LT = R::LT, LX = R::LX, LA = R::LA;
   constexpr int NKB = DK / 32;
   constexpr int oAT = 0;                          // A diagonal blocks^T fp32 [2][16][LA]
@@ -594,27 +593,31 @@ __global__ void __launch_bounds__(64 * (DK / 16))
         xx[1][0] = x10[0]; xx[1][1] = x10[1]; xx[1][2] = x10[2]; xx[1][3] = x10[3];
         xx[1][4] = x11.x; xx[1][5] = x11.y; xx[1][6] = x11.z; xx[1][7] = x11.w;
       }
-      // X diag(beta) as bf16 hi + lo (blocks X00, X01 = 0, X10, X11), on a
-      // wave that is idle in the AP stage
-      if (wave == kXbWave) {
-        const float bt[8] = {rBeta[4 * g], rBeta[4 * g + 1], rBeta[4 * g + 2], rBeta[4 * g + 3],
-                             rBeta[16 + 4 * g], rBeta[17 + 4 * g], rBeta[18 + 4 * g],
-                             rBeta[19 + 4 * g]};
+      // X diag(beta) as bf16 hi + lo (blocks X00, X10, X11; X01 = 0 is not
+      // stored): one block each on three waves that are idle in the AP stage
+      // (with fewer than eight waves, all three on the last)
+      auto xb_block = [&](int rt, int half) __attribute__((always_inline)) {
+        const float4 b4 = *reinterpret_cast<const float4*>(rBeta + 16 * half + 4 * g);
+        const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+        bf16x4_t hv, lv;
+        float xv4[4];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int half = 0; half <= rt; ++half) {  // block X01 is zero and not stored
-            bf16x4_t hv, lv;
-            float xv4[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xv4[j] = xx[rt][4 * half + j] * bt[4 * half + j];
-            split_bf16x4(xv4, hv, lv);
-            if (tri_kept(16 * rt + li, 16 * half + 4 * g)) {
-              const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
-              st64(R::cXH + off, hv);
-              st64(R::cXL + off, lv);
-            }
-          }
+        for (int j = 0; j < 4; ++j) xv4[j] = xx[rt][4 * half + j] * bt[j];
+        split_bf16x4(xv4, hv, lv);
+        if (tri_kept(16 * rt + li, 16 * half + 4 * g)) {
+          const int off = 2 * tri_off(16 * rt + li, 16 * half + 4 * g);
+          st64(R::cXH + off, hv);
+          st64(R::cXL + off, lv);
+        }
+      };
+      if constexpr (NP >= 8) {
+        if (wave == 5) xb_block(0, 0);
+        if (wave == 6) xb_block(1, 0);
+        if (wave == 7) xb_block(1, 1);
+      } else if (wave == NP - 1) {
+        xb_block(0, 0);
+        xb_block(1, 0);
+        xb_block(1, 1);
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
