@@ -1,7 +1,8 @@
 """kda_fwd_chunked_noalloc (the forward whose scratch is the library's fixed
 device array) against kda_fwd_chunked (workspace from the caller) through
-the C ABI: two calls in a row, the second on a smaller input, then a shape
-that needs no scratch at all.  Same tolerance as every bf16 comparison here
+the C ABI: two calls in a row, the second on a smaller input, then four
+4096-token sequences (one block of records for the regular call, blocks in
+sequence in the fixed array), then a shape that needs no scratch at all.  Same tolerance as every bf16 comparison here
 (2e-2 of the reference's RMS); where both entry points cut the work into the
 same blocks the results are bitwise equal."""
 import numpy as np
@@ -56,7 +57,11 @@ def test_noalloc_matches_fwd_chunked():
     _check(synth.custom_workload(w3, s0_std=0.02), [60_000], expect_bitwise=False)
     # 2) a smaller input right after: one block on both sides
     _check(synth.custom_workload(w3, heads=12, s0_std=0.02), [700, 0, 301], expect_bitwise=True)
-    # 3) a shape of the fused kernel (no scratch)
+    # 3) four 4096-token sequences x 32 heads: one block of records for the
+    #    regular call, blocks in sequence inside the fixed array
+    _check(synth.custom_workload(synth.WORKLOADS[1], s0_std=0.02), [4096] * 4,
+           expect_bitwise=False)
+    # 4) a shape of the fused kernel (no scratch)
     _check(synth.custom_workload(synth.WORKLOADS[1], s0_std=0.02), [256, 256, 130, 256],
            expect_bitwise=True)
 
