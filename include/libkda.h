@@ -98,15 +98,17 @@ typedef struct kda_shape {
 } kda_shape;
 
 /* Bytes of device workspace kda_fwd_chunked (and kda_fwd_chunked_ckpt) need
- * for `shape` on the current device.  fp32 inputs: 0.  bf16 inputs with
- * fewer (sequence, head) pairs than the device has compute units run in two
- * passes over 32-token chunks (the chunk operands of every chunk first, in
- * parallel; then the state chain over them), and the workspace holds one
- * block of those chunk records: at most about 4 GiB (more only when 8 chunks
- * of every pair need more), plus the state carried between blocks and b
- * transposed to [H, T] (2 H T bytes); with more pairs the single fused
- * kernel runs and the size is 0.  The size
- * depends on the shape and the current device's compute-unit count.
+ * for `shape` on the current device.  fp32 inputs: 0.  bf16 inputs run in
+ * two passes over 32-token chunks (the chunk operands of every chunk first,
+ * in parallel; then the state chain over them) with fewer (sequence, head)
+ * pairs than the device has compute units, and at d_k = d_v = 128 also with
+ * up to three pairs per four compute units when the records of every chunk
+ * fit one block and sequences average at least 1024 tokens; the workspace
+ * then holds one block of those chunk records: at most about 4 GiB (more
+ * only when 8 chunks of every pair need more), the blocks' record offsets,
+ * the state carried between blocks and b transposed to [H, T] (2 H T
+ * bytes).  Otherwise the single fused kernel runs and the size is 0.  The
+ * size depends on the shape and the current device's compute-unit count.
  * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_DTYPE. */
 KDA_API kda_status kda_fwd_workspace_bytes(const kda_shape* shape, size_t* bytes);
 
