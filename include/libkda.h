@@ -105,7 +105,7 @@ typedef struct kda_shape {
  * up to three pairs per four compute units when the records of every chunk
  * fit one block and sequences average at least 1024 tokens; the workspace
  * then holds one block of those chunk records: at most about 4 GiB (more
- * only when 8 chunks of every pair need more), the blocks' record offsets,
+ * only when 8 chunks of every pair need more), the per-sequence record offsets,
  * the state carried between blocks and b transposed to [H, T] (2 H T
  * bytes).  Otherwise the single fused kernel runs and the size is 0.  The
  * size depends on the shape and the current device's compute-unit count.
