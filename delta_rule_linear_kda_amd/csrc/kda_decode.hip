@@ -49,9 +49,20 @@ __global__ void __launch_bounds__(kTPI * kItems)
   const int cg = t % CG, rg = t / CG;
   float* S = state + item * (int64_t)(DK * DV);
 
-  // 1. Issue the state loads first so HBM traffic is in flight while the
-  //    per-token quantities are computed.  Rows rg, rg+RG, ... : the lanes of
-  //    a wave cover 64 / CG consecutive rows.
+  // 1. The token's inputs first, then the state: the memory counter
+  //    completes in order, so the small loads the norms and the correction
+  //    wait for must not sit behind the state's 64 KB.  Every thread issues
+  //    the same loads (channel t % DK; the gate's place taken by v when there
+  //    is no gate), so the waits do not depend on the path.  The state: rows
+  //    rg, rg+RG, ... ; the lanes of a wave cover 64 / CG consecutive rows.
+  const int tc = t % DK;
+  const float qc0 = ld_elem(q, item * DK + tc);
+  const float kc0 = ld_elem(k, item * DK + tc);
+  const float ac0 = ld_elem(a, item * DK + tc);
+  const float braw = ld_elem(b, item);
+  float vj[4], gj[4];
+  ld4(v + item * DV + 4 * cg, vj);
+  ld4((gate ? gate : v) + item * DV + 4 * cg, gj);
   f32x4_t s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
@@ -63,12 +74,7 @@ __global__ void __launch_bounds__(kTPI * kItems)
 
   // 2. Norms and k.q: threads t < DK of each item own key channel c = t.
   const int wave = t / 64;
-  float qc = 0.f, kc = 0.f, ac = 0.f;
-  if (t < DK) {
-    qc = ld_elem(q, item * DK + t);
-    kc = ld_elem(k, item * DK + t);
-    ac = ld_elem(a, item * DK + t);
-  }
+  const float qc = t < DK ? qc0 : 0.f, kc = t < DK ? kc0 : 0.f, ac = ac0;
   float r0 = wave_sum(qc * qc), r1 = wave_sum(kc * kc), r2 = wave_sum(qc * kc);
   if ((t & 63) == 0 && wave < DK / 64) {
     sh_red[part][0][wave] = r0;
@@ -116,17 +122,13 @@ __global__ void __launch_bounds__(kTPI * kItems)
   }
 
   // 4. Correction u and the output for columns 4cg..4cg+3.
-  const float beta = sigmoidf(ld_elem(b, item));
-  float vj[4];
-  ld4(v + item * DV + 4 * cg, vj);
+  const float beta = sigmoidf(braw);
   const float4 u = {beta * (vj[0] - s1.x), beta * (vj[1] - s1.y), beta * (vj[2] - s1.z),
                     beta * (vj[3] - s1.w)};
   if (!valid) return;  // after the last barrier: the idle half stores nothing
   if (rg == 0) {
     float4 y = {s2.x + kq * u.x, s2.y + kq * u.y, s2.z + kq * u.z, s2.w + kq * u.w};
     if (gate) {
-      float gj[4];
-      ld4(gate + item * DV + 4 * cg, gj);
       y.x *= sigmoidf(gj[0]); y.y *= sigmoidf(gj[1]); y.z *= sigmoidf(gj[2]); y.w *= sigmoidf(gj[3]);
     }
     reinterpret_cast<float4*>(o + item * DV)[cg] = y;
