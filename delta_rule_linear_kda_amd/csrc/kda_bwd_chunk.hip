@@ -31,8 +31,10 @@
 // Kernels:
 //   bwd_plan_kernel       per-sequence chunk and recorded-state offsets
 //   bwd_chainprep_kernel  one workgroup per (chunk, head), all in parallel:
-//                         the adjoint chain's chunk-local operands (Qbar^T,
-//                         (beta Kbar)^T, Kend, P^T, X^T, Gamma_end) as a record
+//                         the adjoint chain's chunk-local operands (Qbar^T -
+//                         W P^T and -W with W = (beta Kbar)^T X^T, Kend,
+//                         Gamma_end) as a record, with P^T, X^T and Mkk for
+//                         the chunk kernel
 //   bwd_chain_kernel      the adjoint chain: one workgroup per (sequence,
 //                         head) walks the chunks last to first over the
 //                         records and stores dS_end of every chunk
@@ -542,25 +544,27 @@ __device__ __forceinline__ void solve_x(int wave, int lane, int g, int li, const
 }
 
 // ---------------------------------------------------------------------------
-// The adjoint chain, in two kernels.  Per chunk it needs only chunk-local
-// operands besides dS:
-//   Y = P^T dO + Kend dS,  Z = X^T Y,  dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z,
-// so bwd_chainprep_kernel forms them for every (chunk, head) in parallel and
-// stores them as a chain record, and bwd_chain_kernel walks each head's
-// chunks last to first reading the records (the next chunk's record and dO
-// are fetched while the current chunk is processed).
+// The adjoint chain, in two kernels.  Per chunk,
+//   dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T X^T (P^T dO + Kend dS)
+//       = diag(Gamma_end) dS + Qc dO + Wn (Kend dS),
+// with the chunk-local Wn = -(beta Kbar)^T X^T and Qc = Qbar^T + Wn P^T, so
+// bwd_chainprep_kernel forms Qc, Wn, Kend and Gamma_end for every (chunk,
+// head) in parallel and stores them as a chain record, and bwd_chain_kernel
+// walks each head's chunks last to first reading the records (the next
+// chunk's record and dO are fetched while the current chunk is processed):
+// two dependent products per chunk (Kend dS, then Wn times it).
 // Record, fp32 (the operands read along the chunk's rows transposed, so that
 // every matrix-core operand is a contiguous read):
-//   Qbar^T [DK][32] | (beta Kbar)^T [DK][32] | Kend [32][DK] | P^T [32][32] |
-//   X^T [32][32] | Gamma_end [DK]
+//   Qc [DK][32] | Wn [DK][32] | Kend [32][DK] | Gamma_end [DK] | P^T [32][32] |
+//   X^T [32][32] | Mkk [32][32]
 // ---------------------------------------------------------------------------
 template <int DK>
 struct ChainRec {
-  // the chain's operands (it reads the first `chain` floats), then Mkk for the
-  // chunk kernel; `floats` is the record's stride
-  static constexpr int oQbT = 0, oKbT = DK * kCB, oKe = 2 * DK * kCB, oPT = 3 * DK * kCB,
-                       oXT = oPT + kCB * kCB, oGe = oXT + kCB * kCB, chain = oGe + DK,
-                       oM = chain, floats = oM + kCB * kCB;
+  // the chain's operands (it reads the first `chain` floats), then P^T, X^T
+  // and Mkk for the chunk kernel; `floats` is the record's stride
+  static constexpr int oQc = 0, oWn = DK * kCB, oKe = 2 * DK * kCB, oGe = 3 * DK * kCB,
+                       chain = oGe + DK, oPT = chain, oXT = oPT + kCB * kCB,
+                       oM = oXT + kCB * kCB, floats = oM + kCB * kCB;
   static_assert(chain % 4 == 0 && floats % 4 == 0, "float4 copies");
 };
 
@@ -647,43 +651,69 @@ __global__ void __launch_bounds__(kPrepThr, 2)
   if (wave == 7) zero_upper(lane, sM, nullptr);
   lds_barrier();
   solve_x(wave, lane, g, li, sM, sBeta, false, sX, sXT, sT);
-  // Qbar^T and (beta Kbar)^T straight into the record, Kend in place
-  // (thread: row idx % 32, channels 4 (idx / 32) + 0..3: row reads spread
-  // over the LDS banks, record writes coalesced along the rows)
-  float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
+  // Kend in place
   for (int idx = t; idx < kCB * DK / 4; idx += kPrepThr) {
     const int row = idx % kCB, c = 4 * (idx / kCB), tt = row / kTl;
-    const float br = sBeta[row];
-    const float4 e = *reinterpret_cast<const float4*>(sE + tt * DK + c);
     const float4 f = *reinterpret_cast<const float4*>(sF + tt * DK + c);
     const float4 f2 = *reinterpret_cast<const float4*>(sF2 + tt * DK + c);
-    const float4 qv = *reinterpret_cast<const float4*>(sQt + row * LDK + c);
-    const float4 kv = *reinterpret_cast<const float4*>(sKt + row * LDK + c);
     float4* kh = reinterpret_cast<float4*>(sKh + row * LDK + c);
     const float4 hv = *kh;
-    dst[R::oQbT + (c + 0) * kCB + row] = qv.x * e.x;
-    dst[R::oQbT + (c + 1) * kCB + row] = qv.y * e.y;
-    dst[R::oQbT + (c + 2) * kCB + row] = qv.z * e.z;
-    dst[R::oQbT + (c + 3) * kCB + row] = qv.w * e.w;
-    dst[R::oKbT + (c + 0) * kCB + row] = kv.x * e.x * br;
-    dst[R::oKbT + (c + 1) * kCB + row] = kv.y * e.y * br;
-    dst[R::oKbT + (c + 2) * kCB + row] = kv.z * e.z * br;
-    dst[R::oKbT + (c + 3) * kCB + row] = kv.w * e.w * br;
     *kh = make_float4(hv.x * f.x * f2.x, hv.y * f.y * f2.y, hv.z * f.z * f2.z, hv.w * f.w * f2.w);
   }
-  lds_barrier();
-  // Kend, P^T, X^T, Gamma_end, Mkk
+  lds_barrier();  // X, X^T and Kend
+  float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
+  // Wn and Qc on the fp32 matrix cores (16 x 16 x 4): wave w, key channels
+  // i = 16 w + li.  Wn^T = -X (beta Kbar) leaves lane (li, g) holding Wn[i][u]
+  // at u = 16 rt + 4 g + j, which is the B operand of Qc^T = Qbar + P Wn^T
+  // over the same u order (k step (rt, j) takes u = 16 rt + 4 g + j in lane
+  // group g; the A operand P[r][u] = (P^T)[u][r] is read in that order).
+  if (16 * wave < DK) {
+    const int i = 16 * wave + li;
+    float kb[kCB / 4];  // -(beta Kbar)[s][i] at s = 4 step + g
+#pragma unroll
+    for (int st = 0; st < kCB / 4; ++st) {
+      const int sr = 4 * st + g;
+      kb[st] = -sBeta[sr] * sKt[sr * LDK + i] * sE[(sr / kTl) * DK + i];
+    }
+    f32x4_t wt[2];  // wt[rt][j] = Wn[i][16 rt + 4 g + j]
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      wt[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < kCB / 4; ++st)
+        wt[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[(16 * rt + li) * kL32 + 4 * st + g],
+                                                      kb[st], wt[rt], 0, 0, 0);
+      *reinterpret_cast<f32x4_t*>(dst + R::oWn + i * kCB + 16 * rt + 4 * g) = wt[rt];
+    }
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot) {  // Qc^T rows r = 16 ot + 4 g + j, column i
+      f32x4_t acc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * ot + 4 * g + j;
+        acc[j] = sQt[r * LDK + i] * sE[ot * DK + i];
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sPT[(16 * rt + 4 * g + j) * kL32 + 16 * ot + li],
+                                                     wt[rt][j], acc, 0, 0, 0);
+      *reinterpret_cast<f32x4_t*>(dst + R::oQc + i * kCB + 16 * ot + 4 * g) = acc;
+    }
+  }
+  // Kend, Gamma_end, P^T, X^T, Mkk
   for (int i4 = t + R::oKe / 4; i4 < R::floats / 4; i4 += kPrepThr) {
     const int e = 4 * i4;
     const float* src;
-    if (e < R::oPT) {
+    if (e < R::oGe) {
       src = sKh + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
+    } else if (e < R::oPT) {
+      src = sGe + (e - R::oGe);
     } else if (e < R::oXT) {
       src = sPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
-    } else if (e < R::oGe) {
-      src = sXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
     } else if (e < R::oM) {
-      src = sGe + (e - R::oGe);
+      src = sXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
     } else {
       src = sM + ((e - R::oM) / kCB) * kL32 + (e - R::oM) % kCB;
     }
@@ -700,12 +730,10 @@ __global__ void __launch_bounds__(kPrepThr, 2)
 template <int DK, int DV>
 struct ChainLayout {
   static constexpr int LDK = DK + 4;
-  static constexpr int oQbT = 0;                 // [DK][36]
-  static constexpr int oKbT = oQbT + DK * kL32;  // [DK][36]
-  static constexpr int oKe = oKbT + DK * kL32;   // [32][LDK]
-  static constexpr int oPT = oKe + kCB * LDK;    // [32][36]
-  static constexpr int oXT = oPT + kCB * kL32;   // [32][36]
-  static constexpr int oGe = oXT + kCB * kL32;   // [DK]
+  static constexpr int oQc = 0;                  // [DK][36]
+  static constexpr int oWn = oQc + DK * kL32;    // [DK][36]
+  static constexpr int oKe = oWn + DK * kL32;    // [32][LDK]
+  static constexpr int oGe = oKe + kCB * LDK;    // [DK]
   static constexpr int oDOT = oGe + DK;          // dO^T [DV][36]
   static constexpr int buf = oDOT + DV * kL32;   // floats per buffer
   static constexpr int total = 2 * buf;
@@ -758,16 +786,12 @@ __device__ __forceinline__ void chain_stash(float* b, int t, bool gated,
     if (NTHR * (i + 1) <= R::chain / 4 || i4 < R::chain / 4) {
       const int e = 4 * i4;
       float* d;
-      if (e < R::oKbT) {
-        d = b + Ly::oQbT + (e / kCB) * kL32 + e % kCB;
+      if (e < R::oWn) {
+        d = b + Ly::oQc + (e / kCB) * kL32 + e % kCB;
       } else if (e < R::oKe) {
-        d = b + Ly::oKbT + ((e - R::oKbT) / kCB) * kL32 + (e - R::oKbT) % kCB;
-      } else if (e < R::oPT) {
-        d = b + Ly::oKe + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
-      } else if (e < R::oXT) {
-        d = b + Ly::oPT + ((e - R::oPT) / kCB) * kL32 + (e - R::oPT) % kCB;
+        d = b + Ly::oWn + ((e - R::oWn) / kCB) * kL32 + (e - R::oWn) % kCB;
       } else if (e < R::oGe) {
-        d = b + Ly::oXT + ((e - R::oXT) / kCB) * kL32 + (e - R::oXT) % kCB;
+        d = b + Ly::oKe + ((e - R::oKe) / DK) * LDK + (e - R::oKe) % DK;
       } else {
         d = b + Ly::oGe + (e - R::oGe);
       }
@@ -828,11 +852,9 @@ __global__ void __launch_bounds__(4 * DV)
   }
   for (int m = nch - 1; m >= 0; --m) {
     const float* b = smem + (m & 1) * Ly::buf;
-    const float* sQbT = b + Ly::oQbT;
-    const float* sKbT = b + Ly::oKbT;
+    const float* sQc = b + Ly::oQc;
+    const float* sWn = b + Ly::oWn;
     const float* sKe = b + Ly::oKe;
-    const float* sPT = b + Ly::oPT;
-    const float* sXT = b + Ly::oXT;
     const float* sGe = b + Ly::oGe;
     const float* sDOT = b + Ly::oDOT;
     // dS_end of this chunk, in the tile layout (each wave writes 1 KB runs)
@@ -860,42 +882,25 @@ __global__ void __launch_bounds__(4 * DV)
       for (int j = 0; j < 8; ++j) bv[j] = dS[2 * kb + (j >> 2)][j & 3];
       dSf[kb] = split8(bv);
     }
-    // Y = P^T dO + Kend dS (rows 16 tt + 4 g + jj, column jl)
+    // Y = Kend dS (rows 16 tt + 4 g + jj, column jl)
     f32x4_t Y[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       Y[tt] = {0.f, 0.f, 0.f, 0.f};
       float av[8];
-      lds8f(sPT + (16 * tt + li) * kL32 + 8 * g, av);
-      mma3(Y[tt], av, dOf);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         lds44f(sKe + (16 * tt + li) * LDK + 32 * kb + 4 * g, av);
         mma3(Y[tt], av, dSf[kb]);
       }
     }
-    // Z = X^T Y
-    f32x4_t Z[2];
+    // dS <- diag(Gamma_end) dS + Qc dO + Wn Y
+    F8 yf;
     {
-      float bv[8];
+      float yv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bv[j] = Y[j >> 2][j & 3];
-      const F8 yf = split8(bv);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        Z[tt] = {0.f, 0.f, 0.f, 0.f};
-        float av[8];
-        lds44f(sXT + (16 * tt + li) * kL32 + 4 * g, av);
-        mma3(Z[tt], av, yf);
-      }
-    }
-    // dS <- diag(Gamma_end) dS + Qbar^T dO - (beta Kbar)^T Z
-    F8 zf;
-    {
-      float zv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zv[j] = Z[j >> 2][j & 3];
-      zf = split8(zv);
+      for (int j = 0; j < 8; ++j) yv[j] = Y[j >> 2][j & 3];
+      yf = split8(yv);
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -905,12 +910,10 @@ __global__ void __launch_bounds__(4 * DV)
       acc[2] = ge.z * dS[ct][2]; acc[3] = ge.w * dS[ct][3];
       const int c = 16 * ct + li;
       float av[8];
-      lds8f(sQbT + c * kL32 + 8 * g, av);
+      lds8f(sQc + c * kL32 + 8 * g, av);
       mma3(acc, av, dOf);
-      lds44f(sKbT + c * kL32 + 4 * g, av);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) av[j] = -av[j];
-      mma3(acc, av, zf);
+      lds44f(sWn + c * kL32 + 4 * g, av);
+      mma3(acc, av, yf);
       dS[ct] = acc;
     }
     if (m > 0)
