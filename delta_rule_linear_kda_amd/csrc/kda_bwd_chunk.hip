@@ -662,43 +662,44 @@ __global__ void __launch_bounds__(kPrepThr, 2)
   }
   lds_barrier();  // X, X^T and Kend
   float* dst = crec + (((int64_t)cbase[n] + m) * H + h) * (int64_t)R::floats;
-  // Wn and Qc on the fp32 matrix cores (16 x 16 x 4): wave w, key channels
+  // Wn and Qc on the matrix cores (bf16x3): wave w, key channels
   // i = 16 w + li.  Wn^T = -X (beta Kbar) leaves lane (li, g) holding Wn[i][u]
-  // at u = 16 rt + 4 g + j, which is the B operand of Qc^T = Qbar + P Wn^T
-  // over the same u order (k step (rt, j) takes u = 16 rt + 4 g + j in lane
-  // group g; the A operand P[r][u] = (P^T)[u][r] is read in that order).
+  // at u = kperm(g, j), which is the B operand of Qc^T = Qbar + P Wn^T over
+  // that u order (the A operand P[r][u] = (P^T)[u][r] is read in it).
   if (16 * wave < DK) {
     const int i = 16 * wave + li;
-    float kb[kCB / 4];  // -(beta Kbar)[s][i] at s = 4 step + g
+    float kb[8];  // -(beta Kbar)[s][i] at s = 8 g + 0..7
 #pragma unroll
-    for (int st = 0; st < kCB / 4; ++st) {
-      const int sr = 4 * st + g;
-      kb[st] = -sBeta[sr] * sKt[sr * LDK + i] * sE[(sr / kTl) * DK + i];
+    for (int j = 0; j < 8; ++j) {
+      const int sr = 8 * g + j;
+      kb[j] = -sBeta[sr] * sKt[sr * LDK + i] * sE[(sr / kTl) * DK + i];
     }
+    const F8 kbf = split8(kb);
     f32x4_t wt[2];  // wt[rt][j] = Wn[i][16 rt + 4 g + j]
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       wt[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < kCB / 4; ++st)
-        wt[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[(16 * rt + li) * kL32 + 4 * st + g],
-                                                      kb[st], wt[rt], 0, 0, 0);
+      float av[8];
+      lds8f(sX + (16 * rt + li) * kL32 + 8 * g, av);
+      mma3(wt[rt], av, kbf);
       *reinterpret_cast<f32x4_t*>(dst + R::oWn + i * kCB + 16 * rt + 4 * g) = wt[rt];
+    }
+    F8 wf;
+    {
+      float wv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = wt[j >> 2][j & 3];
+      wf = split8(wv);
     }
 #pragma unroll
     for (int ot = 0; ot < 2; ++ot) {  // Qc^T rows r = 16 ot + 4 g + j, column i
       f32x4_t acc;
+      float av[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * ot + 4 * g + j;
-        acc[j] = sQt[r * LDK + i] * sE[ot * DK + i];
-      }
+      for (int j = 0; j < 4; ++j) acc[j] = sQt[(16 * ot + 4 * g + j) * LDK + i] * sE[ot * DK + i];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sPT[(16 * rt + 4 * g + j) * kL32 + 16 * ot + li],
-                                                     wt[rt][j], acc, 0, 0, 0);
+      for (int j = 0; j < 8; ++j) av[j] = sPT[kperm(g, j) * kL32 + 16 * ot + li];
+      mma3(acc, av, wf);
       *reinterpret_cast<f32x4_t*>(dst + R::oQc + i * kCB + 16 * ot + 4 * g) = acc;
     }
   }
